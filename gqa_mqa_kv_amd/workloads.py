@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for the GQA decode step.
+
+This module only draws and lays out random inputs; it holds none of the
+attention arithmetic.  Both the GPU path's tests/benchmark and the CPU oracle's
+tests take their inputs from here.
+
+Workloads (shapes follow the model table of "Grouped-Query Attention (GQA) and
+Multi-Query Attention (MQA): Mathematical Foundations, Arithmetic Intensity,
+and KV-Cache Scaling Mechanics", section 5, and the example layer of
+"Grouped-Query Attention Shares Keys Without Sharing Every Query"):
+
+==========================  ==  ===  ====  ===  ======================  =====  ======
+name                        B   H_q  H_kv  d    cached tokens           L      dtype
+==========================  ==  ===  ====  ===  ======================  =====  ======
+tiny-gqa-fp32               1   8    2     64   128                     1      fp32
+llama3-8b-layer             16  32   8     128  4096                    1      bf16
+llama-70b-ragged-layer      32  64   8     128  U[1024, 16384]          1      bf16
+grouping-sweep-mha          8   32   32    128  32768                   1      bf16
+grouping-sweep-gqa          8   32   8     128  32768                   1      bf16
+grouping-sweep-mqa          8   32   1     128  32768                   1      bf16
+llama3-8b-32-layer-stack    64  32   8     128  U[4096, 32768]          32     bf16
+==========================  ==  ===  ====  ===  ======================  =====  ======
+
+Values are N(0, 1) drawn in float32 and rounded to nearest-even into the
+storage dtype.  Draw order: sequence lengths, then q, then K, then V.  Ragged
+lengths are integers uniform on the closed interval.  The three grouping-sweep
+runs share one set of queries (seed 1004); their caches use seed 1004 + H_kv.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    seq_lo: int          # inclusive lower bound on cached tokens
+    seq_hi: int          # inclusive upper bound (== seq_lo for uniform lengths)
+    dtype: torch.dtype
+    seed: int
+    layers: int = 1
+    q_seed: Optional[int] = None   # separate query seed (shared queries)
+    packed: bool = False           # packed ragged layout (only valid tokens stored)
+
+    @property
+    def T_max(self) -> int:
+        return self.seq_hi
+
+    @property
+    def G(self) -> int:
+        return self.H_q // self.H_kv
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny-gqa-fp32", 1, 8, 2, 64, 128, 128, torch.float32, 1001),
+        Workload("llama3-8b-layer", 16, 32, 8, 128, 4096, 4096, torch.bfloat16, 1002),
+        Workload("llama-70b-ragged-layer", 32, 64, 8, 128, 1024, 16384, torch.bfloat16, 1003),
+        Workload("grouping-sweep-mha", 8, 32, 32, 128, 32768, 32768, torch.bfloat16, 1004 + 32, q_seed=1004),
+        Workload("grouping-sweep-gqa", 8, 32, 8, 128, 32768, 32768, torch.bfloat16, 1004 + 8, q_seed=1004),
+        Workload("grouping-sweep-mqa", 8, 32, 1, 128, 32768, 32768, torch.bfloat16, 1004 + 1, q_seed=1004),
+        Workload("llama3-8b-32-layer-stack", 64, 32, 8, 128, 4096, 32768, torch.bfloat16, 1005, layers=32,
+                 packed=True),
+    ]
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _normal(shape, gen, device, dtype) -> torch.Tensor:
+    """N(0,1) in float32, rounded to nearest-even into ``dtype``.  Large
+    tensors are drawn in slabs to bound the float32 temporary."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    slab = 1 << 28
+    for s in range(0, n, slab):
+        e = min(n, s + slab)
+        flat[s:e].copy_(torch.randn(e - s, generator=gen, device=device, dtype=torch.float32))
+    return out
+
+
+def seq_lens_for(w: Workload, device="cpu") -> torch.Tensor:
+    """Cached-token counts [B] (int32), seeded; the first draw of the workload."""
+    g = _gen(w.seed, "cpu")
+    if w.seq_lo == w.seq_hi:
+        sl = torch.full((w.B,), w.seq_lo, dtype=torch.int32)
+    else:
+        sl = torch.randint(w.seq_lo, w.seq_hi + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
+    return sl.to(device)
+
+
+def packed_offsets(seq_lens: torch.Tensor) -> torch.Tensor:
+    """kv_offsets [B+1] (int64) of the packed layout: sequence b owns tokens
+    [off[b], off[b+1]) per KV head, its capacity being exactly seq_lens[b]."""
+    sl = seq_lens.to("cpu", torch.int64)
+    off = torch.zeros(sl.numel() + 1, dtype=torch.int64)
+    off[1:] = torch.cumsum(sl, 0)
+    return off
+
+
+def generate(w: Workload, device="cpu", poison_padding: bool = False, replica: int = 0,
+             seq_lens: Optional[torch.Tensor] = None) -> dict:
+    """Inputs of one decode step of workload ``w``.
+
+    Returns a dict with q [L,B,H_q,d] (L dropped when layers == 1), k/v caches,
+    seq_lens (int32, on ``device``), kv_offsets (int64 [B+1], packed layouts
+    only; on ``device``), scale, and the workload.
+
+    Dense caches are [L][B][H_kv][T_max][d]; positions t >= seq_lens[b] are
+    zero, or NaN with ``poison_padding`` (they must never be read).  Packed
+    caches are flat [L * kv_offsets[B] * H_kv, d].  ``replica`` > 0 draws an
+    independent batch of the same shapes (new values, same lengths).
+    """
+    dev = torch.device(device)
+    sl = seq_lens_for(w, "cpu") if seq_lens is None else seq_lens.to("cpu", torch.int32)
+    q_seed = (w.q_seed if w.q_seed is not None else w.seed) + 7919 * replica
+    kv_seed = w.seed + 7919 * replica + (1000003 if w.q_seed is None else 0)
+    gq = _gen(q_seed, dev)
+    gk = _gen(kv_seed, dev)
+    L = w.layers
+    q = _normal((L, w.B, w.H_q, w.d), gq, dev, w.dtype)
+    out = {"workload": w, "scale": w.scale, "seq_lens": sl.to(dev)}
+    if w.packed:
+        off = packed_offsets(sl)
+        rows = int(off[-1]) * w.H_kv
+        k = _normal((L * rows, w.d), gk, dev, w.dtype)
+        v = _normal((L * rows, w.d), gk, dev, w.dtype)
+        out["kv_offsets"] = off.to(dev)
+    else:
+        shape = (L, w.B, w.H_kv, w.T_max, w.d)
+        k = _normal(shape, gk, dev, w.dtype)
+        v = _normal(shape, gk, dev, w.dtype)
+        pad = float("nan") if poison_padding else 0.0
+        for b in range(w.B):
+            n = int(sl[b])
+            if n < w.T_max:
+                k[:, b, :, n:, :] = pad
+                v[:, b, :, n:, :] = pad
+    if L == 1:
+        q = q[0]
+        if not w.packed:
+            k, v = k[0], v[0]
+    out.update(q=q, k=k, v=v)
+    return out
+
+
+def layer_view(inputs: dict, l: int) -> dict:
+    """Single-layer slice (q [B,H_q,d], k/v of layer l) of a multi-layer input."""
+    w: Workload = inputs["workload"]
+    if w.layers == 1:
+        return inputs
+    res = dict(inputs)
+    res["q"] = inputs["q"][l]
+    if w.packed:
+        rows = inputs["k"].shape[0] // w.layers
+        res["k"] = inputs["k"][l * rows:(l + 1) * rows]
+        res["v"] = inputs["v"][l * rows:(l + 1) * rows]
+    else:
+        res["k"] = inputs["k"][l]
+        res["v"] = inputs["v"][l]
+    return res

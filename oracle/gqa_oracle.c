@@ -1,0 +1,186 @@
+/*
+ * Plain fp64 CPU oracle for one grouped-query-attention decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the GPU library.
+ *
+ * What it computes, and where that is defined:
+ *
+ *   "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA):
+ *    Mathematical Foundations, Arithmetic Intensity, and KV-Cache Scaling
+ *    Mechanics", section 2, subsection "Grouped-Query Attention (GQA)":
+ *    query head i uses the key/value head of its group g(i), with
+ *    g(i) = floor((i-1)/R) + 1 in 1-based numbering, R = H_Q / H_KV, and
+ *        Head_i = softmax(Q_i K_g(i)^T / sqrt(d_k) + M) V_g(i).
+ *   Same page, subsection "Multi-Head Attention (MHA)": M is the causal mask.
+ *
+ * Readings taken where the page leaves a step open (all are the plainest
+ * reading the rest of the page supports):
+ *   - Decode step: the single query is the newest position, so the causal
+ *     mask admits exactly the cached positions t in [0, seq_len).  Positions
+ *     at or beyond seq_len are never read.
+ *   - The 1/sqrt(d_k) factor is an explicit `scale` argument (a float the
+ *     caller passes; the workloads use 1/sqrt(d)).
+ *   - seq_len == 0 (softmax over an empty set) returns a zero vector.
+ *   - The max score is subtracted inside the exponent; this changes nothing
+ *     in exact arithmetic and only keeps exp() in range.
+ *   - bf16 inputs are widened by their definition (the 16 stored bits are the
+ *     upper half of an IEEE binary32), which is exact.
+ *
+ * Parity status: every function here is pinned by CPU tests against
+ * closed forms, invariants, a library routine and the printed tables of the
+ * pages (see the oracle tests); none is "parity unpinned".
+ *
+ * Build: gcc -O2 -fno-fast-math -fopenmp -shared -fPIC gqa_oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+
+/* Widen element `idx` of an array of the given type to double. */
+static double load_elem(const void* base, int64_t idx, int dtype) {
+  if (dtype == ORACLE_F64) return ((const double*)base)[idx];
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+  /* bf16: the stored half-word is the high half of a binary32. */
+  uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Group of query head i (0-based), for R = H_Q / H_KV query heads per group.
+ * Written as the page's 1-based g(i) = floor((i-1)/R) + 1, then moved back to
+ * 0-based numbering. */
+int64_t oracle_group_of(int64_t i, int64_t R) {
+  int64_t i1 = i + 1;
+  int64_t g1 = (i1 - 1) / R + 1;
+  return g1 - 1;
+}
+
+/* Row index (in units of d elements) of token t of KV head h of sequence b.
+ * Sequence b owns tokens [kv_offsets[b], kv_offsets[b+1]) of capacity per KV
+ * head; its H_KV heads are stored one after another, each `cap` rows long.
+ * The dense layout [B][H_KV][T_max][d] is kv_offsets[b] = b * T_max. */
+static int64_t kv_row(const int64_t* kv_offsets, int64_t H_kv, int64_t b, int64_t h, int64_t t) {
+  int64_t cap = kv_offsets[b + 1] - kv_offsets[b];
+  return kv_offsets[b] * H_kv + h * cap + t;
+}
+
+/*
+ * Attention weights and output of one query head.
+ *   q, q_off : query array and the element offset of Q_i's d elements
+ *   k, v  : whole cache arrays, addressed through kv_row()
+ *   w     : optional, receives the n softmax weights (may be NULL)
+ *   out   : receives the d outputs
+ *   s     : scratch of at least the sequence's capacity
+ * Returns 0, or -1 when n is negative or exceeds the sequence's capacity.
+ */
+static int head_forward(const void* q, int64_t q_off, const void* k, const void* v, int dtype, int64_t d,
+                        const int64_t* kv_offsets, int64_t H_kv, int64_t b, int64_t g, int64_t n, double scale,
+                        double* s /* scratch, n */, double* w, double* out) {
+  int64_t cap = kv_offsets[b + 1] - kv_offsets[b];
+  if (n < 0 || n > cap) return -1;
+  for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+  if (n == 0) return 0;
+
+  /* Scores: s_t = scale * (Q_i . K_g,t), the masked-in positions only. */
+  for (int64_t t = 0; t < n; ++t) {
+    int64_t row = kv_row(kv_offsets, H_kv, b, g, t) * d;
+    double acc = 0.0;
+    for (int64_t c = 0; c < d; ++c) acc += load_elem(q, q_off + c, dtype) * load_elem(k, row + c, dtype);
+    s[t] = scale * acc;
+  }
+  /* softmax over t in [0, n). */
+  double m = s[0];
+  for (int64_t t = 1; t < n; ++t) if (s[t] > m) m = s[t];
+  double z = 0.0;
+  for (int64_t t = 0; t < n; ++t) z += exp(s[t] - m);
+  /* Weighted sum of the group's value rows. */
+  for (int64_t t = 0; t < n; ++t) {
+    double wt = exp(s[t] - m) / z;
+    if (w) w[t] = wt;
+    int64_t row = kv_row(kv_offsets, H_kv, b, g, t) * d;
+    for (int64_t c = 0; c < d; ++c) out[c] += wt * load_elem(v, row + c, dtype);
+  }
+  return 0;
+}
+
+static int check_dims(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype) {
+  if (B < 0 || H_q <= 0 || H_kv <= 0 || d <= 0) return -1;
+  if (H_q % H_kv != 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) return -1;
+  return 0;
+}
+
+/*
+ * GQA decode outputs for a list of query heads.
+ *   q          : [B][H_q][d]
+ *   k, v       : cache, layout given by kv_offsets (see kv_row)
+ *   kv_offsets : [B+1] token offsets (capacity prefix sums)
+ *   seq_lens   : [B] valid cached tokens per sequence
+ *   head_ids   : n_heads entries b*H_q + i, or NULL for all B*H_q heads in order
+ *   out        : [n_heads][d] fp64
+ * Returns 0 on success, -1 on invalid arguments (nothing is written then for
+ * the offending head).
+ */
+int oracle_gqa_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype,
+                      const void* q, const void* k, const void* v,
+                      const int64_t* kv_offsets, const int32_t* seq_lens, double scale,
+                      int64_t n_heads, const int64_t* head_ids, double* out) {
+  if (check_dims(B, H_q, H_kv, d, dtype)) return -1;
+  if (!head_ids) n_heads = B * H_q;
+  int64_t R = H_q / H_kv;
+  int64_t max_cap = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    int64_t cap = kv_offsets[b + 1] - kv_offsets[b];
+    if (cap < 0) return -1;
+    if (cap > max_cap) max_cap = cap;
+  }
+  for (int64_t j = 0; j < n_heads; ++j) {
+    int64_t id = head_ids ? head_ids[j] : j;
+    if (id < 0 || id >= B * H_q) return -1;
+  }
+  int status = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(max_cap > 0 ? max_cap : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t j = 0; j < n_heads; ++j) {
+      int64_t id = head_ids ? head_ids[j] : j;
+      int64_t b = id / H_q, i = id % H_q;
+      int64_t g = oracle_group_of(i, R);
+      int rc = s ? head_forward(q, (b * H_q + i) * d, k, v, dtype, d, kv_offsets, H_kv, b, g,
+                                (int64_t)seq_lens[b], scale, s, NULL, out + j * d)
+                 : -1;
+      if (rc) {
+#pragma omp atomic write
+        status = rc;
+      }
+    }
+    free(s);
+  }
+  return status;
+}
+
+/* Softmax weights of one query head (b, i): w[0..seq_lens[b]) and its output. */
+int oracle_gqa_head_weights(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype,
+                            const void* q, const void* k, const void* v,
+                            const int64_t* kv_offsets, const int32_t* seq_lens, double scale,
+                            int64_t b, int64_t i, double* w, double* out) {
+  if (check_dims(B, H_q, H_kv, d, dtype)) return -1;
+  if (b < 0 || b >= B || i < 0 || i >= H_q) return -1;
+  int64_t n = seq_lens[b];
+  int64_t cap = kv_offsets[b + 1] - kv_offsets[b];
+  if (n < 0 || n > cap) return -1;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
+  if (!s) return -1;
+  int rc = head_forward(q, (b * H_q + i) * d, k, v, dtype, d, kv_offsets, H_kv, b,
+                        oracle_group_of(i, H_q / H_kv), n, scale, s, w, out);
+  free(s);
+  return rc;
+}

@@ -1,0 +1,287 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with:
+  * the printed tables/figures of the pages (``tests/golden/``),
+  * closed forms and invariants of softmax attention,
+  * a library routine: ``torch.nn.functional.scaled_dot_product_attention``
+    (CPU, float64), whose ``enable_gqa`` mode expands K/V with
+    repeat_interleave -- the equivalent formulation printed in "Grouped-Query
+    Attention (GQA) and Multi-Query Attention (MQA): ...", section 2,
+    subsection "Grouped-Query Attention (GQA)".
+
+The same pins run against deliberately broken copies of the oracle
+(test_oracle_mutants.py) to show that a plausible mistake anywhere in it fails
+at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle as oracle_mod
+from gqa_mqa_kv_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def case(B, H_q, H_kv, d, T, seed, dtype=torch.float64, lo=None, poison=False):
+    """Small seeded input (dense layout); lengths U[lo, T] when ``lo`` is given."""
+    w = workloads.Workload("pin", B, H_q, H_kv, d, lo if lo is not None else T, T, dtype, seed)
+    return workloads.generate(w, "cpu", poison_padding=poison)
+
+
+def sdpa_reference(x):
+    """Library routine: SDPA (float64 CPU) per sequence over its valid tokens,
+    with enable_gqa (repeat_interleave of K/V along heads)."""
+    q, k, v, sl = x["q"].double(), x["k"].double(), x["v"].double(), x["seq_lens"]
+    B, H_q, d = q.shape
+    out = torch.zeros(B, H_q, d, dtype=torch.float64)
+    for b in range(B):
+        n = int(sl[b])
+        if n == 0:
+            continue
+        o = F.scaled_dot_product_attention(q[b:b + 1, :, None, :], k[b:b + 1, :, :n, :], v[b:b + 1, :, :n, :],
+                                           scale=float(np.float32(x["scale"])), enable_gqa=True)
+        out[b] = o[0, :, 0, :]
+    return out.numpy()
+
+
+def run(orc, x, **kw):
+    return orc.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], **kw)
+
+
+# ---------------------------------------------------------------- group map --
+def pin_group_count_theorem(orc):
+    """E contiguous heads in groups of G touch exactly (E+G-1)/G groups
+    ("Exact-head packing attains the bound: placing E exact heads contiguously
+    in groups of G hits exactly ceil(E/G) groups", the theorem statement)."""
+    for G in range(1, 65):
+        for E in range(0, 65):
+            touched = {orc.group_of(i, G) for i in range(E)}
+            assert len(touched) == (E + G - 1) // G, (E, G, len(touched))
+
+
+def pin_tp_partition_figure(orc):
+    """Figure "TENSOR PARALLEL PARTITIONING (Llama 3 70B on TP=8)": query heads
+    8k..8k+7 read KV head k (H_Q=64, H_KV=8, R=8)."""
+    for gpu, lo, hi, kv in golden_rows("tp8_head_partition_llama3_70b.txt"):
+        for i in range(int(lo), int(hi) + 1):
+            assert orc.group_of(i, 64 // 8) == int(kv), (i, kv)
+
+
+def pin_production_shapes(orc):
+    """Table "ATTENTION ARCHITECTURES IN PRODUCTION": R = H_Q/H_KV, and the
+    contiguous map sends exactly R query heads to each of the H_KV KV heads."""
+    for model, hq, hkv, r, comp in golden_rows("production_attention_shapes.txt"):
+        hq, hkv, r = int(hq), int(hkv), int(r)
+        assert hq // hkv == r and float(comp) == hq / hkv, model
+        counts = np.bincount([orc.group_of(i, r) for i in range(hq)], minlength=hkv)
+        assert counts.shape == (hkv,) and (counts == r).all(), model
+
+
+# ------------------------------------------------------- library routine --
+def pin_gqa_equals_sdpa(orc):
+    """GQA output == SDPA with repeat_interleave'd K/V (float64), several G,
+    ragged lengths, d=64 and 128."""
+    for (B, hq, hkv, d, T, lo, seed) in [(3, 8, 2, 64, 37, 1, 11), (2, 32, 8, 128, 70, 5, 12),
+                                         (2, 64, 8, 128, 33, 1, 13), (2, 12, 3, 64, 50, 20, 14)]:
+        x = case(B, hq, hkv, d, T, seed, lo=lo)
+        got = run(orc, x)
+        ref = sdpa_reference(x)
+        assert np.abs(got - ref).max() < 1e-12, (B, hq, hkv, np.abs(got - ref).max())
+
+
+def pin_mha_equals_sdpa(orc):
+    """H_KV = H_Q reduces to independent per-head attention ("Multi-Head
+    Attention (MHA)" subsection): compare with plain SDPA, no grouping."""
+    x = case(2, 6, 6, 64, 40, 21, lo=3)
+    got = run(orc, x)
+    q, k, v = x["q"], x["k"], x["v"]
+    for b in range(2):
+        n = int(x["seq_lens"][b])
+        ref = F.scaled_dot_product_attention(q[b, :, None, :], k[b, :, :n], v[b, :, :n],
+                                             scale=float(np.float32(x["scale"])))[:, 0]
+        assert np.abs(got[b] - ref.numpy()).max() < 1e-12
+
+
+def pin_mqa_shared_kv(orc):
+    """H_KV = 1 ("Multi-Query Attention (MQA)" subsection): every head reads
+    the one K/V head; heads with equal query rows give equal outputs; equals
+    SDPA with K/V broadcast over heads."""
+    x = case(2, 8, 1, 64, 30, 31, lo=7)
+    x["q"][:, 5] = x["q"][:, 2]
+    got = run(orc, x)
+    assert np.array_equal(got[:, 5], got[:, 2])
+    q, k, v = x["q"], x["k"], x["v"]
+    for b in range(2):
+        n = int(x["seq_lens"][b])
+        kb = k[b, 0:1, :n].expand(8, n, 64)
+        vb = v[b, 0:1, :n].expand(8, n, 64)
+        ref = F.scaled_dot_product_attention(q[b, :, None, :], kb, vb, scale=float(np.float32(x["scale"])))[:, 0]
+        assert np.abs(got[b] - ref.numpy()).max() < 1e-12
+
+
+# -------------------------------------------------------------- invariants --
+def pin_weights_sum_to_one(orc):
+    x = case(2, 8, 2, 64, 50, 41, lo=1)
+    for b in range(2):
+        for i in range(8):
+            w, out = orc.head_weights(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], b, i)
+            assert w.shape == (int(x["seq_lens"][b]),)
+            assert abs(w.sum() - 1.0) < 1e-14 and (w > 0).all()
+            # the output is the weighted sum of the group's value rows
+            g = i // 4
+            n = w.shape[0]
+            assert np.abs(out - w @ x["v"][b, g, :n].numpy()).max() < 1e-14
+
+
+def pin_permutation_invariance(orc):
+    x = case(1, 8, 2, 64, 45, 51)
+    base = run(orc, x)
+    perm = torch.randperm(45, generator=torch.Generator().manual_seed(5))
+    y = dict(x, k=x["k"][:, :, perm].contiguous(), v=x["v"][:, :, perm].contiguous())
+    assert np.abs(run(orc, y) - base).max() < 1e-13
+
+
+def pin_single_token(orc):
+    """One cached token: the weight is exactly 1 and the output is V exactly."""
+    x = case(2, 8, 2, 64, 1, 61)
+    got = run(orc, x)
+    for b in range(2):
+        for i in range(8):
+            assert np.array_equal(got[b, i], x["v"][b, i // 4, 0].numpy())
+
+
+def pin_constant_values(orc):
+    x = case(1, 8, 4, 64, 33, 71)
+    row = torch.linspace(-2, 2, 64, dtype=torch.float64)
+    x["v"][:] = row
+    got = run(orc, x)
+    assert np.abs(got - row.numpy()).max() < 1e-14
+
+
+def pin_zero_query_is_mean(orc):
+    """q = 0 makes every score 0, so the output is the mean of the valid V rows."""
+    x = case(2, 8, 2, 64, 29, 81, lo=4)
+    x["q"].zero_()
+    got = run(orc, x)
+    for b in range(2):
+        n = int(x["seq_lens"][b])
+        for i in range(8):
+            assert np.abs(got[b, i] - x["v"][b, i // 4, :n].mean(0).numpy()).max() < 1e-14
+
+
+def pin_key_shift_invariance(orc):
+    """Adding one vector to every key shifts all scores of a head equally."""
+    x = case(1, 8, 2, 64, 31, 91)
+    base = run(orc, x)
+    shift = torch.randn(1, 2, 1, 64, dtype=torch.float64, generator=torch.Generator().manual_seed(9))
+    y = dict(x, k=x["k"] + shift)
+    assert np.abs(run(orc, y) - base).max() < 1e-12
+
+
+def pin_linearity_in_values(orc):
+    x = case(1, 8, 2, 64, 27, 101)
+    v2 = torch.randn(x["v"].shape, dtype=torch.float64, generator=torch.Generator().manual_seed(3))
+    a = run(orc, x)
+    b = run(orc, dict(x, v=v2))
+    c = run(orc, dict(x, v=2.0 * x["v"] - 3.0 * v2))
+    assert np.abs(c - (2.0 * a - 3.0 * b)).max() < 1e-12
+
+
+def pin_hand_example(orc):
+    """Worked by hand: d=1, scale=1, q=1, keys 0 and ln 3 give weights 1/4 and
+    3/4; values 4 and 8 give 4/4 + 3*8/4 = 7."""
+    q = torch.ones(1, 1, 1, dtype=torch.float64)
+    k = torch.tensor([0.0, math.log(3.0)], dtype=torch.float64).view(1, 1, 2, 1)
+    v = torch.tensor([4.0, 8.0], dtype=torch.float64).view(1, 1, 2, 1)
+    got = orc.decode(q, k, v, [2], 1.0)
+    assert abs(got[0, 0, 0] - 7.0) < 1e-13
+
+
+def pin_empty_sequence_is_zero(orc):
+    x = case(2, 8, 2, 64, 16, 111)
+    x["seq_lens"][1] = 0
+    got = run(orc, x)
+    assert (got[1] == 0).all() and np.isfinite(got[0]).all() and np.abs(got[0]).max() > 0
+
+
+def pin_padding_never_read(orc):
+    """Positions at or beyond seq_len (NaN here) do not reach the output, and
+    the result equals the same cache cut to its valid length."""
+    x = case(3, 8, 2, 64, 40, 121, lo=3, poison=True)
+    got = run(orc, x)
+    assert np.isfinite(got).all()
+    for b in range(3):
+        n = int(x["seq_lens"][b])
+        y = dict(x, q=x["q"][b:b + 1], k=x["k"][b:b + 1, :, :n].contiguous(), v=x["v"][b:b + 1, :, :n].contiguous(),
+                 seq_lens=x["seq_lens"][b:b + 1])
+        assert np.array_equal(run(orc, y)[0], got[b])
+
+
+def pin_bf16_and_fp32_widening(orc):
+    """bf16/fp32 inputs are widened exactly: same result as their float64 copies."""
+    for dt in (torch.bfloat16, torch.float32):
+        x = case(2, 8, 2, 64, 19, 131, dtype=dt, lo=2)
+        y = dict(x, q=x["q"].double(), k=x["k"].double(), v=x["v"].double())
+        assert np.array_equal(run(orc, x), run(orc, y))
+
+
+def pin_packed_layout(orc):
+    """The packed ragged layout addresses the same tokens as the dense one."""
+    x = case(3, 8, 2, 64, 25, 141, lo=1)
+    dense = run(orc, x)
+    sl = x["seq_lens"]
+    offs = workloads.packed_offsets(sl)
+    rows = []
+    for b in range(3):
+        n = int(sl[b])
+        rows.append(x["k"][b, :, :n].reshape(-1, 64))
+    kp = torch.cat(rows)
+    vp = torch.cat([x["v"][b, :, :int(sl[b])].reshape(-1, 64) for b in range(3)])
+    packed = orc.decode(x["q"], kp, vp, sl, x["scale"], kv_offsets=offs.numpy())
+    assert np.array_equal(packed, dense)
+
+
+def pin_head_subset(orc):
+    x = case(2, 8, 2, 64, 21, 151, lo=5)
+    full = run(orc, x).reshape(16, 64)
+    ids = [15, 0, 7, 8]
+    assert np.array_equal(run(orc, x, heads=ids), full[ids])
+
+
+# ------------------------------------------------------ page formulas --
+def pin_kv_cache_table():
+    """Reproduce all nine cells of the printed 70B KV-cache table."""
+    for s, hkv, gb in golden_rows("kv_cache_table_70b.txt"):
+        got = oracle_mod.kv_cache_bytes(b=1, s=int(s), L=80, H_kv=int(hkv), d_k=128, bytes_per_elem=2)
+        assert f"{got / 1e9:.2f}" == gb, (s, hkv, got)
+
+
+def pin_cache_element_ratios():
+    for hq, hkv, num, den in golden_rows("cache_element_ratios.txt"):
+        assert oracle_mod.cache_element_ratio(int(hkv), int(hq)) == int(num) / int(den)
+
+
+def pin_roofline_balance():
+    for f, bw, isat in golden_rows("h100_roofline.txt"):
+        assert f"{oracle_mod.roofline_balance(float(f), float(bw)):.1f}" == isat
+
+
+ORACLE_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and v.__code__.co_argcount == 1]
+FORMULA_PINS = [pin_kv_cache_table, pin_cache_element_ratios, pin_roofline_balance]

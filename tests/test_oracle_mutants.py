@@ -1,0 +1,81 @@
+"""Plants plausible mistakes in copies of the C oracle (never in the GPU path)
+and checks that each one fails at least one pin.  The real oracle source is
+only read; each mutant is compiled into a temporary directory and exercised in
+a subprocess of its own, so a mutant that corrupts memory cannot disturb the
+test process."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+MUTANTS = {
+    # head -> group map off by one (uses i instead of i-1 in the 1-based form)
+    "group_map_off_by_one": ("int64_t g1 = (i1 - 1) / R + 1;", "int64_t g1 = (i1) / R + 1;"),
+    # strided grouping i mod H_kv instead of contiguous i / R
+    "group_map_strided": ("int64_t g = oracle_group_of(i, R);", "int64_t g = i % H_kv;"),
+    # the last valid token is dropped from the weighted sum
+    "drop_last_token": ("for (int64_t t = 0; t < n; ++t) {\n    double wt", "for (int64_t t = 0; t + 1 < n; ++t) {\n    double wt"),
+    # the first token is left out of the normaliser
+    "normaliser_skips_first": ("for (int64_t t = 0; t < n; ++t) z += exp", "for (int64_t t = 1; t < n; ++t) z += exp"),
+    # scale not applied to the scores
+    "scale_dropped": ("s[t] = scale * acc;", "s[t] = acc;"),
+    # sign error in the exponent
+    "exponent_sign": ("exp(s[t] - m)", "exp(m - s[t])"),
+    # no normalisation
+    "no_normalisation": ("double wt = exp(s[t] - m) / z;", "double wt = exp(s[t] - m);"),
+    # values read from the key cache
+    "values_from_keys": ("load_elem(v, row + c, dtype)", "load_elem(k, row + c, dtype)"),
+    # transposed key operand
+    "keys_transposed": ("load_elem(k, row + c, dtype)", "load_elem(k, kv_row(kv_offsets, H_kv, b, g, 0) * d + c * n + t, dtype)"),
+    # query row of the group's first head used for every head
+    "query_of_group": ("(b * H_q + i) * d, k, v, dtype, d, kv_offsets, H_kv, b, g,", "(b * H_q + g * R) * d, k, v, dtype, d, kv_offsets, H_kv, b, g,"),
+    # KV heads interleaved per token instead of stored one after another
+    "kv_layout_interleaved": ("return kv_offsets[b] * H_kv + h * cap + t;", "return kv_offsets[b] * H_kv + h + t * H_kv;"),
+    # bf16 widened with the wrong shift
+    "bf16_widening": ("[idx]) << 16;", "[idx]) << 15;"),
+    # every sequence uses the first sequence's length
+    "seq_len_of_first": ("(int64_t)seq_lens[b], scale, s, NULL", "(int64_t)seq_lens[0], scale, s, NULL"),
+    # one token too many (reads a padding position)
+    "extra_token": ("if (n < 0 || n > cap) return -1;\n  for", "n = n < cap ? n + 1 : n;\n  if (n < 0 || n > cap) return -1;\n  for"),
+}
+
+_RUNNER = r"""
+import json, sys
+sys.path[:0] = [sys.argv[2], sys.argv[3]]
+import oracle
+from oracle_pins import ORACLE_PINS
+orc = oracle.Oracle(sys.argv[1])
+failed = []
+for pin in ORACLE_PINS:
+    try:
+        pin(orc)
+    except Exception:
+        failed.append(pin.__name__)
+print("FAILED_PINS " + json.dumps(failed), flush=True)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, "mutation site not found: %s" % name
+    path = os.path.join(tmp_path, "gqa_oracle_%s.c" % name)
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.build(path, os.path.join(tmp_path, "lib_%s.so" % name))
+    tests_dir = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(tests_dir)
+    r = subprocess.run([sys.executable, "-c", _RUNNER, lib, root, tests_dir], capture_output=True, text=True,
+                       timeout=300, env=dict(os.environ, OMP_NUM_THREADS="2"))
+    lines = [l for l in r.stdout.splitlines() if l.startswith("FAILED_PINS ")]
+    if r.returncode != 0 and not lines:
+        return  # the mutant crashed the process: caught
+    assert lines, r.stdout + r.stderr
+    failed = json.loads(lines[-1][len("FAILED_PINS "):])
+    print(name, "caught by", failed)
+    assert failed, "mutant %s passed every pin" % name
