@@ -1,0 +1,220 @@
+"""GQA decode-step benchmark: effective HBM GB/s and microseconds per step.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+One step = one decode step of the workload (every split-KV chunk and the
+fused merge: one kernel launch) over one batch of synthetic inputs that are
+already resident in HBM.  Steps rotate over enough independent input batches
+(``--replicas``) that the working set exceeds the 256 MB last-level
+(Infinity) cache, so every step streams its K/V from HBM.
+
+Metric: (K + V bytes of the valid tokens + q bytes + out bytes) / time, the
+KV traffic formula of "Grouped-Query Attention (GQA) and Multi-Query
+Attention (MQA): ...", section 1 ("KV Cache Memory Footprint"), per step.
+
+The single JSON line also carries
+  * roofline: the decode kernel's achieved algorithmic GB/s (per-launch HIP
+    events on the launch stream) against the MI355X HBM3E peak of 8 TB/s,
+    and the HBM traffic the rocprofv3 counters recorded (profiles/), if they
+    were taken on the current kernel source;
+  * cpu_baseline: the fp64 CPU oracle timed on this host over whole steps of
+    the same workload (about ten seconds of work);
+  * context: the H100 roofline figures printed on that page (3.35 TB/s,
+    989 TFLOP/s, I_sat ~ 295 FLOP/B), hardware context only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "GQA decode effective HBM GB/s (% of MI355X peak) + µs/step"
+DEFAULT_WORKLOAD = "llama3-8b-layer"
+KERNEL_SOURCES = ["common.h", "kernel_mfma.h", "kernel_valu.h", "gqa_decode.hip"]
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gqa_decode_mfma_llama3_8b_layer_counters.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gqa_mqa_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, seq_lens, out_elem_bytes) -> int:
+    e = 2 if str(w.dtype).endswith("bfloat16") else 4
+    kv = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * e
+    qb = w.layers * w.B * w.H_q * w.d * e
+    ob = w.layers * w.B * w.H_q * w.d * out_elem_bytes
+    return kv + qb + ob
+
+
+def read_traffic(workload_name: str, launches_bytes: int):
+    """HBM bytes per launch from the committed counter summary, when it was
+    recorded on the current kernel source for this workload; else None."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    kv = dict(re.findall(r"^(\w+)\s*[:=]\s*(\S+)\s*$", text, re.M))
+    if kv.get("kernel_source_hash") != kernel_source_hash() or kv.get("workload") != workload_name:
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """Time the fp64 oracle on whole steps of the workload on this host."""
+    import oracle
+    from gqa_mqa_kv_amd import workloads
+
+    orc = oracle.default()
+    x = workloads.generate(w, "cpu") if w.layers == 1 else None
+    if x is None:
+        raise RuntimeError("cpu baseline is defined for single-layer workloads")
+    args = (x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+    orc.decode(*args)   # warm
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.decode(*args)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    per_step = el / n
+    nbytes = algorithmic_bytes(w, x["seq_lens"], 2 if str(w.dtype).endswith("bfloat16") else 4)
+    return {"value": round(nbytes / per_step / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+            "kind": "oracle", "us_per_step": round(per_step * 1e6, 1),
+            "sample": "%d whole steps of %s (fp64 C oracle, OpenMP), %.1f s" % (n, w.name, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--replicas", type=int, default=0, help="input batches rotated over (0: enough for >= 2 GiB)")
+    ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode step is not sharded across GPUs here "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gqa_mqa_kv_amd as gqa
+    from gqa_mqa_kv_amd import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out_dtype = {None: w.dtype, "bf16": torch.bfloat16, "fp32": torch.float32}[args.out_dtype]
+    seq_lens = workloads.seq_lens_for(w)
+    kv_bytes = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * (2 if w.dtype == torch.bfloat16 else 4)
+    resident = kv_bytes if w.packed else 2 * w.layers * w.B * w.H_kv * w.T_max * w.d * (
+        2 if w.dtype == torch.bfloat16 else 4)
+    reps = args.replicas or max(1, min(16, -(-(2 << 30) // resident)))
+    free, _ = torch.cuda.mem_get_info(dev)
+    reps = max(1, min(reps, int((free * 0.85) // max(resident, 1))))
+    print("[bench] workload %s, %d input batch(es) of %.3f GB resident" % (w.name, reps, resident / 1e9),
+          file=sys.stderr, flush=True)
+    batches = [workloads.generate(w, dev, replica=r) for r in range(reps)]
+    stream = torch.cuda.current_stream(dev)
+    kw = dict(out_dtype=out_dtype, chunk_tokens=args.chunk_tokens, path=args.path)
+    launchers = []
+    for x in batches:
+        extra = dict(kv_offsets=x["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if w.packed else {}
+        launchers.append(gqa.prepare(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], **extra, **kw))
+
+    def step(i):
+        return launchers[i % reps]()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps, synchronised on both sides
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4)
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+
+    # per-launch kernel duration: an event pair around each launch on the launch stream
+    pairs = []
+    for i in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    durs = sorted(a.elapsed_time(b) for a, b in pairs)
+    kern_ms = sum(durs) / len(durs)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+
+    d = gqa.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype, out_dtype, chunk_tokens=args.chunk_tokens,
+                      path=args.path)
+    chunk, n_chunks = gqa.plan(d, w.layers)
+    traffic = read_traffic(w.name, nbytes) if args.path in ("auto", "mfma") and not args.chunk_tokens else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_peak_hbm": round(100.0 * gbps / PEAK_HBM_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "G": w.G, "d": w.d,
+                   "cached_tokens": [w.seq_lo, w.seq_hi], "seq_lens_sum": int(seq_lens.sum()), "layers": w.layers,
+                   "layout": "packed" if w.packed else "dense", "accumulate": "fp32",
+                   "out_dtype": "bf16" if out_dtype == torch.bfloat16 else "fp32",
+                   "path": args.path, "chunk_tokens": chunk, "chunks_per_sequence": n_chunks,
+                   "input_batches_rotated": reps, "algorithmic_bytes_per_step": nbytes,
+                   "wall_s_timed_region": round(wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "kernel_ms_avg": round(kern_ms, 5), "kernel_ms_median": round(durs[len(durs) // 2], 5),
+                     "algorithmic_bytes_per_launch": nbytes, "kernel_source_hash": kernel_source_hash()},
+        "cpu_baseline": None,
+        "context": {"h100_sxm5_hbm_TBps": 3.35, "h100_sxm5_dense_bf16_TFLOPs": 989, "h100_I_sat_FLOP_per_B": 295.2},
+    }
+    if not args.no_cpu_baseline and w.layers == 1:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,16 @@
+"""MI355X (gfx950) grouped-query-attention decode step behind a C ABI.
+
+The computation ("Grouped-Query Attention (GQA) and Multi-Query Attention
+(MQA): Mathematical Foundations, Arithmetic Intensity, and KV-Cache Scaling
+Mechanics", section 2): each query head i attends over its sequence's cached
+tokens with the key/value head g = i / G of its contiguous group.  All work
+runs in hand-written HIP kernels (gqa_mqa_kv_amd/csrc); Python only marshals
+arguments.  See include/gqa_decode.h for the ABI.
+
+    from gqa_mqa_kv_amd import decode, decode_layers
+"""
+from ._binding import (GqaDims, GqaError, Prepared, decode, decode_layers, default_workspace, lib, make_dims, plan,
+                       prepare, status_string, workspace_bytes)
+
+__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "default_workspace", "lib", "make_dims", "plan",
+           "status_string", "workspace_bytes"]

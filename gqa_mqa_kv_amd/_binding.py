@@ -1,0 +1,257 @@
+"""ctypes binding of include/gqa_decode.h (argument marshalling only).
+
+Every step of the decode runs in the HIP library; this module only turns
+torch tensors into device pointers and a gqa_dims struct, provides a zeroed
+workspace, and raises on a non-zero status.  It never falls back to any other
+implementation: when the built library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+GQA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+MERGES = {"auto": 0, "fused": 1, "kernel": 2}
+STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
+          4: "GQA_ERR_LAUNCH"}
+SYMBOLS = ("gqa_decode", "gqa_decode_layers", "gqa_decode_workspace_bytes", "gqa_decode_plan",
+           "gqa_status_string")
+
+
+class GqaDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("seq_len_hint", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("path", ctypes.c_int32), ("workgroup_waves", ctypes.c_int32),
+                ("merge", ctypes.c_int32), ("tiles_in_flight", ctypes.c_int32)]
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = _build.LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError("HIP library not built: %s is missing (run gqa_mqa_kv_amd/build.py or "
+                               "__graft_entry__.build())" % path)
+        L = ctypes.CDLL(path)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        dims_p = ctypes.POINTER(GqaDims)
+        L.gqa_decode.restype = ctypes.c_int
+        L.gqa_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_layers.restype = ctypes.c_int
+        L.gqa_decode_layers.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_workspace_bytes.restype = sz
+        L.gqa_decode_workspace_bytes.argtypes = [dims_p, i32]
+        L.gqa_decode_plan.restype = ctypes.c_int
+        L.gqa_decode_plan.argtypes = [dims_p, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.gqa_status_string.restype = ctypes.c_char_p
+        L.gqa_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gqa_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise GqaError(status, status_string(status))
+
+
+def make_dims(B, H_q, H_kv, d, T_max, dtype, out_dtype=None, seq_len_hint=0, chunk_tokens=0,
+              path="auto", waves=0, merge="auto", tiles=0) -> GqaDims:
+    if dtype not in GQA_DTYPE or (out_dtype is not None and out_dtype not in GQA_DTYPE):
+        raise TypeError("dtypes must be float32 or bfloat16")
+    return GqaDims(int(B), int(H_q), int(H_kv), int(d), int(T_max), GQA_DTYPE[dtype],
+                   GQA_DTYPE[out_dtype if out_dtype is not None else dtype], int(seq_len_hint),
+                   int(chunk_tokens), PATHS[path], int(waves), MERGES[merge], int(tiles))
+
+
+def workspace_bytes(dims: GqaDims, num_layers: int = 1) -> int:
+    return int(lib().gqa_decode_workspace_bytes(ctypes.byref(dims), int(num_layers)))
+
+
+def plan(dims: GqaDims, num_layers: int = 1):
+    """(tokens per chunk, chunks of the longest sequence) chosen by the library."""
+    c, n = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().gqa_decode_plan(ctypes.byref(dims), int(num_layers), ctypes.byref(c), ctypes.byref(n)))
+    return c.value, n.value
+
+
+_workspaces = {}
+
+
+def default_workspace(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
+    """A zero-filled device buffer of at least ``nbytes`` (256-byte aligned),
+    cached per device.  The library leaves its counters at zero after each
+    call, so the buffer is shared as is by calls ordered on one stream."""
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(t: torch.Tensor, name: str, device: torch.device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None, chunk_tokens: int = 0,
+           path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
+           merge: str = "auto", tiles: int = 0):
+    """One decode step of one layer.  q [B,H_q,d]; k_cache/v_cache
+    [B,H_kv,T_max,d]; seq_lens int32 [B] on the same device.  Returns out
+    [B,H_q,d] (dtype ``out_dtype``, default q's)."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,H_q,d] and k/v [B,H_kv,T_max,d]")
+    B, H_q, d = q.shape
+    _, H_kv, T_max, _ = k_cache.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != d or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, merge, tiles)
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
+    _require(out, "out", dev)
+    if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
+        raise ValueError("out must be [B,H_q,d] of the output dtype")
+    need = workspace_bytes(dims)
+    ws = default_workspace(need, dev) if workspace is None else workspace
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _check(lib().gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out),
+                            ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                            s))
+    return out
+
+
+def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len: Optional[int] = None,
+                  num_kv_heads: Optional[int] = None, out=None, out_dtype=None, chunk_tokens: int = 0,
+                  path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
+           merge: str = "auto", tiles: int = 0):
+    """One decode step of L independent layers in one launch.  q [L,B,H_q,d].
+    Dense caches are [L,B,H_kv,T_max,d]; with ``kv_offsets`` (int64 [B+1] on
+    the device) the caches are packed (any shape holding L*kv_offsets[B]*H_kv*d
+    elements), and ``max_seq_len`` (the largest capacity) and ``num_kv_heads``
+    must be given."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [L,B,H_q,d]")
+    L, B, H_q, d = q.shape
+    if kv_offsets is None:
+        if k_cache.dim() != 5 or v_cache.shape != k_cache.shape or k_cache.shape[:2] != (L, B) or k_cache.shape[4] != d:
+            raise ValueError("dense caches must be [L,B,H_kv,T_max,d]")
+        H_kv, T_max = k_cache.shape[2], k_cache.shape[3]
+    else:
+        _require(kv_offsets, "kv_offsets", dev)
+        if kv_offsets.dtype != torch.int64 or kv_offsets.shape != (B + 1,):
+            raise ValueError("kv_offsets must be int64 [B+1]")
+        if max_seq_len is None or num_kv_heads is None:
+            raise ValueError("packed caches need max_seq_len and num_kv_heads")
+        if v_cache.numel() != k_cache.numel() or k_cache.numel() % (L * num_kv_heads * d):
+            raise ValueError("packed cache size mismatch")
+        H_kv, T_max = num_kv_heads, max_seq_len
+    if seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32 [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, merge, tiles)
+    if out is None:
+        out = torch.empty(L, B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
+    _require(out, "out", dev)
+    if out.shape != (L, B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
+        raise ValueError("out must be [L,B,H_q,d] of the output dtype")
+    need = workspace_bytes(dims, L)
+    ws = default_workspace(need, dev) if workspace is None else workspace
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _check(lib().gqa_decode_layers(int(L), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
+                                   float(scale), _ptr(out), ctypes.byref(dims), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), s))
+    return out
+
+
+class Prepared:
+    """A decode call with every argument marshalled once; calling it only
+    enqueues the launch (for timing loops where per-call argument checks
+    would cost more host time than the kernel takes)."""
+
+    def __init__(self, layers: bool, args: tuple, keep: tuple):
+        self._fn = lib().gqa_decode_layers if layers else lib().gqa_decode
+        self._args = args
+        self._keep = keep   # tensors whose memory the pointers refer to
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self._keep[0]
+
+
+def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len=None, num_kv_heads=None,
+            out_dtype=None, chunk_tokens: int = 0, path: str = "auto", seq_len_hint: int = 0, stream=None,
+            waves: int = 0, merge: str = "auto", tiles: int = 0):
+    """Validate (by running the call once) and return a Prepared launcher
+    writing into a fresh output tensor, which each call returns.  q [B,H_q,d]
+    selects gqa_decode, q [L,B,H_q,d] selects gqa_decode_layers."""
+    dev = q.device
+    layers = q.dim() == 4
+    out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    if layers:
+        decode_layers(q, k_cache, v_cache, seq_lens, scale, kv_offsets=kv_offsets, max_seq_len=max_seq_len,
+                      num_kv_heads=num_kv_heads, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
+                      path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, merge=merge, tiles=tiles)
+        L, B, H_q, d = q.shape
+        if kv_offsets is None:
+            H_kv, T_max = k_cache.shape[2], k_cache.shape[3]
+        else:
+            H_kv, T_max = num_kv_heads, max_seq_len
+    else:
+        decode(q, k_cache, v_cache, seq_lens, scale, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
+               path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, merge=merge, tiles=tiles)
+        B, H_q, d = q.shape
+        H_kv, T_max = k_cache.shape[1], k_cache.shape[2]
+        L = 1
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, merge, tiles)
+    ws = default_workspace(workspace_bytes(dims, L), dev)
+    nbytes = 0 if ws is None else ws.numel()
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    dref = ctypes.byref(dims)
+    if layers:
+        args = (int(L), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens), float(scale),
+                _ptr(out), dref, _ptr(ws), nbytes, s)
+    else:
+        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out), dref, _ptr(ws),
+                nbytes, s)
+    return Prepared(layers, args, (out, q, k_cache, v_cache, seq_lens, kv_offsets, ws, dims))

@@ -1,0 +1,248 @@
+// Host side of the C ABI declared in include/gqa_decode.h: argument checks,
+// the split-KV planner and kernel dispatch.  Everything here runs on the host
+// and never reads device memory or synchronises.
+#include "gqa_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernel_mfma.h"
+#include "kernel_valu.h"
+
+namespace {
+
+constexpr int kTargetWorkgroups = 256;    // one per CU on a 256-CU part
+constexpr int kMinChunk = 256;            // at least one 32-token tile per wavefront of an 8-wave group
+constexpr int kMaxChunk = 8192;           // bounds the longest workgroup (tail of ragged batches)
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+gqa_status check_dims(const gqa_dims* d, int32_t L) {
+  if (!d) return GQA_ERR_INVALID_ARG;
+  if (L < 1 || d->batch < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->max_seq_len < 1)
+    return GQA_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return GQA_ERR_INVALID_ARG;
+  if (d->dtype != GQA_DTYPE_F32 && d->dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (d->out_dtype != GQA_DTYPE_F32 && d->out_dtype != GQA_DTYPE_BF16) return GQA_ERR_INVALID_ARG;
+  if (d->seq_len_hint < 0 || d->seq_len_hint > d->max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (d->chunk_tokens < 0 || d->chunk_tokens % 64 != 0) return GQA_ERR_INVALID_ARG;
+  if (d->path != GQA_PATH_AUTO && d->path != GQA_PATH_VALU && d->path != GQA_PATH_MFMA) return GQA_ERR_INVALID_ARG;
+  if (d->merge != GQA_MERGE_AUTO && d->merge != GQA_MERGE_FUSED && d->merge != GQA_MERGE_KERNEL)
+    return GQA_ERR_INVALID_ARG;
+  if (d->tiles_in_flight < 0 || d->tiles_in_flight > 2) return GQA_ERR_INVALID_ARG;
+  if (d->workgroup_waves != 0 && d->workgroup_waves != 4 && d->workgroup_waves != 8 && d->workgroup_waves != 16)
+    return GQA_ERR_INVALID_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return GQA_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads > gqa::kMaxGroup) return GQA_ERR_UNSUPPORTED;
+  if (d->path == GQA_PATH_MFMA && d->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  // Grid and index ranges: units * chunks must fit a 32-bit grid.
+  const int64_t units = (int64_t)L * d->batch * d->num_kv_heads;
+  if (units > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+int max_waves(int hb);
+int max_tiles(int hb, int waves);
+
+bool use_mfma(const gqa_dims* d) {
+  return d->path == GQA_PATH_MFMA || (d->path == GQA_PATH_AUTO && d->dtype == GQA_DTYPE_BF16);
+}
+
+struct Plan {
+  int32_t chunk, n_chunks, waves, tiles;
+  bool fused;
+  int64_t units;
+  size_t ws_bytes, cnt_bytes, ml_bytes;
+};
+
+// The fused merge has one workgroup read every chunk state of its unit after
+// a round trip through the arrival counter; measured on MI355X, the separate
+// merge kernel (spread over (unit, head) pairs) finishes sooner, so it is the
+// default and the fused merge is opt-in.
+// The arrival counters occupy a fixed region at the start of every workspace,
+// whatever the dims, and nothing else is ever stored there: calls of different
+// shapes can then share a workspace, each leaving every counter it used at zero.
+constexpr int64_t kCounterSlots = 1 << 18;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+
+// Split each (layer, sequence, KV head) into chunks of `chunk` tokens.  The
+// host never sees seq_lens, so the plan covers the longest possible sequence
+// (seq_len_hint or max_seq_len); workgroups past a sequence's end exit at once.
+Plan make_plan(const gqa_dims* d, int32_t L) {
+  Plan p;
+  p.units = (int64_t)L * d->batch * d->num_kv_heads;
+  const int hb = (d->num_q_heads / d->num_kv_heads + 15) / 16;
+  p.waves = 4;
+  p.tiles = 1;
+  if (use_mfma(d)) {
+    p.waves = d->workgroup_waves ? d->workgroup_waves : 4;
+    if (p.waves > max_waves(hb)) p.waves = max_waves(hb);
+    p.tiles = d->tiles_in_flight ? d->tiles_in_flight : 2;
+    if (p.tiles > max_tiles(hb, p.waves)) p.tiles = max_tiles(hb, p.waves);
+  }
+  const int64_t T = d->seq_len_hint > 0 ? d->seq_len_hint : d->max_seq_len;
+  int64_t c;
+  if (d->chunk_tokens > 0) {
+    c = d->chunk_tokens;
+  } else {
+    const int64_t per_unit = p.units > 0 ? ceil_div(kTargetWorkgroups, p.units) : 1;
+    c = ceil_div(ceil_div(T, per_unit), kMinChunk) * kMinChunk;
+    if (c < kMinChunk) c = kMinChunk;
+    if (c > kMaxChunk) c = kMaxChunk;
+  }
+  p.chunk = (int32_t)c;
+  p.n_chunks = (int32_t)ceil_div(T, c);
+  while (p.units * p.n_chunks > INT32_MAX) {   // only for absurd shapes with a forced tiny chunk
+    p.chunk *= 2;
+    p.n_chunks = (int32_t)ceil_div(T, p.chunk);
+  }
+  const int64_t G = d->num_q_heads / d->num_kv_heads;
+  p.fused = use_mfma(d) && p.units <= kCounterSlots && d->merge == GQA_MERGE_FUSED;
+  if (p.n_chunks <= 1 || p.units == 0) {
+    p.ws_bytes = p.cnt_bytes = p.ml_bytes = 0;
+  } else {
+    p.cnt_bytes = kCounterBytes;
+    p.ml_bytes = (size_t)ceil_div(p.units * p.n_chunks * G * 2 * 4, 256) * 256;
+    p.ws_bytes = p.cnt_bytes + p.ml_bytes + (size_t)(p.units * p.n_chunks * G * d->head_dim * 4);
+  }
+  return p;
+}
+
+typedef void (*kernel_fn)(gqa::Problem);
+
+// Kernel variants instantiated per head-block count hb = ceil(G/16): larger
+// workgroups and more tiles in flight cost registers, and only the variants
+// that fit without spilling exist (4 wavefronts per SIMD allow 128 VGPRs).
+int max_waves(int hb) { return hb == 1 ? 16 : (hb == 2 ? 8 : 4); }
+int max_tiles(int hb, int waves) { return (hb == 1 && waves <= 8) || (hb == 2 && waves == 4) ? 2 : 1; }
+
+template <int D>
+kernel_fn mfma_kernel(int hb, int waves, int tiles) {
+  switch (hb) {
+    case 1:
+      if (waves == 16) return gqa::gqa_decode_mfma<D, 1, 16, 1>;
+      if (waves == 8) return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 8, 2> : gqa::gqa_decode_mfma<D, 1, 8, 1>;
+      return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 4, 1>;
+    case 2:
+      if (waves == 8) return gqa::gqa_decode_mfma<D, 2, 8, 1>;
+      return tiles == 2 ? gqa::gqa_decode_mfma<D, 2, 4, 2> : gqa::gqa_decode_mfma<D, 2, 4, 1>;
+    case 3: return gqa::gqa_decode_mfma<D, 3, 4, 1>;
+    default: return gqa::gqa_decode_mfma<D, 4, 4, 1>;
+  }
+}
+
+kernel_fn pick_kernel(const gqa_dims* d, int waves, int tiles) {
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (use_mfma(d)) {
+    const int hb = (G + 15) / 16;
+    return d->head_dim == 128 ? mfma_kernel<128>(hb, waves, tiles) : mfma_kernel<64>(hb, waves, tiles);
+  }
+  if (d->dtype == GQA_DTYPE_F32)
+    return d->head_dim == 128 ? gqa::gqa_decode_valu<float, 128> : gqa::gqa_decode_valu<float, 64>;
+  return d->head_dim == 128 ? gqa::gqa_decode_valu<uint16_t, 128> : gqa::gqa_decode_valu<uint16_t, 64>;
+}
+
+gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const int64_t* kv_offsets,
+                  const int32_t* seq_lens, float scale, void* out, const gqa_dims* d, void* ws, size_t ws_bytes,
+                  void* stream) {
+  gqa_status st = check_dims(d, L);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (d->batch == 0) return GQA_OK;
+  if (!q || !k || !v || !seq_lens || !out) return GQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
+    return GQA_ERR_INVALID_ARG;
+  if (kv_offsets && !aligned(kv_offsets, 8)) return GQA_ERR_INVALID_ARG;
+  const Plan plan = make_plan(d, L);
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned(ws, 256))) return GQA_ERR_WORKSPACE;
+
+  gqa::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.kv_offsets = kv_offsets;
+  p.seq_lens = seq_lens;
+  char* w = static_cast<char*>(ws);
+  p.ws_cnt = plan.ws_bytes ? reinterpret_cast<int32_t*>(w) : nullptr;
+  p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.cnt_bytes) : nullptr;
+  p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.cnt_bytes + plan.ml_bytes) : nullptr;
+  p.fused_merge = plan.fused;
+  p.B = d->batch;
+  p.H_q = d->num_q_heads;
+  p.H_kv = d->num_kv_heads;
+  p.G = d->num_q_heads / d->num_kv_heads;
+  p.T_max = d->max_seq_len;
+  p.T_cap = d->seq_len_hint > 0 ? d->seq_len_hint : d->max_seq_len;
+  p.L = L;
+  p.chunk = plan.chunk;
+  p.n_chunks = plan.n_chunks;
+  p.out_bf16 = d->out_dtype == GQA_DTYPE_BF16;
+  p.scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* args[] = {&p};
+  const int64_t grid = plan.units * plan.n_chunks;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pick_kernel(d, plan.waves, plan.tiles)), dim3((unsigned)grid),
+                                 dim3(64 * plan.waves), args, 0, s);
+  if (e != hipSuccess) return GQA_ERR_LAUNCH;
+  if (plan.n_chunks > 1 && !plan.fused) {
+    // The kernel boundary orders the chunk states before their merge.
+    const int hpb = 256 / d->head_dim;
+    const int64_t mgrid = plan.units * ((p.G + hpb - 1) / hpb);
+    const void* mk = d->head_dim == 128 ? reinterpret_cast<const void*>(gqa::gqa_merge_chunks<128>)
+                                        : reinterpret_cast<const void*>(gqa::gqa_merge_chunks<64>);
+    if (mgrid > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+    e = hipLaunchKernel(mk, dim3((unsigned)mgrid), dim3(256), args, 0, s);
+    if (e != hipSuccess) return GQA_ERR_LAUNCH;
+  }
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gqa_decode_workspace_bytes(const gqa_dims* dims, int32_t num_layers) {
+  if (check_dims(dims, num_layers) != GQA_OK) return 0;
+  return make_plan(dims, num_layers).ws_bytes;
+}
+
+gqa_status gqa_decode_plan(const gqa_dims* dims, int32_t num_layers, int32_t* chunk_tokens, int32_t* num_chunks) {
+  gqa_status st = check_dims(dims, num_layers);
+  if (st != GQA_OK) return st;
+  if (!chunk_tokens || !num_chunks) return GQA_ERR_INVALID_ARG;
+  const Plan p = make_plan(dims, num_layers);
+  *chunk_tokens = p.chunk;
+  *num_chunks = p.n_chunks;
+  return GQA_OK;
+}
+
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, float scale,
+                      void* out, const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
+  return launch(1, q, k_cache, v_cache, nullptr, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
+                             const int64_t* kv_offsets, const int32_t* seq_lens, float scale, void* out,
+                             const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
+  return launch(num_layers, q, k_cache, v_cache, kv_offsets, seq_lens, scale, out, dims, workspace, workspace_bytes,
+                stream);
+}
+
+const char* gqa_status_string(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG: invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: unsupported shape, dtype or path";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
+    case GQA_ERR_LAUNCH: return "GQA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown gqa_status";
+}
+
+}  // extern "C"

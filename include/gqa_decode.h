@@ -1,0 +1,175 @@
+/*
+ * gqa_decode.h -- C ABI of an MI355X (gfx950) library for one decode step of
+ * grouped-query attention.
+ *
+ * The operation ("Grouped-Query Attention (GQA) and Multi-Query Attention
+ * (MQA): Mathematical Foundations, Arithmetic Intensity, and KV-Cache Scaling
+ * Mechanics", section 2, subsection "Grouped-Query Attention (GQA)"):
+ * H_q query heads are split into H_kv contiguous groups of G = H_q / H_kv;
+ * query head i reads key/value head g = i / G (0-based form of the page's
+ * g(i) = floor((i-1)/R) + 1), and
+ *
+ *     out[b, i, :] = softmax_t( scale * q[b, i, :] . K[b, g, t, :] ) V[b, g, t, :]
+ *
+ * over the cached positions t in [0, seq_lens[b]).  At decode time the single
+ * new query is the last position, so the page's causal mask M admits exactly
+ * those positions.  G = 1 is multi-head attention ("Multi-Head Attention
+ * (MHA)" subsection); H_kv = 1 is multi-query attention ("Multi-Query
+ * Attention (MQA)" subsection).  seq_lens[b] == 0 yields a zero output row.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every tensor pointer is a device pointer owned by the caller; the
+ *   library allocates nothing, keeps no pointer after the call returns and
+ *   has no mutable global state.  All tensors are dense and row-major.
+ *   q, out    : [B][H_q][d]           (per layer, see gqa_decode_layers)
+ *   k_cache,
+ *   v_cache   : [B][H_kv][T_max][d]   (dense layout)
+ *   seq_lens  : [B] int32, device memory; never read by the host.  Values are
+ *               clamped on the device into [0, min(capacity of the sequence,
+ *               seq_len_hint if set, max_seq_len)].
+ *   q, k_cache, v_cache and out must be 16-byte aligned; out must not
+ *   overlap any input.
+ * Types.  q, k_cache and v_cache share dims->dtype (fp32 or bf16); out has
+ *   dims->out_dtype.  Products, softmax and sums are accumulated in fp32; a
+ *   bf16 output is rounded to nearest-even.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *   only enqueue work and return; inputs must stay unchanged, and out is
+ *   valid, once the stream reaches the call.  No host synchronisation.
+ * Workspace.  Split-KV partial results live in a caller-provided device
+ *   workspace of at least gqa_decode_workspace_bytes() bytes, 256-byte
+ *   aligned (may be NULL when that size is 0).  Its first 1 MiB holds
+ *   per-(layer, sequence, KV head) arrival counters and nothing else, for
+ *   every dims: zero-fill the workspace once before its first use; every
+ *   call that completes leaves the counters at zero again, so calls of any
+ *   shape ordered on one stream may share a workspace without clearing it.
+ *   Calls that may overlap in time need separate workspaces.  A call enqueues
+ *   one kernel, or two when the merge of split-KV chunks runs as a separate
+ *   kernel (gqa_merge).
+ * Errors.  Every entry point returns a gqa_status and never throws.  Argument
+ *   errors are detected on the host before anything is enqueued.  Faults
+ *   inside a kernel surface at the next synchronisation, as usual in HIP.
+ * Threads.  Entry points are reentrant and may be called from any thread.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_dtype {
+  GQA_DTYPE_F32 = 0,   /* IEEE binary32 */
+  GQA_DTYPE_BF16 = 1   /* bfloat16: the upper 16 bits of a binary32 */
+} gqa_dtype;
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, H_q % H_kv != 0 */
+  GQA_ERR_UNSUPPORTED = 2,  /* head_dim not 64/128, G > 64, bad dtype pairing */
+  GQA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  GQA_ERR_LAUNCH = 4        /* the HIP runtime refused the launch */
+} gqa_status;
+
+/* Which kernel family runs the step.  AUTO picks the matrix-core kernel for
+ * bf16 inputs and the vector-ALU kernel for fp32 inputs. */
+typedef enum gqa_path {
+  GQA_PATH_AUTO = 0,
+  GQA_PATH_VALU = 1,   /* vector ALU, any supported dtype */
+  GQA_PATH_MFMA = 2    /* matrix cores (v_mfma_f32_16x16x32_bf16), bf16 inputs only */
+} gqa_path;
+
+/* How the partial results of a sequence split over several chunks are
+ * combined.  FUSED: the last workgroup of the (layer, sequence, KV head) to
+ * finish merges them inside the decode kernel (matrix-core path only; the
+ * vector path always uses KERNEL).  KERNEL: a second kernel merges them.
+ * AUTO: KERNEL (the faster of the two on MI355X for the shapes measured).
+ * Shapes with more than 2^18 (layer, sequence, KV head) units always use
+ * KERNEL. */
+typedef enum gqa_merge {
+  GQA_MERGE_AUTO = 0,
+  GQA_MERGE_FUSED = 1,
+  GQA_MERGE_KERNEL = 2
+} gqa_merge;
+
+typedef struct gqa_dims {
+  int32_t batch;         /* B >= 0 (B == 0 is a no-op) */
+  int32_t num_q_heads;   /* H_q >= 1 */
+  int32_t num_kv_heads;  /* H_kv >= 1, divides H_q; G = H_q / H_kv <= 64 */
+  int32_t head_dim;      /* d: 64 or 128 */
+  int32_t max_seq_len;   /* T_max >= 1: rows per (sequence, KV head) of the dense
+                            cache; for a packed cache, an upper bound on every
+                            sequence's capacity */
+  int32_t dtype;         /* gqa_dtype of q, k_cache, v_cache */
+  int32_t out_dtype;     /* gqa_dtype of out */
+  int32_t seq_len_hint;  /* 0, or an upper bound (<= max_seq_len) on every
+                            seq_lens[b]; the split is planned over it and
+                            larger values are clamped to it on the device */
+  int32_t chunk_tokens;  /* 0: the planner chooses the split-KV chunk; otherwise
+                            tokens per chunk, a positive multiple of 64 */
+  int32_t path;          /* gqa_path */
+  int32_t workgroup_waves; /* 0: default; else wavefronts per workgroup of the
+                              matrix-core kernel: 4, 8 or 16 (reduced to 8
+                              when G > 16 and to 4 when G > 32) */
+  int32_t merge;           /* gqa_merge */
+  int32_t tiles_in_flight; /* 0: default; else 16-token tiles each wavefront of
+                              the matrix-core kernel loads before computing
+                              them: 1 or 2 (reduced to 1 where registers do
+                              not allow 2) */
+} gqa_dims;
+
+/*
+ * Bytes of workspace a call with these dims and `num_layers` layers needs
+ * (0 when every sequence fits one chunk).  Pure function of its arguments:
+ * never touches the device.  Returns 0 for invalid dims as well; the decode
+ * call then reports the error.
+ */
+size_t gqa_decode_workspace_bytes(const gqa_dims* dims, int32_t num_layers);
+
+/*
+ * The split-KV plan for these dims: tokens per chunk and the chunk count of
+ * the longest possible sequence.  Returns GQA_OK or GQA_ERR_INVALID_ARG /
+ * GQA_ERR_UNSUPPORTED (outputs untouched then).  Host only.
+ */
+gqa_status gqa_decode_plan(const gqa_dims* dims, int32_t num_layers, int32_t* chunk_tokens,
+                           int32_t* num_chunks);
+
+/*
+ * One decode step of one layer (dense cache [B][H_kv][T_max][d]).
+ * scale multiplies q.K (the page's 1/sqrt(d_k); passed explicitly).
+ */
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                      float scale, void* out, const gqa_dims* dims, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * One decode step of `num_layers` independent layers in a single launch.
+ * Layers share seq_lens; each has its own queries, cache and output:
+ *   q, out     : [L][B][H_q][d]
+ *   kv_offsets : NULL for the dense cache [L][B][H_kv][T_max][d]; otherwise a
+ *                device array of B+1 int64 token offsets (non-decreasing,
+ *                kv_offsets[0] == 0) describing the packed cache: element
+ *                (l, b, h, t, c) sits at
+ *                  l*S + (kv_offsets[b]*H_kv + h*cap_b + t)*d + c,
+ *                cap_b = kv_offsets[b+1] - kv_offsets[b] (<= max_seq_len),
+ *                S = kv_offsets[B]*H_kv*d.  This stores only each sequence's
+ *                own capacity (the logical cache size of "Grouped-Query
+ *                Attention Shares Keys Without Sharing Every Query", without
+ *                padding to T_max).  The dense layout is kv_offsets[b] = b*T_max.
+ * The result equals num_layers separate gqa_decode calls.
+ */
+gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
+                             const int64_t* kv_offsets, const int32_t* seq_lens, float scale, void* out,
+                             const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* gqa_status_string(gqa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

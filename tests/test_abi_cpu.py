@@ -1,0 +1,173 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every
+function include/gqa_decode.h declares, validates arguments before touching
+the device, and plans split-KV chunks as documented.  No kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import gqa_mqa_kv_amd as gqa
+from gqa_mqa_kv_amd import _binding, build, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x100000          # 16-byte aligned stand-in address; never dereferenced on these error paths
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(_binding.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gqa.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", build.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (gqa_\w+)", nm))
+    assert set(declared_functions()) <= exported
+
+
+def test_product_never_links_or_imports_the_oracle():
+    nm = subprocess.run(["nm", "-D", build.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in nm
+    ldd = subprocess.run(["ldd", build.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in ldd
+    pkg = os.path.join(ROOT, "gqa_mqa_kv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".h", ".hip", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "gqa_oracle" not in text and "liboracle" not in text, f
+
+
+def dims(**kw):
+    base = dict(B=2, H_q=8, H_kv=2, d=64, T_max=1024, dtype=torch.bfloat16)
+    base.update({k: v for k, v in kw.items() if k in base})
+    extra = {k: v for k, v in kw.items() if k not in base}
+    return _binding.make_dims(**base, **extra)
+
+
+def call(d, q=FAKE, k=FAKE, v=FAKE, sl=FAKE, out=FAKE, ws=None, ws_bytes=0, scale=0.125):
+    return gqa.lib().gqa_decode(q, k, v, sl, scale, out, ctypes.byref(d), ws, ws_bytes, None)
+
+
+def call_layers(L, d, offs=None, **kw):
+    return gqa.lib().gqa_decode_layers(L, FAKE, FAKE, FAKE, offs, FAKE, 0.125, FAKE, ctypes.byref(d), None, 0, None)
+
+
+def test_status_strings():
+    for code, name in _binding.STATUS.items():
+        assert gqa.status_string(code).startswith(name)
+    assert gqa.status_string(99) == "unknown gqa_status"
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(H_q=8, H_kv=3), INVALID),            # H_q not a multiple of H_kv
+    (dict(H_q=0), INVALID),
+    (dict(H_kv=0), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(T_max=0), INVALID),
+    (dict(d=96), UNSUPPORTED),
+    (dict(d=256), UNSUPPORTED),
+    (dict(H_q=130, H_kv=1), UNSUPPORTED),      # G > 64
+    (dict(dtype=torch.float32, path="mfma"), UNSUPPORTED),
+    (dict(chunk_tokens=100), INVALID),         # not a multiple of 64
+    (dict(chunk_tokens=-64), INVALID),
+    (dict(seq_len_hint=2048), INVALID),        # hint above T_max
+    (dict(waves=2), INVALID),                  # workgroup size not 4, 8 or 16 wavefronts
+    (dict(waves=32), INVALID),
+    (dict(tiles=3), INVALID),                  # tiles in flight not 1 or 2
+    (dict(tiles=-1), INVALID),
+])
+def test_dims_validation(kw, expect):
+    d = dims(**kw)
+    assert call(d) == expect
+    assert gqa.lib().gqa_decode_workspace_bytes(ctypes.byref(d), 1) == 0
+    assert call_layers(3, d) == expect
+
+
+def test_enum_validation():
+    for field in ("dtype", "out_dtype", "path", "merge"):
+        d = dims()
+        setattr(d, field, 7)
+        assert call(d) == INVALID, field
+
+
+def test_null_and_misaligned_pointers():
+    d = dims()
+    assert gqa.lib().gqa_decode(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, 0, None) == INVALID
+    for pos in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[pos] = None
+        assert call(d, *ptrs) == INVALID, pos
+        ptrs[pos] = FAKE + 2          # misaligned
+        assert call(d, *ptrs) == INVALID, pos
+    assert call(d, scale=float("nan")) == INVALID
+    assert call(d, scale=float("inf")) == INVALID
+    assert gqa.lib().gqa_decode_layers(2, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 0.1, FAKE, ctypes.byref(d), None, 0,
+                                       None) == INVALID     # kv_offsets not 8-byte aligned
+    assert call_layers(0, d) == INVALID
+
+
+def test_empty_batch_is_a_noop():
+    d = dims(B=0)
+    assert gqa.lib().gqa_decode(None, None, None, None, 0.1, None, ctypes.byref(d), None, 0, None) == OK
+
+
+def test_workspace_checked_before_launch():
+    d = dims(T_max=4096, chunk_tokens=256)
+    need = gqa.workspace_bytes(d)
+    assert need > 0
+    assert call(d) == WORKSPACE
+    assert call(d, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    assert call(d, ws=FAKE + 128, ws_bytes=need) == WORKSPACE   # not 256-byte aligned
+
+
+def test_workspace_size_formula():
+    d = dims(B=3, H_q=32, H_kv=4, d=128, T_max=5000, chunk_tokens=512)
+    chunk, n = gqa.plan(d)
+    assert (chunk, n) == (512, 10)
+    units, G = 3 * 4, 8
+    up = lambda x: (x + 255) // 256 * 256
+    assert gqa.workspace_bytes(d) == (1 << 20) + up(units * n * G * 2 * 4) + units * n * G * 128 * 4
+    assert gqa.workspace_bytes(d, 5) > gqa.workspace_bytes(d, 1)
+    assert gqa.workspace_bytes(dims(T_max=256, chunk_tokens=256)) == 0   # one chunk: no partial state
+
+
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
+def test_plan_covers_the_sequence(name):
+    w = workloads.WORKLOADS[name]
+    d = _binding.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype)
+    chunk, n = gqa.plan(d, w.layers)
+    assert chunk % 64 == 0 and chunk >= 256
+    assert n * chunk >= w.T_max > (n - 1) * chunk
+    units = w.layers * w.B * w.H_kv
+    assert units * n >= 256 or n * chunk <= 512   # enough workgroups for 256 CUs unless the sequence is short
+    hinted = _binding.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype, seq_len_hint=w.seq_lo)
+    c2, n2 = gqa.plan(hinted, w.layers)
+    assert n2 * c2 >= w.seq_lo and n2 <= n
+
+
+def test_library_missing_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding._build, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.lib()
+
+
+def test_binding_validates_tensors_on_cpu():
+    x = torch.zeros(1, 8, 64)
+    with pytest.raises((ValueError, TypeError)):
+        gqa.decode(x, torch.zeros(1, 2, 16, 64), torch.zeros(1, 2, 16, 64), torch.zeros(1, dtype=torch.int64), 0.1)

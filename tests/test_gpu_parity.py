@@ -1,0 +1,358 @@
+"""GPU path vs the fp64 CPU oracle, element by element, through the C ABI.
+
+Bars (written here, derived in the design notes):
+  * fp32 inputs: max |gpu - oracle| <= 1e-5.
+  * bf16 inputs, fp32 accumulation, fp32 output: max |gpu - oracle| <= 2e-3.
+  * bf16 output: bitwise equal to the fp32 output of the same call rounded to
+    nearest-even (the kernels differ only in the final store), so it is the
+    correctly rounded value of a result that meets the bar above.
+Every input is seeded; padding positions of dense caches hold NaN so that a
+read past seq_len shows up as a NaN output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_mqa_kv_amd as gqa
+import oracle
+from gqa_mqa_kv_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-3}
+
+
+def note(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def to_dev(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def small(B, H_q, H_kv, d, T, seed, dtype=torch.bfloat16, lo=None, poison=True):
+    w = workloads.Workload("case", B, H_q, H_kv, d, lo if lo is not None else T, T, dtype, seed)
+    return workloads.generate(w, "cpu", poison_padding=poison)
+
+
+def seed_of(shape, salt):
+    return sum((j + 1) * (v or 0) for j, v in enumerate(shape)) * 31 + salt
+
+
+def gpu_decode(x, **kw):
+    xd = to_dev(x)
+    out = gqa.decode(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def err(out, ref):
+    o = out.double().cpu().numpy()
+    assert np.isfinite(o).all(), "non-finite output"
+    return float(np.abs(o - ref).max())
+
+
+def check(x, tol=None, label="", **kw):
+    dt = x["q"].dtype
+    tol = TOL[dt] if tol is None else tol
+    ref = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+    note(label, tuple(x["q"].shape), tuple(x["k"].shape), dt, kw)
+    out32 = gpu_decode(x, out_dtype=torch.float32, **kw)
+    e = err(out32, ref)
+    assert e <= tol, "%s: max err %.3e > %.1e" % (label, e, tol)
+    if dt == torch.bfloat16:
+        out16 = gpu_decode(x, out_dtype=torch.bfloat16, **kw)
+        assert torch.equal(out16.cpu(), out32.cpu().to(torch.bfloat16)), "bf16 out is not RNE(fp32 out)"
+    return e
+
+
+# ------------------------------------------------------------ small shapes --
+SHAPES = [
+    # B, H_q, H_kv, d, T_max, lo     (lo < T_max: ragged lengths U[lo, T_max])
+    (1, 8, 2, 64, 128, None),        # the tiny fp32 workload's shape
+    (3, 8, 8, 64, 300, 1),           # MHA, ragged, d=64
+    (2, 32, 8, 128, 1000, 200),      # Llama-3-8B grouping, several chunks, ragged tail
+    (2, 64, 8, 128, 777, 1),         # G = 8
+    (2, 16, 1, 128, 520, 33),        # MQA, G = 16
+    (2, 32, 1, 128, 600, 100),       # MQA, G = 32 (two head blocks)
+    (1, 64, 1, 128, 450, None),      # G = 64 (four head blocks)
+    (2, 12, 4, 128, 333, 10),        # G = 3 (partial head block)
+    (2, 40, 1, 64, 257, 1),          # G = 40, d = 64
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_Hq%d_Hkv%d_d%d_T%d" % s[:5])
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+@pytest.mark.parametrize("chunk", [0, 256])
+def test_small_bf16(shape, path, chunk):
+    B, hq, hkv, d, T, lo = shape
+    x = small(B, hq, hkv, d, T, seed=seed_of(shape, 17), lo=lo)
+    check(x, path=path, chunk_tokens=chunk, label="small-bf16")
+
+
+@pytest.mark.parametrize("shape", SHAPES[:5], ids=lambda s: "B%d_Hq%d_Hkv%d_d%d_T%d" % s[:5])
+@pytest.mark.parametrize("chunk", [0, 128])
+def test_small_fp32(shape, chunk):
+    B, hq, hkv, d, T, lo = shape
+    x = small(B, hq, hkv, d, T, seed=seed_of(shape, 23), dtype=torch.float32, lo=lo)
+    check(x, chunk_tokens=chunk, label="small-fp32")
+
+
+def test_tiny_workload():
+    w = workloads.WORKLOADS["tiny-gqa-fp32"]
+    x = workloads.generate(w, "cpu")
+    check(x, label=w.name)
+    check(x, label=w.name, chunk_tokens=64)
+
+
+# --------------------------------------------------------------- edge cases --
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_empty_and_single_token(path):
+    x = small(4, 16, 4, 128, 300, seed=5)
+    x["seq_lens"] = torch.tensor([0, 1, 0, 257], dtype=torch.int32)
+    for b, n in enumerate([0, 1, 0, 257]):
+        x["k"][b, :, n:] = float("nan")
+        x["v"][b, :, n:] = float("nan")
+    check(x, path=path, chunk_tokens=128, label="empty+single")
+    out = gpu_decode(x, path=path, out_dtype=torch.bfloat16).cpu()
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    # one cached token: weight 1, output = V exactly (also in bf16)
+    for i in range(16):
+        assert torch.equal(out[1, i], x["v"][1, i // 4, 0])
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_spike_at_tile_and_chunk_edges(path, dtype):
+    """Give one token per sequence all the weight; its position walks over
+    tile (32) and chunk (256) boundaries and the ragged end.  A dropped or
+    duplicated token there is an O(1) error, not a 2e-3 one."""
+    if path == "mfma" and dtype == torch.float32:
+        pytest.skip("matrix-core path takes bf16 only")
+    chunk, n = 256, 700
+    pos = [0, 1, 31, 32, 33, 63, 64, 255, 256, 257, 511, 512, 600, 671, 672, 699]
+    B, hq, hkv, d = len(pos), 8, 2, 128
+    x = small(B, hq, hkv, d, n, seed=77, dtype=dtype)
+    x["q"].zero_()
+    x["q"][:, :, 0] = 8.0
+    for b, t in enumerate(pos):
+        x["k"][b, :, t, :] = 0.0
+        x["k"][b, :, t, 0] = 64.0            # score 8*64/sqrt(128) = 45 vs <= ~3.5 elsewhere
+    out = gpu_decode(x, path=path, chunk_tokens=chunk, out_dtype=dtype).cpu()
+    for b, t in enumerate(pos):
+        want = x["v"][b, :, t, :].repeat_interleave(hq // hkv, dim=0)
+        if dtype == torch.bfloat16:
+            assert torch.equal(out[b], want), "spike at %d" % t
+        else:
+            assert (out[b] - want).abs().max() < 1e-6, "spike at %d" % t
+
+
+def test_seq_lens_beyond_capacity_are_clamped():
+    x = small(2, 8, 2, 64, 200, seed=9, poison=False)
+    sl = torch.tensor([500, 37], dtype=torch.int32)
+    xd = to_dev(x)
+    out = gqa.decode(xd["q"], xd["k"], xd["v"], sl.to(DEV), x["scale"], out_dtype=torch.float32)
+    ref = oracle.decode(x["q"], x["k"], x["v"], torch.tensor([200, 37], dtype=torch.int32), x["scale"])
+    assert err(out, ref) <= 2e-3
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_deterministic_and_workspace_reuse(path):
+    """Bitwise identical results run to run, also with a different-shaped call
+    sharing the workspace in between."""
+    x = small(3, 32, 8, 128, 2000, seed=31, lo=900)
+    y = small(2, 8, 1, 128, 1500, seed=32, lo=1)
+    a = gpu_decode(x, path=path, chunk_tokens=256).cpu()
+    gpu_decode(y, path=path, chunk_tokens=128)
+    b = gpu_decode(x, path=path, chunk_tokens=256).cpu()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("shape", [SHAPES[2], SHAPES[3], SHAPES[5], SHAPES[8], (3, 32, 8, 128, 4000, 1)],
+                         ids=lambda s: "B%d_Hq%d_Hkv%d_d%d_T%d" % s[:5])
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+@pytest.mark.parametrize("waves,tiles", [(4, 1), (4, 2), (8, 1), (8, 2), (16, 1)])
+def test_kernel_variants(shape, merge, waves, tiles):
+    """Every instantiated matrix-core variant (workgroup size, tiles in flight)
+    and both ways of combining split-KV chunks (last-arriving workgroup inside
+    the decode kernel, or a separate merge kernel)."""
+    B, hq, hkv, d, T, lo = shape
+    x = small(B, hq, hkv, d, T, seed=seed_of(shape, 29), lo=lo)
+    check(x, path="mfma", chunk_tokens=128 * tiles, merge=merge, waves=waves, tiles=tiles, label="variant-" + merge)
+
+
+def test_workspace_shared_across_shapes():
+    """Differently shaped calls, fused and separate merges, one workspace in
+    stream order: every result stays correct."""
+    cases = [small(3, 32, 8, 128, 900, seed=61, lo=100), small(2, 64, 8, 128, 2000, seed=62, lo=1500),
+             small(5, 16, 2, 64, 700, seed=63, lo=1)]
+    refs = [oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"]) for x in cases]
+    for rep in range(3):
+        for x, ref, merge in zip(cases, refs, ["fused", "kernel", "fused"]):
+            out = gpu_decode(x, path="mfma", chunk_tokens=64 * (rep + 2), merge=merge, out_dtype=torch.float32)
+            assert err(out, ref) <= 2e-3
+
+
+def test_fused_merge_repeats_bitwise():
+    """The fused merge leaves its arrival counters at zero: many calls in a
+    row, on one workspace, give the same bits."""
+    x = small(4, 32, 8, 128, 3000, seed=33, lo=100)
+    first = gpu_decode(x, path="mfma", chunk_tokens=128, merge="fused").cpu()
+    for _ in range(20):
+        assert torch.equal(gpu_decode(x, path="mfma", chunk_tokens=128, merge="fused").cpu(), first)
+
+
+def test_paths_and_chunkings_agree():
+    x = small(2, 32, 8, 128, 1500, seed=41, lo=1000)
+    ref = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+    for path in ("mfma", "valu"):
+        for chunk in (0, 64, 128, 1024, 1536):
+            assert err(gpu_decode(x, path=path, chunk_tokens=chunk, out_dtype=torch.float32), ref) <= 2e-3
+
+
+def test_explicit_stream_and_workspace():
+    x = small(2, 32, 8, 128, 1200, seed=43)
+    xd = to_dev(x)
+    dims = gqa.make_dims(2, 32, 8, 128, 1200, torch.bfloat16, torch.float32, chunk_tokens=256)
+    ws = torch.zeros(gqa.workspace_bytes(dims), dtype=torch.uint8, device=DEV)   # zero-filled once, as required
+    s = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(s):
+        out = gqa.decode(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], out_dtype=torch.float32,
+                         chunk_tokens=256, workspace=ws)
+    s.synchronize()
+    ref = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+    assert err(out, ref) <= 2e-3
+    assert int(ws[:1 << 20].view(torch.int32).abs().sum()) == 0   # arrival counters back at zero
+
+
+# ------------------------------------------------------------ layer batches --
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_layers(packed, path):
+    w = workloads.Workload("layers", 3, 32, 8, 128, 100, 900, torch.bfloat16, 51, layers=4, packed=packed)
+    x = workloads.generate(w, "cpu", poison_padding=True)
+    xd = to_dev(x)
+    note("layers", packed, path)
+    kw = dict(kv_offsets=xd["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if packed else {}
+    out = gqa.decode_layers(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], out_dtype=torch.float32,
+                            path=path, chunk_tokens=256, **kw)
+    torch.cuda.synchronize()
+    for l in range(w.layers):
+        xl = workloads.layer_view(x, l)
+        ref = oracle.decode(xl["q"], xl["k"], xl["v"], x["seq_lens"], x["scale"],
+                            kv_offsets=x["kv_offsets"].numpy() if packed else None, num_kv_heads=w.H_kv)
+        assert err(out[l], ref) <= 2e-3, l
+
+
+# -------------------------------------------------------- full-size loads --
+def sample_heads(B, H_q, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    ids = torch.randperm(B * H_q, generator=g)[:n]
+    return sorted(set(ids.tolist()) | {0, B * H_q - 1})
+
+
+def full_check(name, sample=None, dtype=None, path="auto", extra_tol=None):
+    w = workloads.WORKLOADS[name]
+    if dtype is not None:
+        w = w.replace(dtype=dtype)
+    note("full", w.name, w.dtype, "generate")
+    x = workloads.generate(w, DEV, poison_padding=True)
+    note("full", w.name, "decode")
+    out32 = gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], out_dtype=torch.float32, path=path)
+    out16 = None
+    if w.dtype == torch.bfloat16:
+        out16 = gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], out_dtype=torch.bfloat16, path=path)
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype] if extra_tol is None else extra_tol
+    if out16 is not None:
+        assert torch.equal(out16, out32.to(torch.bfloat16))
+    if sample is None:
+        note("full", w.name, "oracle on every head")
+        xc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+        ref = oracle.decode(xc["q"], xc["k"], xc["v"], xc["seq_lens"], w.scale)
+        e = err(out32, ref)
+    else:
+        heads = sample_heads(w.B, w.H_q, sample, 99)
+        note("full", w.name, "oracle on %d sampled heads" % len(heads))
+        e = 0.0
+        for hid in heads:
+            b, i = divmod(hid, w.H_q)
+            g = i // w.G
+            n = int(x["seq_lens"][b])
+            q1 = x["q"][b:b + 1, i:i + 1].cpu()
+            k1 = x["k"][b:b + 1, g:g + 1, :n].cpu()
+            v1 = x["v"][b:b + 1, g:g + 1, :n].cpu()
+            ref = oracle.decode(q1, k1, v1, torch.tensor([n], dtype=torch.int32), w.scale)[0, 0]
+            e = max(e, err(out32[b, i], ref))
+    note("full", w.name, "max err %.3e" % e)
+    assert e <= tol
+    return e
+
+
+@pytest.mark.timeout(600)
+def test_full_llama3_8b_layer():
+    full_check("llama3-8b-layer")
+
+
+@pytest.mark.timeout(600)
+def test_full_llama3_8b_layer_fp32_inputs():
+    """fp32 copy of the same shape at the fp32 bar: one dropped token at
+    T = 4096 moves an output by ~1e-3, two orders above 1e-5."""
+    full_check("llama3-8b-layer", dtype=torch.float32, path="valu")
+
+
+@pytest.mark.timeout(600)
+def test_full_70b_ragged_layer():
+    full_check("llama-70b-ragged-layer")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["grouping-sweep-mha", "grouping-sweep-gqa", "grouping-sweep-mqa"])
+def test_full_grouping_sweep(name):
+    full_check(name, sample=48)
+
+
+@pytest.mark.timeout(600)
+def test_full_grouping_sweep_mqa_fp32_inputs():
+    full_check("grouping-sweep-mqa", sample=24, dtype=torch.float32, path="valu")
+
+
+@pytest.mark.timeout(900)
+def test_full_32_layer_stack():
+    """The 32-layer packed stack at full size (about 155 GB of cache), one
+    launch; outputs checked on sampled (layer, sequence, head) triples."""
+    w = workloads.WORKLOADS["llama3-8b-32-layer-stack"]
+    torch.cuda.empty_cache()
+    free, total = torch.cuda.mem_get_info(DEV)
+    sl = workloads.seq_lens_for(w)
+    need = 2 * w.layers * int(sl.sum()) * w.H_kv * w.d * 2
+    if need > free - (8 << 30):
+        pytest.skip("needs %.1f GB of device memory, %.1f free" % (need / 1e9, free / 1e9))
+    note("full", w.name, "generate %.1f GB" % (need / 1e9))
+    x = workloads.generate(w, DEV)
+    note("full", w.name, "decode")
+    out = gqa.decode_layers(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], kv_offsets=x["kv_offsets"],
+                            max_seq_len=w.T_max, num_kv_heads=w.H_kv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    off = x["kv_offsets"].cpu()
+    rows_per_layer = int(off[-1]) * w.H_kv
+    g = torch.Generator().manual_seed(5)
+    e = 0.0
+    for _ in range(24):
+        l = int(torch.randint(w.layers, (1,), generator=g))
+        b = int(torch.randint(w.B, (1,), generator=g))
+        i = int(torch.randint(w.H_q, (1,), generator=g))
+        kv = i // w.G
+        n = int(x["seq_lens"][b])
+        cap = int(off[b + 1] - off[b])
+        r0 = l * rows_per_layer + int(off[b]) * w.H_kv + kv * cap
+        k1 = x["k"][r0:r0 + n].cpu().view(1, 1, n, w.d)
+        v1 = x["v"][r0:r0 + n].cpu().view(1, 1, n, w.d)
+        q1 = x["q"][l, b:b + 1, i:i + 1].cpu()
+        ref = oracle.decode(q1, k1, v1, torch.tensor([n], dtype=torch.int32), w.scale)[0, 0]
+        e = max(e, err(out[l, b, i], ref))
+    note("full", w.name, "max err %.3e" % e)
+    assert e <= 2e-3
+    del x
+    torch.cuda.empty_cache()
