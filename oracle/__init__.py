@@ -69,7 +69,13 @@ class Oracle:
         lib.oracle_gqa_head_weights.restype = ctypes.c_int
         lib.oracle_gqa_head_weights.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp,
                                                 dbl, i64, i64, vp, vp]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
         self._lib = lib
+
+    def num_threads(self) -> int:
+        """Threads the oracle's OpenMP loops run on."""
+        return int(self._lib.oracle_num_threads())
 
     # -- head -> group map -------------------------------------------------
     def group_of(self, i: int, R: int) -> int:

@@ -39,6 +39,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
 
@@ -183,4 +186,13 @@ int oracle_gqa_head_weights(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int
                         oracle_group_of(i, H_q / H_kv), n, scale, s, w, out);
   free(s);
   return rc;
+}
+
+/* Threads the oracle's parallel loops use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
