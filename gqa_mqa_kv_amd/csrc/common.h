@@ -10,11 +10,14 @@
 // maximum m of its scores (base-2 domain), the sum l of 2^(s - m) and the
 // un-normalised sum O of 2^(s - m) * V.  A unit with one chunk writes
 // O / l straight to the output.  Otherwise every chunk stores its state in the
-// workspace and the states are combined in chunk order, which keeps the
-// result deterministic, either by the unit's last workgroup to finish (fused
-// merge, below) or by a second small kernel launched behind the first on the
-// same stream (the kernel boundary then makes the states visible):
+// workspace and a second, small kernel launched behind the first on the same
+// stream (the kernel boundary makes the states visible) combines them in
+// chunk order, which keeps the result deterministic:
 //   M = max_k m_k,  out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k.
+//
+// The matrix-core path splits the work differently ("token split", below):
+// all valid tokens of all units, in (layer, sequence, KV head, token) order,
+// form one stream that is cut into equal spans, one per workgroup.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,7 +25,8 @@
 
 namespace gqa {
 
-constexpr int kMaxGroup = 64;   // largest G = H_q / H_kv supported
+constexpr int kMaxGroup = 64;    // largest G = H_q / H_kv supported
+constexpr int kMaxBatch = 4096;  // sequences per call on the token-split path (prefix sums live in LDS)
 
 struct Problem {
   const void* q;              // [L][B][H_q][D]
@@ -31,13 +35,15 @@ struct Problem {
   void* out;                  // [L][B][H_q][D]
   const int64_t* kv_offsets;  // [B+1] or nullptr (dense)
   const int32_t* seq_lens;    // [B]
-  float* ws_ml;               // [units][n_chunks][G][2]   (m, l)
-  float* ws_o;                // [units][n_chunks][G][D]
-  int32_t* ws_cnt;            // [units] arrival counters of the fused merge (zero between calls)
-  int32_t fused_merge;        // 1: the last-arriving workgroup of a unit merges; 0: separate kernel
+  float* ws_ml;               // partial states (m, l): chunk path [units][n_chunks][G][2],
+                              //   token-split path [groups][2][G][2]
+  float* ws_o;                // partial O: [units][n_chunks][G][D] or [groups][2][G][D]
+  int64_t* ws_desc;           // token-split path: [groups][4] merge descriptors
   int32_t B, H_q, H_kv, G, T_max, L;
   int32_t T_cap;              // planned bound on valid tokens (seq_len_hint, else T_max)
-  int32_t chunk, n_chunks;
+  int32_t chunk, n_chunks;    // chunk path: tokens per chunk, chunks of the longest sequence
+  int32_t groups;             // token-split path: decode workgroups launched
+  int32_t span;               // token-split path: tokens per workgroup (0: balanced split)
   int32_t out_bf16;
   float scale_log2;           // scale * log2(e): scores are kept in base 2
 };
@@ -98,57 +104,6 @@ __device__ __forceinline__ void store_out(const Problem& p, int64_t row, int c, 
     reinterpret_cast<float*>(p.out)[row * D + c] = val;
 }
 
-// Agent-coherent 32-bit accesses (global_load/store with sc1 on gfx950): the
-// chunk states of the fused merge travel through these, so they bypass the
-// per-XCD L2s that are not coherent with each other for ordinary accesses.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Fused merge, called by every thread of a workgroup that has published its
-// chunk state with store_coherent (thread 0 of the publishing wavefront
-// passes publisher = true).  Publishing order: the state's agent-coherent
-// stores complete (s_waitcnt), then the unit's arrival counter is bumped with
-// an agent-scope atomic.  The workgroup that brings the count to nck reads
-// every chunk state back with agent-coherent loads, in chunk order, writes
-// the output, and returns the counter to zero for the next call.
-template <int D, int NT>
-__device__ void fused_merge(const Problem& p, int unit, const UnitInfo& ui, int nck, bool publisher, int* sm_flag) {
-  if (publisher) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's coherent stores have completed
-    const int prev = __hip_atomic_fetch_add(p.ws_cnt + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *sm_flag = (prev == nck - 1);
-  }
-  __syncthreads();
-  if (!*sm_flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const int G = p.G;
-  const float* ml = p.ws_ml + (int64_t)unit * p.n_chunks * G * 2;
-  const float* o = p.ws_o + (int64_t)unit * p.n_chunks * G * D;
-  const int64_t orow = out_row0(p, ui);
-  for (int e = threadIdx.x; e < G * D; e += NT) {
-    const int h = e / D, c = e % D;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < nck; ++k) {
-      const float mk = load_coherent(ml + ((int64_t)k * G + h) * 2);
-      const float lk = load_coherent(ml + ((int64_t)k * G + h) * 2 + 1);
-      const float ok = load_coherent(o + ((int64_t)k * G + h) * D + c);
-      const float Mn = fmaxf(M, mk);
-      const float a = exp2f(M - Mn), f = exp2f(mk - Mn);
-      num = num * a + f * ok;
-      den = den * a + f * lk;
-      M = Mn;
-    }
-    store_out(p, orow + h, c, D, den > 0.f ? num / den : 0.f);
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(p.ws_cnt + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Combine the chunk states of every unit that needed more than one chunk.
 // One workgroup of 256 threads per (unit, 256/D heads); thread -> (head, column).
 template <int D>
@@ -178,6 +133,181 @@ __global__ __launch_bounds__(256) void gqa_merge_chunks(Problem p) {
     M = Mn;
   }
   store_out(p, out_row0(p, ui) + h, c, D, den > 0.f ? num / den : 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// Token split.  Sequence b contributes n_b valid tokens to each of its H_kv
+// units per layer; with P the exclusive prefix sums of n_b, the stream
+// position of token t of unit (l, b, g) is
+//     l * H_kv * P[B]  +  H_kv * P[b]  +  g * n_b  +  t.
+// Workgroup w owns positions [w * span, (w + 1) * span); every unit that lies
+// inside one span is finished by that workgroup, and only the first and the
+// last unit piece of a span can be partial (state slots 2w and 2w + 1; a
+// piece covering a whole span uses slot 2w).
+
+// Exclusive prefix sums of the clamped lengths into sm_P[0..B] (all threads of
+// the workgroup take part; B <= kMaxBatch).  sm_wave holds NT/64 ints.
+template <int NT>
+__device__ void build_prefix(const Problem& p, int32_t* sm_P, int32_t* sm_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = p.B;
+  const int E = (B + NT - 1) / NT;   // entries per thread, contiguous
+  const int b0 = tid * E;
+  int local = 0;
+  for (int b = b0; b < b0 + E && b < B; ++b) {
+    int64_t cap = p.kv_offsets ? p.kv_offsets[b + 1] - p.kv_offsets[b] : (int64_t)p.T_max;
+    if (cap > p.T_cap) cap = p.T_cap;
+    int64_t n = p.seq_lens[b];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    sm_P[b] = (int32_t)n;
+    local += (int32_t)n;
+  }
+  int v = local;   // inclusive scan of the per-thread totals within the wavefront
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  if (lane == 63) sm_wave[wave] = v;
+  __syncthreads();
+  int run = v - local;
+  for (int w = 0; w < wave; ++w) run += sm_wave[w];
+  for (int b = b0; b < b0 + E && b < B; ++b) {
+    const int n = sm_P[b];
+    sm_P[b] = run;
+    run += n;
+  }
+  if (b0 < B && b0 + E >= B) sm_P[B] = run;   // the thread holding the last entry writes the total
+  __syncthreads();
+}
+
+// Values every lane of a wavefront holds alike (read back from LDS, so the
+// compiler cannot tell) moved to scalar registers.
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+struct TokenSpace {
+  int64_t per_layer;   // H_kv * P[B]
+  int64_t total;       // L * per_layer
+  int64_t span;        // positions per workgroup, a multiple of 16
+};
+
+__device__ __forceinline__ TokenSpace token_space(const Problem& p, const int32_t* sm_P) {
+  TokenSpace ts;
+  ts.per_layer = (int64_t)p.H_kv * uniform(sm_P[p.B]);
+  ts.total = ts.per_layer * p.L;
+  if (p.span > 0) {
+    ts.span = p.span;
+  } else {
+    const int64_t s = (ts.total + p.groups - 1) / p.groups;
+    ts.span = (s + 15) / 16 * 16;
+    if (ts.span == 0) ts.span = 16;
+  }
+  return ts;
+}
+
+struct Piece {
+  UnitInfo ui;     // row0, n, l, b, g of the unit holding the position
+  int64_t start;   // stream position of the unit's token 0
+  int t;           // token of the unit at the located position
+};
+
+// The unit holding stream position x (0 <= x < total).
+__device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, const TokenSpace& ts, int64_t x) {
+  Piece pc;
+  const int l = (int)(x / ts.per_layer);
+  const int64_t r = x - (int64_t)l * ts.per_layer;
+  int lo = 0, hi = p.B - 1;   // largest b with H_kv * P[b] <= r (such b holds tokens)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)p.H_kv * uniform(sm_P[mid]) <= r) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int32_t pb = uniform(sm_P[b]);
+  const int n = uniform(sm_P[b + 1]) - pb;
+  const int64_t r2 = r - (int64_t)p.H_kv * pb;
+  const int g = (int)(r2 / n);
+  pc.t = (int)(r2 - (int64_t)g * n);
+  pc.start = x - pc.t;
+  pc.ui.l = l;
+  pc.ui.b = b;
+  pc.ui.g = g;
+  pc.ui.n = n;
+  if (p.kv_offsets) {
+    const int64_t o0 = p.kv_offsets[b], cap = p.kv_offsets[b + 1] - o0;
+    pc.ui.row0 = (int64_t)l * p.kv_offsets[p.B] * p.H_kv + o0 * p.H_kv + (int64_t)g * cap;
+  } else {
+    pc.ui.row0 = ((int64_t)(l * p.B + b) * p.H_kv + g) * p.T_max;
+  }
+  return pc;
+}
+
+// Zero the outputs of sequences with no valid token (every layer), spread
+// over the workgroups of a launch.
+template <int D, int NT>
+__device__ void zero_empty_sequences(const Problem& p, const int32_t* sm_P, int wg, int n_wg) {
+  for (int lb = wg; lb < p.L * p.B; lb += n_wg) {
+    const int b = lb % p.B;
+    if (sm_P[b + 1] != sm_P[b]) continue;
+    const int64_t row = (int64_t)lb * p.H_q;
+    for (int e = threadIdx.x; e < p.H_q * D; e += NT) store_out(p, row + e / D, e % D, D, 0.f);
+  }
+}
+
+// Merge descriptor written by decode workgroup m for the merge kernel:
+//   {w0, w_last, output row of the unit's first head, first piece slot}
+// when m's span starts inside a unit that began in an earlier span (w0 < m is
+// the workgroup holding the unit's first token, w_last the one holding its
+// last), else w0 = -1.  The workgroups w0+1 .. w_last of such a unit share
+// its merge.
+__device__ __forceinline__ void write_merge_desc(const Problem& p, const int32_t* sm_P, const TokenSpace& ts, int m) {
+  int64_t d[4] = {-1, -1, 0, 0};
+  const int64_t s0 = (int64_t)m * ts.span;
+  if (s0 < ts.total) {
+    const Piece pc = locate(p, sm_P, ts, s0);
+    if (pc.t > 0) {
+      d[0] = pc.start / ts.span;
+      d[1] = (pc.start + pc.ui.n - 1) / ts.span;
+      d[2] = out_row0(p, pc.ui);
+      d[3] = 2 * d[0] + (pc.start != d[0] * ts.span ? 1 : 0);   // the first piece is w0's last one unless
+                                                                 // the unit starts w0's span
+    }
+  }
+  if (threadIdx.x < 4) p.ws_desc[4 * (int64_t)m + threadIdx.x] = d[threadIdx.x];
+}
+
+// Merge of the token-split path: one workgroup of 256 threads per decode
+// workgroup m.  Helper h = m - w0 - 1 of the H = w_last - w0 helpers of a unit
+// combines, for output elements e = h, h + H, ..., the unit's pieces in order.
+template <int D>
+__global__ __launch_bounds__(256) void gqa_merge_spans(Problem p) {
+  constexpr int NT = 256;
+  const int m = blockIdx.x;
+  const int64_t* dsc = p.ws_desc + 4 * (int64_t)m;
+  const int64_t w0 = dsc[0];
+  if (w0 < 0) return;
+  const int64_t w_last = dsc[1], orow = dsc[2], first_slot = dsc[3];
+  const int G = p.G;
+  const int H = (int)(w_last - w0), h = (int)(m - w0 - 1);
+  for (int e = h + H * (int)threadIdx.x; e < G * D; e += H * NT) {
+    const int hd = e / D, c = e % D;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int64_t w = w0; w <= w_last; ++w) {
+      const int64_t slot = w == w0 ? first_slot : 2 * w;
+      const float mk = p.ws_ml[(slot * G + hd) * 2], lk = p.ws_ml[(slot * G + hd) * 2 + 1];
+      const float ok = p.ws_o[(slot * G + hd) * D + c];
+      const float Mn = fmaxf(M, mk);
+      const float a = exp2f(M - Mn), f = exp2f(mk - Mn);   // M = -inf on the first piece: a = 0
+      num = num * a + f * ok;
+      den = den * a + f * lk;
+      M = Mn;
+    }
+    store_out(p, orow + hd, c, D, den > 0.f ? num / den : 0.f);
+  }
 }
 
 }  // namespace gqa

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -13,13 +14,37 @@
 
 namespace {
 
+// Vector-ALU path: sequences are cut into chunks of a planned size.
 constexpr int kTargetWorkgroups = 256;    // one per CU on a 256-CU part
-constexpr int kMinChunk = 256;            // at least one 32-token tile per wavefront of an 8-wave group
+constexpr int kMinChunk = 256;            // at least one 32-token tile per wavefront
 constexpr int kMaxChunk = 8192;           // bounds the longest workgroup (tail of ragged batches)
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (queried once per device; 256, the
+// MI355X count, when no device answers, e.g. in a build environment).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int max_waves(int hb);
+int max_tiles(int hb, int waves);
+int resident_groups_per_cu(const gqa_dims* d, int waves, int tiles);
+
+bool use_mfma(const gqa_dims* d) {
+  if (d->path == GQA_PATH_MFMA) return true;
+  return d->path == GQA_PATH_AUTO && d->dtype == GQA_DTYPE_BF16 && d->batch <= gqa::kMaxBatch;
+}
 
 gqa_status check_dims(const gqa_dims* d, int32_t L) {
   if (!d) return GQA_ERR_INVALID_ARG;
@@ -31,83 +56,84 @@ gqa_status check_dims(const gqa_dims* d, int32_t L) {
   if (d->seq_len_hint < 0 || d->seq_len_hint > d->max_seq_len) return GQA_ERR_INVALID_ARG;
   if (d->chunk_tokens < 0 || d->chunk_tokens % 64 != 0) return GQA_ERR_INVALID_ARG;
   if (d->path != GQA_PATH_AUTO && d->path != GQA_PATH_VALU && d->path != GQA_PATH_MFMA) return GQA_ERR_INVALID_ARG;
-  if (d->merge != GQA_MERGE_AUTO && d->merge != GQA_MERGE_FUSED && d->merge != GQA_MERGE_KERNEL)
-    return GQA_ERR_INVALID_ARG;
-  if (d->tiles_in_flight < 0 || d->tiles_in_flight > 2) return GQA_ERR_INVALID_ARG;
   if (d->workgroup_waves != 0 && d->workgroup_waves != 4 && d->workgroup_waves != 8 && d->workgroup_waves != 16)
     return GQA_ERR_INVALID_ARG;
+  if (d->tiles_in_flight < 0 || d->tiles_in_flight > 2) return GQA_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return GQA_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads > gqa::kMaxGroup) return GQA_ERR_UNSUPPORTED;
-  if (d->path == GQA_PATH_MFMA && d->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
-  // Grid and index ranges: units * chunks must fit a 32-bit grid.
+  if (d->path == GQA_PATH_MFMA && (d->dtype != GQA_DTYPE_BF16 || d->batch > gqa::kMaxBatch))
+    return GQA_ERR_UNSUPPORTED;
+  const int64_t T = d->seq_len_hint > 0 ? d->seq_len_hint : d->max_seq_len;
+  if ((int64_t)d->batch * T > INT32_MAX) return GQA_ERR_UNSUPPORTED;   // prefix sums are 32-bit
   const int64_t units = (int64_t)L * d->batch * d->num_kv_heads;
   if (units > INT32_MAX) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 
-int max_waves(int hb);
-int max_tiles(int hb, int waves);
-
-bool use_mfma(const gqa_dims* d) {
-  return d->path == GQA_PATH_MFMA || (d->path == GQA_PATH_AUTO && d->dtype == GQA_DTYPE_BF16);
-}
-
 struct Plan {
-  int32_t chunk, n_chunks, waves, tiles;
-  bool fused;
+  bool mfma;
+  int32_t waves, tiles;
+  int32_t chunk, n_chunks;   // vector path
+  int32_t groups, span;      // matrix-core path (span 0: balanced over the groups)
   int64_t units;
-  size_t ws_bytes, cnt_bytes, ml_bytes;
+  size_t ws_bytes, desc_bytes, ml_bytes;
 };
 
-// The fused merge has one workgroup read every chunk state of its unit after
-// a round trip through the arrival counter; measured on MI355X, the separate
-// merge kernel (spread over (unit, head) pairs) finishes sooner, so it is the
-// default and the fused merge is opt-in.
-// The arrival counters occupy a fixed region at the start of every workspace,
-// whatever the dims, and nothing else is ever stored there: calls of different
-// shapes can then share a workspace, each leaving every counter it used at zero.
-constexpr int64_t kCounterSlots = 1 << 18;
-constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
-
-// Split each (layer, sequence, KV head) into chunks of `chunk` tokens.  The
-// host never sees seq_lens, so the plan covers the longest possible sequence
-// (seq_len_hint or max_seq_len); workgroups past a sequence's end exit at once.
 Plan make_plan(const gqa_dims* d, int32_t L) {
   Plan p;
+  p.mfma = use_mfma(d);
   p.units = (int64_t)L * d->batch * d->num_kv_heads;
-  const int hb = (d->num_q_heads / d->num_kv_heads + 15) / 16;
+  const int64_t T = d->seq_len_hint > 0 ? d->seq_len_hint : d->max_seq_len;
+  const int64_t G = d->num_q_heads / d->num_kv_heads;
+  const int hb = (int)((G + 15) / 16);
   p.waves = 4;
   p.tiles = 1;
-  if (use_mfma(d)) {
+  p.chunk = p.n_chunks = p.groups = p.span = 0;
+  int64_t slots;
+  if (p.mfma) {
     p.waves = d->workgroup_waves ? d->workgroup_waves : 4;
     if (p.waves > max_waves(hb)) p.waves = max_waves(hb);
     p.tiles = d->tiles_in_flight ? d->tiles_in_flight : 2;
     if (p.tiles > max_tiles(hb, p.waves)) p.tiles = max_tiles(hb, p.waves);
-  }
-  const int64_t T = d->seq_len_hint > 0 ? d->seq_len_hint : d->max_seq_len;
-  int64_t c;
-  if (d->chunk_tokens > 0) {
-    c = d->chunk_tokens;
+    // Token split: the valid tokens (at most units * T) are shared evenly by
+    // the workgroups; two per CU keep about 128 KB of loads in flight per CU
+    // with 4-wavefront groups.  A forced chunk_tokens sets the span instead.
+    const int64_t upper = p.units * T;
+    if (d->chunk_tokens > 0) {
+      p.span = d->chunk_tokens;
+      p.groups = (int32_t)std::min<int64_t>(std::max<int64_t>(ceil_div(upper, p.span), 1), INT32_MAX);
+    } else {
+      // every workgroup must be resident at once (equal spans: a second
+      // dispatch round would double the time), so take as many per CU as the
+      // kernel's registers and LDS allow, up to two
+      const int64_t per_cu = std::min(2, resident_groups_per_cu(d, p.waves, p.tiles));
+      p.groups = (int32_t)std::max<int64_t>(1, std::min<int64_t>(cu_count() * per_cu, ceil_div(upper, 16)));
+    }
+    slots = 2 * (int64_t)p.groups;
   } else {
-    const int64_t per_unit = p.units > 0 ? ceil_div(kTargetWorkgroups, p.units) : 1;
-    c = ceil_div(ceil_div(T, per_unit), kMinChunk) * kMinChunk;
-    if (c < kMinChunk) c = kMinChunk;
-    if (c > kMaxChunk) c = kMaxChunk;
+    int64_t c;
+    if (d->chunk_tokens > 0) {
+      c = d->chunk_tokens;
+    } else {
+      const int64_t per_unit = p.units > 0 ? ceil_div(kTargetWorkgroups, p.units) : 1;
+      c = ceil_div(ceil_div(T, per_unit), kMinChunk) * kMinChunk;
+      if (c < kMinChunk) c = kMinChunk;
+      if (c > kMaxChunk) c = kMaxChunk;
+    }
+    p.chunk = (int32_t)c;
+    p.n_chunks = (int32_t)ceil_div(T, c);
+    while (p.units * p.n_chunks > INT32_MAX) {   // only for absurd shapes with a forced tiny chunk
+      p.chunk *= 2;
+      p.n_chunks = (int32_t)ceil_div(T, p.chunk);
+    }
+    slots = p.n_chunks > 1 ? p.units * p.n_chunks : 0;
   }
-  p.chunk = (int32_t)c;
-  p.n_chunks = (int32_t)ceil_div(T, c);
-  while (p.units * p.n_chunks > INT32_MAX) {   // only for absurd shapes with a forced tiny chunk
-    p.chunk *= 2;
-    p.n_chunks = (int32_t)ceil_div(T, p.chunk);
-  }
-  const int64_t G = d->num_q_heads / d->num_kv_heads;
-  p.fused = use_mfma(d) && p.units <= kCounterSlots && d->merge == GQA_MERGE_FUSED;
-  if (p.n_chunks <= 1 || p.units == 0) {
-    p.ws_bytes = p.cnt_bytes = p.ml_bytes = 0;
+  if (slots == 0 || p.units == 0) {
+    p.ws_bytes = p.ml_bytes = p.desc_bytes = 0;
   } else {
-    p.cnt_bytes = kCounterBytes;
-    p.ml_bytes = (size_t)ceil_div(p.units * p.n_chunks * G * 2 * 4, 256) * 256;
-    p.ws_bytes = p.cnt_bytes + p.ml_bytes + (size_t)(p.units * p.n_chunks * G * d->head_dim * 4);
+    p.desc_bytes = p.mfma ? (size_t)ceil_div(4 * 8 * (int64_t)p.groups, 256) * 256 : 0;
+    p.ml_bytes = (size_t)ceil_div(slots * G * 2 * 4, 256) * 256;
+    p.ws_bytes = p.desc_bytes + p.ml_bytes + (size_t)(slots * G * d->head_dim * 4);
   }
   return p;
 }
@@ -117,15 +143,15 @@ typedef void (*kernel_fn)(gqa::Problem);
 // Kernel variants instantiated per head-block count hb = ceil(G/16): larger
 // workgroups and more tiles in flight cost registers, and only the variants
 // that fit without spilling exist (4 wavefronts per SIMD allow 128 VGPRs).
-int max_waves(int hb) { return hb == 1 ? 16 : (hb == 2 ? 8 : 4); }
+int max_waves(int hb) { return hb == 1 ? 16 : (hb == 2 ? 8 : 4); }   // 16 only with d = 128, see mfma_kernel
 int max_tiles(int hb, int waves) { return (hb == 1 && waves <= 8) || (hb == 2 && waves == 4) ? 2 : 1; }
 
 template <int D>
 kernel_fn mfma_kernel(int hb, int waves, int tiles) {
   switch (hb) {
     case 1:
-      if (waves == 16) return gqa::gqa_decode_mfma<D, 1, 16, 1>;
-      if (waves == 8) return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 8, 2> : gqa::gqa_decode_mfma<D, 1, 8, 1>;
+      if (waves == 16 && D == 128) return gqa::gqa_decode_mfma<128, 1, 16, 1>;
+      if (waves >= 8) return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 8, 2> : gqa::gqa_decode_mfma<D, 1, 8, 1>;
       return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 4, 1>;
     case 2:
       if (waves == 8) return gqa::gqa_decode_mfma<D, 2, 8, 1>;
@@ -135,15 +161,31 @@ kernel_fn mfma_kernel(int hb, int waves, int tiles) {
   }
 }
 
-kernel_fn pick_kernel(const gqa_dims* d, int waves, int tiles) {
+kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan) {
   const int G = d->num_q_heads / d->num_kv_heads;
-  if (use_mfma(d)) {
+  if (plan.mfma) {
     const int hb = (G + 15) / 16;
-    return d->head_dim == 128 ? mfma_kernel<128>(hb, waves, tiles) : mfma_kernel<64>(hb, waves, tiles);
+    return d->head_dim == 128 ? mfma_kernel<128>(hb, plan.waves, plan.tiles)
+                              : mfma_kernel<64>(hb, plan.waves, plan.tiles);
   }
   if (d->dtype == GQA_DTYPE_F32)
     return d->head_dim == 128 ? gqa::gqa_decode_valu<float, 128> : gqa::gqa_decode_valu<float, 64>;
   return d->head_dim == 128 ? gqa::gqa_decode_valu<uint16_t, 128> : gqa::gqa_decode_valu<uint16_t, 64>;
+}
+
+// Workgroups of the chosen matrix-core kernel that fit on one CU together
+// (HIP occupancy query; 1 when no device answers).
+int resident_groups_per_cu(const gqa_dims* d, int waves, int tiles) {
+  const int hb = (d->num_q_heads / d->num_kv_heads + 15) / 16;
+  const kernel_fn k = d->head_dim == 128 ? mfma_kernel<128>(hb, waves, tiles) : mfma_kernel<64>(hb, waves, tiles);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), 64 * waves, 0) !=
+          hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  return n;
 }
 
 gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const int64_t* kv_offsets,
@@ -168,10 +210,9 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   p.kv_offsets = kv_offsets;
   p.seq_lens = seq_lens;
   char* w = static_cast<char*>(ws);
-  p.ws_cnt = plan.ws_bytes ? reinterpret_cast<int32_t*>(w) : nullptr;
-  p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.cnt_bytes) : nullptr;
-  p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.cnt_bytes + plan.ml_bytes) : nullptr;
-  p.fused_merge = plan.fused;
+  p.ws_desc = plan.ws_bytes ? reinterpret_cast<int64_t*>(w) : nullptr;
+  p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.desc_bytes) : nullptr;
+  p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.desc_bytes + plan.ml_bytes) : nullptr;
   p.B = d->batch;
   p.H_q = d->num_q_heads;
   p.H_kv = d->num_kv_heads;
@@ -181,26 +222,32 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   p.L = L;
   p.chunk = plan.chunk;
   p.n_chunks = plan.n_chunks;
+  p.groups = plan.groups;
+  p.span = plan.span;
   p.out_bf16 = d->out_dtype == GQA_DTYPE_BF16;
   p.scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* args[] = {&p};
-  const int64_t grid = plan.units * plan.n_chunks;
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pick_kernel(d, plan.waves, plan.tiles)), dim3((unsigned)grid),
+  const int64_t grid = plan.mfma ? plan.groups : plan.units * plan.n_chunks;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pick_kernel(d, plan)), dim3((unsigned)grid),
                                  dim3(64 * plan.waves), args, 0, s);
   if (e != hipSuccess) return GQA_ERR_LAUNCH;
-  if (plan.n_chunks > 1 && !plan.fused) {
-    // The kernel boundary orders the chunk states before their merge.
+  // The merge runs as a second kernel: the kernel boundary orders every
+  // partial state before it is read.
+  if (plan.mfma) {
+    const void* mk = d->head_dim == 128 ? reinterpret_cast<const void*>(gqa::gqa_merge_spans<128>)
+                                        : reinterpret_cast<const void*>(gqa::gqa_merge_spans<64>);
+    e = hipLaunchKernel(mk, dim3((unsigned)plan.groups), dim3(256), args, 0, s);
+  } else if (plan.n_chunks > 1) {
     const int hpb = 256 / d->head_dim;
     const int64_t mgrid = plan.units * ((p.G + hpb - 1) / hpb);
+    if (mgrid > INT32_MAX) return GQA_ERR_UNSUPPORTED;
     const void* mk = d->head_dim == 128 ? reinterpret_cast<const void*>(gqa::gqa_merge_chunks<128>)
                                         : reinterpret_cast<const void*>(gqa::gqa_merge_chunks<64>);
-    if (mgrid > INT32_MAX) return GQA_ERR_UNSUPPORTED;
     e = hipLaunchKernel(mk, dim3((unsigned)mgrid), dim3(256), args, 0, s);
-    if (e != hipSuccess) return GQA_ERR_LAUNCH;
   }
-  return GQA_OK;
+  return e == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -217,8 +264,8 @@ gqa_status gqa_decode_plan(const gqa_dims* dims, int32_t num_layers, int32_t* ch
   if (st != GQA_OK) return st;
   if (!chunk_tokens || !num_chunks) return GQA_ERR_INVALID_ARG;
   const Plan p = make_plan(dims, num_layers);
-  *chunk_tokens = p.chunk;
-  *num_chunks = p.n_chunks;
+  *chunk_tokens = p.mfma ? p.span : p.chunk;
+  *num_chunks = p.mfma ? p.groups : p.n_chunks;
   return GQA_OK;
 }
 

@@ -1,12 +1,15 @@
 // Matrix-core GQA decode kernel for bf16 caches, D = 64 or 128, G <= 16*HB.
 //
-// One workgroup (NW wavefronts) per (unit, chunk).  Wavefront w streams the
-// 16-token tiles w, w+NW, w+2NW, ... of the chunk (so the wavefronts of a
-// workgroup sweep adjacent memory together) straight from HBM into
-// registers; every K/V byte of the chunk is read once and serves all G query
-// heads of the group.  A wavefront issues the loads of TPW tiles before it
-// computes them; with the other wavefronts of the CU that keeps enough bytes
-// in flight to cover HBM latency without deep per-wave pipelines.
+// Work split ("token split", see common.h): the valid tokens of all units
+// form one stream cut into equal spans, one per workgroup (about two per CU),
+// so every workgroup streams the same number of bytes whatever the sequence
+// lengths.  A workgroup walks its span unit piece by unit piece; for each
+// piece, wavefront w streams the 16-token tiles w, w+NW, w+2NW, ... (the
+// wavefronts sweep adjacent memory together) straight from HBM into
+// registers, and every K/V byte is read once and serves all G query heads of
+// the group.  A wavefront issues the loads of TPW tiles before it computes
+// them; with the other wavefronts of the CU that keeps enough bytes in flight
+// to cover HBM latency without deep per-wave pipelines.
 //
 // Scores: S^T[token][head] = K Q^T on v_mfma_f32_16x16x32_bf16, with
 //   A = 16 key rows x 32 columns (lane (m = lane%16, q4 = lane/16) holds 8
@@ -82,261 +85,261 @@ struct Tile16 {
 
 template <int D, int HB, int NW, int TPW>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
-  constexpr int TILE = 16, KS = D / 32, VW = D / 16;
+  constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
   constexpr int HP = HB * 16;             // padded heads
   constexpr int SLOT = HB * VW * 4 * 64;  // floats of one wavefront's O in lane order
   typedef typename VRow<D>::type vrow_t;
 
   __shared__ float sm_slot[(NW > 1 ? NW / 2 : 1) * SLOT];
   __shared__ float sm_wm[NW][HP], sm_wl[NW][HP];
-  __shared__ int sm_flag;
+  __shared__ int32_t sm_P[kMaxBatch + 1];
+  __shared__ int32_t sm_wave[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
-  const int unit = blockIdx.x / p.n_chunks, chunk = blockIdx.x % p.n_chunks;
-  const UnitInfo ui = unit_info(p, unit);
-  const int c0 = chunk * p.chunk;
-  if (c0 >= (ui.n > 0 ? ui.n : 1)) return;   // beyond this sequence: nothing to do
-  const int c1 = min(ui.n, c0 + p.chunk);
   const int G = p.G;
   const float sl2 = p.scale_log2;
 
-  const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + ui.row0 * D;
-  const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + ui.row0 * D;
-  const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + out_row0(p, ui) * D;
+  build_prefix<NT>(p, sm_P, sm_wave);
+  const TokenSpace ts = token_space(p, sm_P);
+  zero_empty_sequences<D, NT>(p, sm_P, blockIdx.x, gridDim.x);
+  write_merge_desc(p, sm_P, ts, blockIdx.x);
+  const int64_t s0 = (int64_t)blockIdx.x * ts.span;
+  const int64_t s1 = min(s0 + ts.span, ts.total);
 
-  // B operands of the score product: query head hb*16 + m16, columns 32s + 8q4 .. +7.
-  u32x4 qf[HB][KS];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int h = hb * 16 + m16;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + (int64_t)h * D + 32 * s + 8 * q4) : u32x4{0, 0, 0, 0};
-  }
-
-  float m_run[HB], l_run[HB];
-  f32x4 oacc[VW][HB];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    m_run[hb] = -INFINITY;
-    l_run[hb] = 0.f;
-#pragma unroll
-    for (int r = 0; r < VW; ++r) oacc[r][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int ntiles = (c1 - c0 + TILE - 1) / TILE;
-  const int last = c1 - 1;
   // Per-lane element offsets inside a tile (relative to the tile's first row).
   const uint32_t koff = (uint32_t)(m16 * D + 8 * q4);
   const uint32_t voff = (uint32_t)(4 * q4 * D + VW * m16);
 
-  // Each iteration issues the loads of TPW tiles (w + NW*(TPW*it + u)) before
-  // computing any of them, so a wavefront keeps TPW tiles in flight.
-  auto load_tile = [&](Tile16<D>& T, int t0) {
-    if (t0 + TILE <= c1) {
-      // full tile: one base address per lane, the rest are immediate offsets
-      const uint16_t* kt = kg + (int64_t)t0 * D + koff;
-      const uint16_t* vt = vg + (int64_t)t0 * D + voff;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vrow_t*>(vt + i * D));
-    } else {
-      // ragged tail: rows past the chunk are clamped to its last valid row
-      // (in bounds and finite); their weights are forced to 0 below
-      const uint16_t* kt = kg + (int64_t)min(t0 + m16, last) * D + 8 * q4;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        T.v[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const vrow_t*>(vg + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
-    }
-  };
-  auto compute_tile = [&](const Tile16<D>& T, int t0) {
-    u32x2 phi[HB], plo[HB];
+  for (int64_t x = s0; x < s1;) {
+    const Piece pc = locate(p, sm_P, ts, x);
+    const UnitInfo& ui = pc.ui;
+    const int c0 = pc.t;
+    const int c1 = (int)min((int64_t)ui.n, pc.t + (s1 - x));
+    const bool whole = c0 == 0 && c1 == ui.n;
+    const int slot_id = x == s0 ? 0 : 1;   // only the first and the last piece of a span can be partial
+    x += c1 - c0;
+
+    const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + ui.row0 * D;
+    const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + ui.row0 * D;
+    const int64_t orow = out_row0(p, ui);
+    const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + orow * D;
+
+    // B operands of the score product: query head hb*16 + m16, columns 32s + 8q4 .. +7.
+    u32x4 qf[HB][KS];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int h = hb * 16 + m16;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sc = mfma_k32(T.k[s], qf[hb][s], sc);
-      float x[4];
+      for (int s = 0; s < KS; ++s)
+        qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + (int64_t)h * D + 32 * s + 8 * q4) : u32x4{0, 0, 0, 0};
+    }
+
+    float m_run[HB], l_run[HB];
+    f32x4 oacc[VW][HB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = sc[i] * sl2;
-      if (t0 + TILE > c1) {
+    for (int hb = 0; hb < HB; ++hb) {
+      m_run[hb] = -INFINITY;
+      l_run[hb] = 0.f;
+#pragma unroll
+      for (int r = 0; r < VW; ++r) oacc[r][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int ntiles = (c1 - c0 + TILE - 1) / TILE;
+    const int last = c1 - 1;
+    // Each iteration issues the loads of TPW tiles (w + NW*(TPW*it + u)) before
+    // computing any of them, so a wavefront keeps TPW tiles in flight.
+    auto load_tile = [&](Tile16<D>& T, int t0) {
+      if (t0 + TILE <= c1) {
+        // full tile: one base address per lane, the rest are immediate offsets
+        const uint16_t* kt = kg + (int64_t)t0 * D + koff;
+        const uint16_t* vt = vg + (int64_t)t0 * D + voff;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vrow_t*>(vt + i * D));
+      } else {
+        // ragged tail: rows past the chunk are clamped to its last valid row
+        // (in bounds and finite); their weights are forced to 0 below
+        const uint16_t* kt = kg + (int64_t)min(t0 + m16, last) * D + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t0 + 4 * q4 + i >= c1) x[i] = -INFINITY;
+          T.v[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const vrow_t*>(vg + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
       }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__any(mx > m_run[hb])) {   // wave-uniform: some head's maximum grew
-        const float m_new = fmaxf(m_run[hb], mx);
-        const float alpha = exp2f(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
-        m_run[hb] = m_new;
-        l_run[hb] *= alpha;
-#pragma unroll
-        for (int r = 0; r < VW; ++r) oacc[r][hb] *= alpha;
-      }
-      float pv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = exp2f(x[i] - m_run[hb]);
-        l_run[hb] += pv[i];
-      }
-      const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
-      const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
-      const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
-      phi[hb] = u32x2{h01, h23};
-      plo[hb] = u32x2{l01, l23};
-    }
-#pragma unroll
-    for (int r = 0; r < VW; ++r) {
-      const int w = r >> 1;
-      u32x2 va;
-      if (r & 1)
-        va = u32x2{pack_halves<true>(T.v[0][w], T.v[1][w]), pack_halves<true>(T.v[2][w], T.v[3][w])};
-      else
-        va = u32x2{pack_halves<false>(T.v[0][w], T.v[1][w]), pack_halves<false>(T.v[2][w], T.v[3][w])};
+    };
+    auto compute_tile = [&](const Tile16<D>& T, int t0) {
+      u32x2 phi[HB], plo[HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        oacc[r][hb] = mfma_k16(va, phi[hb], oacc[r][hb]);
-        oacc[r][hb] = mfma_k16(va, plo[hb], oacc[r][hb]);
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sc = mfma_k32(T.k[s], qf[hb][s], sc);
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = sc[i] * sl2;
+        if (t0 + TILE > c1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (t0 + 4 * q4 + i >= c1) x[i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (__any(mx > m_run[hb])) {   // wave-uniform: some head's maximum grew
+          const float m_new = fmaxf(m_run[hb], mx);
+          const float alpha = exp2f(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
+          m_run[hb] = m_new;
+          l_run[hb] *= alpha;
+#pragma unroll
+          for (int r = 0; r < VW; ++r) oacc[r][hb] *= alpha;
+        }
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = exp2f(x[i] - m_run[hb]);
+          l_run[hb] += pv[i];
+        }
+        const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
+        const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
+        const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
+        phi[hb] = u32x2{h01, h23};
+        plo[hb] = u32x2{l01, l23};
       }
-    }
-  };
-  for (int j = wave; j < ntiles; j += NW * TPW) {
-    Tile16<D> T[TPW];
-    // Loads are issued unconditionally (a tile index past the end is clamped
-    // to the last tile: in bounds, and its compute is skipped) so that the
-    // number of loads in flight is the same on every path; a conditional load
-    // would make the compiler wait for all of them before the first compute.
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) load_tile(T[u], c0 + min(j + NW * u, ntiles - 1) * TILE);
+      for (int r = 0; r < VW; ++r) {
+        const int w = r >> 1;
+        u32x2 va;
+        if (r & 1)
+          va = u32x2{pack_halves<true>(T.v[0][w], T.v[1][w]), pack_halves<true>(T.v[2][w], T.v[3][w])};
+        else
+          va = u32x2{pack_halves<false>(T.v[0][w], T.v[1][w]), pack_halves<false>(T.v[2][w], T.v[3][w])};
 #pragma unroll
-    for (int u = 0; u < TPW; ++u)
-      if (j + NW * u < ntiles) compute_tile(T[u], c0 + (j + NW * u) * TILE);
-  }
-
-  // ---- combine the wavefronts of the workgroup -----------------------------
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    float lt = l_run[hb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    if (q4 == 0) {
-      sm_wm[wave][hb * 16 + m16] = m_run[hb];
-      sm_wl[wave][hb * 16 + m16] = lt;
-    }
-  }
-  __syncthreads();
-  float Mh[HB], Lh[HB];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int h = hb * 16 + m16;
-    float M = sm_wm[0][h];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_wm[w][h]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-      if (sm_wm[w][h] != -INFINITY) L += exp2f(sm_wm[w][h] - M) * sm_wl[w][h];
-    Mh[hb] = M;
-    Lh[hb] = L;
-    const float f = (m_run[hb] == -INFINITY) ? 0.f : exp2f(m_run[hb] - M);
-#pragma unroll
-    for (int r = 0; r < VW; ++r) oacc[r][hb] *= f;
-  }
-  // Tree over wavefronts: in each round the upper half hands its O to the lower half.
-#pragma unroll
-  for (int s = NW / 2; s >= 1; s /= 2) {
-    if (wave >= s && wave < 2 * s) {
-      float* dst = sm_slot + (wave - s) * SLOT + lane;
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int r = 0; r < VW; ++r)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[((hb * VW + r) * 4 + i) * 64] = oacc[r][hb][i];
-    }
-    __syncthreads();
-    if (wave < s) {
-      const float* src = sm_slot + wave * SLOT + lane;
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int r = 0; r < VW; ++r)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[r][hb][i] += src[((hb * VW + r) * 4 + i) * 64];
-    }
-    if (s > 1) __syncthreads();
-  }
-  const int nck = chunks_of(ui.n, p.chunk);
-  const bool fused = nck > 1 && p.fused_merge;
-  if (wave != 0 && !fused) return;
-  if (wave == 0) {
-  // ---- wavefront 0 stores the workgroup's result ---------------------------
-  // Lane (q4, m16) holds head m16 of each head block, columns D/16*(4*q4+i) + r.
-  const int64_t orow = out_row0(p, ui);
-  const int64_t slot = (int64_t)unit * p.n_chunks + chunk;
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int h = hb * 16 + m16;
-    if (h >= G) continue;
-    if (nck == 1) {
-      const float inv = Lh[hb] > 0.f ? 1.f / Lh[hb] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = VW * (4 * q4 + i);
-        if (p.out_bf16) {
-          uint32_t wds[VW / 2];
-#pragma unroll
-          for (int r = 0; r < VW; r += 2)
-            wds[r / 2] = f32_to_bf16_rne(oacc[r][hb][i] * inv) | (f32_to_bf16_rne(oacc[r + 1][hb][i] * inv) << 16);
-          uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (orow + h) * D + col;
-          if constexpr (VW == 8)
-            *reinterpret_cast<u32x4*>(dst) = u32x4{wds[0], wds[1], wds[2], wds[3]};
-          else
-            *reinterpret_cast<u32x2*>(dst) = u32x2{wds[0], wds[1]};
-        } else {
-          float* dst = reinterpret_cast<float*>(p.out) + (orow + h) * D + col;
-#pragma unroll
-          for (int r = 0; r < VW; r += 4)
-            *reinterpret_cast<f32x4*>(dst + r) =
-                f32x4{oacc[r][hb][i] * inv, oacc[r + 1][hb][i] * inv, oacc[r + 2][hb][i] * inv,
-                      oacc[r + 3][hb][i] * inv};
+        for (int hb = 0; hb < HB; ++hb) {
+          oacc[r][hb] = mfma_k16(va, phi[hb], oacc[r][hb]);
+          oacc[r][hb] = mfma_k16(va, plo[hb], oacc[r][hb]);
         }
       }
-    } else if (fused) {
-      float* wo = p.ws_o + (slot * G + h) * D;
+    };
+    for (int j = wave; j < ntiles; j += NW * TPW) {
+      Tile16<D> T[TPW];
+      // Loads are issued unconditionally (a tile index past the end is clamped
+      // to the last tile: in bounds, and its compute is skipped) so that the
+      // number of loads in flight is the same on every path; a conditional load
+      // would make the compiler wait for all of them before the first compute.
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int u = 0; u < TPW; ++u) load_tile(T[u], c0 + min(j + NW * u, ntiles - 1) * TILE);
 #pragma unroll
-        for (int r = 0; r < VW; ++r) store_coherent(wo + VW * (4 * q4 + i) + r, oacc[r][hb][i]);
+      for (int u = 0; u < TPW; ++u)
+        if (j + NW * u < ntiles) compute_tile(T[u], c0 + (j + NW * u) * TILE);
+    }
+
+    // ---- combine the wavefronts of the workgroup ---------------------------
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      float lt = l_run[hb];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
       if (q4 == 0) {
-        store_coherent(p.ws_ml + (slot * G + h) * 2, Mh[hb]);
-        store_coherent(p.ws_ml + (slot * G + h) * 2 + 1, Lh[hb]);
+        sm_wm[wave][hb * 16 + m16] = m_run[hb];
+        sm_wl[wave][hb * 16 + m16] = lt;
       }
-    } else {
-      float* wo = p.ws_o + (slot * G + h) * D;
+    }
+    __syncthreads();
+    float Mh[HB], Lh[HB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = VW * (4 * q4 + i);
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = hb * 16 + m16;
+      float M = sm_wm[0][h];
 #pragma unroll
-        for (int r = 0; r < VW; r += 4)
-          *reinterpret_cast<f32x4*>(wo + col + r) =
-              f32x4{oacc[r][hb][i], oacc[r + 1][hb][i], oacc[r + 2][hb][i], oacc[r + 3][hb][i]};
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_wm[w][h]);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (sm_wm[w][h] != -INFINITY) L += exp2f(sm_wm[w][h] - M) * sm_wl[w][h];
+      Mh[hb] = M;
+      Lh[hb] = L;
+      const float f = (m_run[hb] == -INFINITY) ? 0.f : exp2f(m_run[hb] - M);
+#pragma unroll
+      for (int r = 0; r < VW; ++r) oacc[r][hb] *= f;
+    }
+    // Tree over wavefronts: in each round the upper half hands its O to the lower half.
+#pragma unroll
+    for (int s = NW / 2; s >= 1; s /= 2) {
+      if (wave >= s && wave < 2 * s) {
+        float* dst = sm_slot + (wave - s) * SLOT + lane;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int r = 0; r < VW; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[((hb * VW + r) * 4 + i) * 64] = oacc[r][hb][i];
       }
-      if (q4 == 0) {
-        p.ws_ml[(slot * G + h) * 2] = Mh[hb];
-        p.ws_ml[(slot * G + h) * 2 + 1] = Lh[hb];
+      __syncthreads();
+      if (wave < s) {
+        const float* src = sm_slot + wave * SLOT + lane;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int r = 0; r < VW; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[r][hb][i] += src[((hb * VW + r) * 4 + i) * 64];
+      }
+      __syncthreads();
+    }
+
+    // ---- wavefront 0 stores the piece's result -----------------------------
+    // Lane (q4, m16) holds head m16 of each head block, columns D/16*(4*q4+i) + r.
+    if (wave == 0) {
+      const int64_t slot = 2 * (int64_t)blockIdx.x + slot_id;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const int h = hb * 16 + m16;
+        if (h >= G) continue;
+        if (whole) {
+          const float inv = Lh[hb] > 0.f ? 1.f / Lh[hb] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int col = VW * (4 * q4 + i);
+            if (p.out_bf16) {
+              uint32_t wds[VW / 2];
+#pragma unroll
+              for (int r = 0; r < VW; r += 2)
+                wds[r / 2] = f32_to_bf16_rne(oacc[r][hb][i] * inv) | (f32_to_bf16_rne(oacc[r + 1][hb][i] * inv) << 16);
+              uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (orow + h) * D + col;
+              if constexpr (VW == 8)
+                *reinterpret_cast<u32x4*>(dst) = u32x4{wds[0], wds[1], wds[2], wds[3]};
+              else
+                *reinterpret_cast<u32x2*>(dst) = u32x2{wds[0], wds[1]};
+            } else {
+              float* dst = reinterpret_cast<float*>(p.out) + (orow + h) * D + col;
+#pragma unroll
+              for (int r = 0; r < VW; r += 4)
+                *reinterpret_cast<f32x4*>(dst + r) =
+                    f32x4{oacc[r][hb][i] * inv, oacc[r + 1][hb][i] * inv, oacc[r + 2][hb][i] * inv,
+                          oacc[r + 3][hb][i] * inv};
+            }
+          }
+        } else {
+          float* wo = p.ws_o + (slot * G + h) * D;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int col = VW * (4 * q4 + i);
+#pragma unroll
+            for (int r = 0; r < VW; r += 4)
+              *reinterpret_cast<f32x4*>(wo + col + r) =
+                  f32x4{oacc[r][hb][i], oacc[r + 1][hb][i], oacc[r + 2][hb][i], oacc[r + 3][hb][i]};
+          }
+          if (q4 == 0) {
+            p.ws_ml[(slot * G + h) * 2] = Mh[hb];
+            p.ws_ml[(slot * G + h) * 2 + 1] = Lh[hb];
+          }
+        }
       }
     }
   }
-  }
-  if (fused) fused_merge<D, NW * 64>(p, unit, ui, nck, wave == 0 && lane == 0, &sm_flag);
 }
 
 }  // namespace gqa

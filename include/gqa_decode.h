@@ -36,16 +36,18 @@
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
  *   only enqueue work and return; inputs must stay unchanged, and out is
  *   valid, once the stream reaches the call.  No host synchronisation.
- * Workspace.  Split-KV partial results live in a caller-provided device
+ * Work split.  The matrix-core path divides all valid tokens of the call,
+ *   in (layer, sequence, KV head, token) order, evenly among its workgroups
+ *   (about two per CU), whatever the sequence lengths; the vector path cuts
+ *   each sequence into chunks of a planned size.  Pieces of a (layer,
+ *   sequence, KV head) computed by different workgroups leave partial
+ *   softmax states in the workspace, and a second kernel on the same stream
+ *   combines them, in a fixed order (results are deterministic).
+ * Workspace.  Those partial states live in a caller-provided device
  *   workspace of at least gqa_decode_workspace_bytes() bytes, 256-byte
- *   aligned (may be NULL when that size is 0).  Its first 1 MiB holds
- *   per-(layer, sequence, KV head) arrival counters and nothing else, for
- *   every dims: zero-fill the workspace once before its first use; every
- *   call that completes leaves the counters at zero again, so calls of any
- *   shape ordered on one stream may share a workspace without clearing it.
- *   Calls that may overlap in time need separate workspaces.  A call enqueues
- *   one kernel, or two when the merge of split-KV chunks runs as a separate
- *   kernel (gqa_merge).
+ *   aligned (may be NULL when that size is 0).  It needs no initialisation
+ *   and is scratch between calls.  Calls ordered on one stream may share a
+ *   workspace; calls that may overlap in time need separate ones.
  * Errors.  Every entry point returns a gqa_status and never throws.  Argument
  *   errors are detected on the host before anything is enqueued.  Faults
  *   inside a kernel surface at the next synchronisation, as usual in HIP.
@@ -69,31 +71,19 @@ typedef enum gqa_dtype {
 typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, H_q % H_kv != 0 */
-  GQA_ERR_UNSUPPORTED = 2,  /* head_dim not 64/128, G > 64, bad dtype pairing */
+  GQA_ERR_UNSUPPORTED = 2,  /* head_dim not 64/128, G > 64, dtype/path pairing, more than
+                               4096 sequences on the matrix-core path */
   GQA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   GQA_ERR_LAUNCH = 4        /* the HIP runtime refused the launch */
 } gqa_status;
 
 /* Which kernel family runs the step.  AUTO picks the matrix-core kernel for
- * bf16 inputs and the vector-ALU kernel for fp32 inputs. */
+ * bf16 inputs (up to 4096 sequences) and the vector-ALU kernel otherwise. */
 typedef enum gqa_path {
   GQA_PATH_AUTO = 0,
   GQA_PATH_VALU = 1,   /* vector ALU, any supported dtype */
   GQA_PATH_MFMA = 2    /* matrix cores (v_mfma_f32_16x16x32_bf16), bf16 inputs only */
 } gqa_path;
-
-/* How the partial results of a sequence split over several chunks are
- * combined.  FUSED: the last workgroup of the (layer, sequence, KV head) to
- * finish merges them inside the decode kernel (matrix-core path only; the
- * vector path always uses KERNEL).  KERNEL: a second kernel merges them.
- * AUTO: KERNEL (the faster of the two on MI355X for the shapes measured).
- * Shapes with more than 2^18 (layer, sequence, KV head) units always use
- * KERNEL. */
-typedef enum gqa_merge {
-  GQA_MERGE_AUTO = 0,
-  GQA_MERGE_FUSED = 1,
-  GQA_MERGE_KERNEL = 2
-} gqa_merge;
 
 typedef struct gqa_dims {
   int32_t batch;         /* B >= 0 (B == 0 is a no-op) */
@@ -108,13 +98,13 @@ typedef struct gqa_dims {
   int32_t seq_len_hint;  /* 0, or an upper bound (<= max_seq_len) on every
                             seq_lens[b]; the split is planned over it and
                             larger values are clamped to it on the device */
-  int32_t chunk_tokens;  /* 0: the planner chooses the split-KV chunk; otherwise
-                            tokens per chunk, a positive multiple of 64 */
+  int32_t chunk_tokens;  /* 0: the planner splits the work; otherwise a positive
+                            multiple of 64: tokens per workgroup (matrix-core
+                            path) or per chunk of a sequence (vector path) */
   int32_t path;          /* gqa_path */
   int32_t workgroup_waves; /* 0: default; else wavefronts per workgroup of the
                               matrix-core kernel: 4, 8 or 16 (reduced to 8
                               when G > 16 and to 4 when G > 32) */
-  int32_t merge;           /* gqa_merge */
   int32_t tiles_in_flight; /* 0: default; else 16-token tiles each wavefront of
                               the matrix-core kernel loads before computing
                               them: 1 or 2 (reduced to 1 where registers do
@@ -123,16 +113,20 @@ typedef struct gqa_dims {
 
 /*
  * Bytes of workspace a call with these dims and `num_layers` layers needs
- * (0 when every sequence fits one chunk).  Pure function of its arguments:
- * never touches the device.  Returns 0 for invalid dims as well; the decode
+ * (0 when no partial state can arise).  Depends on its arguments and on the
+ * CU count of the current device (taken as 256 when no device answers);
+ * touches no device memory.  Returns 0 for invalid dims as well; the decode
  * call then reports the error.
  */
 size_t gqa_decode_workspace_bytes(const gqa_dims* dims, int32_t num_layers);
 
 /*
- * The split-KV plan for these dims: tokens per chunk and the chunk count of
- * the longest possible sequence.  Returns GQA_OK or GQA_ERR_INVALID_ARG /
- * GQA_ERR_UNSUPPORTED (outputs untouched then).  Host only.
+ * The work split planned for these dims.  Matrix-core path: *chunk_tokens is
+ * the forced tokens per workgroup (0 when the valid tokens are shared evenly
+ * at run time) and *num_chunks the number of workgroups.  Vector path: tokens
+ * per chunk and the chunk count of the longest possible sequence.  Returns
+ * GQA_OK or GQA_ERR_INVALID_ARG / GQA_ERR_UNSUPPORTED (outputs untouched
+ * then).  Host only (it may ask the HIP runtime for the CU count).
  */
 gqa_status gqa_decode_plan(const gqa_dims* dims, int32_t num_layers, int32_t* chunk_tokens,
                            int32_t* num_chunks);

