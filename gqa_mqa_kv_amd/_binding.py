@@ -17,6 +17,7 @@ from . import build as _build
 
 GQA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
 SYMBOLS = ("gqa_decode", "gqa_decode_layers", "gqa_decode_workspace_bytes", "gqa_decode_plan",
@@ -28,7 +29,7 @@ class GqaDims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("seq_len_hint", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("path", ctypes.c_int32), ("workgroup_waves", ctypes.c_int32),
-                ("tiles_in_flight", ctypes.c_int32)]
+                ("tiles_in_flight", ctypes.c_int32), ("merge", ctypes.c_int32)]
 
 
 class GqaError(RuntimeError):
@@ -75,12 +76,12 @@ def _check(status: int):
 
 
 def make_dims(B, H_q, H_kv, d, T_max, dtype, out_dtype=None, seq_len_hint=0, chunk_tokens=0,
-              path="auto", waves=0, tiles=0) -> GqaDims:
+              path="auto", waves=0, tiles=0, merge="auto") -> GqaDims:
     if dtype not in GQA_DTYPE or (out_dtype is not None and out_dtype not in GQA_DTYPE):
         raise TypeError("dtypes must be float32 or bfloat16")
     return GqaDims(int(B), int(H_q), int(H_kv), int(d), int(T_max), GQA_DTYPE[dtype],
                    GQA_DTYPE[out_dtype if out_dtype is not None else dtype], int(seq_len_hint),
-                   int(chunk_tokens), PATHS[path], int(waves), int(tiles))
+                   int(chunk_tokens), PATHS[path], int(waves), int(tiles), MERGES[merge])
 
 
 def workspace_bytes(dims: GqaDims, num_layers: int = 1) -> int:
@@ -100,14 +101,15 @@ _workspaces = {}
 
 
 def default_workspace(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
-    """A device buffer of at least ``nbytes`` (256-byte aligned), cached per
-    device and shared by calls ordered on one stream."""
+    """A zero-filled device buffer of at least ``nbytes`` (256-byte aligned),
+    cached per device.  The library leaves its arrival counters at zero after
+    each call, so the buffer is shared as is by calls ordered on one stream."""
     if nbytes == 0:
         return None
     key = (device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -127,7 +129,7 @@ def _require(t: torch.Tensor, name: str, device: torch.device):
 
 def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None, chunk_tokens: int = 0,
            path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
-           tiles: int = 0):
+           tiles: int = 0, merge: str = "auto"):
     """One decode step of one layer.  q [B,H_q,d]; k_cache/v_cache
     [B,H_kv,T_max,d]; seq_lens int32 [B] on the same device.  Returns out
     [B,H_q,d] (dtype ``out_dtype``, default q's)."""
@@ -142,7 +144,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
         raise ValueError("shape mismatch between q, caches and seq_lens")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache and v_cache must share one dtype")
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles)
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge)
     if out is None:
         out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
     _require(out, "out", dev)
@@ -160,7 +162,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
 def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len: Optional[int] = None,
                   num_kv_heads: Optional[int] = None, out=None, out_dtype=None, chunk_tokens: int = 0,
                   path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
-           tiles: int = 0):
+           tiles: int = 0, merge: str = "auto"):
     """One decode step of L independent layers in one launch.  q [L,B,H_q,d].
     Dense caches are [L,B,H_kv,T_max,d]; with ``kv_offsets`` (int64 [B+1] on
     the device) the caches are packed (any shape holding L*kv_offsets[B]*H_kv*d
@@ -189,7 +191,7 @@ def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, 
         raise ValueError("seq_lens must be int32 [B]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache and v_cache must share one dtype")
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles)
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge)
     if out is None:
         out = torch.empty(L, B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
     _require(out, "out", dev)
@@ -221,7 +223,7 @@ class Prepared:
 
 def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len=None, num_kv_heads=None,
             out_dtype=None, chunk_tokens: int = 0, path: str = "auto", seq_len_hint: int = 0, stream=None,
-            waves: int = 0, tiles: int = 0):
+            waves: int = 0, tiles: int = 0, merge: str = "auto"):
     """Validate (by running the call once) and return a Prepared launcher
     writing into a fresh output tensor, which each call returns.  q [B,H_q,d]
     selects gqa_decode, q [L,B,H_q,d] selects gqa_decode_layers."""
@@ -231,7 +233,7 @@ def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_se
     if layers:
         decode_layers(q, k_cache, v_cache, seq_lens, scale, kv_offsets=kv_offsets, max_seq_len=max_seq_len,
                       num_kv_heads=num_kv_heads, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
-                      path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles)
+                      path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge)
         L, B, H_q, d = q.shape
         if kv_offsets is None:
             H_kv, T_max = k_cache.shape[2], k_cache.shape[3]
@@ -239,11 +241,11 @@ def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_se
             H_kv, T_max = num_kv_heads, max_seq_len
     else:
         decode(q, k_cache, v_cache, seq_lens, scale, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
-               path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles)
+               path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge)
         B, H_q, d = q.shape
         H_kv, T_max = k_cache.shape[1], k_cache.shape[2]
         L = 1
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles)
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge)
     ws = default_workspace(workspace_bytes(dims, L), dev)
     nbytes = 0 if ws is None else ws.numel()
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream

@@ -39,6 +39,8 @@ struct Problem {
                               //   token-split path [groups][2][G][2]
   float* ws_o;                // partial O: [units][n_chunks][G][D] or [groups][2][G][D]
   int64_t* ws_desc;           // token-split path: [groups][4] merge descriptors
+  int32_t* ws_cnt;            // token-split path, fused merge: [groups] arrival counters (zero between calls)
+  int32_t fused;              // token-split path: 1 = the last piece of a split unit to finish merges it
   int32_t B, H_q, H_kv, G, T_max, L;
   int32_t T_cap;              // planned bound on valid tokens (seq_len_hint, else T_max)
   int32_t chunk, n_chunks;    // chunk path: tokens per chunk, chunks of the longest sequence
@@ -256,6 +258,61 @@ __device__ void zero_empty_sequences(const Problem& p, const int32_t* sm_P, int 
     const int64_t row = (int64_t)lb * p.H_q;
     for (int e = threadIdx.x; e < p.H_q * D; e += NT) store_out(p, row + e / D, e % D, D, 0.f);
   }
+}
+
+// Agent-coherent 32-bit accesses (global_load/store ... sc1 on gfx950, the
+// instructions agent-scope atomic loads and stores compile to).  The fused
+// merge moves partial states between workgroups through these: they are
+// coherent across the XCDs' separate L2 caches without the L2 write-back and
+// invalidate that an agent-scope release/acquire fence would cost.
+__device__ __forceinline__ void store_coherent(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* a) {
+  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Fused merge of a split unit, run by every thread of the workgroup that just
+// published one piece of it with store_coherent (from wavefront 0).  Thread 0
+// waits until those stores have completed, then counts the piece in the
+// unit's arrival counter (indexed by w0, the workgroup holding the unit's
+// first token; agent-scope atomic).  The workgroup that brings the count to
+// the number of pieces reads every piece back with load_coherent, in piece
+// order (deterministic), writes the output and resets the counter to zero
+// for the next call.  Pieces: w0's slot first_slot, then slot 2w of every
+// later workgroup w <= w_last.
+template <int D, int NT>
+__device__ void fused_merge(const Problem& p, int64_t w0, int64_t w_last, int64_t first_slot, int64_t orow,
+                            int* sm_flag) {
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);   // the publishing stores (this wavefront's) have completed
+    const int prev = __hip_atomic_fetch_add(p.ws_cnt + w0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sm_flag = prev == (int)(w_last - w0);
+  }
+  __syncthreads();
+  const bool last = *sm_flag;
+  __syncthreads();   // sm_flag is reused by the next piece
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const int G = p.G;
+  for (int e = threadIdx.x; e < G * D; e += NT) {
+    const int hd = e / D, c = e % D;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int64_t w = w0; w <= w_last; ++w) {
+      const int64_t slot = w == w0 ? first_slot : 2 * w;
+      const float mk = load_coherent(p.ws_ml + (slot * G + hd) * 2);
+      const float lk = load_coherent(p.ws_ml + (slot * G + hd) * 2 + 1);
+      const float ok = load_coherent(p.ws_o + (slot * G + hd) * D + c);
+      const float Mn = fmaxf(M, mk);
+      const float a = exp2f(M - Mn), f = exp2f(mk - Mn);
+      num = num * a + f * ok;
+      den = den * a + f * lk;
+      M = Mn;
+    }
+    store_out(p, orow + hd, c, D, den > 0.f ? num / den : 0.f);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(p.ws_cnt + w0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merge descriptor written by decode workgroup m for the merge kernel:

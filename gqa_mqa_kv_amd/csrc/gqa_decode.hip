@@ -59,6 +59,8 @@ gqa_status check_dims(const gqa_dims* d, int32_t L) {
   if (d->workgroup_waves != 0 && d->workgroup_waves != 4 && d->workgroup_waves != 8 && d->workgroup_waves != 16)
     return GQA_ERR_INVALID_ARG;
   if (d->tiles_in_flight < 0 || d->tiles_in_flight > 2) return GQA_ERR_INVALID_ARG;
+  if (d->merge != GQA_MERGE_AUTO && d->merge != GQA_MERGE_FUSED && d->merge != GQA_MERGE_KERNEL)
+    return GQA_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return GQA_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads > gqa::kMaxGroup) return GQA_ERR_UNSUPPORTED;
   if (d->path == GQA_PATH_MFMA && (d->dtype != GQA_DTYPE_BF16 || d->batch > gqa::kMaxBatch))
@@ -70,13 +72,21 @@ gqa_status check_dims(const gqa_dims* d, int32_t L) {
   return GQA_OK;
 }
 
+// Fused merge: arrival counters live at the start of the workspace in a
+// region of fixed size for every dims, so that calls of any shape can share
+// a workspace (each leaves every counter it used at zero; nothing else is
+// stored there while the counters are in use).
+constexpr int64_t kCounterSlots = 1 << 18;
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
+constexpr int64_t kFusedMaxPieces = 8;
+
 struct Plan {
-  bool mfma;
+  bool mfma, fused;
   int32_t waves, tiles;
   int32_t chunk, n_chunks;   // vector path
   int32_t groups, span;      // matrix-core path (span 0: balanced over the groups)
   int64_t units;
-  size_t ws_bytes, desc_bytes, ml_bytes;
+  size_t ws_bytes, cnt_bytes, desc_bytes, ml_bytes;
 };
 
 Plan make_plan(const gqa_dims* d, int32_t L) {
@@ -128,12 +138,22 @@ Plan make_plan(const gqa_dims* d, int32_t L) {
     }
     slots = p.n_chunks > 1 ? p.units * p.n_chunks : 0;
   }
+  // Fused merge while a unit spans few workgroups (one workgroup then reads
+  // all of its pieces at the end); with many pieces per unit the separate
+  // merge kernel spreads the merge over every workgroup the unit touches.
+  p.fused = false;
+  if (p.mfma && p.groups <= kCounterSlots) {
+    const int64_t span_est = p.span > 0 ? p.span : std::max<int64_t>(16, ceil_div(p.units * T, p.groups));
+    const int64_t pieces = ceil_div(T, span_est) + 1;
+    p.fused = d->merge == GQA_MERGE_FUSED || (d->merge == GQA_MERGE_AUTO && pieces <= kFusedMaxPieces);
+  }
   if (slots == 0 || p.units == 0) {
-    p.ws_bytes = p.ml_bytes = p.desc_bytes = 0;
+    p.ws_bytes = p.cnt_bytes = p.ml_bytes = p.desc_bytes = 0;
   } else {
+    p.cnt_bytes = kCounterBytes;   // reserved on every path: nothing but counters is ever stored there
     p.desc_bytes = p.mfma ? (size_t)ceil_div(4 * 8 * (int64_t)p.groups, 256) * 256 : 0;
     p.ml_bytes = (size_t)ceil_div(slots * G * 2 * 4, 256) * 256;
-    p.ws_bytes = p.desc_bytes + p.ml_bytes + (size_t)(slots * G * d->head_dim * 4);
+    p.ws_bytes = p.cnt_bytes + p.desc_bytes + p.ml_bytes + (size_t)(slots * G * d->head_dim * 4);
   }
   return p;
 }
@@ -210,9 +230,14 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   p.kv_offsets = kv_offsets;
   p.seq_lens = seq_lens;
   char* w = static_cast<char*>(ws);
+  p.ws_cnt = plan.ws_bytes ? reinterpret_cast<int32_t*>(w) : nullptr;
+  w += plan.cnt_bytes;
   p.ws_desc = plan.ws_bytes ? reinterpret_cast<int64_t*>(w) : nullptr;
-  p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.desc_bytes) : nullptr;
-  p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(w + plan.desc_bytes + plan.ml_bytes) : nullptr;
+  w += plan.desc_bytes;
+  p.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  w += plan.ml_bytes;
+  p.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  p.fused = plan.fused;
   p.B = d->batch;
   p.H_q = d->num_q_heads;
   p.H_kv = d->num_kv_heads;
@@ -235,7 +260,7 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   if (e != hipSuccess) return GQA_ERR_LAUNCH;
   // The merge runs as a second kernel: the kernel boundary orders every
   // partial state before it is read.
-  if (plan.mfma) {
+  if (plan.mfma && !plan.fused) {
     const void* mk = d->head_dim == 128 ? reinterpret_cast<const void*>(gqa::gqa_merge_spans<128>)
                                         : reinterpret_cast<const void*>(gqa::gqa_merge_spans<64>);
     e = hipLaunchKernel(mk, dim3((unsigned)plan.groups), dim3(256), args, 0, s);

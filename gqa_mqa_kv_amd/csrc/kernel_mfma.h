@@ -94,6 +94,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   __shared__ float sm_wm[NW][HP], sm_wl[NW][HP];
   __shared__ int32_t sm_P[kMaxBatch + 1];
   __shared__ int32_t sm_wave[NW];
+  __shared__ int sm_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m16 = lane & 15, q4 = lane >> 4;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   build_prefix<NT>(p, sm_P, sm_wave);
   const TokenSpace ts = token_space(p, sm_P);
   zero_empty_sequences<D, NT>(p, sm_P, blockIdx.x, gridDim.x);
-  write_merge_desc(p, sm_P, ts, blockIdx.x);
+  if (!p.fused) write_merge_desc(p, sm_P, ts, blockIdx.x);
   const int64_t s0 = (int64_t)blockIdx.x * ts.span;
   const int64_t s1 = min(s0 + ts.span, ts.total);
 
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     const int c1 = (int)min((int64_t)ui.n, pc.t + (s1 - x));
     const bool whole = c0 == 0 && c1 == ui.n;
     const int slot_id = x == s0 ? 0 : 1;   // only the first and the last piece of a span can be partial
+    const int64_t w0 = pc.start / ts.span, w_last = (pc.start + ui.n - 1) / ts.span;
     x += c1 - c0;
 
     const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + ui.row0 * D;
@@ -322,6 +324,16 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
                           oacc[r + 3][hb][i] * inv};
             }
           }
+        } else if (p.fused) {
+          float* wo = p.ws_o + (slot * G + h) * D;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < VW; ++r) store_coherent(wo + VW * (4 * q4 + i) + r, oacc[r][hb][i]);
+          if (q4 == 0) {
+            store_coherent(p.ws_ml + (slot * G + h) * 2, Mh[hb]);
+            store_coherent(p.ws_ml + (slot * G + h) * 2 + 1, Lh[hb]);
+          }
         } else {
           float* wo = p.ws_o + (slot * G + h) * D;
 #pragma unroll
@@ -338,6 +350,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
           }
         }
       }
+    }
+    if (!whole && p.fused) {
+      // the piece of w0 is its last piece (slot 2*w0 + 1) unless the unit starts w0's span
+      const int64_t first_slot = 2 * w0 + (pc.start != w0 * ts.span ? 1 : 0);
+      fused_merge<D, NT>(p, w0, w_last, first_slot, orow, &sm_flag);
     }
   }
 }

@@ -38,16 +38,21 @@
  *   valid, once the stream reaches the call.  No host synchronisation.
  * Work split.  The matrix-core path divides all valid tokens of the call,
  *   in (layer, sequence, KV head, token) order, evenly among its workgroups
- *   (about two per CU), whatever the sequence lengths; the vector path cuts
+ *   (up to two per CU), whatever the sequence lengths; the vector path cuts
  *   each sequence into chunks of a planned size.  Pieces of a (layer,
  *   sequence, KV head) computed by different workgroups leave partial
- *   softmax states in the workspace, and a second kernel on the same stream
- *   combines them, in a fixed order (results are deterministic).
+ *   softmax states in the workspace that are combined in a fixed order
+ *   (results are deterministic), either inside the decode kernel by the
+ *   last workgroup to finish a piece of it, or by a second kernel on the same
+ *   stream (see gqa_merge).
  * Workspace.  Those partial states live in a caller-provided device
  *   workspace of at least gqa_decode_workspace_bytes() bytes, 256-byte
- *   aligned (may be NULL when that size is 0).  It needs no initialisation
- *   and is scratch between calls.  Calls ordered on one stream may share a
- *   workspace; calls that may overlap in time need separate ones.
+ *   aligned (may be NULL when that size is 0).  Its first 1 MiB holds
+ *   arrival counters and nothing else, for every dims and path:
+ *   zero-fill a workspace once before its first use; every call that
+ *   completes leaves the counters at zero again, so calls of any shape
+ *   ordered on one stream may share a workspace without clearing it.  Calls
+ *   that may overlap in time need separate workspaces.
  * Errors.  Every entry point returns a gqa_status and never throws.  Argument
  *   errors are detected on the host before anything is enqueued.  Faults
  *   inside a kernel surface at the next synchronisation, as usual in HIP.
@@ -85,6 +90,19 @@ typedef enum gqa_path {
   GQA_PATH_MFMA = 2    /* matrix cores (v_mfma_f32_16x16x32_bf16), bf16 inputs only */
 } gqa_path;
 
+/* How the partial states of a (layer, sequence, KV head) split between
+ * workgroups are combined on the matrix-core path.  FUSED: the workgroup that
+ * finishes the last piece merges them inside the decode kernel (one kernel
+ * per call).  KERNEL: a second kernel merges them, spread over every
+ * workgroup the split touched.  AUTO: FUSED while a sequence can span at
+ * most about 8 workgroups, else KERNEL.  The vector path always uses a second
+ * kernel. */
+typedef enum gqa_merge {
+  GQA_MERGE_AUTO = 0,
+  GQA_MERGE_FUSED = 1,
+  GQA_MERGE_KERNEL = 2
+} gqa_merge;
+
 typedef struct gqa_dims {
   int32_t batch;         /* B >= 0 (B == 0 is a no-op) */
   int32_t num_q_heads;   /* H_q >= 1 */
@@ -109,6 +127,7 @@ typedef struct gqa_dims {
                               the matrix-core kernel loads before computing
                               them: 1 or 2 (reduced to 1 where registers do
                               not allow 2) */
+  int32_t merge;           /* gqa_merge */
 } gqa_dims;
 
 /*

@@ -99,7 +99,7 @@ def test_dims_validation(kw, expect):
 
 
 def test_enum_validation():
-    for field in ("dtype", "out_dtype", "path"):
+    for field in ("dtype", "out_dtype", "path", "merge"):
         d = dims()
         setattr(d, field, 7)
         assert call(d) == INVALID, field
@@ -141,14 +141,14 @@ def test_workspace_size_formula():
     d = dims(B=3, H_q=32, H_kv=4, d=128, T_max=5000, chunk_tokens=512, path="valu")
     assert gqa.plan(d) == (512, 10)
     units, G, n = 3 * 4, 8, 10
-    assert gqa.workspace_bytes(d) == up(units * n * G * 2 * 4) + units * n * G * 128 * 4
+    assert gqa.workspace_bytes(d) == (1 << 20) + up(units * n * G * 2 * 4) + units * n * G * 128 * 4
     assert gqa.workspace_bytes(d, 5) > gqa.workspace_bytes(d, 1)
     assert gqa.workspace_bytes(dims(T_max=256, chunk_tokens=256, path="valu")) == 0   # one chunk: no partial state
     # matrix-core path with a forced span: two state slots per workgroup
     d = dims(B=3, H_q=32, H_kv=4, d=128, T_max=5000, chunk_tokens=512)
     span, groups = gqa.plan(d)
     assert (span, groups) == (512, -(-units * 5000 // 512))
-    assert gqa.workspace_bytes(d) == up(4 * 8 * groups) + up(2 * groups * G * 2 * 4) + 2 * groups * G * 128 * 4
+    assert gqa.workspace_bytes(d) == (1 << 20) + up(4 * 8 * groups) + up(2 * groups * G * 2 * 4) + 2 * groups * G * 128 * 4
 
 
 @pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))

@@ -175,13 +175,15 @@ def test_deterministic_and_workspace_reuse(path):
                          ids=lambda s: "B%d_Hq%d_Hkv%d_d%d_T%d" % s[:5])
 @pytest.mark.parametrize("waves,tiles", [(4, 1), (4, 2), (8, 1), (8, 2), (16, 1)])
 @pytest.mark.parametrize("span", [0, 64, 192])
-def test_kernel_variants(shape, waves, tiles, span):
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+def test_kernel_variants(shape, waves, tiles, span, merge):
     """Every instantiated matrix-core variant (workgroup size, tiles in flight),
     with the even token split and with short forced spans that cut units at
-    arbitrary token positions (many pieces per unit to merge)."""
+    arbitrary token positions (many pieces per unit to merge), merged inside
+    the decode kernel or by the merge kernel."""
     B, hq, hkv, d, T, lo = shape
     x = small(B, hq, hkv, d, T, seed=seed_of(shape, 29), lo=lo)
-    check(x, path="mfma", chunk_tokens=span, waves=waves, tiles=tiles, label="variant")
+    check(x, path="mfma", chunk_tokens=span, waves=waves, tiles=tiles, merge=merge, label="variant-" + merge)
 
 
 def test_token_split_with_empty_and_tiny_sequences():
@@ -195,7 +197,8 @@ def test_token_split_with_empty_and_tiny_sequences():
         x["k"][b, :, n:] = float("nan")
         x["v"][b, :, n:] = float("nan")
     for span in (0, 64, 128, 320, 1024):
-        check(x, path="mfma", chunk_tokens=span, label="token-split span %d" % span)
+        for merge in ("fused", "kernel"):
+            check(x, path="mfma", chunk_tokens=span, merge=merge, label="token-split span %d %s" % (span, merge))
     out = gpu_decode(x, path="mfma", out_dtype=torch.bfloat16).cpu()
     assert (out[0] == 0).all() and (out[5] == 0).all() and (out[9] == 0).all()
 
@@ -215,17 +218,32 @@ def test_workspace_shared_across_shapes():
              small(5, 16, 2, 64, 700, seed=63, lo=1)]
     refs = [oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"]) for x in cases]
     for rep in range(3):
-        for x, ref, path in zip(cases, refs, ["mfma", "valu", "mfma"]):
-            out = gpu_decode(x, path=path, chunk_tokens=64 * (rep + 2), out_dtype=torch.float32)
+        for x, ref, path, merge in zip(cases, refs, ["mfma", "valu", "mfma"], ["fused", "auto", "kernel"]):
+            out = gpu_decode(x, path=path, chunk_tokens=64 * (rep + 2), merge=merge, out_dtype=torch.float32)
+            assert err(out, ref) <= 2e-3
+            out = gpu_decode(x, path=path, chunk_tokens=64 * (rep + 3), merge="fused", out_dtype=torch.float32)
             assert err(out, ref) <= 2e-3
 
 
-def test_repeats_bitwise():
-    """Many calls in a row on one workspace give the same bits."""
+def test_workspace_shared_across_paths():
+    """The vector path's partial states never land in the counter region the
+    fused merge relies on: alternate paths on one workspace."""
+    x = small(3, 32, 8, 128, 1500, seed=64, lo=200)
+    ref = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+    for rep in range(4):
+        for path in ("valu", "mfma"):
+            out = gpu_decode(x, path=path, chunk_tokens=256, merge="fused", out_dtype=torch.float32)
+            assert err(out, ref) <= 2e-3, (rep, path)
+
+
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+def test_repeats_bitwise(merge):
+    """Many calls in a row on one workspace give the same bits (the fused
+    merge leaves its arrival counters at zero)."""
     x = small(4, 32, 8, 128, 3000, seed=33, lo=100)
-    first = gpu_decode(x, path="mfma").cpu()
+    first = gpu_decode(x, path="mfma", chunk_tokens=256, merge=merge).cpu()
     for _ in range(20):
-        assert torch.equal(gpu_decode(x, path="mfma").cpu(), first)
+        assert torch.equal(gpu_decode(x, path="mfma", chunk_tokens=256, merge=merge).cpu(), first)
 
 
 def test_paths_and_chunkings_agree():
@@ -240,7 +258,7 @@ def test_explicit_stream_and_workspace():
     x = small(2, 32, 8, 128, 1200, seed=43)
     xd = to_dev(x)
     dims = gqa.make_dims(2, 32, 8, 128, 1200, torch.bfloat16, torch.float32, chunk_tokens=256)
-    ws = torch.full((gqa.workspace_bytes(dims),), 0xFF, dtype=torch.uint8, device=DEV)   # scratch: contents irrelevant
+    ws = torch.zeros(gqa.workspace_bytes(dims), dtype=torch.uint8, device=DEV)   # zero-filled once, as required
     s = torch.cuda.Stream(DEV)
     with torch.cuda.stream(s):
         out = gqa.decode(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], out_dtype=torch.float32,
@@ -248,6 +266,7 @@ def test_explicit_stream_and_workspace():
     s.synchronize()
     ref = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
     assert err(out, ref) <= 2e-3
+    assert int(ws[:1 << 20].view(torch.int32).abs().sum()) == 0   # arrival counters back at zero
 
 
 # ------------------------------------------------------------ layer batches --
