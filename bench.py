@@ -2,9 +2,10 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
-One step = one decode step of the workload (every split-KV chunk and the
-fused merge: one kernel launch) over one batch of synthetic inputs that are
-already resident in HBM.  Steps rotate over enough independent input batches
+One step = one decode step of the workload (every split-KV piece and the
+merge of the pieces: one kernel launch when the merge is fused into the
+decode kernel, else the decode kernel and a small merge kernel) over one
+batch of synthetic inputs that are already resident in HBM.  Steps rotate over enough independent input batches
 (``--replicas``) that the working set exceeds the 256 MB last-level
 (Infinity) cache, so every step streams its K/V from HBM.
 
@@ -98,6 +99,18 @@ def cpu_baseline(w, budget_s: float = 10.0):
             "sample": "%d whole steps of %s (fp64 C oracle, OpenMP), %.1f s" % (n, w.name, el)}
 
 
+def copy_calibration(torch, dev, nbytes: int, launches: int) -> None:
+    """A plain copy of known size: each launch reads and writes nbytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        torch.neg(src, out=dst)     # elementwise: one fp32 read and one fp32 write per element
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "elementwise neg, fp32", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": launches}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +123,8 @@ def main():
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain N-MiB device copy (counter calibration kernel)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,9 +137,12 @@ def main():
     import gqa_mqa_kv_amd as gqa
     from gqa_mqa_kv_amd import workloads
 
-    w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib:
+        copy_calibration(torch, dev, args.copy_calibration_mib << 20, args.steps)
+        return
+    w = workloads.WORKLOADS[args.workload]
     out_dtype = {None: w.dtype, "bf16": torch.bfloat16, "fp32": torch.float32}[args.out_dtype]
     seq_lens = workloads.seq_lens_for(w)
     kv_bytes = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * (2 if w.dtype == torch.bfloat16 else 4)

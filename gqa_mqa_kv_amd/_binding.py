@@ -29,7 +29,8 @@ class GqaDims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("seq_len_hint", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("path", ctypes.c_int32), ("workgroup_waves", ctypes.c_int32),
-                ("tiles_in_flight", ctypes.c_int32), ("merge", ctypes.c_int32)]
+                ("tiles_in_flight", ctypes.c_int32), ("merge", ctypes.c_int32),
+                ("workgroups_per_cu", ctypes.c_int32)]
 
 
 class GqaError(RuntimeError):
@@ -76,12 +77,12 @@ def _check(status: int):
 
 
 def make_dims(B, H_q, H_kv, d, T_max, dtype, out_dtype=None, seq_len_hint=0, chunk_tokens=0,
-              path="auto", waves=0, tiles=0, merge="auto") -> GqaDims:
+              path="auto", waves=0, tiles=0, merge="auto", per_cu=0) -> GqaDims:
     if dtype not in GQA_DTYPE or (out_dtype is not None and out_dtype not in GQA_DTYPE):
         raise TypeError("dtypes must be float32 or bfloat16")
     return GqaDims(int(B), int(H_q), int(H_kv), int(d), int(T_max), GQA_DTYPE[dtype],
                    GQA_DTYPE[out_dtype if out_dtype is not None else dtype], int(seq_len_hint),
-                   int(chunk_tokens), PATHS[path], int(waves), int(tiles), MERGES[merge])
+                   int(chunk_tokens), PATHS[path], int(waves), int(tiles), MERGES[merge], int(per_cu))
 
 
 def workspace_bytes(dims: GqaDims, num_layers: int = 1) -> int:
@@ -129,7 +130,7 @@ def _require(t: torch.Tensor, name: str, device: torch.device):
 
 def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None, chunk_tokens: int = 0,
            path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
-           tiles: int = 0, merge: str = "auto"):
+           tiles: int = 0, merge: str = "auto", per_cu: int = 0):
     """One decode step of one layer.  q [B,H_q,d]; k_cache/v_cache
     [B,H_kv,T_max,d]; seq_lens int32 [B] on the same device.  Returns out
     [B,H_q,d] (dtype ``out_dtype``, default q's)."""
@@ -144,7 +145,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
         raise ValueError("shape mismatch between q, caches and seq_lens")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache and v_cache must share one dtype")
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge)
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge, per_cu)
     if out is None:
         out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
     _require(out, "out", dev)
@@ -162,7 +163,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
 def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len: Optional[int] = None,
                   num_kv_heads: Optional[int] = None, out=None, out_dtype=None, chunk_tokens: int = 0,
                   path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
-           tiles: int = 0, merge: str = "auto"):
+           tiles: int = 0, merge: str = "auto", per_cu: int = 0):
     """One decode step of L independent layers in one launch.  q [L,B,H_q,d].
     Dense caches are [L,B,H_kv,T_max,d]; with ``kv_offsets`` (int64 [B+1] on
     the device) the caches are packed (any shape holding L*kv_offsets[B]*H_kv*d
@@ -191,7 +192,7 @@ def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, 
         raise ValueError("seq_lens must be int32 [B]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache and v_cache must share one dtype")
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge)
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge, per_cu)
     if out is None:
         out = torch.empty(L, B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
     _require(out, "out", dev)
@@ -223,7 +224,7 @@ class Prepared:
 
 def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len=None, num_kv_heads=None,
             out_dtype=None, chunk_tokens: int = 0, path: str = "auto", seq_len_hint: int = 0, stream=None,
-            waves: int = 0, tiles: int = 0, merge: str = "auto"):
+            waves: int = 0, tiles: int = 0, merge: str = "auto", per_cu: int = 0):
     """Validate (by running the call once) and return a Prepared launcher
     writing into a fresh output tensor, which each call returns.  q [B,H_q,d]
     selects gqa_decode, q [L,B,H_q,d] selects gqa_decode_layers."""
@@ -233,7 +234,7 @@ def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_se
     if layers:
         decode_layers(q, k_cache, v_cache, seq_lens, scale, kv_offsets=kv_offsets, max_seq_len=max_seq_len,
                       num_kv_heads=num_kv_heads, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
-                      path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge)
+                      path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge, per_cu=per_cu)
         L, B, H_q, d = q.shape
         if kv_offsets is None:
             H_kv, T_max = k_cache.shape[2], k_cache.shape[3]
@@ -241,11 +242,11 @@ def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_se
             H_kv, T_max = num_kv_heads, max_seq_len
     else:
         decode(q, k_cache, v_cache, seq_lens, scale, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
-               path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge)
+               path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge, per_cu=per_cu)
         B, H_q, d = q.shape
         H_kv, T_max = k_cache.shape[1], k_cache.shape[2]
         L = 1
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge)
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge, per_cu)
     ws = default_workspace(workspace_bytes(dims, L), dev)
     nbytes = 0 if ws is None else ws.numel()
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream

@@ -25,6 +25,11 @@
 
 namespace gqa {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kMaxGroup = 64;    // largest G = H_q / H_kv supported
 constexpr int kMaxBatch = 4096;  // sequences per call on the token-split path (prefix sums live in LDS)
 
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(256) void gqa_merge_chunks(Problem p) {
 // Exclusive prefix sums of the clamped lengths into sm_P[0..B] (all threads of
 // the workgroup take part; B <= kMaxBatch).  sm_wave holds NT/64 ints.
 template <int NT>
-__device__ void build_prefix(const Problem& p, int32_t* sm_P, int32_t* sm_wave) {
+__device__ __forceinline__ void build_prefix(const Problem& p, int32_t* sm_P, int32_t* sm_wave) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = p.B;
   const int E = (B + NT - 1) / NT;   // entries per thread, contiguous
@@ -251,7 +256,7 @@ __device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, c
 // Zero the outputs of sequences with no valid token (every layer), spread
 // over the workgroups of a launch.
 template <int D, int NT>
-__device__ void zero_empty_sequences(const Problem& p, const int32_t* sm_P, int wg, int n_wg) {
+__device__ __forceinline__ void zero_empty_sequences(const Problem& p, const int32_t* sm_P, int wg, int n_wg) {
   for (int lb = wg; lb < p.L * p.B; lb += n_wg) {
     const int b = lb % p.B;
     if (sm_P[b + 1] != sm_P[b]) continue;
@@ -260,29 +265,101 @@ __device__ void zero_empty_sequences(const Problem& p, const int32_t* sm_P, int 
   }
 }
 
-// Agent-coherent 32-bit accesses (global_load/store ... sc1 on gfx950, the
-// instructions agent-scope atomic loads and stores compile to).  The fused
-// merge moves partial states between workgroups through these: they are
-// coherent across the XCDs' separate L2 caches without the L2 write-back and
-// invalidate that an agent-scope release/acquire fence would cost.
-__device__ __forceinline__ void store_coherent(float* a, float v) {
-  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Agent-coherent accesses to one state slot of the workspace: buffer
+// instructions with the sc1 cache policy (stores write through the XCD's L2
+// to memory, loads miss in it), the policy agent-scope atomic accesses get on
+// gfx950.  The fused merge moves partial states between workgroups through
+// these: they are coherent across the XCDs' separate L2 caches without the L2
+// write-back and invalidate that an agent-scope release/acquire fence would
+// cost.  The buffer descriptor covers the slot only (offsets are 32-bit;
+// accesses beyond it would be dropped by the hardware range check).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kPolicySc1 = 16;                 // cache-policy operand of the buffer builtins: sc1
+constexpr int kRsrcWord3 = 0x00020000;         // raw 32-bit buffer, no swizzle, no stride
+__device__ __forceinline__ Rsrc slot_rsrc(const float* base, int floats) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, floats * 4, kRsrcWord3);
 }
-__device__ __forceinline__ float load_coherent(const float* a) {
-  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store4_coherent(Rsrc r, int idx, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, idx * 4, 0, kPolicySc1);
+}
+__device__ __forceinline__ void store2_coherent(Rsrc r, int idx, float a, float b) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{a, b}), r, idx * 4, 0, kPolicySc1);
+}
+__device__ __forceinline__ f32x4 load4_coherent(Rsrc r, int idx) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, idx * 4, 0, kPolicySc1));
+}
+__device__ __forceinline__ f32x2 load2_coherent(Rsrc r, int idx) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, idx * 4, 0, kPolicySc1));
+}
+
+// Combined output columns c .. c+3 (c a multiple of 4) of head hd of a split
+// unit: the pieces of workgroups w0 .. w_last (w0's in slot first_slot,
+// workgroup w's in slot 2w) merged in piece order,
+//   M = max_k m_k,  out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k,
+// with a running maximum.  The loads of kMergeBatch pieces are issued
+// together (indices past the last piece are clamped to it and their values
+// unused).  COHERENT: the pieces were published with the sc1 stores above.
+constexpr int kMergeBatch = 8;
+template <bool COHERENT>
+__device__ __forceinline__ f32x4 merge_pieces(const Problem& p, int64_t w0, int64_t w_last, int64_t first_slot, int hd,
+                                              int c, int D) {
+  const int G = p.G;
+  float M = -INFINITY, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t wb = w0; wb <= w_last; wb += kMergeBatch) {
+    f32x2 ml[kMergeBatch];
+    f32x4 ok[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int64_t w = min(wb + u, w_last);
+      const int64_t slot = w == w0 ? first_slot : 2 * w;
+      if (COHERENT) {
+        ml[u] = load2_coherent(slot_rsrc(p.ws_ml + slot * G * 2, G * 2), 2 * hd);
+        ok[u] = load4_coherent(slot_rsrc(p.ws_o + slot * G * D, G * D), hd * D + c);
+      } else {
+        ml[u] = *reinterpret_cast<const f32x2*>(p.ws_ml + (slot * G + hd) * 2);
+        ok[u] = *reinterpret_cast<const f32x4*>(p.ws_o + (slot * G + hd) * D + c);
+      }
+    }
+    // A clamped index is a no-op (a = 1, f = 0) taken by selects, not a
+    // branch: a branch would let the compiler sink each load to its use.
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const bool real = wb + u <= w_last;
+      const float Mn = real ? fmaxf(M, ml[u][0]) : M;
+      const float a = real ? exp2f(M - Mn) : 1.f;   // M = -inf on the first piece: a = 0
+      const float f = real ? exp2f(ml[u][0] - Mn) : 0.f;
+      num = num * a + f * ok[u];
+      den = den * a + f * ml[u][1];
+      M = Mn;
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  return num * inv;
+}
+
+// Final store of four consecutive output columns.
+__device__ __forceinline__ void store_out4(const Problem& p, int64_t row, int c, int D, f32x4 v) {
+  if (p.out_bf16) {
+    const uint32_t w0 = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+    const uint32_t w1 = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row * D + c) = u32x2{w0, w1};
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + row * D + c) = v;
+  }
 }
 
 // Fused merge of a split unit, run by every thread of the workgroup that just
-// published one piece of it with store_coherent (from wavefront 0).  Thread 0
+// published one piece of it with the sc1 stores (from wavefront 0).  Thread 0
 // waits until those stores have completed, then counts the piece in the
 // unit's arrival counter (indexed by w0, the workgroup holding the unit's
 // first token; agent-scope atomic).  The workgroup that brings the count to
-// the number of pieces reads every piece back with load_coherent, in piece
+// the number of pieces reads every piece back with sc1 loads, in piece
 // order (deterministic), writes the output and resets the counter to zero
 // for the next call.  Pieces: w0's slot first_slot, then slot 2w of every
 // later workgroup w <= w_last.
 template <int D, int NT>
-__device__ void fused_merge(const Problem& p, int64_t w0, int64_t w_last, int64_t first_slot, int64_t orow,
+__device__ __forceinline__ void fused_merge(const Problem& p, int64_t w0, int64_t w_last, int64_t first_slot, int64_t orow,
                             int* sm_flag) {
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -296,22 +373,10 @@ __device__ void fused_merge(const Problem& p, int64_t w0, int64_t w_last, int64_
   if (!last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   const int G = p.G;
-  for (int e = threadIdx.x; e < G * D; e += NT) {
-    const int hd = e / D, c = e % D;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int64_t w = w0; w <= w_last; ++w) {
-      const int64_t slot = w == w0 ? first_slot : 2 * w;
-      const float mk = load_coherent(p.ws_ml + (slot * G + hd) * 2);
-      const float lk = load_coherent(p.ws_ml + (slot * G + hd) * 2 + 1);
-      const float ok = load_coherent(p.ws_o + (slot * G + hd) * D + c);
-      const float Mn = fmaxf(M, mk);
-      const float a = exp2f(M - Mn), f = exp2f(mk - Mn);
-      num = num * a + f * ok;
-      den = den * a + f * lk;
-      M = Mn;
-    }
-    store_out(p, orow + hd, c, D, den > 0.f ? num / den : 0.f);
-  }
+  // four columns per thread
+  const int nq = G * D / 4;
+  for (int q = threadIdx.x; q < nq; q += NT)
+    store_out4(p, orow + 4 * q / D, 4 * q % D, D, merge_pieces<true>(p, w0, w_last, first_slot, 4 * q / D, 4 * q % D, D));
   if (threadIdx.x == 0) __hip_atomic_store(p.ws_cnt + w0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -334,36 +399,29 @@ __device__ __forceinline__ void write_merge_desc(const Problem& p, const int32_t
                                                                  // the unit starts w0's span
     }
   }
-  if (threadIdx.x < 4) p.ws_desc[4 * (int64_t)m + threadIdx.x] = d[threadIdx.x];
+  const int i = threadIdx.x;
+  if (i < 4) p.ws_desc[4 * (int64_t)m + i] = i == 0 ? d[0] : (i == 1 ? d[1] : (i == 2 ? d[2] : d[3]));
 }
 
 // Merge of the token-split path: one workgroup of 256 threads per decode
-// workgroup m.  Helper h = m - w0 - 1 of the H = w_last - w0 helpers of a unit
-// combines, for output elements e = h, h + H, ..., the unit's pieces in order.
+// workgroup m.  The H = w_last - w0 workgroups w0+1 .. w_last of a split unit
+// share its merge: helper h = m - w0 - 1 combines a contiguous block of the
+// unit's output quads (four columns of one head), one quad per thread.
 template <int D>
 __global__ __launch_bounds__(256) void gqa_merge_spans(Problem p) {
   constexpr int NT = 256;
   const int m = blockIdx.x;
   const int64_t* dsc = p.ws_desc + 4 * (int64_t)m;
-  const int64_t w0 = dsc[0];
+  const int64_t w0 = uniform(dsc[0]);
   if (w0 < 0) return;
-  const int64_t w_last = dsc[1], orow = dsc[2], first_slot = dsc[3];
-  const int G = p.G;
+  const int64_t w_last = uniform(dsc[1]), orow = uniform(dsc[2]), first_slot = uniform(dsc[3]);
+  const int nq = p.G * D / 4;
   const int H = (int)(w_last - w0), h = (int)(m - w0 - 1);
-  for (int e = h + H * (int)threadIdx.x; e < G * D; e += H * NT) {
-    const int hd = e / D, c = e % D;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int64_t w = w0; w <= w_last; ++w) {
-      const int64_t slot = w == w0 ? first_slot : 2 * w;
-      const float mk = p.ws_ml[(slot * G + hd) * 2], lk = p.ws_ml[(slot * G + hd) * 2 + 1];
-      const float ok = p.ws_o[(slot * G + hd) * D + c];
-      const float Mn = fmaxf(M, mk);
-      const float a = exp2f(M - Mn), f = exp2f(mk - Mn);   // M = -inf on the first piece: a = 0
-      num = num * a + f * ok;
-      den = den * a + f * lk;
-      M = Mn;
-    }
-    store_out(p, orow + hd, c, D, den > 0.f ? num / den : 0.f);
+  const int per = (nq + H - 1) / H;
+  const int q1 = min(nq, (h + 1) * per);
+  for (int q = h * per + (int)threadIdx.x; q < q1; q += NT) {
+    const f32x4 v = merge_pieces<false>(p, w0, w_last, first_slot, 4 * q / D, 4 * q % D, D);
+    store_out4(p, orow + 4 * q / D, 4 * q % D, D, v);
   }
 }
 

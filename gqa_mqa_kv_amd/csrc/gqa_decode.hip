@@ -61,6 +61,7 @@ gqa_status check_dims(const gqa_dims* d, int32_t L) {
   if (d->tiles_in_flight < 0 || d->tiles_in_flight > 2) return GQA_ERR_INVALID_ARG;
   if (d->merge != GQA_MERGE_AUTO && d->merge != GQA_MERGE_FUSED && d->merge != GQA_MERGE_KERNEL)
     return GQA_ERR_INVALID_ARG;
+  if (d->workgroups_per_cu < 0 || d->workgroups_per_cu > 4) return GQA_ERR_INVALID_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return GQA_ERR_UNSUPPORTED;
   if (d->num_q_heads / d->num_kv_heads > gqa::kMaxGroup) return GQA_ERR_UNSUPPORTED;
   if (d->path == GQA_PATH_MFMA && (d->dtype != GQA_DTYPE_BF16 || d->batch > gqa::kMaxBatch))
@@ -103,20 +104,22 @@ Plan make_plan(const gqa_dims* d, int32_t L) {
   if (p.mfma) {
     p.waves = d->workgroup_waves ? d->workgroup_waves : 4;
     if (p.waves > max_waves(hb)) p.waves = max_waves(hb);
-    p.tiles = d->tiles_in_flight ? d->tiles_in_flight : 2;
+    p.tiles = d->tiles_in_flight ? d->tiles_in_flight : 1;
     if (p.tiles > max_tiles(hb, p.waves)) p.tiles = max_tiles(hb, p.waves);
     // Token split: the valid tokens (at most units * T) are shared evenly by
-    // the workgroups; two per CU keep about 128 KB of loads in flight per CU
-    // with 4-wavefront groups.  A forced chunk_tokens sets the span instead.
+    // the workgroups, by default one per CU: co-resident workgroups (and
+    // wavefronts beyond four per CU) are served unevenly by the memory
+    // system, and with equal static shares the slowest one sets the time.
+    // A forced chunk_tokens sets the span instead.
     const int64_t upper = p.units * T;
     if (d->chunk_tokens > 0) {
       p.span = d->chunk_tokens;
       p.groups = (int32_t)std::min<int64_t>(std::max<int64_t>(ceil_div(upper, p.span), 1), INT32_MAX);
     } else {
       // every workgroup must be resident at once (equal spans: a second
-      // dispatch round would double the time), so take as many per CU as the
-      // kernel's registers and LDS allow, up to two
-      const int64_t per_cu = std::min(2, resident_groups_per_cu(d, p.waves, p.tiles));
+      // dispatch round would double the time)
+      const int want = d->workgroups_per_cu ? d->workgroups_per_cu : 1;
+      const int64_t per_cu = std::max(1, std::min(want, resident_groups_per_cu(d, p.waves, p.tiles)));
       p.groups = (int32_t)std::max<int64_t>(1, std::min<int64_t>(cu_count() * per_cu, ceil_div(upper, 16)));
     }
     slots = 2 * (int64_t)p.groups;
@@ -161,21 +164,20 @@ Plan make_plan(const gqa_dims* d, int32_t L) {
 typedef void (*kernel_fn)(gqa::Problem);
 
 // Kernel variants instantiated per head-block count hb = ceil(G/16): larger
-// workgroups and more tiles in flight cost registers, and only the variants
-// that fit without spilling exist (4 wavefronts per SIMD allow 128 VGPRs).
-int max_waves(int hb) { return hb == 1 ? 16 : (hb == 2 ? 8 : 4); }   // 16 only with d = 128, see mfma_kernel
-int max_tiles(int hb, int waves) { return (hb == 1 && waves <= 8) || (hb == 2 && waves == 4) ? 2 : 1; }
+// workgroups and more tiles per load batch cost registers (a wavefront holds
+// two batches: the one it computes and the next one, loading), and only the
+// variants that fit (or nearly fit) the register file exist.
+int max_waves(int hb) { return hb <= 2 ? 8 : 4; }
+int max_tiles(int hb, int waves) { return hb == 1 && waves == 4 ? 2 : 1; }
 
 template <int D>
 kernel_fn mfma_kernel(int hb, int waves, int tiles) {
   switch (hb) {
     case 1:
-      if (waves == 16 && D == 128) return gqa::gqa_decode_mfma<128, 1, 16, 1>;
-      if (waves >= 8) return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 8, 2> : gqa::gqa_decode_mfma<D, 1, 8, 1>;
+      if (waves >= 8) return gqa::gqa_decode_mfma<D, 1, 8, 1>;
       return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 4, 1>;
     case 2:
-      if (waves == 8) return gqa::gqa_decode_mfma<D, 2, 8, 1>;
-      return tiles == 2 ? gqa::gqa_decode_mfma<D, 2, 4, 2> : gqa::gqa_decode_mfma<D, 2, 4, 1>;
+      return waves >= 8 ? gqa::gqa_decode_mfma<D, 2, 8, 1> : gqa::gqa_decode_mfma<D, 2, 4, 1>;
     case 3: return gqa::gqa_decode_mfma<D, 3, 4, 1>;
     default: return gqa::gqa_decode_mfma<D, 4, 4, 1>;
   }

@@ -1,15 +1,16 @@
 // Matrix-core GQA decode kernel for bf16 caches, D = 64 or 128, G <= 16*HB.
 //
 // Work split ("token split", see common.h): the valid tokens of all units
-// form one stream cut into equal spans, one per workgroup (about two per CU),
+// form one stream cut into equal spans, one per workgroup (one per CU),
 // so every workgroup streams the same number of bytes whatever the sequence
 // lengths.  A workgroup walks its span unit piece by unit piece; for each
 // piece, wavefront w streams the 16-token tiles w, w+NW, w+2NW, ... (the
 // wavefronts sweep adjacent memory together) straight from HBM into
 // registers, and every K/V byte is read once and serves all G query heads of
-// the group.  A wavefront issues the loads of TPW tiles before it computes
-// them; with the other wavefronts of the CU that keeps enough bytes in flight
-// to cover HBM latency without deep per-wave pipelines.
+// the group.  Each wavefront holds two batches of TPW tiles in registers: it
+// computes one while the next one (of the same piece, or the first batch of
+// the span's next piece) is loading, so the stream does not stop at piece
+// boundaries, where the wavefronts combine their softmax states.
 //
 // Scores: S^T[token][head] = K Q^T on v_mfma_f32_16x16x32_bf16, with
 //   A = 16 key rows x 32 columns (lane (m = lane%16, q4 = lane/16) holds 8
@@ -36,9 +37,6 @@
 
 namespace gqa {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -96,7 +94,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   __shared__ int32_t sm_wave[NW];
   __shared__ int sm_flag;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);   // wavefront index, in a scalar register (everything derived from it is too)
   const int m16 = lane & 15, q4 = lane >> 4;
   const int G = p.G;
   const float sl2 = p.scale_log2;
@@ -108,27 +107,44 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   const int64_t s0 = (int64_t)blockIdx.x * ts.span;
   const int64_t s1 = min(s0 + ts.span, ts.total);
 
+  if (s0 >= s1) return;   // no tokens for this workgroup (uniform)
+
   // Per-lane element offsets inside a tile (relative to the tile's first row).
   const uint32_t koff = (uint32_t)(m16 * D + 8 * q4);
   const uint32_t voff = (uint32_t)(4 * q4 * D + VW * m16);
 
-  for (int64_t x = s0; x < s1;) {
+  // One piece: the part [c0, c1) of a unit that lies in this span.
+  struct Ctx {
+    const uint16_t* kg;
+    const uint16_t* vg;
+    int64_t x;        // stream position of token c0
+    int64_t start;    // stream position of the unit's token 0
+    int64_t orow;     // output row of the unit's first head
+    int64_t w0, w_last;
+    int c0, c1, ntiles;
+    bool whole;
+    int slot_id;      // only the first and the last piece of a span can be partial
+  };
+  auto open_piece = [&](int64_t x) __attribute__((always_inline)) {
     const Piece pc = locate(p, sm_P, ts, x);
-    const UnitInfo& ui = pc.ui;
-    const int c0 = pc.t;
-    const int c1 = (int)min((int64_t)ui.n, pc.t + (s1 - x));
-    const bool whole = c0 == 0 && c1 == ui.n;
-    const int slot_id = x == s0 ? 0 : 1;   // only the first and the last piece of a span can be partial
-    const int64_t w0 = pc.start / ts.span, w_last = (pc.start + ui.n - 1) / ts.span;
-    x += c1 - c0;
-
-    const uint16_t* kg = reinterpret_cast<const uint16_t*>(p.k) + ui.row0 * D;
-    const uint16_t* vg = reinterpret_cast<const uint16_t*>(p.v) + ui.row0 * D;
-    const int64_t orow = out_row0(p, ui);
-    const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + orow * D;
-
-    // B operands of the score product: query head hb*16 + m16, columns 32s + 8q4 .. +7.
-    u32x4 qf[HB][KS];
+    Ctx c;
+    c.x = x;
+    c.start = pc.start;
+    c.c0 = pc.t;
+    c.c1 = (int)min((int64_t)pc.ui.n, pc.t + (s1 - x));
+    c.ntiles = (c.c1 - c.c0 + TILE - 1) / TILE;
+    c.whole = c.c0 == 0 && c.c1 == pc.ui.n;
+    c.slot_id = x == s0 ? 0 : 1;
+    c.w0 = pc.start / ts.span;
+    c.w_last = (pc.start + pc.ui.n - 1) / ts.span;
+    c.kg = reinterpret_cast<const uint16_t*>(p.k) + pc.ui.row0 * D;
+    c.vg = reinterpret_cast<const uint16_t*>(p.v) + pc.ui.row0 * D;
+    c.orow = out_row0(p, pc.ui);
+    return c;
+  };
+  // B operands of the score product: query head hb*16 + m16, columns 32s + 8q4 .. +7.
+  auto load_q = [&](u32x4 (&qf)[HB][KS], const Ctx& c) __attribute__((always_inline)) {
+    const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + c.orow * D;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       const int h = hb * 16 + m16;
@@ -136,9 +152,42 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       for (int s = 0; s < KS; ++s)
         qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + (int64_t)h * D + 32 * s + 8 * q4) : u32x4{0, 0, 0, 0};
     }
+  };
+  auto load_tile = [&](Tile16<D>& T, const Ctx& c, int t0) __attribute__((always_inline)) {
+    if (t0 + TILE <= c.c1) {
+      // full tile: one base address per lane, the rest are immediate offsets
+      const uint16_t* kt = c.kg + (int64_t)t0 * D + koff;
+      const uint16_t* vt = c.vg + (int64_t)t0 * D + voff;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vrow_t*>(vt + i * D));
+    } else {
+      // ragged tail: rows past the piece are clamped to its last valid row
+      // (in bounds and finite); their weights are forced to 0 below
+      const int last = c.c1 - 1;
+      const uint16_t* kt = c.kg + (int64_t)min(t0 + m16, last) * D + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        T.v[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const vrow_t*>(c.vg + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
+    }
+  };
+  // The TPW tiles j, j+NW, ... of a batch.  Every load is issued (an index past
+  // the piece's last tile is clamped to it: in bounds, its compute skipped), so
+  // the number of loads in flight is the same on every path; a conditional
+  // load would make the compiler wait for all of them before any compute.
+  auto load_batch = [&](Tile16<D> (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) load_tile(T[u], c, c.c0 + min(j + NW * u, c.ntiles - 1) * TILE);
+  };
 
-    float m_run[HB], l_run[HB];
-    f32x4 oacc[VW][HB];
+  u32x4 qf[HB][KS];
+  float m_run[HB], l_run[HB];
+  f32x4 oacc[VW][HB];
+  auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       m_run[hb] = -INFINITY;
@@ -146,99 +195,70 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 #pragma unroll
       for (int r = 0; r < VW; ++r) oacc[r][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
 
-    const int ntiles = (c1 - c0 + TILE - 1) / TILE;
-    const int last = c1 - 1;
-    // Each iteration issues the loads of TPW tiles (w + NW*(TPW*it + u)) before
-    // computing any of them, so a wavefront keeps TPW tiles in flight.
-    auto load_tile = [&](Tile16<D>& T, int t0) {
-      if (t0 + TILE <= c1) {
-        // full tile: one base address per lane, the rest are immediate offsets
-        const uint16_t* kt = kg + (int64_t)t0 * D + koff;
-        const uint16_t* vt = vg + (int64_t)t0 * D + voff;
+  auto compute_tile = [&](const Tile16<D>& T, int t0, int c1) __attribute__((always_inline)) {
+    u32x2 phi[HB], plo[HB];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vrow_t*>(vt + i * D));
-      } else {
-        // ragged tail: rows past the chunk are clamped to its last valid row
-        // (in bounds and finite); their weights are forced to 0 below
-        const uint16_t* kt = kg + (int64_t)min(t0 + m16, last) * D + 8 * q4;
+      for (int s = 0; s < KS; ++s) sc = mfma_k32(T.k[s], qf[hb][s], sc);
+      float x[4];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
+      for (int i = 0; i < 4; ++i) x[i] = sc[i] * sl2;
+      if (t0 + TILE > c1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          T.v[i] = __builtin_nontemporal_load(
-              reinterpret_cast<const vrow_t*>(vg + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
+          if (t0 + 4 * q4 + i >= c1) x[i] = -INFINITY;
       }
-    };
-    auto compute_tile = [&](const Tile16<D>& T, int t0) {
-      u32x2 phi[HB], plo[HB];
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__any(mx > m_run[hb])) {   // wave-uniform: some head's maximum grew
+        const float m_new = fmaxf(m_run[hb], mx);
+        const float alpha = exp2f(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
+        m_run[hb] = m_new;
+        l_run[hb] *= alpha;
+#pragma unroll
+        for (int r = 0; r < VW; ++r) oacc[r][hb] *= alpha;
+      }
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = exp2f(x[i] - m_run[hb]);
+        l_run[hb] += pv[i];
+      }
+      const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
+      const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
+      const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
+      phi[hb] = u32x2{h01, h23};
+      plo[hb] = u32x2{l01, l23};
+    }
+#pragma unroll
+    for (int r = 0; r < VW; ++r) {
+      const int w = r >> 1;
+      u32x2 va;
+      if (r & 1)
+        va = u32x2{pack_halves<true>(T.v[0][w], T.v[1][w]), pack_halves<true>(T.v[2][w], T.v[3][w])};
+      else
+        va = u32x2{pack_halves<false>(T.v[0][w], T.v[1][w]), pack_halves<false>(T.v[2][w], T.v[3][w])};
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sc = mfma_k32(T.k[s], qf[hb][s], sc);
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = sc[i] * sl2;
-        if (t0 + TILE > c1) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t0 + 4 * q4 + i >= c1) x[i] = -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any(mx > m_run[hb])) {   // wave-uniform: some head's maximum grew
-          const float m_new = fmaxf(m_run[hb], mx);
-          const float alpha = exp2f(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
-          m_run[hb] = m_new;
-          l_run[hb] *= alpha;
-#pragma unroll
-          for (int r = 0; r < VW; ++r) oacc[r][hb] *= alpha;
-        }
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = exp2f(x[i] - m_run[hb]);
-          l_run[hb] += pv[i];
-        }
-        const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
-        const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
-        const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
-        phi[hb] = u32x2{h01, h23};
-        plo[hb] = u32x2{l01, l23};
+        oacc[r][hb] = mfma_k16(va, phi[hb], oacc[r][hb]);
+        oacc[r][hb] = mfma_k16(va, plo[hb], oacc[r][hb]);
       }
-#pragma unroll
-      for (int r = 0; r < VW; ++r) {
-        const int w = r >> 1;
-        u32x2 va;
-        if (r & 1)
-          va = u32x2{pack_halves<true>(T.v[0][w], T.v[1][w]), pack_halves<true>(T.v[2][w], T.v[3][w])};
-        else
-          va = u32x2{pack_halves<false>(T.v[0][w], T.v[1][w]), pack_halves<false>(T.v[2][w], T.v[3][w])};
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          oacc[r][hb] = mfma_k16(va, phi[hb], oacc[r][hb]);
-          oacc[r][hb] = mfma_k16(va, plo[hb], oacc[r][hb]);
-        }
-      }
-    };
-    for (int j = wave; j < ntiles; j += NW * TPW) {
-      Tile16<D> T[TPW];
-      // Loads are issued unconditionally (a tile index past the end is clamped
-      // to the last tile: in bounds, and its compute is skipped) so that the
-      // number of loads in flight is the same on every path; a conditional load
-      // would make the compiler wait for all of them before the first compute.
-#pragma unroll
-      for (int u = 0; u < TPW; ++u) load_tile(T[u], c0 + min(j + NW * u, ntiles - 1) * TILE);
-#pragma unroll
-      for (int u = 0; u < TPW; ++u)
-        if (j + NW * u < ntiles) compute_tile(T[u], c0 + (j + NW * u) * TILE);
     }
+  };
+  auto compute_batch = [&](const Tile16<D> (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+      if (j + NW * u < c.ntiles) compute_tile(T[u], c.c0 + (j + NW * u) * TILE, c.c1);
+  };
 
-    // ---- combine the wavefronts of the workgroup ---------------------------
+  // End of a piece: combine the wavefronts' states, then wavefront 0 stores
+  // the normalised output (whole unit) or the piece's state (split unit).
+  auto end_piece = [&](const Ctx& c) __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       float lt = l_run[hb];
@@ -292,15 +312,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       __syncthreads();
     }
 
-    // ---- wavefront 0 stores the piece's result -----------------------------
     // Lane (q4, m16) holds head m16 of each head block, columns D/16*(4*q4+i) + r.
     if (wave == 0) {
-      const int64_t slot = 2 * (int64_t)blockIdx.x + slot_id;
+      const int64_t slot = 2 * (int64_t)blockIdx.x + c.slot_id;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         const int h = hb * 16 + m16;
         if (h >= G) continue;
-        if (whole) {
+        if (c.whole) {
           const float inv = Lh[hb] > 0.f ? 1.f / Lh[hb] : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -310,13 +329,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 #pragma unroll
               for (int r = 0; r < VW; r += 2)
                 wds[r / 2] = f32_to_bf16_rne(oacc[r][hb][i] * inv) | (f32_to_bf16_rne(oacc[r + 1][hb][i] * inv) << 16);
-              uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (orow + h) * D + col;
+              uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (c.orow + h) * D + col;
               if constexpr (VW == 8)
                 *reinterpret_cast<u32x4*>(dst) = u32x4{wds[0], wds[1], wds[2], wds[3]};
               else
                 *reinterpret_cast<u32x2*>(dst) = u32x2{wds[0], wds[1]};
             } else {
-              float* dst = reinterpret_cast<float*>(p.out) + (orow + h) * D + col;
+              float* dst = reinterpret_cast<float*>(p.out) + (c.orow + h) * D + col;
 #pragma unroll
               for (int r = 0; r < VW; r += 4)
                 *reinterpret_cast<f32x4*>(dst + r) =
@@ -325,15 +344,18 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
             }
           }
         } else if (p.fused) {
-          float* wo = p.ws_o + (slot * G + h) * D;
+          // 16-byte stores that write through to memory, so that a workgroup
+          // on another XCD reads them back (see fused_merge)
+          const Rsrc ro = slot_rsrc(p.ws_o + slot * G * D, G * D);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            const int col = VW * (4 * q4 + i);
 #pragma unroll
-            for (int r = 0; r < VW; ++r) store_coherent(wo + VW * (4 * q4 + i) + r, oacc[r][hb][i]);
-          if (q4 == 0) {
-            store_coherent(p.ws_ml + (slot * G + h) * 2, Mh[hb]);
-            store_coherent(p.ws_ml + (slot * G + h) * 2 + 1, Lh[hb]);
+            for (int r = 0; r < VW; r += 4)
+              store4_coherent(ro, h * D + col + r,
+                              f32x4{oacc[r][hb][i], oacc[r + 1][hb][i], oacc[r + 2][hb][i], oacc[r + 3][hb][i]});
           }
+          if (q4 == 0) store2_coherent(slot_rsrc(p.ws_ml + slot * G * 2, G * 2), 2 * h, Mh[hb], Lh[hb]);
         } else {
           float* wo = p.ws_o + (slot * G + h) * D;
 #pragma unroll
@@ -351,12 +373,57 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         }
       }
     }
-    if (!whole && p.fused) {
+    if (!c.whole && p.fused) {
       // the piece of w0 is its last piece (slot 2*w0 + 1) unless the unit starts w0's span
-      const int64_t first_slot = 2 * w0 + (pc.start != w0 * ts.span ? 1 : 0);
-      fused_merge<D, NT>(p, w0, w_last, first_slot, orow, &sm_flag);
+      const int64_t first_slot = 2 * c.w0 + (c.start != c.w0 * ts.span ? 1 : 0);
+      fused_merge<D, NT>(p, c.w0, c.w_last, first_slot, c.orow, &sm_flag);
+    }
+  };
+
+  // ---- main loop ------------------------------------------------------------
+  // Two tile buffers in turn: while one batch is computed the next one (of the
+  // same piece, or the first batch of the next piece of the span) is already
+  // loading, so the end of a piece (the combine across wavefronts and the
+  // stores) overlaps the next piece's first loads.
+  Ctx pc = open_piece(s0);
+  int j = wave;
+  load_q(qf, pc);
+  reset_state();
+  Tile16<D> TA[TPW], TB[TPW];
+  load_batch(TA, pc, j);
+  // One step with `cur` loaded: false if it is the span's last batch (left
+  // for the caller), else load the next batch into `nxt` and compute `cur`.
+  auto step = [&](const Tile16<D> (&cur)[TPW], Tile16<D> (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
+    const bool piece_done = j + NW * TPW >= pc.ntiles;
+    const int64_t xn = pc.x + (pc.c1 - pc.c0);
+    if (piece_done && xn >= s1) return false;
+    if (piece_done) {
+      const Ctx pn = open_piece(xn);
+      load_batch(nxt, pn, wave);
+      compute_batch(cur, pc, j);
+      load_q(qf, pn);   // the next piece's queries: their latency overlaps end_piece
+      end_piece(pc);
+      reset_state();
+      pc = pn;
+      j = wave;
+    } else {
+      load_batch(nxt, pc, j + NW * TPW);
+      compute_batch(cur, pc, j);
+      j += NW * TPW;
+    }
+    return true;
+  };
+  for (;;) {
+    if (!step(TA, TB)) {
+      compute_batch(TA, pc, j);
+      break;
+    }
+    if (!step(TB, TA)) {
+      compute_batch(TB, pc, j);
+      break;
     }
   }
+  end_piece(pc);
 }
 
 }  // namespace gqa

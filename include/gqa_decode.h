@@ -38,7 +38,7 @@
  *   valid, once the stream reaches the call.  No host synchronisation.
  * Work split.  The matrix-core path divides all valid tokens of the call,
  *   in (layer, sequence, KV head, token) order, evenly among its workgroups
- *   (up to two per CU), whatever the sequence lengths; the vector path cuts
+ *   (one per CU by default), whatever the sequence lengths; the vector path cuts
  *   each sequence into chunks of a planned size.  Pieces of a (layer,
  *   sequence, KV head) computed by different workgroups leave partial
  *   softmax states in the workspace that are combined in a fixed order
@@ -120,14 +120,20 @@ typedef struct gqa_dims {
                             multiple of 64: tokens per workgroup (matrix-core
                             path) or per chunk of a sequence (vector path) */
   int32_t path;          /* gqa_path */
-  int32_t workgroup_waves; /* 0: default; else wavefronts per workgroup of the
-                              matrix-core kernel: 4, 8 or 16 (reduced to 8
-                              when G > 16 and to 4 when G > 32) */
-  int32_t tiles_in_flight; /* 0: default; else 16-token tiles each wavefront of
-                              the matrix-core kernel loads before computing
-                              them: 1 or 2 (reduced to 1 where registers do
-                              not allow 2) */
+  int32_t workgroup_waves; /* 0: default (4); else wavefronts per workgroup of
+                              the matrix-core kernel: 4, 8 or 16 (16 is run
+                              as 8, and G > 32 runs 4) */
+  int32_t tiles_in_flight; /* 0: default (1); else 16-token tiles per load
+                              batch of each wavefront of the matrix-core
+                              kernel: 1 or 2 (2 only for G <= 16 with 4
+                              wavefronts, else 1).  A wavefront computes one
+                              batch while the next one loads. */
   int32_t merge;           /* gqa_merge */
+  int32_t workgroups_per_cu; /* 0: default (1); else matrix-core workgroups
+                                launched per compute unit when the split is
+                                balanced (no chunk_tokens): 1 to 4, reduced to
+                                what the kernel's registers and LDS let reside
+                                on one CU together */
 } gqa_dims;
 
 /*

@@ -90,6 +90,8 @@ def test_status_strings():
     (dict(waves=32), INVALID),
     (dict(tiles=3), INVALID),                  # tiles in flight not 1 or 2
     (dict(tiles=-1), INVALID),
+    (dict(per_cu=5), INVALID),                 # workgroups per CU: 0 (default) or 1 to 4
+    (dict(per_cu=-1), INVALID),
 ])
 def test_dims_validation(kw, expect):
     d = dims(**kw)

@@ -186,6 +186,16 @@ def test_kernel_variants(shape, waves, tiles, span, merge):
     check(x, path="mfma", chunk_tokens=span, waves=waves, tiles=tiles, merge=merge, label="variant-" + merge)
 
 
+@pytest.mark.parametrize("per_cu", [1, 2, 3, 4])
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+def test_workgroups_per_cu(per_cu, merge):
+    """The even token split over one to four resident workgroups per CU."""
+    for shape in (SHAPES[3], SHAPES[5], (3, 32, 8, 128, 4000, 1)):
+        B, hq, hkv, d, T, lo = shape
+        x = small(B, hq, hkv, d, T, seed=seed_of(shape, 37), lo=lo)
+        check(x, path="mfma", per_cu=per_cu, merge=merge, label="per_cu %d %s" % (per_cu, merge))
+
+
 def test_token_split_with_empty_and_tiny_sequences():
     """Sequences of 0, 1, 15, 16, 17 and many tokens in one batch: the token
     stream skips empty sequences (their outputs are zero) and spans cross
