@@ -191,7 +191,12 @@ def main():
 
     d = gqa.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype, out_dtype, chunk_tokens=args.chunk_tokens,
                       path=args.path)
-    chunk, n_chunks = gqa.plan(d, w.layers)
+    a, b = gqa.plan(d, w.layers)
+    mfma = args.path == "mfma" or (args.path == "auto" and w.dtype == torch.bfloat16 and w.B <= 4096)
+    if mfma:   # token split: (forced tokens per workgroup or 0 for an even split, workgroups)
+        split = {"kernel": "matrix-core, token split", "workgroups": b, "tokens_per_workgroup": a or "even"}
+    else:      # vector path: (tokens per chunk, chunks of the longest sequence)
+        split = {"kernel": "vector ALU, chunked", "chunk_tokens": a, "chunks_per_sequence": b}
     traffic = read_traffic(w.name, nbytes) if args.path in ("auto", "mfma") and not args.chunk_tokens else None
 
     result = {
@@ -213,7 +218,7 @@ def main():
                    "cached_tokens": [w.seq_lo, w.seq_hi], "seq_lens_sum": int(seq_lens.sum()), "layers": w.layers,
                    "layout": "packed" if w.packed else "dense", "accumulate": "fp32",
                    "out_dtype": "bf16" if out_dtype == torch.bfloat16 else "fp32",
-                   "path": args.path, "chunk_tokens": chunk, "chunks_per_sequence": n_chunks,
+                   "path": args.path, "work_split": split,
                    "input_batches_rotated": reps, "algorithmic_bytes_per_step": nbytes,
                    "wall_s_timed_region": round(wall, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
