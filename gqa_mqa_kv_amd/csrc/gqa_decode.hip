@@ -163,21 +163,18 @@ Plan make_plan(const gqa_dims* d, int32_t L) {
 
 typedef void (*kernel_fn)(gqa::Problem);
 
-// Kernel variants instantiated per head-block count hb = ceil(G/16): larger
-// workgroups and more tiles per load batch cost registers (a wavefront holds
-// two batches: the one it computes and the next one, loading), and only the
-// variants that fit (or nearly fit) the register file exist.
-int max_waves(int hb) { return hb <= 2 ? 8 : 4; }
-int max_tiles(int hb, int waves) { return hb == 1 && waves == 4 ? 2 : 1; }
+// Kernel variants instantiated per head-block count hb = ceil(G/16).  Each
+// wavefront holds two tile batches in registers (the one it computes and the
+// next one, loading), which leaves room for one wavefront per SIMD: the
+// workgroup has 4 wavefronts, and 2 tiles per batch only fit for hb = 1.
+int max_waves(int) { return 4; }
+int max_tiles(int hb, int) { return hb == 1 ? 2 : 1; }
 
 template <int D>
-kernel_fn mfma_kernel(int hb, int waves, int tiles) {
+kernel_fn mfma_kernel(int hb, int, int tiles) {
   switch (hb) {
-    case 1:
-      if (waves >= 8) return gqa::gqa_decode_mfma<D, 1, 8, 1>;
-      return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 4, 1>;
-    case 2:
-      return waves >= 8 ? gqa::gqa_decode_mfma<D, 2, 8, 1> : gqa::gqa_decode_mfma<D, 2, 4, 1>;
+    case 1: return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 4, 1>;
+    case 2: return gqa::gqa_decode_mfma<D, 2, 4, 1>;
     case 3: return gqa::gqa_decode_mfma<D, 3, 4, 1>;
     default: return gqa::gqa_decode_mfma<D, 4, 4, 1>;
   }

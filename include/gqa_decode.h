@@ -120,9 +120,11 @@ typedef struct gqa_dims {
                             multiple of 64: tokens per workgroup (matrix-core
                             path) or per chunk of a sequence (vector path) */
   int32_t path;          /* gqa_path */
-  int32_t workgroup_waves; /* 0: default (4); else wavefronts per workgroup of
-                              the matrix-core kernel: 4, 8 or 16 (16 is run
-                              as 8, and G > 32 runs 4) */
+  int32_t workgroup_waves; /* 0, 4, 8 or 16 (others are invalid): wavefronts
+                              per workgroup of the matrix-core kernel.  Every
+                              value runs as 4: each wavefront keeps two tile
+                              batches in registers, which leaves room for one
+                              wavefront per SIMD */
   int32_t tiles_in_flight; /* 0: default (1); else 16-token tiles per load
                               batch of each wavefront of the matrix-core
                               kernel: 1 or 2 (2 only for G <= 16 with 4
