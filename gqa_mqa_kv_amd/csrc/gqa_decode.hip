@@ -39,6 +39,7 @@ int cu_count() {
 
 int max_waves(int hb);
 int max_tiles(int hb, int waves);
+int default_tiles(int hb);
 int resident_groups_per_cu(const gqa_dims* d, int waves, int tiles);
 
 bool use_mfma(const gqa_dims* d) {
@@ -104,7 +105,7 @@ Plan make_plan(const gqa_dims* d, int32_t L) {
   if (p.mfma) {
     p.waves = d->workgroup_waves ? d->workgroup_waves : 4;
     if (p.waves > max_waves(hb)) p.waves = max_waves(hb);
-    p.tiles = d->tiles_in_flight ? d->tiles_in_flight : 1;
+    p.tiles = d->tiles_in_flight ? d->tiles_in_flight : default_tiles(hb);
     if (p.tiles > max_tiles(hb, p.waves)) p.tiles = max_tiles(hb, p.waves);
     // Token split: the valid tokens (at most units * T) are shared evenly by
     // the workgroups, by default one per CU: co-resident workgroups (and
@@ -163,20 +164,21 @@ Plan make_plan(const gqa_dims* d, int32_t L) {
 
 typedef void (*kernel_fn)(gqa::Problem);
 
-// Kernel variants instantiated per head-block count hb = ceil(G/16).  Each
-// wavefront holds two tile batches in registers (the one it computes and the
-// next one, loading), which leaves room for one wavefront per SIMD: the
-// workgroup has 4 wavefronts, and 2 tiles per batch only fit for hb = 1.
+// Kernel variants per head-block count hb = ceil(G/16).  A wavefront serves
+// one block of 16 heads (G <= 16) or two (G <= 64); beyond 32 heads the four
+// wavefronts form two head groups.  Each wavefront holds two tile batches in
+// registers (the one it computes and the next one, loading), which leaves
+// room for one wavefront per SIMD; two tiles per batch fit for G <= 16 only.
 int max_waves(int) { return 4; }
 int max_tiles(int hb, int) { return hb == 1 ? 2 : 1; }
+int default_tiles(int) { return 1; }
 
 template <int D>
 kernel_fn mfma_kernel(int hb, int, int tiles) {
   switch (hb) {
-    case 1: return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 4, 1>;
-    case 2: return gqa::gqa_decode_mfma<D, 2, 4, 1>;
-    case 3: return gqa::gqa_decode_mfma<D, 3, 4, 1>;
-    default: return gqa::gqa_decode_mfma<D, 4, 4, 1>;
+    case 1: return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 1, 4, 1>;
+    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1>;
+    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1>;
   }
 }
 

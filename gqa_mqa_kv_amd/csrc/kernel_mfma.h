@@ -1,16 +1,20 @@
-// Matrix-core GQA decode kernel for bf16 caches, D = 64 or 128, G <= 16*HB.
+// Matrix-core GQA decode kernel for bf16 caches, D = 64 or 128, G <= 16*HB*HG.
 //
 // Work split ("token split", see common.h): the valid tokens of all units
 // form one stream cut into equal spans, one per workgroup (one per CU),
 // so every workgroup streams the same number of bytes whatever the sequence
-// lengths.  A workgroup walks its span unit piece by unit piece; for each
-// piece, wavefront w streams the 16-token tiles w, w+NW, w+2NW, ... (the
-// wavefronts sweep adjacent memory together) straight from HBM into
-// registers, and every K/V byte is read once and serves all G query heads of
-// the group.  Each wavefront holds two batches of TPW tiles in registers: it
-// computes one while the next one (of the same piece, or the first batch of
-// the span's next piece) is loading, so the stream does not stop at piece
-// boundaries, where the wavefronts combine their softmax states.
+// lengths.  A workgroup walks its span unit piece by unit piece.  Its
+// wavefronts each serve HB blocks of 16 heads (one block for up to 16 heads,
+// two beyond) and are laid out as (head group, tile lane): up to 32 heads all
+// four wavefronts are tile lanes of one group, 33..64 heads use two groups
+// of two lanes.  For each piece, lane l
+// streams the 16-token tiles l, l+NL, l+2NL, ... straight from HBM into
+// registers (the lanes sweep adjacent memory together), and every K/V byte
+// leaves HBM once for all G query heads of the group.  Each wavefront holds
+// two batches of TPW tiles in registers: it computes one while the next one
+// (of the same piece, or the first batch of the span's next piece) is
+// loading, so the stream does not stop at piece boundaries, where the
+// wavefronts combine their softmax states.
 //
 // Scores: S^T[token][head] = K Q^T on v_mfma_f32_16x16x32_bf16, with
 //   A = 16 key rows x 32 columns (lane (m = lane%16, q4 = lane/16) holds 8
@@ -81,14 +85,20 @@ struct Tile16 {
   typename VRow<D>::type v[4];   // V rows 4*q4 + i, columns D/16*m16 ..
 };
 
-template <int D, int HB, int NW, int TPW>
+// Heads: each wavefront serves HB blocks of 16 query heads; the wavefronts
+// form HG groups (wavefront w is in group w % HG and streams tile lane w / HG
+// of the NW / HG lanes), so the workgroup covers 16 * HB * HG heads.  With
+// HG > 1 a tile is read once per group; the repeats are served by the caches.
+template <int D, int HB, int HG, int NW, int TPW>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
+  static_assert(NW % HG == 0, "head groups must divide the wavefronts");
   constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
-  constexpr int HP = HB * 16;             // padded heads
+  constexpr int NL = NW / HG;             // tile lanes
+  constexpr int HP = HB * 16;             // heads per wavefront
   constexpr int SLOT = HB * VW * 4 * 64;  // floats of one wavefront's O in lane order
   typedef typename VRow<D>::type vrow_t;
 
-  __shared__ float sm_slot[(NW > 1 ? NW / 2 : 1) * SLOT];
+  __shared__ float sm_slot[(NL > 1 ? HG * (NL / 2) : 1) * SLOT];
   __shared__ float sm_wm[NW][HP], sm_wl[NW][HP];
   __shared__ int32_t sm_P[kMaxBatch + 1];
   __shared__ int32_t sm_wave[NW];
@@ -96,8 +106,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);   // wavefront index, in a scalar register (everything derived from it is too)
+  const int hg = wave % HG, tl = wave / HG;
   const int m16 = lane & 15, q4 = lane >> 4;
   const int G = p.G;
+  const int head0 = hg * HP + m16;      // this lane's query head of block 0 (block hb: head0 + 16 hb)
   const float sl2 = p.scale_log2;
 
   build_prefix<NT>(p, sm_P, sm_wave);
@@ -142,15 +154,15 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     c.orow = out_row0(p, pc.ui);
     return c;
   };
-  // B operands of the score product: query head hb*16 + m16, columns 32s + 8q4 .. +7.
+  // B operands of the score product: query head head0 + 16 hb, columns 32s + 8q4 .. +7.
   auto load_q = [&](u32x4 (&qf)[HB][KS], const Ctx& c) __attribute__((always_inline)) {
-    const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + c.orow * D;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      const int h = hb * 16 + m16;
+      const int h = head0 + 16 * hb;
+      const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + (c.orow + h) * D;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + (int64_t)h * D + 32 * s + 8 * q4) : u32x4{0, 0, 0, 0};
+        qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + 32 * s + 8 * q4) : u32x4{0, 0, 0, 0};
     }
   };
   auto load_tile = [&](Tile16<D>& T, const Ctx& c, int t0) __attribute__((always_inline)) {
@@ -175,13 +187,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
             reinterpret_cast<const vrow_t*>(c.vg + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
     }
   };
-  // The TPW tiles j, j+NW, ... of a batch.  Every load is issued (an index past
+  // The TPW tiles j, j+NL, ... of a batch.  Every load is issued (an index past
   // the piece's last tile is clamped to it: in bounds, its compute skipped), so
   // the number of loads in flight is the same on every path; a conditional
   // load would make the compiler wait for all of them before any compute.
   auto load_batch = [&](Tile16<D> (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) load_tile(T[u], c, c.c0 + min(j + NW * u, c.ntiles - 1) * TILE);
+    for (int u = 0; u < TPW; ++u) load_tile(T[u], c, c.c0 + min(j + NL * u, c.ntiles - 1) * TILE);
   };
 
   u32x4 qf[HB][KS];
@@ -253,11 +265,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   auto compute_batch = [&](const Tile16<D> (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
-      if (j + NW * u < c.ntiles) compute_tile(T[u], c.c0 + (j + NW * u) * TILE, c.c1);
+      if (j + NL * u < c.ntiles) compute_tile(T[u], c.c0 + (j + NL * u) * TILE, c.c1);
   };
 
-  // End of a piece: combine the wavefronts' states, then wavefront 0 stores
-  // the normalised output (whole unit) or the piece's state (split unit).
+  // End of a piece: combine the states of the wavefronts of each head group,
+  // then the first wavefront of each group stores its heads: the normalised
+  // output (whole unit) or the piece's state (split unit).
   auto end_piece = [&](const Ctx& c) __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -273,25 +286,28 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     float Mh[HB], Lh[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      const int h = hb * 16 + m16;
-      float M = sm_wm[0][h];
+      const int e = hb * 16 + m16;
+      float M = sm_wm[hg][e];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_wm[w][h]);
+      for (int k = 1; k < NL; ++k) M = fmaxf(M, sm_wm[hg + HG * k][e]);
       float L = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w)
-        if (sm_wm[w][h] != -INFINITY) L += exp2f(sm_wm[w][h] - M) * sm_wl[w][h];
+      for (int k = 0; k < NL; ++k) {
+        const float mk = sm_wm[hg + HG * k][e];
+        if (mk != -INFINITY) L += exp2f(mk - M) * sm_wl[hg + HG * k][e];
+      }
       Mh[hb] = M;
       Lh[hb] = L;
       const float f = (m_run[hb] == -INFINITY) ? 0.f : exp2f(m_run[hb] - M);
 #pragma unroll
       for (int r = 0; r < VW; ++r) oacc[r][hb] *= f;
     }
-    // Tree over wavefronts: in each round the upper half hands its O to the lower half.
+    // Tree over the tile lanes of each head group: in each round the upper
+    // half hands its O to the lower half.
 #pragma unroll
-    for (int s = NW / 2; s >= 1; s /= 2) {
-      if (wave >= s && wave < 2 * s) {
-        float* dst = sm_slot + (wave - s) * SLOT + lane;
+    for (int s = NL / 2; s >= 1; s /= 2) {
+      if (tl >= s && tl < 2 * s) {
+        float* dst = sm_slot + (hg * (NL / 2) + (tl - s)) * SLOT + lane;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -300,8 +316,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
             for (int i = 0; i < 4; ++i) dst[((hb * VW + r) * 4 + i) * 64] = oacc[r][hb][i];
       }
       __syncthreads();
-      if (wave < s) {
-        const float* src = sm_slot + wave * SLOT + lane;
+      if (tl < s) {
+        const float* src = sm_slot + (hg * (NL / 2) + tl) * SLOT + lane;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -312,12 +328,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       __syncthreads();
     }
 
-    // Lane (q4, m16) holds head m16 of each head block, columns D/16*(4*q4+i) + r.
-    if (wave == 0) {
+    // Lane (q4, m16) holds head head0 + 16 hb of each block, columns D/16*(4*q4+i) + r.
+    if (tl == 0) {
       const int64_t slot = 2 * (int64_t)blockIdx.x + c.slot_id;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const int h = hb * 16 + m16;
+        const int h = head0 + 16 * hb;
         if (h >= G) continue;
         if (c.whole) {
           const float inv = Lh[hb] > 0.f ? 1.f / Lh[hb] : 0.f;
@@ -374,6 +390,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       }
     }
     if (!c.whole && p.fused) {
+      if constexpr (HG > 1) {
+        // every storing wavefront's stores complete before thread 0 counts the piece
+        if (tl == 0 && hg > 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+      }
       // the piece of w0 is its last piece (slot 2*w0 + 1) unless the unit starts w0's span
       const int64_t first_slot = 2 * c.w0 + (c.start != c.w0 * ts.span ? 1 : 0);
       fused_merge<D, NT>(p, c.w0, c.w_last, first_slot, c.orow, &sm_flag);
@@ -386,7 +410,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   // loading, so the end of a piece (the combine across wavefronts and the
   // stores) overlaps the next piece's first loads.
   Ctx pc = open_piece(s0);
-  int j = wave;
+  int j = tl;
   load_q(qf, pc);
   reset_state();
   Tile16<D> TA[TPW], TB[TPW];
@@ -394,22 +418,22 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   // One step with `cur` loaded: false if it is the span's last batch (left
   // for the caller), else load the next batch into `nxt` and compute `cur`.
   auto step = [&](const Tile16<D> (&cur)[TPW], Tile16<D> (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
-    const bool piece_done = j + NW * TPW >= pc.ntiles;
+    const bool piece_done = j + NL * TPW >= pc.ntiles;
     const int64_t xn = pc.x + (pc.c1 - pc.c0);
     if (piece_done && xn >= s1) return false;
     if (piece_done) {
       const Ctx pn = open_piece(xn);
-      load_batch(nxt, pn, wave);
+      load_batch(nxt, pn, tl);
       compute_batch(cur, pc, j);
       load_q(qf, pn);   // the next piece's queries: their latency overlaps end_piece
       end_piece(pc);
       reset_state();
       pc = pn;
-      j = wave;
+      j = tl;
     } else {
-      load_batch(nxt, pc, j + NW * TPW);
+      load_batch(nxt, pc, j + NL * TPW);
       compute_batch(cur, pc, j);
-      j += NW * TPW;
+      j += NL * TPW;
     }
     return true;
   };

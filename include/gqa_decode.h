@@ -125,11 +125,11 @@ typedef struct gqa_dims {
                               value runs as 4: each wavefront keeps two tile
                               batches in registers, which leaves room for one
                               wavefront per SIMD */
-  int32_t tiles_in_flight; /* 0: default (1); else 16-token tiles per load
-                              batch of each wavefront of the matrix-core
-                              kernel: 1 or 2 (2 only for G <= 16 with 4
-                              wavefronts, else 1).  A wavefront computes one
-                              batch while the next one loads. */
+  int32_t tiles_in_flight; /* 0: default (1); else 1 or 2: 16-token tiles per
+                              load batch of each wavefront of the matrix-core
+                              kernel (2 only for G <= 16, else 1).  A
+                              wavefront computes one batch while the next one
+                              loads. */
   int32_t merge;           /* gqa_merge */
   int32_t workgroups_per_cu; /* 0: default (1); else matrix-core workgroups
                                 launched per compute unit when the split is

@@ -78,6 +78,7 @@ SHAPES = [
     (2, 32, 1, 128, 600, 100),       # MQA, G = 32 (two head blocks)
     (1, 64, 1, 128, 450, None),      # G = 64 (four head blocks)
     (2, 12, 4, 128, 333, 10),        # G = 3 (partial head block)
+    (2, 48, 1, 64, 300, 7),          # G = 48: three head blocks (run as four, one empty), d = 64
     (2, 40, 1, 64, 257, 1),          # G = 40, d = 64
 ]
 
