@@ -1,6 +1,6 @@
 // Vector-ALU GQA decode kernel: any G <= 64, fp32 or bf16 storage, D = 64/128.
 //
-// One workgroup of 256 threads per (unit, chunk).  Tiles of 32 tokens of K and
+// One workgroup of 256 threads per (unit, chunk).  Tiles of 64 tokens of K and
 // V are staged through LDS (converted to fp32); scores for all G heads of the
 // group are computed from that single copy, the running softmax is updated
 // one wavefront per head, and P.V is accumulated in fp32 registers, thread t
@@ -24,7 +24,7 @@ struct Elem<uint16_t> {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gqa_decode_valu(Problem p) {
-  constexpr int NT = 256, TT = 32, NW = NT / 64;
+  constexpr int NT = 256, TT = 64, NW = NT / 64;
   constexpr int OMAX = kMaxGroup * D / NT;   // output elements per thread at G = 64
   constexpr int KP = D + 1;                  // padded LDS row (conflict-free column walks)
   __shared__ float q_s[kMaxGroup][D];
@@ -55,18 +55,30 @@ __global__ __launch_bounds__(256) void gqa_decode_valu(Problem p) {
   for (int r = 0; r < OMAX; ++r) o[r] = 0.f;
   __syncthreads();
 
+  // Tile t+1's K/V elements are loaded into registers while tile t is
+  // computed; thread tid owns elements e = tid + NT * r of a tile (row e / D,
+  // column e % D).  Rows past the chunk load a clamped (valid) row, stored
+  // as 0.
+  constexpr int EPT = TT * D / NT;
+  float kr[EPT], vr[EPT];
+  auto load_regs = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int e = tid + NT * r, t = min(t0 + e / D, c1 - 1);
+      kr[r] = Elem<T>::get(kg, (int64_t)t * D + e % D);
+      vr[r] = Elem<T>::get(vg, (int64_t)t * D + e % D);
+    }
+  };
+  if (c1 > c0) load_regs(c0);   // an empty sequence has no row to load
   for (int t0 = c0; t0 < c1; t0 += TT) {
     const int nt = min(TT, c1 - t0);
-    for (int e = tid; e < TT * D; e += NT) {
-      int t = e / D, c = e % D;
-      float kv = 0.f, vv = 0.f;
-      if (t < nt) {
-        kv = Elem<T>::get(kg, (int64_t)(t0 + t) * D + c);
-        vv = Elem<T>::get(vg, (int64_t)(t0 + t) * D + c);
-      }
-      k_s[t][c] = kv;
-      v_s[t][c] = vv;
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+      const int e = tid + NT * r, t = e / D, c = e % D;
+      k_s[t][c] = t < nt ? kr[r] : 0.f;
+      v_s[t][c] = t < nt ? vr[r] : 0.f;
     }
+    load_regs(min(t0 + TT, c1 - 1));   // the next tile (the last one again at the end: in bounds, unused)
     __syncthreads();
     // scores, base 2: s = (q . k) * scale * log2(e)
     for (int e = tid; e < G * TT; e += NT) {
