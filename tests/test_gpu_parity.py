@@ -257,6 +257,35 @@ def test_repeats_bitwise(merge):
         assert torch.equal(gpu_decode(x, path="mfma", chunk_tokens=256, merge=merge).cpu(), first)
 
 
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+def test_graph_replays_match_eager(merge):
+    """Decode calls captured in a HIP graph (a decode loop is commonly
+    captured): the library records no memset and leaves its arrival counters
+    at zero, so every replay gives the eager result bitwise, with eager work
+    and synchronisations between the replays."""
+    shapes = [(3, 32, 8, 128, 4000, 1), (2, 32, 1, 128, 600, 100)]
+    xs = [to_dev(small(*sh[:5], seed=seed_of(sh, 41), lo=sh[5])) for sh in shapes]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ls = [gqa.prepare(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], merge=merge, stream=s.cuda_stream,
+                          chunk_tokens=256) for x in xs]
+        eager = [l().clone() for l in ls]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        outs = [l() for l in ls] + [l() for l in ls]
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager + eager):
+            assert torch.equal(o, e), "replay %d differs from the eager result" % rep
+        gpu_decode(small(2, 8, 2, 64, 100, seed=43))   # eager work on the device between replays
+
+
 def test_paths_and_chunkings_agree():
     x = small(2, 32, 8, 128, 1500, seed=41, lo=1000)
     ref = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
