@@ -11,6 +11,9 @@ Contents
   "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): Mathematical
   Foundations, Arithmetic Intensity, and KV-Cache Scaling Mechanics",
   section 2, subsection "Grouped-Query Attention (GQA)".
+* :meth:`Oracle.rope` -- fp64 rotary position embedding (section 4 of the
+  same page, "Rotary Position Embeddings (RoPE) Interaction"), for the step
+  that appends the new token's keys and values.
 * :func:`kv_cache_bytes` -- the KV-cache size formula of the same page,
   section 1, "KV Cache Memory Footprint" (also stated on "Grouped-Query
   Attention Shares Keys Without Sharing Every Query").
@@ -69,6 +72,8 @@ class Oracle:
         lib.oracle_gqa_head_weights.restype = ctypes.c_int
         lib.oracle_gqa_head_weights.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp,
                                                 dbl, i64, i64, vp, vp]
+        lib.oracle_rope.restype = ctypes.c_int
+        lib.oracle_rope.argtypes = [i64, i64, ctypes.c_int, vp, vp, dbl, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         self._lib = lib
@@ -149,6 +154,24 @@ class Oracle:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return out
 
+    def rope(self, x, positions, base: float) -> np.ndarray:
+        """fp64 rotary embedding of ``x`` [..., d] at ``positions`` (one per
+        vector: broadcastable to x.shape[:-1]), base ``base``."""
+        if x.dtype not in _DTYPE_CODE:
+            raise TypeError("oracle takes float32, bfloat16 or float64 tensors")
+        x = x.detach().to("cpu").contiguous()
+        d = x.shape[-1]
+        n = x.numel() // d if d else 0
+        pos = np.ascontiguousarray(np.broadcast_to(np.asarray(
+            positions.cpu() if isinstance(positions, torch.Tensor) else positions, dtype=np.int64),
+            tuple(x.shape[:-1])).reshape(-1))
+        out = np.zeros(tuple(x.shape), dtype=np.float64)
+        rc = self._lib.oracle_rope(n, d, _DTYPE_CODE[x.dtype], x.data_ptr(), pos.ctypes.data, float(base),
+                                   out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return out
+
     def head_weights(self, q, k, v, seq_lens, scale: float, b: int, i: int, kv_offsets=None,
                      num_kv_heads: Optional[int] = None):
         """Softmax weights over the n valid tokens, and the output, of head (b, i)."""
@@ -183,6 +206,10 @@ def decode(*args, **kwargs) -> np.ndarray:
 
 def group_of(i: int, R: int) -> int:
     return default().group_of(i, R)
+
+
+def rope(x, positions, base: float) -> np.ndarray:
+    return default().rope(x, positions, base)
 
 
 def kv_cache_bytes(b: int, s: int, L: int, H_kv: int, d_k: int, bytes_per_elem: int = 2) -> int:

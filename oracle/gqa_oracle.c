@@ -29,6 +29,10 @@
  *   - bf16 inputs are widened by their definition (the 16 stored bits are the
  *     upper half of an IEEE binary32), which is exact.
  *
+ * Also: the rotary position embedding of section 4 of the same page
+ * ("Rotary Position Embeddings (RoPE) Interaction"), for the step that
+ * appends the new token's keys and values to the cache (oracle_rope).
+ *
  * Parity status: every function here is pinned by CPU tests against
  * closed forms, invariants, a library routine and the printed tables of the
  * pages (see the oracle tests); none is "parity unpinned".
@@ -186,6 +190,36 @@ int oracle_gqa_head_weights(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int
                         oracle_group_of(i, H_q / H_kv), n, scale, s, w, out);
   free(s);
   return rc;
+}
+
+/*
+ * Rotary position embedding of n vectors of d elements (d even):
+ * "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): ...",
+ * section 4, "Rotary Position Embeddings (RoPE) Interaction".  R_{Theta,m}
+ * is block diagonal with one 2x2 rotation R_{theta_j,m} per pair of
+ * consecutive elements, so elements 2j and 2j+1 (0-based) turn by the angle
+ * m * theta_j.  The page leaves theta_j and the orientation open; read as
+ * theta_j = base^(-2j/d) for j = 0 .. d/2-1 (base a parameter) and
+ * R = [[cos, -sin], [sin, cos]] acting on the pair as a column vector.
+ *   x   : n*d elements of the given dtype (vector v at x[v*d])
+ *   pos : n positions m, one per vector
+ *   out : n*d doubles
+ * Returns 0, or -1 for an odd or non-positive d, or a non-positive base.
+ */
+int oracle_rope(int64_t n, int64_t d, int dtype, const void* x, const int64_t* pos, double base, double* out) {
+  if (d <= 0 || d % 2 != 0 || !(base > 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t v = 0; v < n; ++v) {
+    for (int64_t j = 0; j < d / 2; ++j) {
+      const double theta = pow(base, -2.0 * (double)j / (double)d);
+      const double a = (double)pos[v] * theta;
+      const double c = cos(a), s = sin(a);
+      const double x0 = load_elem(x, v * d + 2 * j, dtype), x1 = load_elem(x, v * d + 2 * j + 1, dtype);
+      out[v * d + 2 * j] = x0 * c - x1 * s;
+      out[v * d + 2 * j + 1] = x0 * s + x1 * c;
+    }
+  }
+  return 0;
 }
 
 /* Threads the oracle's parallel loops use (1 without OpenMP). */

@@ -265,6 +265,67 @@ def pin_head_subset(orc):
     assert np.array_equal(run(orc, x, heads=ids), full[ids])
 
 
+# --------------------------------------------- rotary position embedding --
+# "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): ...",
+# section 4, "Rotary Position Embeddings (RoPE) Interaction".
+def pin_rope_closed_form(orc):
+    """Block-diagonal rotation of consecutive pairs, by m * base^(-2j/d):
+    d = 4, base 100 -> theta = (1, 1/10).  e_0 at position m goes to
+    (cos m, sin m, 0, 0); e_3 to (0, 0, -sin(m/10), cos(m/10))."""
+    x = torch.zeros(2, 4, dtype=torch.float64)
+    x[0, 0] = 1.0
+    x[1, 3] = 1.0
+    for m in (0, 1, 7, 1000):
+        got = orc.rope(x, [m, m], 100.0)
+        want = np.array([[math.cos(m), math.sin(m), 0.0, 0.0],
+                         [0.0, 0.0, -math.sin(m / 10.0), math.cos(m / 10.0)]])
+        assert np.abs(got - want).max() < 1e-12, m
+
+
+def pin_rope_identity_norm_composition(orc):
+    """Position 0 is the identity; every pair keeps its length; turning by a
+    then by b is turning by a + b."""
+    g = torch.Generator().manual_seed(201)
+    x = torch.randn(6, 128, dtype=torch.float64, generator=g)
+    assert np.array_equal(orc.rope(x, 0, 10000.0), x.numpy())
+    pos = [0, 1, 17, 4095, 32767, 131071]
+    y = orc.rope(x, pos, 10000.0)
+    n0 = (x.numpy().reshape(6, 64, 2) ** 2).sum(-1)
+    n1 = (y.reshape(6, 64, 2) ** 2).sum(-1)
+    assert np.abs(n0 - n1).max() < 1e-11
+    a, b = [3, 100, 5000, 1, 0, 77], [9, 28, 11111, 32766, 131071, 2]
+    two = orc.rope(torch.from_numpy(orc.rope(x, a, 10000.0)), b, 10000.0)
+    one = orc.rope(x, [i + j for i, j in zip(a, b)], 10000.0)
+    assert np.abs(two - one).max() < 1e-9
+
+
+def pin_rope_relative_position(orc):
+    """The page's identity: <R_m q, R_n k> = <R_(m-n) q, k> (the score of a
+    query head with its group's key depends on the distance only)."""
+    g = torch.Generator().manual_seed(202)
+    q = torch.randn(1, 64, dtype=torch.float64, generator=g)
+    k = torch.randn(1, 64, dtype=torch.float64, generator=g)
+    for m, n in ((5, 3), (0, 9), (4096, 4000), (30000, 12)):
+        lhs = float((orc.rope(q, m, 10000.0) * orc.rope(k, n, 10000.0)).sum())
+        rhs = float((orc.rope(q, m - n, 10000.0) * k.numpy()).sum())
+        assert abs(lhs - rhs) < 1e-9 * max(1.0, abs(rhs)), (m, n)
+
+
+def pin_rope_attention_shift(orc):
+    """Rotating every query at position p and every cached key at its own
+    position t leaves the GQA outputs unchanged when all positions move by
+    the same offset (scores depend on p - t only)."""
+    x = case(2, 8, 2, 64, 12, 211, lo=3)
+    T = x["k"].shape[2]
+    outs = []
+    for off in (0, 1000):
+        pq = torch.tensor([int(n) - 1 + off for n in x["seq_lens"]])
+        q = torch.from_numpy(orc.rope(x["q"], pq.view(2, 1), 10000.0))
+        k = torch.from_numpy(orc.rope(x["k"], (torch.arange(T) + off).view(1, 1, T), 10000.0))
+        outs.append(run(orc, dict(x, q=q, k=k)))
+    assert np.abs(outs[0] - outs[1]).max() < 1e-10
+
+
 # ------------------------------------------------------ page formulas --
 def pin_kv_cache_table():
     """Reproduce all nine cells of the printed 70B KV-cache table."""

@@ -41,6 +41,15 @@ MUTANTS = {
     "seq_len_of_first": ("(int64_t)seq_lens[b], scale, s, NULL", "(int64_t)seq_lens[0], scale, s, NULL"),
     # one token too many (reads a padding position)
     "extra_token": ("if (n < 0 || n > cap) return -1;\n  for", "n = n < cap ? n + 1 : n;\n  if (n < 0 || n > cap) return -1;\n  for"),
+    # rotary embedding: turning the other way
+    "rope_orientation": ("out[v * d + 2 * j] = x0 * c - x1 * s;", "out[v * d + 2 * j] = x0 * c + x1 * s;"),
+    # rotary embedding: pairs (j, j + d/2) instead of consecutive elements
+    "rope_half_split_pairs": ("load_elem(x, v * d + 2 * j, dtype), x1 = load_elem(x, v * d + 2 * j + 1, dtype);",
+                              "load_elem(x, v * d + j, dtype), x1 = load_elem(x, v * d + j + d / 2, dtype);"),
+    # rotary embedding: frequencies base^(-j/d) instead of base^(-2j/d)
+    "rope_frequency": ("pow(base, -2.0 * (double)j / (double)d)", "pow(base, -1.0 * (double)j / (double)d)"),
+    # rotary embedding: position off by one
+    "rope_position_off_by_one": ("const double a = (double)pos[v] * theta;", "const double a = (double)(pos[v] + 1) * theta;"),
 }
 
 _RUNNER = r"""
