@@ -7,10 +7,14 @@ tokens with the key/value head g = i / G of its contiguous group.  All work
 runs in hand-written HIP kernels (gqa_mqa_kv_amd/csrc); Python only marshals
 arguments.  See include/gqa_decode.h for the ABI.
 
-    from gqa_mqa_kv_amd import decode, decode_layers
-"""
-from ._binding import (GqaDims, GqaError, Prepared, decode, decode_layers, default_workspace, lib, make_dims, plan,
-                       prepare, status_string, workspace_bytes)
+    from gqa_mqa_kv_amd import decode, decode_layers, append_rope
 
-__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "default_workspace", "lib", "make_dims", "plan",
-           "status_string", "workspace_bytes"]
+append_rope is the step before a decode step: it turns the new token's
+queries and keys by the rotary position embedding of section 4 of the same
+page and appends its key and value to the cache.
+"""
+from ._binding import (GqaDims, GqaError, Prepared, append_rope, decode, decode_layers, default_workspace, lib,
+                       make_dims, plan, prepare, status_string, workspace_bytes)
+
+__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "append_rope", "default_workspace",
+           "lib", "make_dims", "plan", "status_string", "workspace_bytes"]

@@ -20,7 +20,7 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
-SYMBOLS = ("gqa_decode", "gqa_decode_layers", "gqa_decode_workspace_bytes", "gqa_decode_plan",
+SYMBOLS = ("gqa_append_rope", "gqa_decode", "gqa_decode_layers", "gqa_decode_workspace_bytes", "gqa_decode_plan",
            "gqa_status_string")
 
 
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode_workspace_bytes.argtypes = [dims_p, i32]
         L.gqa_decode_plan.restype = ctypes.c_int
         L.gqa_decode_plan.argtypes = [dims_p, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.gqa_append_rope.restype = ctypes.c_int
+        L.gqa_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp]
         L.gqa_status_string.restype = ctypes.c_char_p
         L.gqa_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -205,6 +207,59 @@ def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, 
                                    float(scale), _ptr(out), ctypes.byref(dims), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(), s))
     return out
+
+
+def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
+                max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None):
+    """Append each sequence's new token to one layer's cache with rotary
+    position embedding at position seq_lens[b] (see gqa_append_rope in
+    include/gqa_decode.h).  q [B,H_q,d]; k_new/v_new [B,H_kv,d]; caches dense
+    [B,H_kv,T_max,d], or packed with ``kv_offsets`` (int64 [B+1]) and
+    ``max_seq_len``.  Writes the caches in place; returns (q_out,
+    new_seq_lens): the rotated queries (a new tensor unless ``q_out`` is
+    given, which may be q itself) and the lengths after the append (a new
+    int32 tensor unless ``new_seq_lens`` is given, which may be seq_lens)."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k_new.dim() != 3 or v_new.shape != k_new.shape:
+        raise ValueError("expected q [B,H_q,d] and k_new/v_new [B,H_kv,d]")
+    B, H_q, d = q.shape
+    H_kv = k_new.shape[1]
+    if k_new.shape[0] != B or k_new.shape[2] != d or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("shape mismatch between q, k_new/v_new and seq_lens")
+    if kv_offsets is None:
+        if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.shape[:2] != (B, H_kv) or \
+                k_cache.shape[3] != d:
+            raise ValueError("dense caches must be [B,H_kv,T_max,d]")
+        T_max = k_cache.shape[2]
+    else:
+        _require(kv_offsets, "kv_offsets", dev)
+        if kv_offsets.dtype != torch.int64 or kv_offsets.shape != (B + 1,) or max_seq_len is None:
+            raise ValueError("packed caches need kv_offsets int64 [B+1] and max_seq_len")
+        if v_cache.numel() != k_cache.numel() or k_cache.numel() % (H_kv * d):
+            raise ValueError("packed cache size mismatch")
+        T_max = max_seq_len
+    for t in (k_new, v_new, k_cache, v_cache):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k_new, v_new and the caches must share one dtype")
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _require(q_out, "q_out", dev)
+    if q_out.shape != q.shape or q_out.dtype != q.dtype:
+        raise ValueError("q_out must match q")
+    if new_seq_lens is None:
+        new_seq_lens = torch.empty_like(seq_lens)
+    _require(new_seq_lens, "new_seq_lens", dev)
+    if new_seq_lens.shape != (B,) or new_seq_lens.dtype != torch.int32:
+        raise ValueError("new_seq_lens must be int32 [B]")
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _check(lib().gqa_append_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets),
+                                 _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), _ptr(q_out),
+                                 ctypes.byref(dims), s))
+    return q_out, new_seq_lens
 
 
 class Prepared:

@@ -10,6 +10,7 @@
 #include <cstdint>
 
 #include "kernel_mfma.h"
+#include "kernel_rope.h"
 #include "kernel_valu.h"
 
 namespace {
@@ -305,6 +306,47 @@ gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_ca
                              const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
   return launch(num_layers, q, k_cache, v_cache, kv_offsets, seq_lens, scale, out, dims, workspace, workspace_bytes,
                 stream);
+}
+
+gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                           float rope_base, void* q_out, const gqa_dims* dims, void* stream) {
+  gqa_status st = check_dims(dims, 1);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return GQA_ERR_INVALID_ARG;
+  if (dims->batch == 0) return GQA_OK;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !seq_lens || !q_out) return GQA_ERR_INVALID_ARG;
+  const uintptr_t e = dims->dtype == GQA_DTYPE_F32 ? 4 : 2;
+  if (!aligned(q, e) || !aligned(k_new, e) || !aligned(v_new, e) || !aligned(k_cache, e) || !aligned(v_cache, e) ||
+      !aligned(q_out, e) || !aligned(seq_lens, 4) || (new_seq_lens && !aligned(new_seq_lens, 4)) ||
+      (kv_offsets && !aligned(kv_offsets, 8)))
+    return GQA_ERR_INVALID_ARG;
+  gqa::RopeProblem p;
+  p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.q_out = q_out;
+  p.kv_offsets = kv_offsets;
+  p.seq_lens = seq_lens;
+  p.new_seq_lens = new_seq_lens;
+  p.B = dims->batch;
+  p.H_q = dims->num_q_heads;
+  p.H_kv = dims->num_kv_heads;
+  p.T_max = dims->max_seq_len;
+  p.base = (double)rope_base;
+  typedef void (*rope_fn)(gqa::RopeProblem);
+  rope_fn k;
+  if (dims->dtype == GQA_DTYPE_F32)
+    k = dims->head_dim == 128 ? gqa::gqa_append_rope<float, 128> : gqa::gqa_append_rope<float, 64>;
+  else
+    k = dims->head_dim == 128 ? gqa::gqa_append_rope<uint16_t, 128> : gqa::gqa_append_rope<uint16_t, 64>;
+  void* args[] = {&p};
+  if (hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)dims->batch), dim3(256), args, 0,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GQA_ERR_LAUNCH;
+  return GQA_OK;
 }
 
 const char* gqa_status_string(gqa_status s) {

@@ -1,0 +1,104 @@
+// Append the new token of every sequence to the KV cache, with rotary
+// position embedding ("Grouped-Query Attention (GQA) and Multi-Query
+// Attention (MQA): ...", section 4, "Rotary Position Embeddings (RoPE)
+// Interaction"): the token of sequence b is at position m = seq_lens[b];
+// every query head and, once per KV head, the key are turned by R_{Theta,m},
+// a 2x2 rotation of each pair of consecutive elements (2j, 2j+1) by the
+// angle m * theta_j, theta_j = base^(-2j/d).
+//
+// One workgroup of 256 threads per sequence.  The d/2 angles are computed
+// once, in double precision (m * theta_j reaches 1e5 radians), and shared
+// through LDS as single-precision cosine and sine; each thread then turns
+// element pairs of the queries and keys.
+#pragma once
+
+#include "common.h"
+
+namespace gqa {
+
+struct RopeProblem {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  void* q_out;
+  const int64_t* kv_offsets;   // [B+1] or nullptr (dense [B][H_kv][T_max][D])
+  const int32_t* seq_lens;     // [B]
+  int32_t* new_seq_lens;       // [B] or nullptr (may equal seq_lens)
+  int32_t B, H_q, H_kv, T_max;
+  double base;
+};
+
+template <typename T>
+struct RopeElem;
+template <>
+struct RopeElem<float> {
+  static __device__ __forceinline__ float get(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  static __device__ __forceinline__ void put(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
+};
+template <>
+struct RopeElem<uint16_t> {
+  static __device__ __forceinline__ float get(const void* p, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+  static __device__ __forceinline__ void put(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_rne(v);
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gqa_append_rope(RopeProblem p) {
+  constexpr int NT = 256, P = D / 2;
+  __shared__ float sm_cos[P], sm_sin[P];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int64_t cap = p.kv_offsets ? p.kv_offsets[b + 1] - p.kv_offsets[b] : (int64_t)p.T_max;
+  const int32_t len = p.seq_lens[b];
+  const int64_t m = len < 0 ? 0 : len;     // the new token's position
+  const bool append = m < cap;             // a full cache is left as it is
+  for (int j = tid; j < P; j += NT) {
+    const double a = (double)m * pow(p.base, -2.0 * (double)j / (double)D);
+    double s, c;
+    sincos(a, &s, &c);
+    sm_cos[j] = (float)c;
+    sm_sin[j] = (float)s;
+  }
+  __syncthreads();
+
+  // rows of this token: q and out [B][H_q][D], k_new/v_new [B][H_kv][D]
+  const int64_t qrow = (int64_t)b * p.H_q, krow = (int64_t)b * p.H_kv;
+  int64_t crow0, cstride;   // cache row of KV head g: crow0 + g * cstride
+  if (p.kv_offsets) {
+    crow0 = p.kv_offsets[b] * p.H_kv + m;
+    cstride = cap;
+  } else {
+    crow0 = (int64_t)b * p.H_kv * p.T_max + m;
+    cstride = p.T_max;
+  }
+  const int nq = p.H_q * P, nk = p.H_kv * P;
+  for (int e = tid; e < nq + nk; e += NT) {
+    const int j = e % P;
+    const float c = sm_cos[j], s = sm_sin[j];
+    if (e < nq) {
+      const int64_t i0 = (qrow + e / P) * D + 2 * j;
+      const float x0 = RopeElem<T>::get(p.q, i0), x1 = RopeElem<T>::get(p.q, i0 + 1);
+      RopeElem<T>::put(p.q_out, i0, x0 * c - x1 * s);
+      RopeElem<T>::put(p.q_out, i0 + 1, x0 * s + x1 * c);
+    } else if (append) {
+      const int g = (e - nq) / P;
+      const int64_t i0 = (krow + g) * D + 2 * j, o0 = (crow0 + g * cstride) * D + 2 * j;
+      const float x0 = RopeElem<T>::get(p.k_new, i0), x1 = RopeElem<T>::get(p.k_new, i0 + 1);
+      RopeElem<T>::put(p.k_cache, o0, x0 * c - x1 * s);
+      RopeElem<T>::put(p.k_cache, o0 + 1, x0 * s + x1 * c);
+      // the value row is stored as it is
+      RopeElem<T>::put(p.v_cache, o0, RopeElem<T>::get(p.v_new, i0));
+      RopeElem<T>::put(p.v_cache, o0 + 1, RopeElem<T>::get(p.v_new, i0 + 1));
+    }
+  }
+  if (p.new_seq_lens) {
+    __syncthreads();   // every thread has read seq_lens[b] (new_seq_lens may be the same array)
+    if (tid == 0) p.new_seq_lens[b] = append ? (int32_t)(m + 1) : len;
+  }
+}
+
+}  // namespace gqa

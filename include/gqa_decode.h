@@ -186,6 +186,39 @@ gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_ca
                              const int64_t* kv_offsets, const int32_t* seq_lens, float scale, void* out,
                              const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The step before a decode step: append each sequence's new token to the
+ * cache of one layer, with rotary position embedding ("Grouped-Query
+ * Attention (GQA) and Multi-Query Attention (MQA): ...", section 4, "Rotary
+ * Position Embeddings (RoPE) Interaction": the rotation R_{Theta,m} turns each
+ * pair of consecutive elements (2j, 2j+1) of a head by m * theta_j).  The
+ * page leaves theta_j open; here theta_j = rope_base^(-2j/d), j < d/2, and a
+ * pair (x0, x1) becomes (x0 cos - x1 sin, x0 sin + x1 cos).
+ * The new token of sequence b is at position m = max(seq_lens[b], 0) (the
+ * cache holds tokens 0 .. m-1).  Every one of its H_q query heads is turned
+ * by R_{Theta,m} into q_out; its key is turned once per KV head (the G query
+ * heads of a group share it) and written, with its value, to cache row m of
+ * that KV head; new_seq_lens[b] = m + 1.  A sequence whose cache is full
+ * (m >= capacity) is not appended: its cache is untouched and its length is
+ * copied unchanged (its queries are still turned, at position m).
+ *   q, q_out      : [B][H_q][d], dims->dtype (q_out may equal q)
+ *   k_new, v_new  : [B][H_kv][d], dims->dtype
+ *   k_cache, v_cache : dense [B][H_kv][T_max][d] when kv_offsets is NULL,
+ *                  else the packed layout of gqa_decode_layers (one layer)
+ *   seq_lens      : [B] int32, tokens already cached (device)
+ *   new_seq_lens  : [B] int32 or NULL (device; may equal seq_lens)
+ *   rope_base     : finite and > 0
+ * Pointers need the alignment of their element type (4 bytes for fp32,
+ * 2 for bf16, 4 for seq_lens, 8 for kv_offsets).  dims->dtype, head_dim,
+ * batch, num_q_heads, num_kv_heads and max_seq_len are used; the other fields
+ * are validated as for gqa_decode but have no effect.  Rotation in fp32 with angles in double precision;
+ * bf16 results are rounded to nearest-even.  Enqueues one kernel on `stream`.
+ * Errors as for gqa_decode (GQA_ERR_INVALID_ARG for a bad rope_base).
+ */
+gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                           float rope_base, void* q_out, const gqa_dims* dims, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* gqa_status_string(gqa_status status);
 

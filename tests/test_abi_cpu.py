@@ -175,6 +175,37 @@ def test_matrix_core_path_limits():
     assert call(dims(B=64, T_max=1 << 26)) == UNSUPPORTED            # 32-bit prefix sums of lengths
 
 
+def call_append(d, ptrs=None, base=10000.0, offs=None, new_lens=FAKE):
+    p = [FAKE] * 5 if ptrs is None else ptrs
+    return gqa.lib().gqa_append_rope(p[0], p[1], p[2], p[3], p[4], offs, FAKE, new_lens, base, FAKE,
+                                     ctypes.byref(d), None)
+
+
+def test_append_rope_validation():
+    """The append step checks its arguments before touching the device."""
+    assert call_append(dims(d=96)) == UNSUPPORTED
+    assert call_append(dims(H_q=8, H_kv=3)) == INVALID
+    assert call_append(dims(T_max=0)) == INVALID
+    d = dims()
+    for base in (0.0, -1.0, float("nan"), float("inf")):
+        assert call_append(d, base=base) == INVALID, base
+    for pos in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[pos] = None
+        assert call_append(d, ptrs) == INVALID, pos
+        ptrs[pos] = FAKE + 1                       # not bf16-aligned
+        assert call_append(d, ptrs) == INVALID, pos
+    ptrs = [FAKE + 2] * 5                          # bf16-aligned but not fp32-aligned
+    assert call_append(dims(dtype=torch.float32), ptrs) == INVALID
+    assert call_append(d, offs=FAKE + 4) == INVALID     # kv_offsets not 8-byte aligned
+    assert call_append(d, new_lens=FAKE + 2) == INVALID
+    d0 = dims(B=0)
+    assert gqa.lib().gqa_append_rope(None, None, None, None, None, None, None, None, 10000.0, None,
+                                     ctypes.byref(d0), None) == OK
+    assert gqa.lib().gqa_append_rope(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 10000.0, FAKE, None,
+                                     None) == INVALID
+
+
 def test_library_missing_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding._build, "LIB_PATH", str(tmp_path / "absent.so"))

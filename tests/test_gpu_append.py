@@ -1,0 +1,175 @@
+"""The append step (rotary position embedding of the new token, written into
+the cache) on the GPU against the fp64 oracle, through the C ABI.
+
+Bars:
+  * rotated fp32 values: max |gpu - oracle| <= 1e-5 (the rotation runs in
+    fp32 with cosines and sines of double-precision angles: a few fp32
+    roundings of values of size ~5 at most);
+  * rotated bf16 values: |gpu - oracle| <= 2^-8 |oracle| + 1e-6 (one rounding
+    to bf16 of such an fp32 result, plus its own tiny error);
+  * values copied into the cache, rows that must not change, and the new
+    lengths: bitwise;
+  * an append followed by a decode step: the attention bars (1e-5 fp32,
+    2e-3 bf16 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_mqa_kv_amd as gqa
+import oracle
+from gqa_mqa_kv_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def note(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def rot_err_ok(gpu, ref, dtype):
+    g = gpu.double().cpu().numpy()
+    assert np.isfinite(g).all()
+    if dtype == torch.float32:
+        return float(np.abs(g - ref).max()) <= 1e-5
+    return bool((np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6).all())
+
+
+def make(B, H_q, H_kv, d, T_max, dtype, seed, lens):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=g).to(dtype)
+    x = dict(q=r(B, H_q, d), k_new=r(B, H_kv, d), v_new=r(B, H_kv, d),
+             k=r(B, H_kv, T_max, d), v=r(B, H_kv, T_max, d),
+             seq_lens=torch.tensor(lens, dtype=torch.int32))
+    return x
+
+
+CASES = [
+    # B, H_q, H_kv, d, T_max, lengths before the append (T_max = full: not appended)
+    (4, 32, 8, 128, 64, [0, 17, 63, 64]),
+    (3, 8, 8, 64, 40, [1, 39, 40]),            # MHA, d = 64
+    (2, 32, 1, 128, 33, [32, 5]),              # MQA
+    (2, 12, 4, 128, 300, [299, 150]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d_T%d" % c[:5])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("base", [10000.0, 500000.0])
+def test_append_rope_matches_oracle(case, dtype, base):
+    B, H_q, H_kv, d, T_max, lens = case
+    x = make(B, H_q, H_kv, d, T_max, dtype, seed=sum(case[:5]) + len(lens), lens=lens)
+    note("append", case, dtype, base)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    q_out, new_lens = gqa.append_rope(xd["q"], xd["k_new"], xd["v_new"], xd["k"], xd["v"], xd["seq_lens"], base)
+    torch.cuda.synchronize()
+    pos = torch.tensor(lens).clamp(min=0)
+    orc = oracle.default()
+    assert rot_err_ok(q_out, orc.rope(x["q"], pos.view(B, 1), base), dtype)
+    k_rot = orc.rope(x["k_new"], pos.view(B, 1), base)
+    k_after, v_after = xd["k"].cpu(), xd["v"].cpu()
+    for b in range(B):
+        m = int(pos[b])
+        if m < T_max:
+            assert rot_err_ok(k_after[b, :, m], k_rot[b], dtype)
+            assert torch.equal(v_after[b, :, m], x["v_new"][b])
+            keep = [t for t in range(T_max) if t != m]
+            assert int(new_lens[b]) == m + 1
+        else:
+            keep = list(range(T_max))
+            assert int(new_lens[b]) == lens[b]
+        assert torch.equal(k_after[b, :, keep], x["k"][b, :, keep])
+        assert torch.equal(v_after[b, :, keep], x["v"][b, :, keep])
+
+
+def test_append_in_place_and_large_positions():
+    """q_out may be q and new_seq_lens may be seq_lens; angles at positions
+    near 131072 (m * theta up to 1.3e5 radians) stay accurate in fp32."""
+    B, H_q, H_kv, d, T_max = 2, 16, 2, 128, 131072
+    lens = [131071, 100000]
+    x = make(B, H_q, H_kv, d, 4, torch.float32, seed=5, lens=[0, 0])
+    k = torch.zeros(B, H_kv, T_max, d, device=DEV)
+    v = torch.zeros(B, H_kv, T_max, d, device=DEV)
+    q = x["q"].to(DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    note("append in place, large positions")
+    q_out, nl = gqa.append_rope(q, x["k_new"].to(DEV), x["v_new"].to(DEV), k, v, sl, 10000.0, q_out=q,
+                                new_seq_lens=sl)
+    torch.cuda.synchronize()
+    assert q_out.data_ptr() == q.data_ptr() and nl.data_ptr() == sl.data_ptr()
+    orc = oracle.default()
+    pos = torch.tensor(lens)
+    assert rot_err_ok(q, orc.rope(x["q"], pos.view(B, 1), 10000.0), torch.float32)
+    kr = orc.rope(x["k_new"], pos.view(B, 1), 10000.0)
+    for b in range(B):
+        assert rot_err_ok(k[b, :, lens[b]], kr[b], torch.float32)
+    assert sl.cpu().tolist() == [l + 1 for l in lens]
+
+
+def test_append_packed_layout():
+    """The packed layout (one layer): row kv_offsets[b]*H_kv + g*cap_b + m."""
+    B, H_q, H_kv, d = 3, 16, 4, 64
+    caps = [10, 3, 7]
+    lens = [4, 3, 0]                       # sequence 1 is full
+    offs = torch.tensor([0, 10, 13, 20], dtype=torch.int64)
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn(B, H_q, d, generator=g).to(torch.bfloat16)
+    kn = torch.randn(B, H_kv, d, generator=g).to(torch.bfloat16)
+    vn = torch.randn(B, H_kv, d, generator=g).to(torch.bfloat16)
+    kc = torch.randn(int(offs[-1]) * H_kv, d, generator=g).to(torch.bfloat16)
+    vc = torch.randn(int(offs[-1]) * H_kv, d, generator=g).to(torch.bfloat16)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    note("append packed")
+    q_out, nl = gqa.append_rope(q.to(DEV), kn.to(DEV), vn.to(DEV), kd, vd,
+                                torch.tensor(lens, dtype=torch.int32, device=DEV), 10000.0,
+                                kv_offsets=offs.to(DEV), max_seq_len=max(caps))
+    torch.cuda.synchronize()
+    orc = oracle.default()
+    kr = orc.rope(kn, torch.tensor(lens).view(B, 1), 10000.0)
+    k_after, v_after = kd.cpu(), vd.cpu()
+    changed = set()
+    for b in range(B):
+        if lens[b] < caps[b]:
+            for h in range(H_kv):
+                row = int(offs[b]) * H_kv + h * caps[b] + lens[b]
+                changed.add(row)
+                assert rot_err_ok(k_after[row], kr[b, h], torch.bfloat16)
+                assert torch.equal(v_after[row], vn[b, h])
+    keep = [r for r in range(kc.shape[0]) if r not in changed]
+    assert torch.equal(k_after[keep], kc[keep]) and torch.equal(v_after[keep], vc[keep])
+    assert nl.cpu().tolist() == [5, 3, 1]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+def test_append_then_decode(dtype):
+    """A whole decode step: append the new token with its rotation, then
+    attend with the rotated query over the cache including it.  Reference:
+    the oracle's rotation of q and of every cached key at its own position,
+    then the oracle's attention, all in fp64."""
+    B, H_q, H_kv, d, T_max = 3, 32, 8, 128, 700
+    g = torch.Generator().manual_seed(77)
+    lens = torch.randint(0, T_max, (B,), generator=g, dtype=torch.int32)
+    raw_k = torch.randn(B, H_kv, T_max, d, generator=g).to(dtype)     # unrotated keys of every position
+    v = torch.randn(B, H_kv, T_max, d, generator=g).to(dtype)
+    q = torch.randn(B, H_q, d, generator=g).to(dtype)
+    base = 10000.0
+    orc = oracle.default()
+    # the cache as earlier appends left it: keys rotated at their positions
+    rot_k = torch.from_numpy(orc.rope(raw_k, torch.arange(T_max).view(1, 1, T_max), base)).to(dtype)
+    kd, vd = rot_k.clone().to(DEV), v.clone().to(DEV)
+    m = lens.long()
+    kn = raw_k[torch.arange(B), :, m]                                     # the new token's key and value
+    vn = v[torch.arange(B), :, m]
+    note("append then decode", dtype)
+    q_rot, nl = gqa.append_rope(q.to(DEV), kn.contiguous().to(DEV), vn.contiguous().to(DEV), kd, vd,
+                                lens.to(DEV), base)
+    out = gqa.decode(q_rot, kd, vd, nl, d ** -0.5, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_q = torch.from_numpy(orc.rope(q.double(), m.view(B, 1), base))
+    ref_k = torch.from_numpy(orc.rope(raw_k.double(), torch.arange(T_max).view(1, 1, T_max), base))
+    ref = orc.decode(ref_q, ref_k, v.double(), (lens + 1).tolist(), d ** -0.5)
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    err = float(np.abs(out.double().cpu().numpy() - ref).max())
+    assert err <= tol, err
