@@ -112,6 +112,34 @@ def copy_calibration(torch, dev, nbytes: int, launches: int) -> None:
                       "bytes_written_per_launch": nbytes, "launches": launches}), flush=True)
 
 
+def time_append(torch, gqa, w, x, stream, steps: int, warmup: int):
+    """The step before a decode step (gqa_append_rope: rotary embedding of the
+    new token's H_q queries and H_kv keys, its key and value written into the
+    cache) at the workload's shape, timed like the decode step.  Every
+    sequence appends at row T_max - 1 (the call never writes anywhere else).
+    Bytes: q read and written, the new K/V rows read and written to the
+    cache, the lengths read and written."""
+    g = torch.Generator(device=x["q"].device).manual_seed(w.seed + 17)
+    kn = torch.randn(w.B, w.H_kv, w.d, device=x["q"].device, generator=g).to(w.dtype)
+    vn = torch.randn(w.B, w.H_kv, w.d, device=x["q"].device, generator=g).to(w.dtype)
+    lens = torch.full((w.B,), w.T_max - 1, dtype=torch.int32, device=x["q"].device)
+    call = gqa.prepare_append(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    e = 2
+    nbytes = 2 * w.B * w.H_q * w.d * e + 4 * w.B * w.H_kv * w.d * e + 8 * w.B
+    return {"us_per_call": round(us, 2), "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "bound": "launch latency (the call moves %d bytes)" % nbytes, "rope_base": 500000.0}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +256,8 @@ def main():
         "cpu_baseline": None,
         "context": {"h100_sxm5_hbm_TBps": 3.35, "h100_sxm5_dense_bf16_TFLOPs": 989, "h100_I_sat_FLOP_per_B": 295.2},
     }
+    if w.layers == 1 and w.dtype == torch.bfloat16:
+        result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -14,7 +14,7 @@ queries and keys by the rotary position embedding of section 4 of the same
 page and appends its key and value to the cache.
 """
 from ._binding import (GqaDims, GqaError, Prepared, append_rope, decode, decode_layers, default_workspace, lib,
-                       make_dims, plan, prepare, status_string, workspace_bytes)
+                       make_dims, plan, prepare, prepare_append, status_string, workspace_bytes)
 
 __all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "append_rope", "default_workspace",
-           "lib", "make_dims", "plan", "status_string", "workspace_bytes"]
+           "lib", "make_dims", "plan", "prepare_append", "status_string", "workspace_bytes"]

@@ -262,6 +262,29 @@ def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k
     return q_out, new_seq_lens
 
 
+def prepare_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
+                   max_seq_len: Optional[int] = None, stream=None):
+    """Validate (by running it once) and return a callable that enqueues the
+    same append_rope call again (for timing loops); it returns the rotated
+    queries.  The new lengths go to a tensor of their own, so every call
+    appends at the same rows."""
+    q_out, new_lens = append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets=kv_offsets,
+                                  max_seq_len=max_seq_len, stream=stream)
+    B, H_q, d = q.shape
+    T_max = k_cache.shape[2] if kv_offsets is None else max_seq_len
+    dims = make_dims(B, H_q, k_new.shape[1], d, T_max, q.dtype)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
+            _ptr(new_lens), float(rope_base), _ptr(q_out), ctypes.byref(dims), s)
+    fn = lib().gqa_append_rope
+    keep = (q_out, q, k_new, v_new, k_cache, v_cache, seq_lens, new_lens, kv_offsets, dims)
+
+    def call():
+        _check(fn(*args))
+        return keep[0]
+    return call
+
+
 class Prepared:
     """A decode call with every argument marshalled once; calling it only
     enqueues the launch (for timing loops where per-call argument checks
