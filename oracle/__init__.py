@@ -11,6 +11,8 @@ Contents
   "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): Mathematical
   Foundations, Arithmetic Intensity, and KV-Cache Scaling Mechanics",
   section 2, subsection "Grouped-Query Attention (GQA)".
+* :meth:`Oracle.decode_paged` -- the same attention with the cache held in
+  pages of a pool, found through a per-sequence block table.
 * :meth:`Oracle.rope` -- fp64 rotary position embedding (section 4 of the
   same page, "Rotary Position Embeddings (RoPE) Interaction"), for the step
   that appends the new token's keys and values.
@@ -72,6 +74,9 @@ class Oracle:
         lib.oracle_gqa_head_weights.restype = ctypes.c_int
         lib.oracle_gqa_head_weights.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp,
                                                 dbl, i64, i64, vp, vp]
+        lib.oracle_gqa_decode_paged.restype = ctypes.c_int
+        lib.oracle_gqa_decode_paged.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, i64, i64, vp, dbl,
+                                                i64, vp, vp]
         lib.oracle_rope.restype = ctypes.c_int
         lib.oracle_rope.argtypes = [i64, i64, ctypes.c_int, vp, vp, dbl, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -150,6 +155,36 @@ class Oracle:
         rc = self._lib.oracle_gqa_decode(B, H_q, H_kv, d, _DTYPE_CODE[q.dtype], q.data_ptr(),
                                          k.data_ptr(), v.data_ptr(), offs.ctypes.data, sl.ctypes.data,
                                          sc, n, ids_ptr, out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return out
+
+    def decode_paged(self, q, k_pool, v_pool, block_table, page: int, seq_lens, scale: float) -> np.ndarray:
+        """fp64 outputs for q [B, H_q, d] with the cache in pages: k_pool and
+        v_pool [num_pages, H_kv, page, d]; sequence b's token t is in page
+        block_table[b, t // page] (block_table int32 [B, max_pages])."""
+        if q.dtype not in _DTYPE_CODE or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+            raise TypeError("q and the pools must share one of float32, bfloat16, float64")
+        q = q.detach().to("cpu").contiguous()
+        k_pool = k_pool.detach().to("cpu").contiguous()
+        v_pool = v_pool.detach().to("cpu").contiguous()
+        B, H_q, d = q.shape
+        if k_pool.dim() != 4 or k_pool.shape[2] != page or k_pool.shape[3] != d or v_pool.shape != k_pool.shape:
+            raise ValueError("pools must be [num_pages, H_kv, page, d]")
+        H_kv = k_pool.shape[1]
+        bt = np.ascontiguousarray(np.asarray(
+            block_table.cpu() if isinstance(block_table, torch.Tensor) else block_table, dtype=np.int32))
+        if bt.ndim != 2 or bt.shape[0] != B:
+            raise ValueError("block_table must be [B, max_pages]")
+        if bt.size and (bt.min() < 0 or bt.max() >= k_pool.shape[0]):
+            raise ValueError("page id out of the pool")
+        sl = np.ascontiguousarray(np.asarray(
+            seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens, dtype=np.int32))
+        out = np.zeros((B, H_q, d), dtype=np.float64)
+        rc = self._lib.oracle_gqa_decode_paged(B, H_q, H_kv, d, _DTYPE_CODE[q.dtype], q.data_ptr(), k_pool.data_ptr(),
+                                               v_pool.data_ptr(), bt.ctypes.data, bt.shape[1], int(page),
+                                               sl.ctypes.data, float(np.float32(scale)), B * H_q, None,
+                                               out.ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return out

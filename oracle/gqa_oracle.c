@@ -78,26 +78,49 @@ static int64_t kv_row(const int64_t* kv_offsets, int64_t H_kv, int64_t b, int64_
   return kv_offsets[b] * H_kv + h * cap + t;
 }
 
+/* Where the cache rows of a call live: the dense/packed layout of kv_row(),
+ * or a paged one -- a pool of pages of `page` tokens, page p holding rows
+ * (p * H_kv + h) * page + j for its token j of KV head h, and sequence b's
+ * token t in page block_table[b * max_pages + t / page]. */
+typedef struct {
+  const int64_t* kv_offsets; /* dense/packed: [B+1]; NULL when paged */
+  const int32_t* block_table;
+  int64_t max_pages, page;
+  int64_t H_kv;
+} cache_layout;
+
+static int64_t cache_row(const cache_layout* L, int64_t b, int64_t h, int64_t t) {
+  if (L->block_table) {
+    int64_t p = L->block_table[b * L->max_pages + t / L->page];
+    return (p * L->H_kv + h) * L->page + t % L->page;
+  }
+  return kv_row(L->kv_offsets, L->H_kv, b, h, t);
+}
+
+static int64_t cache_capacity(const cache_layout* L, int64_t b) {
+  return L->block_table ? L->max_pages * L->page : L->kv_offsets[b + 1] - L->kv_offsets[b];
+}
+
 /*
  * Attention weights and output of one query head.
  *   q, q_off : query array and the element offset of Q_i's d elements
- *   k, v  : whole cache arrays, addressed through kv_row()
+ *   k, v  : whole cache arrays, addressed through cache_row()
  *   w     : optional, receives the n softmax weights (may be NULL)
  *   out   : receives the d outputs
  *   s     : scratch of at least the sequence's capacity
  * Returns 0, or -1 when n is negative or exceeds the sequence's capacity.
  */
 static int head_forward(const void* q, int64_t q_off, const void* k, const void* v, int dtype, int64_t d,
-                        const int64_t* kv_offsets, int64_t H_kv, int64_t b, int64_t g, int64_t n, double scale,
+                        const cache_layout* L, int64_t b, int64_t g, int64_t n, double scale,
                         double* s /* scratch, n */, double* w, double* out) {
-  int64_t cap = kv_offsets[b + 1] - kv_offsets[b];
+  int64_t cap = cache_capacity(L, b);
   if (n < 0 || n > cap) return -1;
   for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
   if (n == 0) return 0;
 
   /* Scores: s_t = scale * (Q_i . K_g,t), the masked-in positions only. */
   for (int64_t t = 0; t < n; ++t) {
-    int64_t row = kv_row(kv_offsets, H_kv, b, g, t) * d;
+    int64_t row = cache_row(L, b, g, t) * d;
     double acc = 0.0;
     for (int64_t c = 0; c < d; ++c) acc += load_elem(q, q_off + c, dtype) * load_elem(k, row + c, dtype);
     s[t] = scale * acc;
@@ -111,7 +134,7 @@ static int head_forward(const void* q, int64_t q_off, const void* k, const void*
   for (int64_t t = 0; t < n; ++t) {
     double wt = exp(s[t] - m) / z;
     if (w) w[t] = wt;
-    int64_t row = kv_row(kv_offsets, H_kv, b, g, t) * d;
+    int64_t row = cache_row(L, b, g, t) * d;
     for (int64_t c = 0; c < d; ++c) out[c] += wt * load_elem(v, row + c, dtype);
   }
   return 0;
@@ -135,16 +158,15 @@ static int check_dims(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype
  * Returns 0 on success, -1 on invalid arguments (nothing is written then for
  * the offending head).
  */
-int oracle_gqa_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype,
-                      const void* q, const void* k, const void* v,
-                      const int64_t* kv_offsets, const int32_t* seq_lens, double scale,
-                      int64_t n_heads, const int64_t* head_ids, double* out) {
+static int decode_heads(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype, const void* q, const void* k,
+                        const void* v, const cache_layout* L, const int32_t* seq_lens, double scale,
+                        int64_t n_heads, const int64_t* head_ids, double* out) {
   if (check_dims(B, H_q, H_kv, d, dtype)) return -1;
   if (!head_ids) n_heads = B * H_q;
   int64_t R = H_q / H_kv;
   int64_t max_cap = 0;
   for (int64_t b = 0; b < B; ++b) {
-    int64_t cap = kv_offsets[b + 1] - kv_offsets[b];
+    int64_t cap = cache_capacity(L, b);
     if (cap < 0) return -1;
     if (cap > max_cap) max_cap = cap;
   }
@@ -161,7 +183,7 @@ int oracle_gqa_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype
       int64_t id = head_ids ? head_ids[j] : j;
       int64_t b = id / H_q, i = id % H_q;
       int64_t g = oracle_group_of(i, R);
-      int rc = s ? head_forward(q, (b * H_q + i) * d, k, v, dtype, d, kv_offsets, H_kv, b, g,
+      int rc = s ? head_forward(q, (b * H_q + i) * d, k, v, dtype, d, L, b, g,
                                 (int64_t)seq_lens[b], scale, s, NULL, out + j * d)
                  : -1;
       if (rc) {
@@ -172,6 +194,30 @@ int oracle_gqa_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype
     free(s);
   }
   return status;
+}
+
+int oracle_gqa_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype,
+                      const void* q, const void* k, const void* v,
+                      const int64_t* kv_offsets, const int32_t* seq_lens, double scale,
+                      int64_t n_heads, const int64_t* head_ids, double* out) {
+  cache_layout L = {kv_offsets, NULL, 0, 0, H_kv};
+  return decode_heads(B, H_q, H_kv, d, dtype, q, k, v, &L, seq_lens, scale, n_heads, head_ids, out);
+}
+
+/*
+ * The same outputs with the cache in pages: k_pool, v_pool hold pages of
+ * `page` tokens (page p, KV head h, token j at row (p * H_kv + h) * page + j),
+ * and sequence b's token t is in page block_table[b * max_pages + t / page]
+ * (capacity max_pages * page tokens).  Page ids must be valid for the pool.
+ */
+int oracle_gqa_decode_paged(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype,
+                            const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, int64_t max_pages, int64_t page,
+                            const int32_t* seq_lens, double scale, int64_t n_heads, const int64_t* head_ids,
+                            double* out) {
+  if (!block_table || max_pages < 0 || page <= 0) return -1;
+  cache_layout L = {NULL, block_table, max_pages, page, H_kv};
+  return decode_heads(B, H_q, H_kv, d, dtype, q, k_pool, v_pool, &L, seq_lens, scale, n_heads, head_ids, out);
 }
 
 /* Softmax weights of one query head (b, i): w[0..seq_lens[b]) and its output. */
@@ -186,7 +232,8 @@ int oracle_gqa_head_weights(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int
   if (n < 0 || n > cap) return -1;
   double* s = (double*)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
   if (!s) return -1;
-  int rc = head_forward(q, (b * H_q + i) * d, k, v, dtype, d, kv_offsets, H_kv, b,
+  cache_layout L = {kv_offsets, NULL, 0, 0, H_kv};
+  int rc = head_forward(q, (b * H_q + i) * d, k, v, dtype, d, &L, b,
                         oracle_group_of(i, H_q / H_kv), n, scale, s, w, out);
   free(s);
   return rc;

@@ -265,6 +265,38 @@ def pin_head_subset(orc):
     assert np.array_equal(run(orc, x, heads=ids), full[ids])
 
 
+def paged_copy(x, page, seed, spare=3):
+    """The dense cache of ``x`` cut into pages of ``page`` tokens, spread over
+    a shuffled pool with ``spare`` unused pages (NaN), and its block table."""
+    B, H_kv, T, d = x["k"].shape
+    mp = -(-T // page)
+    n_pages = B * mp + spare
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(seed))
+    kp = torch.full((n_pages, H_kv, page, d), float("nan"), dtype=x["k"].dtype)
+    vp = torch.full((n_pages, H_kv, page, d), float("nan"), dtype=x["k"].dtype)
+    table = torch.zeros(B, mp, dtype=torch.int32)
+    for b in range(B):
+        for j in range(mp):
+            pid = int(perm[b * mp + j])
+            table[b, j] = pid
+            n = min(page, T - j * page)
+            kp[pid, :, :n] = x["k"][b, :, j * page:j * page + n]
+            vp[pid, :, :n] = x["v"][b, :, j * page:j * page + n]
+    return kp, vp, table
+
+
+def pin_paged_layout(orc):
+    """A cache held in shuffled pages of a pool (unused pages and page tails
+    NaN) gives bitwise the dense cache's result, for pages of 1, 16 and the
+    whole capacity."""
+    x = case(3, 8, 2, 64, 48, 161, lo=1, poison=True)
+    dense = run(orc, x)
+    for page in (1, 16, 48):
+        kp, vp, table = paged_copy(x, page, seed=page)
+        got = orc.decode_paged(x["q"], kp, vp, table, page, x["seq_lens"], x["scale"])
+        assert np.array_equal(got, dense), page
+
+
 # --------------------------------------------- rotary position embedding --
 # "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): ...",
 # section 4, "Rotary Position Embeddings (RoPE) Interaction".

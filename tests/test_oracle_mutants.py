@@ -30,9 +30,9 @@ MUTANTS = {
     # values read from the key cache
     "values_from_keys": ("load_elem(v, row + c, dtype)", "load_elem(k, row + c, dtype)"),
     # transposed key operand
-    "keys_transposed": ("load_elem(k, row + c, dtype)", "load_elem(k, kv_row(kv_offsets, H_kv, b, g, 0) * d + c * n + t, dtype)"),
+    "keys_transposed": ("load_elem(k, row + c, dtype)", "load_elem(k, cache_row(L, b, g, 0) * d + c * n + t, dtype)"),
     # query row of the group's first head used for every head
-    "query_of_group": ("(b * H_q + i) * d, k, v, dtype, d, kv_offsets, H_kv, b, g,", "(b * H_q + g * R) * d, k, v, dtype, d, kv_offsets, H_kv, b, g,"),
+    "query_of_group": ("(b * H_q + i) * d, k, v, dtype, d, L, b, g,", "(b * H_q + g * R) * d, k, v, dtype, d, L, b, g,"),
     # KV heads interleaved per token instead of stored one after another
     "kv_layout_interleaved": ("return kv_offsets[b] * H_kv + h * cap + t;", "return kv_offsets[b] * H_kv + h + t * H_kv;"),
     # bf16 widened with the wrong shift
@@ -41,6 +41,10 @@ MUTANTS = {
     "seq_len_of_first": ("(int64_t)seq_lens[b], scale, s, NULL", "(int64_t)seq_lens[0], scale, s, NULL"),
     # one token too many (reads a padding position)
     "extra_token": ("if (n < 0 || n > cap) return -1;\n  for", "n = n < cap ? n + 1 : n;\n  if (n < 0 || n > cap) return -1;\n  for"),
+    # paged cache: token offset and page index swapped
+    "paged_row_swapped": ("return (p * L->H_kv + h) * L->page + t % L->page;", "return (p * L->H_kv + h) * L->page + t / L->page;"),
+    # paged cache: pages stored token-major instead of head-major
+    "paged_head_major": ("return (p * L->H_kv + h) * L->page + t % L->page;", "return (p * L->page + t % L->page) * L->H_kv + h;"),
     # rotary embedding: turning the other way
     "rope_orientation": ("out[v * d + 2 * j] = x0 * c - x1 * s;", "out[v * d + 2 * j] = x0 * c + x1 * s;"),
     # rotary embedding: pairs (j, j + d/2) instead of consecutive elements
