@@ -1,13 +1,15 @@
 """GQA decode-step benchmark: effective HBM GB/s and microseconds per step.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--paged PAGE] [--gpus 1]
 
 One step = one decode step of the workload (every split-KV piece and the
 merge of the pieces: one kernel launch when the merge is fused into the
 decode kernel, else the decode kernel and a small merge kernel) over one
 batch of synthetic inputs that are already resident in HBM.  Steps rotate over enough independent input batches
 (``--replicas``) that the working set exceeds the 256 MB last-level
-(Infinity) cache, so every step streams its K/V from HBM.
+(Infinity) cache, so every step streams its K/V from HBM.  ``--paged PAGE`` lays each batch's
+cache out in pages of PAGE tokens (shuffled in a pool, read through a block
+table) and times gqa_decode_paged instead.
 
 Metric: (K + V bytes of the valid tokens + q bytes + out bytes) / time, the
 KV traffic formula of "Grouped-Query Attention (GQA) and Multi-Query
@@ -41,7 +43,11 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "GQA decode effective HBM GB/s (% of MI355X peak) + µs/step"
 DEFAULT_WORKLOAD = "llama3-8b-layer"
 KERNEL_SOURCES = ["common.h", "kernel_mfma.h", "kernel_valu.h", "gqa_decode.hip"]
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gqa_decode_mfma_llama3_8b_layer_counters.txt")
+
+
+def traffic_profile(key: str) -> str:
+    """The committed counter summary of a workload ("name" or "name/pagedN")."""
+    return os.path.join(ROOT, "profiles", "gqa_decode_mfma_%s_counters.txt" % re.sub(r"[-/]", "_", key))
 
 
 def kernel_source_hash() -> str:
@@ -52,20 +58,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, seq_lens, out_elem_bytes) -> int:
+def algorithmic_bytes(w, seq_lens, out_elem_bytes, page: int = 0) -> int:
+    """K/V of the valid tokens, q and out; with pages, also the block-table
+    entries of the pages in use (4 bytes each, read once)."""
     e = 2 if str(w.dtype).endswith("bfloat16") else 4
     kv = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * e
     qb = w.layers * w.B * w.H_q * w.d * e
     ob = w.layers * w.B * w.H_q * w.d * out_elem_bytes
-    return kv + qb + ob
+    tb = 4 * sum(-(-int(n) // page) for n in seq_lens.tolist()) if page else 0
+    return kv + qb + ob + tb
 
 
 def read_traffic(workload_name: str, launches_bytes: int):
     """HBM bytes per launch from the committed counter summary, when it was
     recorded on the current kernel source for this workload; else None."""
-    if not os.path.exists(TRAFFIC_PROFILE):
+    path = traffic_profile(workload_name)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_PROFILE).read()
+    text = open(path).read()
     kv = dict(re.findall(r"^(\w+)\s*[:=]\s*(\S+)\s*$", text, re.M))
     if kv.get("kernel_source_hash") != kernel_source_hash() or kv.get("workload") != workload_name:
         return None
@@ -148,6 +158,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--replicas", type=int, default=0, help="input batches rotated over (0: enough for >= 2 GiB)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE",
+                    help="cache in shuffled pages of PAGE tokens (a multiple of 16), read through a block table")
     ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -172,6 +184,9 @@ def main():
         copy_calibration(torch, dev, args.copy_calibration_mib << 20, args.steps)
         return
     w = workloads.WORKLOADS[args.workload]
+    if args.paged and (w.layers != 1 or w.packed or w.dtype != torch.bfloat16 or args.paged % 16):
+        print("--paged takes a single-layer bf16 workload and a page that is a multiple of 16", file=sys.stderr)
+        sys.exit(2)
     out_dtype = {None: w.dtype, "bf16": torch.bfloat16, "fp32": torch.float32}[args.out_dtype]
     seq_lens = workloads.seq_lens_for(w)
     kv_bytes = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * (2 if w.dtype == torch.bfloat16 else 4)
@@ -186,7 +201,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
     kw = dict(out_dtype=out_dtype, chunk_tokens=args.chunk_tokens, path=args.path)
     launchers = []
-    for x in batches:
+    for r, x in enumerate(batches):
+        if args.paged:
+            kp, vp, table = workloads.to_pages(x, args.paged, seed=1000 + r, spare=1)
+            del x["k"], x["v"]   # the pool holds the cache now
+            launchers.append(gqa.prepare_paged(x["q"], kp, vp, table, x["seq_lens"], x["scale"],
+                                               max_seq_len=w.T_max, out_dtype=out_dtype,
+                                               chunk_tokens=args.chunk_tokens))
+            continue
         extra = dict(kv_offsets=x["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if w.packed else {}
         launchers.append(gqa.prepare(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], **extra, **kw))
 
@@ -207,7 +229,7 @@ def main():
     wall = time.perf_counter() - t0
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / args.steps
-    nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4)
+    nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4, args.paged)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
     # The decode kernel's duration per launch: the HIP events above bracket the
@@ -220,12 +242,13 @@ def main():
     d = gqa.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype, out_dtype, chunk_tokens=args.chunk_tokens,
                       path=args.path)
     a, b = gqa.plan(d, w.layers)
-    mfma = args.path == "mfma" or (args.path == "auto" and w.dtype == torch.bfloat16 and w.B <= 4096)
+    mfma = args.paged or args.path == "mfma" or (args.path == "auto" and w.dtype == torch.bfloat16 and w.B <= 4096)
     if mfma:   # token split: (forced tokens per workgroup or 0 for an even split, workgroups)
         split = {"kernel": "matrix-core, token split", "workgroups": b, "tokens_per_workgroup": a or "even"}
     else:      # vector path: (tokens per chunk, chunks of the longest sequence)
         split = {"kernel": "vector ALU, chunked", "chunk_tokens": a, "chunks_per_sequence": b}
-    traffic = read_traffic(w.name, nbytes) if args.path in ("auto", "mfma") and not args.chunk_tokens else None
+    traffic = (read_traffic(w.name + ("/paged%d" % args.paged if args.paged else ""), nbytes)
+               if args.path in ("auto", "mfma") and not args.chunk_tokens else None)
 
     result = {
         "metric": METRIC,
@@ -244,7 +267,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "G": w.G, "d": w.d,
                    "cached_tokens": [w.seq_lo, w.seq_hi], "seq_lens_sum": int(seq_lens.sum()), "layers": w.layers,
-                   "layout": "packed" if w.packed else "dense", "accumulate": "fp32",
+                   "layout": ("paged, %d tokens per page" % args.paged if args.paged
+                              else "packed" if w.packed else "dense"), "accumulate": "fp32",
                    "out_dtype": "bf16" if out_dtype == torch.bfloat16 else "fp32",
                    "path": args.path, "work_split": split,
                    "input_batches_rotated": reps, "algorithmic_bytes_per_step": nbytes,
@@ -256,7 +280,7 @@ def main():
         "cpu_baseline": None,
         "context": {"h100_sxm5_hbm_TBps": 3.35, "h100_sxm5_dense_bf16_TFLOPs": 989, "h100_I_sat_FLOP_per_B": 295.2},
     }
-    if w.layers == 1 and w.dtype == torch.bfloat16:
+    if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged:
         result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

@@ -7,14 +7,15 @@ tokens with the key/value head g = i / G of its contiguous group.  All work
 runs in hand-written HIP kernels (gqa_mqa_kv_amd/csrc); Python only marshals
 arguments.  See include/gqa_decode.h for the ABI.
 
-    from gqa_mqa_kv_amd import decode, decode_layers, append_rope
+    from gqa_mqa_kv_amd import decode, decode_layers, decode_paged, append_rope
 
 append_rope is the step before a decode step: it turns the new token's
 queries and keys by the rotary position embedding of section 4 of the same
-page and appends its key and value to the cache.
+page and appends its key and value to the cache.  decode_paged reads a cache
+held in fixed-size pages of a pool through a per-sequence table of page ids.
 """
-from ._binding import (GqaDims, GqaError, Prepared, append_rope, decode, decode_layers, default_workspace, lib,
-                       make_dims, plan, prepare, prepare_append, status_string, workspace_bytes)
+from ._binding import (GqaDims, GqaError, Prepared, append_rope, decode, decode_layers, decode_paged, default_workspace,
+                       lib, make_dims, plan, prepare, prepare_append, prepare_paged, status_string, workspace_bytes)
 
-__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "append_rope", "default_workspace",
-           "lib", "make_dims", "plan", "prepare_append", "status_string", "workspace_bytes"]
+__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "decode_paged", "append_rope", "default_workspace",
+           "lib", "make_dims", "plan", "prepare_append", "prepare_paged", "status_string", "workspace_bytes"]

@@ -20,8 +20,8 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
-SYMBOLS = ("gqa_append_rope", "gqa_decode", "gqa_decode_layers", "gqa_decode_workspace_bytes", "gqa_decode_plan",
-           "gqa_status_string")
+SYMBOLS = ("gqa_append_rope", "gqa_decode", "gqa_decode_layers", "gqa_decode_paged", "gqa_decode_workspace_bytes",
+           "gqa_decode_plan", "gqa_status_string")
 
 
 class GqaDims(ctypes.Structure):
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_layers.restype = ctypes.c_int
         L.gqa_decode_layers.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_paged.restype = ctypes.c_int
+        L.gqa_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_workspace_bytes.restype = sz
         L.gqa_decode_workspace_bytes.argtypes = [dims_p, i32]
         L.gqa_decode_plan.restype = ctypes.c_int
@@ -160,6 +162,52 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
                             ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                             s))
     return out
+
+
+def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype, max_seq_len, chunk_tokens,
+                seq_len_hint, workspace, stream, tiles, merge, per_cu):
+    dev = q.device
+    for t, n in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape or block_table.dim() != 2:
+        raise ValueError("expected q [B,H_q,d], k/v pools [num_pages,H_kv,page,d] and block_table [B,max_pages]")
+    B, H_q, d = q.shape
+    _, H_kv, page, _ = k_pool.shape
+    max_pages = block_table.shape[1]
+    if (k_pool.shape[3] != d or block_table.shape[0] != B or block_table.dtype != torch.int32
+            or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32):
+        raise ValueError("shape mismatch between q, pools, block_table and seq_lens")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q, k_pool and v_pool must share one dtype")
+    T = max_pages * page if max_seq_len is None else int(max_seq_len)
+    dims = make_dims(B, H_q, H_kv, d, T, q.dtype, out_dtype, seq_len_hint, chunk_tokens, "mfma", 0, tiles, merge,
+                     per_cu)
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
+    _require(out, "out", dev)
+    if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
+        raise ValueError("out must be [B,H_q,d] of the output dtype")
+    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages), int(page), _ptr(seq_lens),
+            float(scale), _ptr(out), ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+            s)
+    return args, (out, q, k_pool, v_pool, block_table, seq_lens, ws, dims)
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float, out=None, out_dtype=None,
+                 max_seq_len: Optional[int] = None, chunk_tokens: int = 0, seq_len_hint: int = 0, workspace=None,
+                 stream=None, tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """One decode step of one layer whose cache lives in pages of a pool.
+    q [B,H_q,d]; k_pool/v_pool [num_pages,H_kv,page,d]; block_table int32
+    [B,max_pages] (token t of sequence b in page block_table[b, t // page]);
+    seq_lens int32 [B].  max_seq_len defaults to max_pages * page.  Returns
+    out [B,H_q,d]."""
+    args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype, max_seq_len,
+                             chunk_tokens, seq_len_hint, workspace, stream, tiles, merge, per_cu)
+    _check(lib().gqa_decode_paged(*args))
+    return keep[0]
 
 
 def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len: Optional[int] = None,
@@ -290,8 +338,8 @@ class Prepared:
     enqueues the launch (for timing loops where per-call argument checks
     would cost more host time than the kernel takes)."""
 
-    def __init__(self, layers: bool, args: tuple, keep: tuple):
-        self._fn = lib().gqa_decode_layers if layers else lib().gqa_decode
+    def __init__(self, layers, args: tuple, keep: tuple):
+        self._fn = layers if callable(layers) else (lib().gqa_decode_layers if layers else lib().gqa_decode)
         self._args = args
         self._keep = keep   # tensors whose memory the pointers refer to
 
@@ -336,3 +384,14 @@ def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_se
         args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out), dref, _ptr(ws),
                 nbytes, s)
     return Prepared(layers, args, (out, q, k_cache, v_cache, seq_lens, kv_offsets, ws, dims))
+
+
+def prepare_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float, out_dtype=None, max_seq_len=None,
+                  chunk_tokens: int = 0, seq_len_hint: int = 0, stream=None, tiles: int = 0, merge: str = "auto",
+                  per_cu: int = 0):
+    """As prepare, for gqa_decode_paged."""
+    args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, None, out_dtype, max_seq_len,
+                             chunk_tokens, seq_len_hint, None, stream, tiles, merge, per_cu)
+    pr = Prepared(lib().gqa_decode_paged, args, keep)
+    pr()
+    return pr

@@ -53,6 +53,8 @@ struct Problem {
   int32_t span;               // token-split path: tokens per workgroup (0: balanced split)
   int32_t out_bf16;
   float scale_log2;           // scale * log2(e): scores are kept in base 2
+  const int32_t* block_table; // paged cache: [B][max_pages] page ids, or nullptr
+  int32_t max_pages, page;    // paged cache: table entries per sequence, tokens per page (a multiple of 16)
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -152,10 +154,14 @@ __global__ __launch_bounds__(256) void gqa_merge_chunks(Problem p) {
 // last unit piece of a span can be partial (state slots 2w and 2w + 1; a
 // piece covering a whole span uses slot 2w).
 
-// Exclusive prefix sums of the clamped lengths into sm_P[0..B] (all threads of
-// the workgroup take part; B <= kMaxBatch).  sm_wave holds NT/64 ints.
-template <int NT>
-__device__ __forceinline__ void build_prefix(const Problem& p, int32_t* sm_P, int32_t* sm_wave) {
+// Exclusive prefix sums of the units' stream lengths into sm_P[0..B] (all
+// threads of the workgroup take part; B <= kMaxBatch).  A unit's stream
+// length is its valid token count; for a paged cache (PAGED) it is rounded up
+// to a multiple of 16, so that every 16-token tile of a unit starts at a
+// multiple of 16 and lies in one page, and the clamped counts go to
+// sm_N[0..B).  sm_wave holds NT/64 ints.
+template <int NT, bool PAGED>
+__device__ __forceinline__ void build_prefix(const Problem& p, int32_t* sm_P, int32_t* sm_N, int32_t* sm_wave) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = p.B;
   const int E = (B + NT - 1) / NT;   // entries per thread, contiguous
@@ -166,6 +172,10 @@ __device__ __forceinline__ void build_prefix(const Problem& p, int32_t* sm_P, in
     if (cap > p.T_cap) cap = p.T_cap;
     int64_t n = p.seq_lens[b];
     n = n < 0 ? 0 : (n > cap ? cap : n);
+    if constexpr (PAGED) {
+      sm_N[b] = (int32_t)n;
+      n = (n + 15) / 16 * 16;
+    }
     sm_P[b] = (int32_t)n;
     local += (int32_t)n;
   }
@@ -218,13 +228,16 @@ __device__ __forceinline__ TokenSpace token_space(const Problem& p, const int32_
 }
 
 struct Piece {
-  UnitInfo ui;     // row0, n, l, b, g of the unit holding the position
+  UnitInfo ui;     // row0, n (valid tokens), l, b, g of the unit holding the position
   int64_t start;   // stream position of the unit's token 0
   int t;           // token of the unit at the located position
+  int npad;        // stream positions of the unit (n, rounded up to 16 for a paged cache)
 };
 
 // The unit holding stream position x (0 <= x < total).
-__device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, const TokenSpace& ts, int64_t x) {
+template <bool PAGED>
+__device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, const int32_t* sm_N,
+                                        const TokenSpace& ts, int64_t x) {
   Piece pc;
   const int l = (int)(x / ts.per_layer);
   const int64_t r = x - (int64_t)l * ts.per_layer;
@@ -235,15 +248,21 @@ __device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, c
   }
   const int b = lo;
   const int32_t pb = uniform(sm_P[b]);
-  const int n = uniform(sm_P[b + 1]) - pb;
+  const int v = uniform(sm_P[b + 1]) - pb;   // stream positions of each unit of sequence b
   const int64_t r2 = r - (int64_t)p.H_kv * pb;
-  const int g = (int)(r2 / n);
-  pc.t = (int)(r2 - (int64_t)g * n);
+  const int g = (int)(r2 / v);
+  pc.t = (int)(r2 - (int64_t)g * v);
   pc.start = x - pc.t;
+  pc.npad = v;
   pc.ui.l = l;
   pc.ui.b = b;
   pc.ui.g = g;
-  pc.ui.n = n;
+  if constexpr (PAGED) {
+    pc.ui.n = uniform(sm_N[b]);
+    pc.ui.row0 = (int64_t)g * p.page;   // KV head g's rows of a page (the page comes per tile)
+    return pc;
+  }
+  pc.ui.n = v;
   if (p.kv_offsets) {
     const int64_t o0 = p.kv_offsets[b], cap = p.kv_offsets[b + 1] - o0;
     pc.ui.row0 = (int64_t)l * p.kv_offsets[p.B] * p.H_kv + o0 * p.H_kv + (int64_t)g * cap;
@@ -386,11 +405,13 @@ __device__ __forceinline__ void fused_merge(const Problem& p, int64_t w0, int64_
 // the workgroup holding the unit's first token, w_last the one holding its
 // last), else w0 = -1.  The workgroups w0+1 .. w_last of such a unit share
 // its merge.
-__device__ __forceinline__ void write_merge_desc(const Problem& p, const int32_t* sm_P, const TokenSpace& ts, int m) {
+template <bool PAGED>
+__device__ __forceinline__ void write_merge_desc(const Problem& p, const int32_t* sm_P, const int32_t* sm_N,
+                                                 const TokenSpace& ts, int m) {
   int64_t d[4] = {-1, -1, 0, 0};
   const int64_t s0 = (int64_t)m * ts.span;
   if (s0 < ts.total) {
-    const Piece pc = locate(p, sm_P, ts, s0);
+    const Piece pc = locate<PAGED>(p, sm_P, sm_N, ts, s0);
     if (pc.t > 0) {
       d[0] = pc.start / ts.span;
       d[1] = (pc.start + pc.ui.n - 1) / ts.span;

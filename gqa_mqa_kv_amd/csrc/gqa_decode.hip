@@ -113,7 +113,10 @@ Plan make_plan(const gqa_dims* d, int32_t L) {
     // wavefronts beyond four per CU) are served unevenly by the memory
     // system, and with equal static shares the slowest one sets the time.
     // A forced chunk_tokens sets the span instead.
-    const int64_t upper = p.units * T;
+    // stream positions, at most: a paged cache counts each unit's length
+    // rounded up to 16 (plain caches use the same bound, so one workspace size
+    // serves both)
+    const int64_t upper = p.units * ((T + 15) / 16 * 16);
     if (d->chunk_tokens > 0) {
       p.span = d->chunk_tokens;
       p.groups = (int32_t)std::min<int64_t>(std::max<int64_t>(ceil_div(upper, p.span), 1), INT32_MAX);
@@ -174,19 +177,23 @@ int max_waves(int) { return 4; }
 int max_tiles(int hb, int) { return hb == 1 ? 2 : 1; }
 int default_tiles(int) { return 1; }
 
-template <int D>
+template <int D, bool PAGED = false>
 kernel_fn mfma_kernel(int hb, int, int tiles) {
   switch (hb) {
-    case 1: return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2> : gqa::gqa_decode_mfma<D, 1, 1, 4, 1>;
-    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1>;
-    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1>;
+    case 1:
+      return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, PAGED> : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, PAGED>;
+    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1, PAGED>;
+    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, PAGED>;
   }
 }
 
-kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan) {
+kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan, bool paged) {
   const int G = d->num_q_heads / d->num_kv_heads;
   if (plan.mfma) {
     const int hb = (G + 15) / 16;
+    if (paged)
+      return d->head_dim == 128 ? mfma_kernel<128, true>(hb, plan.waves, plan.tiles)
+                                : mfma_kernel<64, true>(hb, plan.waves, plan.tiles);
     return d->head_dim == 128 ? mfma_kernel<128>(hb, plan.waves, plan.tiles)
                               : mfma_kernel<64>(hb, plan.waves, plan.tiles);
   }
@@ -210,7 +217,9 @@ int resident_groups_per_cu(const gqa_dims* d, int waves, int tiles) {
   return n;
 }
 
+// A paged cache (block_table != nullptr): L == 1, page_size a multiple of 16.
 gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const int64_t* kv_offsets,
+                  const int32_t* block_table, int32_t max_pages, int32_t page_size,
                   const int32_t* seq_lens, float scale, void* out, const gqa_dims* d, void* ws, size_t ws_bytes,
                   void* stream) {
   gqa_status st = check_dims(d, L);
@@ -230,6 +239,9 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   p.v = v;
   p.out = out;
   p.kv_offsets = kv_offsets;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page = page_size;
   p.seq_lens = seq_lens;
   char* w = static_cast<char*>(ws);
   p.ws_cnt = plan.ws_bytes ? reinterpret_cast<int32_t*>(w) : nullptr;
@@ -257,7 +269,7 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* args[] = {&p};
   const int64_t grid = plan.mfma ? plan.groups : plan.units * plan.n_chunks;
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pick_kernel(d, plan)), dim3((unsigned)grid),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(pick_kernel(d, plan, block_table != nullptr)), dim3((unsigned)grid),
                                  dim3(64 * plan.waves), args, 0, s);
   if (e != hipSuccess) return GQA_ERR_LAUNCH;
   // The merge runs as a second kernel: the kernel boundary orders every
@@ -298,14 +310,29 @@ gqa_status gqa_decode_plan(const gqa_dims* dims, int32_t num_layers, int32_t* ch
 
 gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, float scale,
                       void* out, const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
-  return launch(1, q, k_cache, v_cache, nullptr, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+  return launch(1, q, k_cache, v_cache, nullptr, nullptr, 0, 0, seq_lens, scale, out, dims, workspace,
+                workspace_bytes, stream);
 }
 
 gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
                              const int64_t* kv_offsets, const int32_t* seq_lens, float scale, void* out,
                              const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
-  return launch(num_layers, q, k_cache, v_cache, kv_offsets, seq_lens, scale, out, dims, workspace, workspace_bytes,
-                stream);
+  return launch(num_layers, q, k_cache, v_cache, kv_offsets, nullptr, 0, 0, seq_lens, scale, out, dims, workspace,
+                workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                            int32_t max_pages, int32_t page_size, const int32_t* seq_lens, float scale, void* out,
+                            const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
+  gqa_status st = check_dims(dims, 1);
+  if (st != GQA_OK) return st;
+  if (page_size <= 0 || page_size % 16 != 0 || max_pages <= 0) return GQA_ERR_INVALID_ARG;
+  if ((int64_t)max_pages * page_size < dims->max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (!use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // the matrix-core kernel only (bf16)
+  if (dims->batch == 0) return GQA_OK;
+  if (!block_table || !aligned(block_table, 4)) return GQA_ERR_INVALID_ARG;
+  return launch(1, q, k_pool, v_pool, nullptr, block_table, max_pages, page_size, seq_lens, scale, out, dims,
+                workspace, workspace_bytes, stream);
 }
 
 gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

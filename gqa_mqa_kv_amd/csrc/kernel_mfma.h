@@ -89,7 +89,10 @@ struct Tile16 {
 // form HG groups (wavefront w is in group w % HG and streams tile lane w / HG
 // of the NW / HG lanes), so the workgroup covers 16 * HB * HG heads.  With
 // HG > 1 a tile is read once per group; the repeats are served by the caches.
-template <int D, int HB, int HG, int NW, int TPW>
+// PAGED: the cache is held in pages of a pool (p.block_table); every tile
+// then lies in one page, whose id is fetched one batch ahead of the tile's
+// loads so that the loads never wait for the table.
+template <int D, int HB, int HG, int NW, int TPW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   static_assert(NW % HG == 0, "head groups must divide the wavefronts");
   constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
@@ -101,6 +104,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   __shared__ float sm_slot[(NL > 1 ? HG * (NL / 2) : 1) * SLOT];
   __shared__ float sm_wm[NW][HP], sm_wl[NW][HP];
   __shared__ int32_t sm_P[kMaxBatch + 1];
+  __shared__ int32_t sm_N[PAGED ? kMaxBatch : 1];
   __shared__ int32_t sm_wave[NW];
   __shared__ int sm_flag;
 
@@ -112,10 +116,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   const int head0 = hg * HP + m16;      // this lane's query head of block 0 (block hb: head0 + 16 hb)
   const float sl2 = p.scale_log2;
 
-  build_prefix<NT>(p, sm_P, sm_wave);
+  build_prefix<NT, PAGED>(p, sm_P, sm_N, sm_wave);
   const TokenSpace ts = token_space(p, sm_P);
   zero_empty_sequences<D, NT>(p, sm_P, blockIdx.x, gridDim.x);
-  if (!p.fused) write_merge_desc(p, sm_P, ts, blockIdx.x);
+  if (!p.fused) write_merge_desc<PAGED>(p, sm_P, sm_N, ts, blockIdx.x);
   const int64_t s0 = (int64_t)blockIdx.x * ts.span;
   const int64_t s1 = min(s0 + ts.span, ts.total);
 
@@ -127,9 +131,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 
   // One piece: the part [c0, c1) of a unit that lies in this span.
   struct Ctx {
-    const uint16_t* kg;
+    const uint16_t* kg;      // dense/packed: the unit's row 0; paged: the pool shifted to KV head g
     const uint16_t* vg;
+    const int32_t* pages;    // paged: the sequence's block-table row
     int64_t x;        // stream position of token c0
+    int64_t next;     // stream position after the piece (past the unit's padding when it ends the unit)
     int64_t start;    // stream position of the unit's token 0
     int64_t orow;     // output row of the unit's first head
     int64_t w0, w_last;
@@ -138,12 +144,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     int slot_id;      // only the first and the last piece of a span can be partial
   };
   auto open_piece = [&](int64_t x) __attribute__((always_inline)) {
-    const Piece pc = locate(p, sm_P, ts, x);
+    const Piece pc = locate<PAGED>(p, sm_P, sm_N, ts, x);
     Ctx c;
     c.x = x;
     c.start = pc.start;
     c.c0 = pc.t;
     c.c1 = (int)min((int64_t)pc.ui.n, pc.t + (s1 - x));
+    if constexpr (PAGED) c.next = c.c1 == pc.ui.n ? pc.start + pc.npad : x + (c.c1 - c.c0);
+    if constexpr (PAGED) c.pages = p.block_table + (int64_t)pc.ui.b * p.max_pages;
     c.ntiles = (c.c1 - c.c0 + TILE - 1) / TILE;
     c.whole = c.c0 == 0 && c.c1 == pc.ui.n;
     c.slot_id = x == s0 ? 0 : 1;
@@ -165,11 +173,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + 32 * s + 8 * q4) : u32x4{0, 0, 0, 0};
     }
   };
-  auto load_tile = [&](Tile16<D>& T, const Ctx& c, int t0) __attribute__((always_inline)) {
+  // A tile's 16 rows are consecutive in memory, from row tr of kg/vg: row t0
+  // of the unit, or, in a paged cache, row t0 % page of the page holding
+  // token t0 (tiles start at multiples of 16 there and never cross a page).
+  auto load_tile = [&](Tile16<D>& T, const Ctx& c, int t0, int64_t tr) __attribute__((always_inline)) {
     if (t0 + TILE <= c.c1) {
       // full tile: one base address per lane, the rest are immediate offsets
-      const uint16_t* kt = c.kg + (int64_t)t0 * D + koff;
-      const uint16_t* vt = c.vg + (int64_t)t0 * D + voff;
+      const uint16_t* kt = c.kg + tr * D + koff;
+      const uint16_t* vt = c.vg + tr * D + voff;
 #pragma unroll
       for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
 #pragma unroll
@@ -177,23 +188,50 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     } else {
       // ragged tail: rows past the piece are clamped to its last valid row
       // (in bounds and finite); their weights are forced to 0 below
+      // (tr - t0: the offset of the tile's page from the unit's row 0)
       const int last = c.c1 - 1;
-      const uint16_t* kt = c.kg + (int64_t)min(t0 + m16, last) * D + 8 * q4;
+      const uint16_t* kb = PAGED ? c.kg + (tr - t0) * D : c.kg;
+      const uint16_t* vb = PAGED ? c.vg + (tr - t0) * D : c.vg;
+      const uint16_t* kt = kb + (int64_t)min(t0 + m16, last) * D + 8 * q4;
 #pragma unroll
       for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         T.v[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const vrow_t*>(c.vg + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
+            reinterpret_cast<const vrow_t*>(vb + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
     }
   };
   // The TPW tiles j, j+NL, ... of a batch.  Every load is issued (an index past
   // the piece's last tile is clamped to it: in bounds, its compute skipped), so
   // the number of loads in flight is the same on every path; a conditional
   // load would make the compiler wait for all of them before any compute.
-  auto load_batch = [&](Tile16<D> (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
+  auto tile_t0 = [&](const Ctx& c, int j, int u) __attribute__((always_inline)) {
+    return c.c0 + min(j + NL * u, c.ntiles - 1) * TILE;
+  };
+  // Paged: page ids of the tiles of batch j (clamped like the loads).  The
+  // table is read through the constant address space (it is not written
+  // while the kernel runs): a wave-uniform load there is a scalar load,
+  // counted apart from the tile loads, so waiting for an id never waits for
+  // the tiles issued before it.
+  auto fetch_pages = [&](int32_t (&pid)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      typedef const __attribute__((address_space(4))) int32_t* table_ptr;
+      const table_ptr row = (table_ptr)c.pages;
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) load_tile(T[u], c, c.c0 + min(j + NL * u, c.ntiles - 1) * TILE);
+      for (int u = 0; u < TPW; ++u) pid[u] = row[tile_t0(c, j, u) / p.page];
+    }
+  };
+  const int64_t page_rows = (int64_t)p.H_kv * p.page;   // pool rows per page
+  auto load_batch = [&](Tile16<D> (&T)[TPW], const Ctx& c, int j, const int32_t (&pid)[TPW])
+                        __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t0 = tile_t0(c, j, u);
+      if constexpr (PAGED)
+        load_tile(T[u], c, t0, (int64_t)pid[u] * page_rows + t0 % p.page);
+      else
+        load_tile(T[u], c, t0, t0);
+    }
   };
 
   u32x4 qf[HB][KS];
@@ -411,19 +449,24 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   // stores) overlaps the next piece's first loads.
   Ctx pc = open_piece(s0);
   int j = tl;
+  int32_t pid[TPW];   // paged: page ids of the next batch to load
+  fetch_pages(pid, pc, j);
   load_q(qf, pc);
   reset_state();
   Tile16<D> TA[TPW], TB[TPW];
-  load_batch(TA, pc, j);
+  load_batch(TA, pc, j, pid);
+  fetch_pages(pid, pc, j + NL * TPW);
   // One step with `cur` loaded: false if it is the span's last batch (left
   // for the caller), else load the next batch into `nxt` and compute `cur`.
   auto step = [&](const Tile16<D> (&cur)[TPW], Tile16<D> (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
     const bool piece_done = j + NL * TPW >= pc.ntiles;
-    const int64_t xn = pc.x + (pc.c1 - pc.c0);
+    const int64_t xn = PAGED ? pc.next : pc.x + (pc.c1 - pc.c0);
     if (piece_done && xn >= s1) return false;
     if (piece_done) {
       const Ctx pn = open_piece(xn);
-      load_batch(nxt, pn, tl);
+      fetch_pages(pid, pn, tl);
+      load_batch(nxt, pn, tl, pid);
+      fetch_pages(pid, pn, tl + NL * TPW);
       compute_batch(cur, pc, j);
       load_q(qf, pn);   // the next piece's queries: their latency overlaps end_piece
       end_piece(pc);
@@ -431,7 +474,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       pc = pn;
       j = tl;
     } else {
-      load_batch(nxt, pc, j + NL * TPW);
+      load_batch(nxt, pc, j + NL * TPW, pid);
+      fetch_pages(pid, pc, j + 2 * NL * TPW);
       compute_batch(cur, pc, j);
       j += NL * TPW;
     }

@@ -25,6 +25,10 @@ Values are N(0, 1) drawn in float32 and rounded to nearest-even into the
 storage dtype.  Draw order: sequence lengths, then q, then K, then V.  Ragged
 lengths are integers uniform on the closed interval.  The three grouping-sweep
 runs share one set of queries (seed 1004); their caches use seed 1004 + H_kv.
+
+to_pages lays a dense cache out in pages of a pool (any workload can be
+read through a block table that way); the order of the pages in the pool is a
+seeded random permutation.
 """
 from __future__ import annotations
 
@@ -179,3 +183,49 @@ def layer_view(inputs: dict, l: int) -> dict:
         res["k"] = inputs["k"][l]
         res["v"] = inputs["v"][l]
     return res
+
+
+def to_pages(inputs: dict, page: int, seed: int, spare: int = 3, share_first_page: bool = False,
+             shuffle: bool = True):
+    """The dense cache of ``inputs`` (k, v [B, H_kv, T, d]) in pages of
+    ``page`` tokens: returns (k_pool, v_pool [num_pages, H_kv, page, d],
+    block_table int32 [B, ceil(T / page)]) on the cache's device.
+
+    Sequence b (its length clamped to [0, T]) gets ceil(len / page) pages,
+    taken in the order of a seeded permutation of the pool (in pool order
+    when ``shuffle`` is false), which has ``spare`` pages more than the
+    sequences use.  Spare pages and the rows of
+    a last page past the sequence's length are NaN; table entries past a
+    sequence's last page name the last page of the permutation, which is spare
+    (spare >= 1).  ``share_first_page`` points sequence 1's first entry at
+    sequence 0's first page (a shared prefix), when sequence 0 fills that page
+    and sequence 1 uses a page.
+    """
+    if spare < 1:
+        raise ValueError("spare must be at least 1")
+    k, v = inputs["k"], inputs["v"]
+    B, H_kv, T, d = k.shape
+    dev = k.device
+    lens = [max(0, min(int(n), T)) for n in inputs["seq_lens"].tolist()]
+    used = [-(-n // page) for n in lens]
+    total = sum(used) + spare
+    perm = (torch.randperm(total, generator=torch.Generator().manual_seed(seed)) if shuffle
+            else torch.arange(total)).tolist()
+    k_pool = torch.full((total, H_kv, page, d), float("nan"), dtype=k.dtype, device=dev)
+    v_pool = torch.full_like(k_pool, float("nan"))
+    table = torch.full((B, -(-T // page)), perm[-1], dtype=torch.int32)
+    o = 0
+    for b in range(B):
+        u = used[b]
+        if u == 0:
+            continue
+        ids = perm[o:o + u]
+        o += u
+        for src, pool in ((k, k_pool), (v, v_pool)):
+            rows = torch.full((H_kv, u * page, d), float("nan"), dtype=k.dtype, device=dev)
+            rows[:, :lens[b]] = src[b, :, :lens[b]]
+            pool[torch.tensor(ids, device=dev)] = rows.view(H_kv, u, page, d).permute(1, 0, 2, 3)
+        table[b, :u] = torch.tensor(ids, dtype=torch.int32)
+    if share_first_page and B > 1 and lens[0] >= page and used[1] > 0:
+        table[1, 0] = table[0, 0]
+    return k_pool, v_pool, table.to(dev)

@@ -187,6 +187,32 @@ gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_ca
                              const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step of one layer whose cache is held in pages of a pool.
+ * "Grouped-Query Attention Shares Keys Without Sharing Every Query" counts
+ * paging among the allocations a serving system adds on top of the logical
+ * cache size; the attention is the one defined above, only the place of each
+ * cached row changes:
+ *   k_pool, v_pool : pages of page_size tokens, [num_pages][H_kv][page_size][d]
+ *                    (page p, KV head h, token j of the page at row
+ *                    (p * H_kv + h) * page_size + j)
+ *   block_table    : [B][max_pages] int32 page ids (device): token t of
+ *                    sequence b is in page block_table[b][t / page_size]
+ *   page_size      : a positive multiple of 16
+ *   max_pages      : entries per sequence; max_pages * page_size >=
+ *                    dims->max_seq_len, the capacity each sequence's lengths
+ *                    are clamped to.
+ * The pools are 16-byte aligned and the table 4-byte aligned
+ * (GQA_ERR_INVALID_ARG otherwise).  Only the table entries of valid tokens
+ * are read; they must name pages of the pool, and sequences may share pages.
+ * bf16 caches on the matrix-core path only (otherwise
+ * GQA_ERR_UNSUPPORTED); the workspace is gqa_decode_workspace_bytes(dims, 1).
+ * q, out, seq_lens, scale, stream and the errors as for gqa_decode.
+ */
+gqa_status gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                            int32_t max_pages, int32_t page_size, const int32_t* seq_lens, float scale, void* out,
+                            const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The step before a decode step: append each sequence's new token to the
  * cache of one layer, with rotary position embedding ("Grouped-Query
  * Attention (GQA) and Multi-Query Attention (MQA): ...", section 4, "Rotary

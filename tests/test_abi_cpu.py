@@ -206,6 +206,34 @@ def test_append_rope_validation():
                                      None) == INVALID
 
 
+def call_paged(d, ptrs=None, bt=FAKE, max_pages=64, page=16, scale=0.125):
+    q, k, v, sl, out = ptrs or [FAKE] * 5
+    return gqa.lib().gqa_decode_paged(q, k, v, bt, max_pages, page, sl, scale, out, ctypes.byref(d), None, 0, None)
+
+
+def test_decode_paged_validation():
+    """The paged entry point checks its arguments before touching the device."""
+    d = dims(T_max=1024)
+    for page in (0, -16, 8, 24, 100):
+        assert call_paged(d, page=page) == INVALID, page
+    assert call_paged(d, max_pages=0) == INVALID
+    assert call_paged(d, max_pages=63, page=16) == INVALID       # 63 * 16 < max_seq_len
+    assert call_paged(d, max_pages=16, page=64) == WORKSPACE     # exactly max_seq_len: valid, needs a workspace
+    assert call_paged(dims(dtype=torch.float32)) == UNSUPPORTED  # fp32 runs on the vector path only
+    assert call_paged(dims(path="valu")) == UNSUPPORTED
+    assert call_paged(dims(d=96)) == UNSUPPORTED
+    assert call_paged(d, bt=None) == INVALID
+    assert call_paged(d, bt=FAKE + 2) == INVALID                 # not 4-byte aligned
+    for pos in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[pos] = None
+        assert call_paged(d, ptrs) == INVALID, pos
+    assert call_paged(d, scale=float("nan")) == INVALID
+    assert gqa.lib().gqa_decode_paged(FAKE, FAKE, FAKE, FAKE, 64, 16, FAKE, 0.125, FAKE, None, None, 0,
+                                      None) == INVALID
+    assert call_paged(dims(B=0), [None] * 5, bt=None) == OK
+
+
 def test_library_missing_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding._build, "LIB_PATH", str(tmp_path / "absent.so"))
@@ -217,3 +245,29 @@ def test_binding_validates_tensors_on_cpu():
     x = torch.zeros(1, 8, 64)
     with pytest.raises((ValueError, TypeError)):
         gqa.decode(x, torch.zeros(1, 2, 16, 64), torch.zeros(1, 2, 16, 64), torch.zeros(1, dtype=torch.int64), 0.1)
+
+
+def test_page_layout_of_the_input_generator():
+    """workloads.to_pages puts every valid row where the block table says and
+    nothing else: token t of sequence b, KV head g, is row t % page of page
+    table[b, t // page]; spare pages, page tails and unused entries are NaN."""
+    w = workloads.Workload("pages", 4, 8, 2, 16, 1, 70, torch.bfloat16, 3)
+    x = workloads.generate(w, "cpu")
+    x["seq_lens"] = torch.tensor([0, 33, 70, 200], dtype=torch.int32)   # the last is clamped to T = 70
+    kp, vp, table = workloads.to_pages(x, 32, seed=1, spare=2)
+    lens = [0, 33, 70, 70]
+    used = [0, 2, 3, 3]
+    assert kp.shape == (sum(used) + 2, 2, 32, 16) and table.shape == (4, 3)
+    seen = set()
+    for b in range(4):
+        for t in range(lens[b]):
+            pid = int(table[b, t // 32])
+            seen.add(pid)
+            assert torch.equal(kp[pid, :, t % 32], x["k"][b, :, t])
+            assert torch.equal(vp[pid, :, t % 32], x["v"][b, :, t])
+        for j in range(used[b], 3):
+            assert bool(torch.isnan(kp[int(table[b, j])]).all())
+    assert len(seen) == sum(used)
+    spare = [p for p in range(kp.shape[0]) if p not in seen]
+    assert len(spare) == 2 and all(bool(torch.isnan(kp[p]).all()) for p in spare)
+    assert bool(torch.isnan(kp[int(table[1, 1]), :, 1:]).all())   # tail of sequence 1's last page
