@@ -229,3 +229,28 @@ def to_pages(inputs: dict, page: int, seed: int, spare: int = 3, share_first_pag
     if share_first_page and B > 1 and lens[0] >= page and used[1] > 0:
         table[1, 0] = table[0, 0]
     return k_pool, v_pool, table.to(dev)
+
+
+E4M3_MAX = 448.0   # largest finite OCP E4M3 value
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """``x`` as one-byte OCP E4M3 codes and one scale: scale = max|x| / 448
+    over the finite elements (a float32 value), codes = torch's
+    round-to-nearest-even conversion of x / scale to float8_e4m3fn, as uint8.
+    Non-finite elements become NaN codes.  Returns (codes, scale)."""
+    xf = x.float()
+    fin = torch.isfinite(xf)
+    amax = float(xf[fin].abs().max()) if bool(fin.any()) else 0.0
+    scale = float(torch.tensor(amax / E4M3_MAX if amax > 0 else 1.0, dtype=torch.float32))
+    y = torch.where(fin, xf / scale, torch.full_like(xf, float("nan")))
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
+
+
+def to_e4m3(inputs: dict) -> dict:
+    """A copy of ``inputs`` whose k and v are E4M3 codes (uint8, same layout)
+    with their scales k_scale and v_scale; NaN padding stays NaN."""
+    out = dict(inputs)
+    out["k"], out["k_scale"] = quantize_e4m3(inputs["k"])
+    out["v"], out["v_scale"] = quantize_e4m3(inputs["v"])
+    return out

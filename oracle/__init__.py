@@ -13,6 +13,10 @@ Contents
   section 2, subsection "Grouped-Query Attention (GQA)".
 * :meth:`Oracle.decode_paged` -- the same attention with the cache held in
   pages of a pool, found through a per-sequence block table.
+* :meth:`Oracle.decode_fp8` -- the same attention over a cache of one-byte
+  OCP E4M3 elements with one scale for the keys and one for the values (the
+  bytes-per-element term of section 1, "KV Cache Memory Footprint", below
+  two); :meth:`Oracle.e4m3` decodes such bytes.
 * :meth:`Oracle.rope` -- fp64 rotary position embedding (section 4 of the
   same page, "Rotary Position Embeddings (RoPE) Interaction"), for the step
   that appends the new token's keys and values.
@@ -77,6 +81,11 @@ class Oracle:
         lib.oracle_gqa_decode_paged.restype = ctypes.c_int
         lib.oracle_gqa_decode_paged.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, i64, i64, vp, dbl,
                                                 i64, vp, vp]
+        lib.oracle_gqa_decode_fp8.restype = ctypes.c_int
+        lib.oracle_gqa_decode_fp8.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, dbl, dbl, dbl,
+                                              i64, vp, vp]
+        lib.oracle_e4m3_decode.restype = ctypes.c_int
+        lib.oracle_e4m3_decode.argtypes = [i64, vp, vp]
         lib.oracle_rope.restype = ctypes.c_int
         lib.oracle_rope.argtypes = [i64, i64, ctypes.c_int, vp, vp, dbl, vp]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -185,6 +194,55 @@ class Oracle:
                                                v_pool.data_ptr(), bt.ctypes.data, bt.shape[1], int(page),
                                                sl.ctypes.data, float(np.float32(scale)), B * H_q, None,
                                                out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return out
+
+    def e4m3(self, codes) -> np.ndarray:
+        """fp64 values of OCP E4M3 bytes (uint8 array or tensor, any shape)."""
+        c = np.ascontiguousarray(np.asarray(codes.cpu() if isinstance(codes, torch.Tensor) else codes,
+                                            dtype=np.uint8))
+        out = np.zeros(c.shape, dtype=np.float64)
+        self._lib.oracle_e4m3_decode(c.size, c.ctypes.data, out.ctypes.data)
+        return out
+
+    def decode_fp8(self, q, k8, v8, seq_lens, scale: float, k_scale: float, v_scale: float, kv_offsets=None,
+                   heads=None, num_kv_heads: Optional[int] = None) -> np.ndarray:
+        """fp64 outputs for q [B, H_q, d] over a cache of E4M3 bytes: ``k8`` and
+        ``v8`` (uint8, or float8_e4m3fn tensors, which are read as their bytes)
+        in the dense [B, H_kv, T_max, d] or packed layout of :meth:`decode`; a
+        key element stands for k_scale times its E4M3 value, a value element for
+        v_scale times its own.  The three scales are widened from float32, as
+        float32 arguments reach the GPU path."""
+        if q.dtype not in _DTYPE_CODE:
+            raise TypeError("oracle takes float32, bfloat16 or float64 queries")
+        k8 = k8.detach().to("cpu").contiguous().view(torch.uint8)
+        v8 = v8.detach().to("cpu").contiguous().view(torch.uint8)
+        if v8.shape != k8.shape:
+            raise ValueError("k8 and v8 must have one shape")
+        q = q.detach().to("cpu").contiguous()
+        B, H_q, d = q.shape
+        if kv_offsets is None:
+            if k8.dim() != 4 or k8.shape[0] != B or k8.shape[3] != d:
+                raise ValueError("dense cache must be [B, H_kv, T_max, d]")
+            H_kv, T_max = k8.shape[1], k8.shape[2]
+            offs = np.arange(B + 1, dtype=np.int64) * T_max
+        else:
+            offs = np.ascontiguousarray(np.asarray(kv_offsets, dtype=np.int64))
+            H_kv = num_kv_heads if num_kv_heads else H_q
+        sl = np.ascontiguousarray(np.asarray(
+            seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens, dtype=np.int32))
+        if heads is None:
+            out = np.zeros((B, H_q, d), dtype=np.float64)
+            ids_ptr, n = None, B * H_q
+        else:
+            ids = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+            out = np.zeros((ids.shape[0], d), dtype=np.float64)
+            ids_ptr, n = ids.ctypes.data, ids.shape[0]
+        f32 = lambda x: float(np.float32(x))
+        rc = self._lib.oracle_gqa_decode_fp8(B, H_q, H_kv, d, _DTYPE_CODE[q.dtype], q.data_ptr(), k8.data_ptr(),
+                                             v8.data_ptr(), offs.ctypes.data, sl.ctypes.data, f32(scale),
+                                             f32(k_scale), f32(v_scale), n, ids_ptr, out.ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return out

@@ -29,6 +29,17 @@
  *   - bf16 inputs are widened by their definition (the 16 stored bits are the
  *     upper half of an IEEE binary32), which is exact.
  *
+ * Lower-precision caches (oracle_gqa_decode_fp8): the same page's KV
+ * footprint formula (section 1, "KV Cache Memory Footprint") carries the
+ * bytes per element as a factor of its own (2 for FP16/BF16), and
+ * "Grouped-Query Attention Shares Keys Without Sharing Every Query" keeps it
+ * as "bytes per element".  The pages give no format or dequantisation rule;
+ * read as one byte per element in the OCP 8-bit floating-point format E4M3
+ * (sign, 4 exponent bits of bias 7, 3 mantissa bits; subnormals; no
+ * infinities; S.1111.111 is NaN; largest finite 448), and a cached key
+ * (value) equal to k_scale (v_scale) times its E4M3 value, one scale per
+ * array.  The attention then runs on those values as above.
+ *
  * Also: the rotary position embedding of section 4 of the same page
  * ("Rotary Position Embeddings (RoPE) Interaction"), for the step that
  * appends the new token's keys and values to the cache (oracle_rope).
@@ -47,11 +58,23 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2, ORACLE_E4M3 = 3 };
+
+/* The value of one OCP E4M3 byte, from the format's definition: sign bit,
+ * exponent field e (bias 7), mantissa field m; e = 0 is subnormal
+ * (m/8 * 2^(1-7)), e = 15 with m = 7 is NaN, anything else is normal
+ * ((1 + m/8) * 2^(e-7)). */
+static double e4m3_value(uint8_t x) {
+  const int sign = x >> 7, e = (x >> 3) & 0xF, m = x & 0x7;
+  if (e == 0xF && m == 0x7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m / 8.0, 1 - 7) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
 
 /* Widen element `idx` of an array of the given type to double. */
 static double load_elem(const void* base, int64_t idx, int dtype) {
   if (dtype == ORACLE_F64) return ((const double*)base)[idx];
+  if (dtype == ORACLE_E4M3) return e4m3_value(((const uint8_t*)base)[idx]);
   if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
   /* bf16: the stored half-word is the high half of a binary32. */
   uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
@@ -101,16 +124,27 @@ static int64_t cache_capacity(const cache_layout* L, int64_t b) {
   return L->block_table ? L->max_pages * L->page : L->kv_offsets[b + 1] - L->kv_offsets[b];
 }
 
+/* A cached key or value array: element idx stands for scale * (its stored
+ * value); scale is 1 for full-precision caches. */
+typedef struct {
+  const void* data;
+  int dtype;
+  double scale;
+} kv_array;
+
+static double kv_elem(const kv_array* a, int64_t idx) { return a->scale * load_elem(a->data, idx, a->dtype); }
+
 /*
  * Attention weights and output of one query head.
- *   q, q_off : query array and the element offset of Q_i's d elements
- *   k, v  : whole cache arrays, addressed through cache_row()
+ *   q, q_off : query array (elements of type dtype) and the element offset
+ *              of Q_i's d elements
+ *   K, V  : whole cache arrays, addressed through cache_row()
  *   w     : optional, receives the n softmax weights (may be NULL)
  *   out   : receives the d outputs
  *   s     : scratch of at least the sequence's capacity
  * Returns 0, or -1 when n is negative or exceeds the sequence's capacity.
  */
-static int head_forward(const void* q, int64_t q_off, const void* k, const void* v, int dtype, int64_t d,
+static int head_forward(const void* q, int64_t q_off, int dtype, const kv_array* K, const kv_array* V, int64_t d,
                         const cache_layout* L, int64_t b, int64_t g, int64_t n, double scale,
                         double* s /* scratch, n */, double* w, double* out) {
   int64_t cap = cache_capacity(L, b);
@@ -122,7 +156,7 @@ static int head_forward(const void* q, int64_t q_off, const void* k, const void*
   for (int64_t t = 0; t < n; ++t) {
     int64_t row = cache_row(L, b, g, t) * d;
     double acc = 0.0;
-    for (int64_t c = 0; c < d; ++c) acc += load_elem(q, q_off + c, dtype) * load_elem(k, row + c, dtype);
+    for (int64_t c = 0; c < d; ++c) acc += load_elem(q, q_off + c, dtype) * kv_elem(K, row + c);
     s[t] = scale * acc;
   }
   /* softmax over t in [0, n). */
@@ -135,7 +169,7 @@ static int head_forward(const void* q, int64_t q_off, const void* k, const void*
     double wt = exp(s[t] - m) / z;
     if (w) w[t] = wt;
     int64_t row = cache_row(L, b, g, t) * d;
-    for (int64_t c = 0; c < d; ++c) out[c] += wt * load_elem(v, row + c, dtype);
+    for (int64_t c = 0; c < d; ++c) out[c] += wt * kv_elem(V, row + c);
   }
   return 0;
 }
@@ -158,8 +192,8 @@ static int check_dims(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype
  * Returns 0 on success, -1 on invalid arguments (nothing is written then for
  * the offending head).
  */
-static int decode_heads(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype, const void* q, const void* k,
-                        const void* v, const cache_layout* L, const int32_t* seq_lens, double scale,
+static int decode_heads(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype, const void* q, const kv_array* K,
+                        const kv_array* V, const cache_layout* L, const int32_t* seq_lens, double scale,
                         int64_t n_heads, const int64_t* head_ids, double* out) {
   if (check_dims(B, H_q, H_kv, d, dtype)) return -1;
   if (!head_ids) n_heads = B * H_q;
@@ -183,7 +217,7 @@ static int decode_heads(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dty
       int64_t id = head_ids ? head_ids[j] : j;
       int64_t b = id / H_q, i = id % H_q;
       int64_t g = oracle_group_of(i, R);
-      int rc = s ? head_forward(q, (b * H_q + i) * d, k, v, dtype, d, L, b, g,
+      int rc = s ? head_forward(q, (b * H_q + i) * d, dtype, K, V, d, L, b, g,
                                 (int64_t)seq_lens[b], scale, s, NULL, out + j * d)
                  : -1;
       if (rc) {
@@ -201,7 +235,31 @@ int oracle_gqa_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype
                       const int64_t* kv_offsets, const int32_t* seq_lens, double scale,
                       int64_t n_heads, const int64_t* head_ids, double* out) {
   cache_layout L = {kv_offsets, NULL, 0, 0, H_kv};
-  return decode_heads(B, H_q, H_kv, d, dtype, q, k, v, &L, seq_lens, scale, n_heads, head_ids, out);
+  const kv_array K = {k, dtype, 1.0}, V = {v, dtype, 1.0};
+  return decode_heads(B, H_q, H_kv, d, dtype, q, &K, &V, &L, seq_lens, scale, n_heads, head_ids, out);
+}
+
+/*
+ * The same outputs for a cache of one-byte OCP E4M3 elements (see the file
+ * header): k8, v8 in the dense/packed layout of kv_row(), each key element
+ * standing for k_scale times its E4M3 value and each value element for
+ * v_scale times its own.  q (and the outputs) as for oracle_gqa_decode.
+ * Returns -1 also for a non-finite scale.
+ */
+int oracle_gqa_decode_fp8(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype,
+                          const void* q, const void* k8, const void* v8,
+                          const int64_t* kv_offsets, const int32_t* seq_lens, double scale,
+                          double k_scale, double v_scale, int64_t n_heads, const int64_t* head_ids, double* out) {
+  if (!isfinite(k_scale) || !isfinite(v_scale)) return -1;
+  cache_layout L = {kv_offsets, NULL, 0, 0, H_kv};
+  const kv_array K = {k8, ORACLE_E4M3, k_scale}, V = {v8, ORACLE_E4M3, v_scale};
+  return decode_heads(B, H_q, H_kv, d, dtype, q, &K, &V, &L, seq_lens, scale, n_heads, head_ids, out);
+}
+
+/* The values of n OCP E4M3 bytes (the decoder the fp8 attention uses). */
+int oracle_e4m3_decode(int64_t n, const uint8_t* codes, double* out) {
+  for (int64_t j = 0; j < n; ++j) out[j] = e4m3_value(codes[j]);
+  return 0;
 }
 
 /*
@@ -217,7 +275,8 @@ int oracle_gqa_decode_paged(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int
                             double* out) {
   if (!block_table || max_pages < 0 || page <= 0) return -1;
   cache_layout L = {NULL, block_table, max_pages, page, H_kv};
-  return decode_heads(B, H_q, H_kv, d, dtype, q, k_pool, v_pool, &L, seq_lens, scale, n_heads, head_ids, out);
+  const kv_array K = {k_pool, dtype, 1.0}, V = {v_pool, dtype, 1.0};
+  return decode_heads(B, H_q, H_kv, d, dtype, q, &K, &V, &L, seq_lens, scale, n_heads, head_ids, out);
 }
 
 /* Softmax weights of one query head (b, i): w[0..seq_lens[b]) and its output. */
@@ -233,7 +292,8 @@ int oracle_gqa_head_weights(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int
   double* s = (double*)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1));
   if (!s) return -1;
   cache_layout L = {kv_offsets, NULL, 0, 0, H_kv};
-  int rc = head_forward(q, (b * H_q + i) * d, k, v, dtype, d, &L, b,
+  const kv_array K = {k, dtype, 1.0}, V = {v, dtype, 1.0};
+  int rc = head_forward(q, (b * H_q + i) * d, dtype, &K, &V, d, &L, b,
                         oracle_group_of(i, H_q / H_kv), n, scale, s, w, out);
   free(s);
   return rc;

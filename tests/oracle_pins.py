@@ -297,6 +297,56 @@ def pin_paged_layout(orc):
         assert np.array_equal(got, dense), page
 
 
+# ------------------------------------------------ one-byte E4M3 caches --
+# The bytes-per-element factor of "Grouped-Query Attention (GQA) and
+# Multi-Query Attention (MQA): ...", section 1, "KV Cache Memory Footprint"
+# (2 for FP16/BF16), taken to one byte: OCP E4M3 elements with one scale per
+# array (the pages give no format; this is the reading the oracle states).
+def pin_e4m3_decode(orc):
+    """All 256 codes against torch's float8_e4m3fn widening (a library
+    routine), and the format's landmarks: 0x38 = 1, 0x7E = 448 (largest
+    finite), 0x08 = 2^-6 (smallest normal), 0x07 = 7 * 2^-9 and 0x01 = 2^-9
+    (subnormals), 0x80 = -0, 0x7F and 0xFF NaN."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    got = orc.e4m3(codes)
+    lib = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(got, lib, equal_nan=True)
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x08] == 2.0 ** -6 and got[0x07] == 7 * 2.0 ** -9 and got[0x01] == 2.0 ** -9
+    assert got[0x80] == 0.0 and np.signbit(got[0x80])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.isfinite(np.delete(got, [0x7F, 0xFF])).all()
+
+
+def pin_fp8_attention_is_dequantised_attention(orc):
+    """The E4M3-cache attention equals the fp64 attention over K =
+    k_scale * E4M3(k8) and V = v_scale * E4M3(v8), widened by torch; ragged
+    lengths with NaN codes in the padding, GQA and MQA, distinct scales."""
+    for shape, seed in (((3, 8, 2, 64, 40), 71), ((2, 16, 1, 32, 33), 72)):
+        x = case(*shape, seed=seed, dtype=torch.bfloat16, lo=0, poison=True)
+        x8 = workloads.to_e4m3(x)
+        ks, vs = x8["k_scale"], x8["v_scale"] * 1.5
+        got = orc.decode_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], ks, vs)
+        kd = x8["k"].view(torch.float8_e4m3fn).to(torch.float64) * float(np.float32(ks))
+        vd = x8["v"].view(torch.float8_e4m3fn).to(torch.float64) * float(np.float32(vs))
+        want = orc.decode(x["q"].double(), kd, vd, x["seq_lens"], x["scale"])
+        assert np.isfinite(got).all() and np.abs(got - want).max() <= 1e-12, shape
+
+
+def pin_fp8_scale_placement(orc):
+    """k_scale multiplies the scores and v_scale the output: with powers of
+    two every product stays exact, so trading k_scale against ``scale`` and
+    pulling v_scale out of the sum change nothing, bitwise."""
+    x = case(2, 8, 2, 32, 24, 73, dtype=torch.bfloat16, lo=1)
+    x8 = workloads.to_e4m3(x)
+    a = orc.decode_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], 2.0, 1.0)
+    b = orc.decode_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], 2.0 * x["scale"], 1.0, 1.0)
+    c = orc.decode_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], 1.0, 4.0)
+    d = orc.decode_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], 1.0, 1.0)
+    assert np.array_equal(a, b)
+    assert np.array_equal(c, 4.0 * d)
+    assert not np.allclose(a, d)
+
+
 # --------------------------------------------- rotary position embedding --
 # "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): ...",
 # section 4, "Rotary Position Embeddings (RoPE) Interaction".

@@ -28,11 +28,11 @@ MUTANTS = {
     # no normalisation
     "no_normalisation": ("double wt = exp(s[t] - m) / z;", "double wt = exp(s[t] - m);"),
     # values read from the key cache
-    "values_from_keys": ("load_elem(v, row + c, dtype)", "load_elem(k, row + c, dtype)"),
+    "values_from_keys": ("kv_elem(V, row + c)", "kv_elem(K, row + c)"),
     # transposed key operand
-    "keys_transposed": ("load_elem(k, row + c, dtype)", "load_elem(k, cache_row(L, b, g, 0) * d + c * n + t, dtype)"),
+    "keys_transposed": ("kv_elem(K, row + c)", "kv_elem(K, cache_row(L, b, g, 0) * d + c * n + t)"),
     # query row of the group's first head used for every head
-    "query_of_group": ("(b * H_q + i) * d, k, v, dtype, d, L, b, g,", "(b * H_q + g * R) * d, k, v, dtype, d, L, b, g,"),
+    "query_of_group": ("(b * H_q + i) * d, dtype, K, V, d, L, b, g,", "(b * H_q + g * R) * d, dtype, K, V, d, L, b, g,"),
     # KV heads interleaved per token instead of stored one after another
     "kv_layout_interleaved": ("return kv_offsets[b] * H_kv + h * cap + t;", "return kv_offsets[b] * H_kv + h + t * H_kv;"),
     # bf16 widened with the wrong shift
@@ -45,6 +45,15 @@ MUTANTS = {
     "paged_row_swapped": ("return (p * L->H_kv + h) * L->page + t % L->page;", "return (p * L->H_kv + h) * L->page + t / L->page;"),
     # paged cache: pages stored token-major instead of head-major
     "paged_head_major": ("return (p * L->H_kv + h) * L->page + t % L->page;", "return (p * L->page + t % L->page) * L->H_kv + h;"),
+    # E4M3: exponent bias 8 instead of 7
+    "e4m3_bias": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    # E4M3: subnormals decoded with the implicit leading one
+    "e4m3_subnormal_as_normal": ("e == 0 ? ldexp((double)m / 8.0, 1 - 7)", "e == 0 ? ldexp(1.0 + (double)m / 8.0, 1 - 7)"),
+    # E4M3: the NaN code read as a finite value (480)
+    "e4m3_nan_code": ("if (e == 0xF && m == 0x7) return NAN;", ""),
+    # E4M3 cache: the key and value scales swapped
+    "fp8_scales_swapped": ("const kv_array K = {k8, ORACLE_E4M3, k_scale}, V = {v8, ORACLE_E4M3, v_scale};",
+                           "const kv_array K = {k8, ORACLE_E4M3, v_scale}, V = {v8, ORACLE_E4M3, k_scale};"),
     # rotary embedding: turning the other way
     "rope_orientation": ("out[v * d + 2 * j] = x0 * c - x1 * s;", "out[v * d + 2 * j] = x0 * c + x1 * s;"),
     # rotary embedding: pairs (j, j + d/2) instead of consecutive elements
