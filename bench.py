@@ -1,6 +1,6 @@
 """GQA decode-step benchmark: effective HBM GB/s and microseconds per step.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--paged PAGE] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--paged PAGE] [--kv fp8] [--gpus 1]
 
 One step = one decode step of the workload (every split-KV piece and the
 merge of the pieces: one kernel launch when the merge is fused into the
@@ -9,7 +9,9 @@ batch of synthetic inputs that are already resident in HBM.  Steps rotate over e
 (``--replicas``) that the working set exceeds the 256 MB last-level
 (Infinity) cache, so every step streams its K/V from HBM.  ``--paged PAGE`` lays each batch's
 cache out in pages of PAGE tokens (shuffled in a pool, read through a block
-table) and times gqa_decode_paged instead.
+table) and times gqa_decode_paged instead.  ``--kv fp8`` stores each batch's
+cache as one-byte E4M3 codes with one scale per array and times
+gqa_decode_fp8 (the bytes per cached element halve).
 
 Metric: (K + V bytes of the valid tokens + q bytes + out bytes) / time, the
 KV traffic formula of "Grouped-Query Attention (GQA) and Multi-Query
@@ -58,11 +60,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, seq_lens, out_elem_bytes, page: int = 0) -> int:
+def algorithmic_bytes(w, seq_lens, out_elem_bytes, page: int = 0, kv_elem_bytes: int = 0) -> int:
     """K/V of the valid tokens, q and out; with pages, also the block-table
-    entries of the pages in use (4 bytes each, read once)."""
+    entries of the pages in use (4 bytes each, read once).  kv_elem_bytes
+    overrides the cache element size (1 for E4M3)."""
     e = 2 if str(w.dtype).endswith("bfloat16") else 4
-    kv = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * e
+    kv = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * (kv_elem_bytes or e)
     qb = w.layers * w.B * w.H_q * w.d * e
     ob = w.layers * w.B * w.H_q * w.d * out_elem_bytes
     tb = 4 * sum(-(-int(n) // page) for n in seq_lens.tolist()) if page else 0
@@ -160,6 +163,8 @@ def main():
     ap.add_argument("--chunk-tokens", type=int, default=0)
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE",
                     help="cache in shuffled pages of PAGE tokens (a multiple of 16), read through a block table")
+    ap.add_argument("--kv", default="same", choices=["same", "fp8"],
+                    help="cache elements: the workload's dtype, or one-byte E4M3 codes with per-array scales")
     ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -187,11 +192,17 @@ def main():
     if args.paged and (w.layers != 1 or w.packed or w.dtype != torch.bfloat16 or args.paged % 16):
         print("--paged takes a single-layer bf16 workload and a page that is a multiple of 16", file=sys.stderr)
         sys.exit(2)
+    fp8 = args.kv == "fp8"
+    if fp8 and (w.layers != 1 or w.packed or w.dtype != torch.bfloat16 or args.paged):
+        print("--kv fp8 takes a single-layer bf16 workload in the dense layout", file=sys.stderr)
+        sys.exit(2)
     out_dtype = {None: w.dtype, "bf16": torch.bfloat16, "fp32": torch.float32}[args.out_dtype]
     seq_lens = workloads.seq_lens_for(w)
     kv_bytes = 2 * w.layers * int(seq_lens.sum()) * w.H_kv * w.d * (2 if w.dtype == torch.bfloat16 else 4)
     resident = kv_bytes if w.packed else 2 * w.layers * w.B * w.H_kv * w.T_max * w.d * (
         2 if w.dtype == torch.bfloat16 else 4)
+    if fp8:
+        resident //= 2
     reps = args.replicas or max(1, min(16, -(-(2 << 30) // resident)))
     free, _ = torch.cuda.mem_get_info(dev)
     reps = max(1, min(reps, int((free * 0.85) // max(resident, 1))))
@@ -202,6 +213,12 @@ def main():
     kw = dict(out_dtype=out_dtype, chunk_tokens=args.chunk_tokens, path=args.path)
     launchers = []
     for r, x in enumerate(batches):
+        if fp8:
+            x8 = workloads.to_e4m3(x)
+            del x["k"], x["v"]   # the E4M3 copy holds the cache now
+            launchers.append(gqa.prepare_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], x8["k_scale"],
+                                             x8["v_scale"], out_dtype=out_dtype, chunk_tokens=args.chunk_tokens))
+            continue
         if args.paged:
             kp, vp, table = workloads.to_pages(x, args.paged, seed=1000 + r, spare=1)
             del x["k"], x["v"]   # the pool holds the cache now
@@ -229,7 +246,7 @@ def main():
     wall = time.perf_counter() - t0
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / args.steps
-    nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4, args.paged)
+    nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4, args.paged, 1 if fp8 else 0)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
     # The decode kernel's duration per launch: the HIP events above bracket the
@@ -242,12 +259,12 @@ def main():
     d = gqa.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype, out_dtype, chunk_tokens=args.chunk_tokens,
                       path=args.path)
     a, b = gqa.plan(d, w.layers)
-    mfma = args.paged or args.path == "mfma" or (args.path == "auto" and w.dtype == torch.bfloat16 and w.B <= 4096)
+    mfma = args.paged or fp8 or args.path == "mfma" or (args.path == "auto" and w.dtype == torch.bfloat16 and w.B <= 4096)
     if mfma:   # token split: (forced tokens per workgroup or 0 for an even split, workgroups)
         split = {"kernel": "matrix-core, token split", "workgroups": b, "tokens_per_workgroup": a or "even"}
     else:      # vector path: (tokens per chunk, chunks of the longest sequence)
         split = {"kernel": "vector ALU, chunked", "chunk_tokens": a, "chunks_per_sequence": b}
-    traffic = (read_traffic(w.name + ("/paged%d" % args.paged if args.paged else ""), nbytes)
+    traffic = (read_traffic(w.name + ("/paged%d" % args.paged if args.paged else "") + ("/fp8" if fp8 else ""), nbytes)
                if args.path in ("auto", "mfma") and not args.chunk_tokens else None)
 
     result = {
@@ -263,12 +280,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp32",
+        "dtype": ("fp8 e4m3 cache, bf16 q" if fp8 else "bf16" if w.dtype == torch.bfloat16 else "fp32"),
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "G": w.G, "d": w.d,
                    "cached_tokens": [w.seq_lo, w.seq_hi], "seq_lens_sum": int(seq_lens.sum()), "layers": w.layers,
                    "layout": ("paged, %d tokens per page" % args.paged if args.paged
                               else "packed" if w.packed else "dense"), "accumulate": "fp32",
+                   "kv_elements": "OCP E4M3 (1 byte), per-array scales" if fp8 else
+                   ("bf16" if w.dtype == torch.bfloat16 else "fp32"),
                    "out_dtype": "bf16" if out_dtype == torch.bfloat16 else "fp32",
                    "path": args.path, "work_split": split,
                    "input_batches_rotated": reps, "algorithmic_bytes_per_step": nbytes,
@@ -280,7 +299,7 @@ def main():
         "cpu_baseline": None,
         "context": {"h100_sxm5_hbm_TBps": 3.35, "h100_sxm5_dense_bf16_TFLOPs": 989, "h100_I_sat_FLOP_per_B": 295.2},
     }
-    if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged:
+    if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged and not fp8:
         result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

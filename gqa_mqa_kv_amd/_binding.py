@@ -20,8 +20,8 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
-SYMBOLS = ("gqa_append_rope", "gqa_decode", "gqa_decode_layers", "gqa_decode_paged", "gqa_decode_workspace_bytes",
-           "gqa_decode_plan", "gqa_status_string")
+SYMBOLS = ("gqa_append_rope", "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_paged",
+           "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
 
 
 class GqaDims(ctypes.Structure):
@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode_layers.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_paged.restype = ctypes.c_int
         L.gqa_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_fp8.restype = ctypes.c_int
+        L.gqa_decode_fp8.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, dims_p, vp,
+                                     sz, vp]
         L.gqa_decode_workspace_bytes.restype = sz
         L.gqa_decode_workspace_bytes.argtypes = [dims_p, i32]
         L.gqa_decode_plan.restype = ctypes.c_int
@@ -207,6 +210,49 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float, out=Non
     args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype, max_seq_len,
                              chunk_tokens, seq_len_hint, workspace, stream, tiles, merge, per_cu)
     _check(lib().gqa_decode_paged(*args))
+    return keep[0]
+
+
+E4M3_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _fp8_args(q, k8, v8, seq_lens, scale, k_scale, v_scale, out, out_dtype, chunk_tokens, seq_len_hint, workspace,
+              stream, tiles, merge, per_cu):
+    dev = q.device
+    for t, n in ((q, "q"), (k8, "k_cache"), (v8, "v_cache"), (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k8.dim() != 4 or v8.shape != k8.shape:
+        raise ValueError("expected q [B,H_q,d] and k/v [B,H_kv,T_max,d]")
+    if q.dtype != torch.bfloat16 or k8.dtype not in E4M3_DTYPES or v8.dtype not in E4M3_DTYPES:
+        raise TypeError("expected bf16 q and one-byte E4M3 caches (uint8 or float8_e4m3fn)")
+    B, H_q, d = q.shape
+    _, H_kv, T_max, _ = k8.shape
+    if k8.shape[0] != B or k8.shape[3] != d or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, "mfma", 0, tiles, merge,
+                     per_cu)
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
+    _require(out, "out", dev)
+    if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
+        raise ValueError("out must be [B,H_q,d] of the output dtype")
+    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    args = (_ptr(q), _ptr(k8), _ptr(v8), _ptr(seq_lens), float(scale), float(k_scale), float(v_scale), _ptr(out),
+            ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
+    return args, (out, q, k8, v8, seq_lens, ws, dims)
+
+
+def decode_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_scale: float, out=None, out_dtype=None,
+               chunk_tokens: int = 0, seq_len_hint: int = 0, workspace=None, stream=None, tiles: int = 0,
+               merge: str = "auto", per_cu: int = 0):
+    """One decode step of one layer over one-byte OCP E4M3 caches: q bf16
+    [B,H_q,d]; k_cache/v_cache uint8 or float8_e4m3fn [B,H_kv,T_max,d], a key
+    (value) element standing for k_scale (v_scale) times its E4M3 value.
+    Returns out [B,H_q,d]."""
+    args, keep = _fp8_args(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, out, out_dtype, chunk_tokens,
+                           seq_len_hint, workspace, stream, tiles, merge, per_cu)
+    _check(lib().gqa_decode_fp8(*args))
     return keep[0]
 
 
@@ -393,5 +439,16 @@ def prepare_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float, out_dt
     args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, None, out_dtype, max_seq_len,
                              chunk_tokens, seq_len_hint, None, stream, tiles, merge, per_cu)
     pr = Prepared(lib().gqa_decode_paged, args, keep)
+    pr()
+    return pr
+
+
+def prepare_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_scale: float, out_dtype=None,
+                chunk_tokens: int = 0, seq_len_hint: int = 0, stream=None, tiles: int = 0, merge: str = "auto",
+                per_cu: int = 0):
+    """As prepare, for gqa_decode_fp8."""
+    args, keep = _fp8_args(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, None, out_dtype, chunk_tokens,
+                           seq_len_hint, None, stream, tiles, merge, per_cu)
+    pr = Prepared(lib().gqa_decode_fp8, args, keep)
     pr()
     return pr

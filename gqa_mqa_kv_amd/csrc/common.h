@@ -55,6 +55,7 @@ struct Problem {
   float scale_log2;           // scale * log2(e): scores are kept in base 2
   const int32_t* block_table; // paged cache: [B][max_pages] page ids, or nullptr
   int32_t max_pages, page;    // paged cache: table entries per sequence, tokens per page (a multiple of 16)
+  float out_mul;              // factor of every normalised output (the value scale of an E4M3 cache, else 1)
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -353,7 +354,7 @@ __device__ __forceinline__ f32x4 merge_pieces(const Problem& p, int64_t w0, int6
       M = Mn;
     }
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float inv = den > 0.f ? p.out_mul / den : 0.f;
   return num * inv;
 }
 

@@ -37,6 +37,8 @@
 // head of the wavefront; otherwise the rescale factor would be exactly 1.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace gqa {
@@ -85,6 +87,40 @@ struct Tile16 {
   typename VRow<D>::type v[4];   // V rows 4*q4 + i, columns D/16*m16 ..
 };
 
+// A tile of one-byte E4M3 elements as loaded: lane (q4, m16) holds bytes
+// q4*D/4 .. q4*D/4 + D/4 - 1 of K row m16 (the A operands of every score
+// step, see load_q) and bytes D/16*m16 .. of V rows 4*q4 + i.
+template <int D>
+struct Tile16F8 {
+  u32x4 k[D / 64];
+  typename std::conditional<D == 128, u32x2, uint32_t>::type v[4];
+};
+
+// Two E4M3 bytes (the low or the high half-word of w) to two bf16.  Every
+// E4M3 value is a bf16 value, so the conversion (scale 1) is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
+               e4m3x2_to_bf16x2<true>(w1)};
+}
+template <int D>
+__device__ __forceinline__ Tile16<D> widen(const Tile16F8<D>& t) {
+  Tile16<D> w;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) w.k[s] = e4m3x8_to_bf16x8(t.k[s / 2][2 * (s % 2)], t.k[s / 2][2 * (s % 2) + 1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (D == 128)
+      w.v[i] = e4m3x8_to_bf16x8(t.v[i][0], t.v[i][1]);
+    else
+      w.v[i] = u32x2{e4m3x2_to_bf16x2<false>(t.v[i]), e4m3x2_to_bf16x2<true>(t.v[i])};
+  }
+  return w;
+}
+
 // Heads: each wavefront serves HB blocks of 16 query heads; the wavefronts
 // form HG groups (wavefront w is in group w % HG and streams tile lane w / HG
 // of the NW / HG lanes), so the workgroup covers 16 * HB * HG heads.  With
@@ -92,7 +128,10 @@ struct Tile16 {
 // PAGED: the cache is held in pages of a pool (p.block_table); every tile
 // then lies in one page, whose id is fetched one batch ahead of the tile's
 // loads so that the loads never wait for the table.
-template <int D, int HB, int HG, int NW, int TPW, bool PAGED>
+// KV8: cache elements are one-byte E4M3 values (bf16 queries).  Tiles move
+// as bytes and are widened to bf16, exactly, just before the products; the
+// key scale is folded into p.scale_log2 and the value scale into p.out_mul.
+template <int D, int HB, int HG, int NW, int TPW, bool PAGED, bool KV8>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   static_assert(NW % HG == 0, "head groups must divide the wavefronts");
   constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
@@ -100,6 +139,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   constexpr int HP = HB * 16;             // heads per wavefront
   constexpr int SLOT = HB * VW * 4 * 64;  // floats of one wavefront's O in lane order
   typedef typename VRow<D>::type vrow_t;
+  typedef typename std::conditional<KV8, uint8_t, uint16_t>::type kv_t;   // one cache element
+  typedef typename std::conditional<KV8, Tile16F8<D>, Tile16<D>>::type tile_t;
 
   __shared__ float sm_slot[(NL > 1 ? HG * (NL / 2) : 1) * SLOT];
   __shared__ float sm_wm[NW][HP], sm_wl[NW][HP];
@@ -126,13 +167,15 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   if (s0 >= s1) return;   // no tokens for this workgroup (uniform)
 
   // Per-lane element offsets inside a tile (relative to the tile's first row).
-  const uint32_t koff = (uint32_t)(m16 * D + 8 * q4);
+  // E4M3 keys: the lane's D/4 columns are contiguous (step s of the score
+  // product takes columns q4*D/4 + 8s .. +7 of K and of q alike).
+  const uint32_t koff = KV8 ? (uint32_t)(m16 * D + q4 * (D / 4)) : (uint32_t)(m16 * D + 8 * q4);
   const uint32_t voff = (uint32_t)(4 * q4 * D + VW * m16);
 
   // One piece: the part [c0, c1) of a unit that lies in this span.
   struct Ctx {
-    const uint16_t* kg;      // dense/packed: the unit's row 0; paged: the pool shifted to KV head g
-    const uint16_t* vg;
+    const kv_t* kg;          // dense/packed: the unit's row 0; paged: the pool shifted to KV head g
+    const kv_t* vg;
     const int32_t* pages;    // paged: the sequence's block-table row
     int64_t x;        // stream position of token c0
     int64_t next;     // stream position after the piece (past the unit's padding when it ends the unit)
@@ -157,8 +200,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     c.slot_id = x == s0 ? 0 : 1;
     c.w0 = pc.start / ts.span;
     c.w_last = (pc.start + pc.ui.n - 1) / ts.span;
-    c.kg = reinterpret_cast<const uint16_t*>(p.k) + pc.ui.row0 * D;
-    c.vg = reinterpret_cast<const uint16_t*>(p.v) + pc.ui.row0 * D;
+    c.kg = reinterpret_cast<const kv_t*>(p.k) + pc.ui.row0 * D;
+    c.vg = reinterpret_cast<const kv_t*>(p.v) + pc.ui.row0 * D;
     c.orow = out_row0(p, pc.ui);
     return c;
   };
@@ -169,15 +212,33 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       const int h = head0 + 16 * hb;
       const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + (c.orow + h) * D;
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + 32 * s + 8 * q4) : u32x4{0, 0, 0, 0};
+      for (int s = 0; s < KS; ++s) {
+        const int col = KV8 ? q4 * (D / 4) + 8 * s : 32 * s + 8 * q4;   // the columns K's step s holds
+        qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + col) : u32x4{0, 0, 0, 0};
+      }
     }
   };
   // A tile's 16 rows are consecutive in memory, from row tr of kg/vg: row t0
   // of the unit, or, in a paged cache, row t0 % page of the page holding
   // token t0 (tiles start at multiples of 16 there and never cross a page).
-  auto load_tile = [&](Tile16<D>& T, const Ctx& c, int t0, int64_t tr) __attribute__((always_inline)) {
-    if (t0 + TILE <= c.c1) {
+  auto load_tile = [&](tile_t& T, const Ctx& c, int t0, int64_t tr) __attribute__((always_inline)) {
+    if constexpr (KV8) {
+      typedef typename std::remove_reference<decltype(T.v[0])>::type vraw_t;
+      const int last = c.c1 - 1;
+      const bool full = t0 + TILE <= c.c1;
+      // full tile: rows tr .. tr+15; ragged tail: rows past the piece are
+      // clamped to its last valid row (in bounds), their weights forced to 0
+      const kv_t* kb = PAGED ? c.kg + (tr - t0) * D : c.kg;
+      const kv_t* vb = PAGED ? c.vg + (tr - t0) * D : c.vg;
+      const kv_t* kt = full ? c.kg + tr * D + koff : kb + (int64_t)min(t0 + m16, last) * D + q4 * (D / 4);
+#pragma unroll
+      for (int s = 0; s < D / 64; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 16 * s));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const kv_t* vr = full ? c.vg + tr * D + voff + i * D : vb + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16;
+        T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vraw_t*>(vr));
+      }
+    } else if (t0 + TILE <= c.c1) {
       // full tile: one base address per lane, the rest are immediate offsets
       const uint16_t* kt = c.kg + tr * D + koff;
       const uint16_t* vt = c.vg + tr * D + voff;
@@ -222,7 +283,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     }
   };
   const int64_t page_rows = (int64_t)p.H_kv * p.page;   // pool rows per page
-  auto load_batch = [&](Tile16<D> (&T)[TPW], const Ctx& c, int j, const int32_t (&pid)[TPW])
+  auto load_batch = [&](tile_t (&T)[TPW], const Ctx& c, int j, const int32_t (&pid)[TPW])
                         __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -300,10 +361,16 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       }
     }
   };
-  auto compute_batch = [&](const Tile16<D> (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
+  auto compute_batch = [&](const tile_t (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u)
-      if (j + NL * u < c.ntiles) compute_tile(T[u], c.c0 + (j + NL * u) * TILE, c.c1);
+    for (int u = 0; u < TPW; ++u) {
+      if (j + NL * u < c.ntiles) {
+        if constexpr (KV8)
+          compute_tile(widen(T[u]), c.c0 + (j + NL * u) * TILE, c.c1);
+        else
+          compute_tile(T[u], c.c0 + (j + NL * u) * TILE, c.c1);
+      }
+    }
   };
 
   // End of a piece: combine the states of the wavefronts of each head group,
@@ -374,7 +441,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         const int h = head0 + 16 * hb;
         if (h >= G) continue;
         if (c.whole) {
-          const float inv = Lh[hb] > 0.f ? 1.f / Lh[hb] : 0.f;
+          const float inv = Lh[hb] > 0.f ? p.out_mul / Lh[hb] : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int col = VW * (4 * q4 + i);
@@ -453,12 +520,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   fetch_pages(pid, pc, j);
   load_q(qf, pc);
   reset_state();
-  Tile16<D> TA[TPW], TB[TPW];
+  tile_t TA[TPW], TB[TPW];
   load_batch(TA, pc, j, pid);
   fetch_pages(pid, pc, j + NL * TPW);
   // One step with `cur` loaded: false if it is the span's last batch (left
   // for the caller), else load the next batch into `nxt` and compute `cur`.
-  auto step = [&](const Tile16<D> (&cur)[TPW], Tile16<D> (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
+  auto step = [&](const tile_t (&cur)[TPW], tile_t (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
     const bool piece_done = j + NL * TPW >= pc.ntiles;
     const int64_t xn = PAGED ? pc.next : pc.x + (pc.c1 - pc.c0);
     if (piece_done && xn >= s1) return false;

@@ -125,11 +125,14 @@ typedef struct gqa_dims {
                               value runs as 4: each wavefront keeps two tile
                               batches in registers, which leaves room for one
                               wavefront per SIMD */
-  int32_t tiles_in_flight; /* 0: default (1); else 1 or 2: 16-token tiles per
+  int32_t tiles_in_flight; /* 0: default; else 1, 2 or 4: 16-token tiles per
                               load batch of each wavefront of the matrix-core
-                              kernel (2 only for G <= 16, else 1).  A
-                              wavefront computes one batch while the next one
-                              loads. */
+                              kernel.  A wavefront computes one batch while
+                              the next one loads.  bf16 caches: default 1,
+                              at most 2 for G <= 16, else 1.  E4M3 caches
+                              (gqa_decode_fp8): default 2 and at most 4
+                              for G <= 16, else 1.  Larger requests run at the
+                              variant's limit. */
   int32_t merge;           /* gqa_merge */
   int32_t workgroups_per_cu; /* 0: default (1); else matrix-core workgroups
                                 launched per compute unit when the split is
@@ -185,6 +188,30 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
 gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
                              const int64_t* kv_offsets, const int32_t* seq_lens, float scale, void* out,
                              const gqa_dims* dims, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of one layer over a cache of one-byte elements.  The KV
+ * footprint formula of "Grouped-Query Attention (GQA) and Multi-Query
+ * Attention (MQA): ...", section 1 ("KV Cache Memory Footprint"), counts the
+ * bytes per element as a factor of its own (two for FP16/BF16); this call
+ * halves it.  The pages name no format: each element is an OCP E4M3 byte
+ * (sign, 4 exponent bits of bias 7, 3 mantissa bits, subnormals, no
+ * infinities, S.1111.111 NaN, largest finite 448), and the cached key (value)
+ * it stands for is k_scale (v_scale) times its E4M3 value.
+ *   k_cache, v_cache : [B][H_kv][T_max][d] bytes, 16-byte aligned
+ *   k_scale, v_scale : finite; one scale per array (GQA_ERR_INVALID_ARG
+ *                      otherwise)
+ *   q, out           : bf16 queries [B][H_q][d], out as for gqa_decode
+ *                      (dims->dtype must be GQA_DTYPE_BF16)
+ * The attention is the one above on those values, accumulated in fp32; the
+ * E4M3 values are widened to bf16, which is exact.  Matrix-core path only
+ * (otherwise GQA_ERR_UNSUPPORTED); seq_lens, scale, workspace
+ * (gqa_decode_workspace_bytes(dims, 1)), stream and the errors as for
+ * gqa_decode.
+ */
+gqa_status gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, float scale,
+                          float k_scale, float v_scale, void* out, const gqa_dims* dims, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * One decode step of one layer whose cache is held in pages of a pool.

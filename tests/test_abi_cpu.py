@@ -88,7 +88,8 @@ def test_status_strings():
     (dict(seq_len_hint=2048), INVALID),        # hint above T_max
     (dict(waves=2), INVALID),                  # workgroup size not 4, 8 or 16 wavefronts
     (dict(waves=32), INVALID),
-    (dict(tiles=3), INVALID),                  # tiles in flight not 1 or 2
+    (dict(tiles=3), INVALID),                  # tiles in flight not 1, 2 or 4
+    (dict(tiles=5), INVALID),
     (dict(tiles=-1), INVALID),
     (dict(per_cu=5), INVALID),                 # workgroups per CU: 0 (default) or 1 to 4
     (dict(per_cu=-1), INVALID),
@@ -232,6 +233,36 @@ def test_decode_paged_validation():
     assert gqa.lib().gqa_decode_paged(FAKE, FAKE, FAKE, FAKE, 64, 16, FAKE, 0.125, FAKE, None, None, 0,
                                       None) == INVALID
     assert call_paged(dims(B=0), [None] * 5, bt=None) == OK
+
+
+def call_fp8(d, ptrs=None, scale=0.125, ks=0.01, vs=0.02):
+    q, k, v, sl, out = ptrs or [FAKE] * 5
+    return gqa.lib().gqa_decode_fp8(q, k, v, sl, scale, ks, vs, out, ctypes.byref(d), None, 0, None)
+
+
+def test_decode_fp8_validation():
+    """The E4M3-cache entry point checks its arguments before touching the
+    device: bf16 queries on the matrix-core path only, finite scales,
+    16-byte aligned caches."""
+    d = dims()
+    assert call_fp8(d) == WORKSPACE                                    # valid: only the workspace is missing
+    assert call_fp8(dims(dtype=torch.float32)) == UNSUPPORTED
+    assert call_fp8(dims(path="valu")) == UNSUPPORTED
+    assert call_fp8(dims(d=96)) == UNSUPPORTED
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert call_fp8(d, ks=bad) == INVALID
+        assert call_fp8(d, vs=bad) == INVALID
+        assert call_fp8(d, scale=bad) == INVALID
+    for pos in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[pos] = None
+        assert call_fp8(d, ptrs) == INVALID, pos
+    for pos in (1, 2):                                                 # caches must be 16-byte aligned
+        ptrs = [FAKE] * 5
+        ptrs[pos] = FAKE + 8
+        assert call_fp8(d, ptrs) == INVALID, pos
+    assert gqa.lib().gqa_decode_fp8(FAKE, FAKE, FAKE, FAKE, 0.1, 1.0, 1.0, FAKE, None, None, 0, None) == INVALID
+    assert call_fp8(dims(B=0), [None] * 5) == OK
 
 
 def test_library_missing_fails_loudly(monkeypatch, tmp_path):

@@ -1,0 +1,178 @@
+"""The decode step over a cache of one-byte OCP E4M3 elements, on the GPU
+against the fp64 oracle (oracle_gqa_decode_fp8), through the C ABI.
+
+Both sides read the same bytes and scales, so the bar is the bf16-input bar:
+max |gpu - oracle| <= 2e-3 with an fp32 output (the E4M3 values are widened
+to bf16 exactly; the remaining error is that of the fp32 accumulation and of
+the softmax weights' bf16 split).  A bf16 output is bitwise the
+round-to-nearest-even of the fp32 output of the same call.  The hardware's
+decoding of every one of the 256 codes is checked exactly (a one-token
+attention returns v_scale times the value row).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_mqa_kv_amd as gqa
+import oracle
+from gqa_mqa_kv_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOL = 2e-3
+
+
+def note(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def small(B, H_q, H_kv, d, T, seed, lo=None, lens=None):
+    """Seeded bf16 inputs, NaN past each length, as E4M3 codes with scales."""
+    w = workloads.Workload("fp8", B, H_q, H_kv, d, lo if lo is not None else T, T, torch.bfloat16, seed)
+    x = workloads.generate(w, "cpu", poison_padding=lens is None)
+    if lens is not None:
+        x["seq_lens"] = torch.tensor(lens, dtype=torch.int32)
+        for b, n in enumerate(lens):
+            x["k"][b, :, n:] = float("nan")
+            x["v"][b, :, n:] = float("nan")
+    return workloads.to_e4m3(x)
+
+
+def check(x, label="", **kw):
+    T = x["k"].shape[2]
+    clamped = x["seq_lens"].clamp(0, T)
+    ref = oracle.default().decode_fp8(x["q"], x["k"], x["v"], clamped, x["scale"], x["k_scale"], x["v_scale"])
+    note(label, tuple(x["q"].shape), tuple(x["k"].shape), kw)
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    args = (xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], x["k_scale"], x["v_scale"])
+    o32 = gqa.decode_fp8(*args, out_dtype=torch.float32, **kw)
+    o16 = gqa.decode_fp8(*args, out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    o = o32.double().cpu().numpy()
+    assert np.isfinite(o).all(), "non-finite output"
+    e = float(np.abs(o - ref).max())
+    assert e <= TOL, "%s: max err %.3e" % (label, e)
+    assert torch.equal(o16.cpu(), o32.cpu().to(torch.bfloat16)), "bf16 out is not RNE(fp32 out)"
+    return o32
+
+
+def test_every_code_decodes_exactly():
+    """One cached token: every output column is v_scale times the value
+    element (weights are exactly 1).  The value rows hold all 256 codes; the
+    two NaN codes give NaN in their own column only."""
+    B, H_q, H_kv, d = 1, 8, 2, 128
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn(B, H_q, d, generator=g).to(torch.bfloat16)
+    k8 = torch.randint(0, 0x7E, (B, H_kv, 16, d), generator=g, dtype=torch.uint8)   # finite keys
+    v8 = torch.zeros(B, H_kv, 16, d, dtype=torch.uint8)
+    v8[0, :, 0, :] = torch.arange(256, dtype=torch.uint8).view(H_kv, d)
+    sl = torch.tensor([1], dtype=torch.int32)
+    note("every E4M3 code")
+    out = gqa.decode_fp8(q.to(DEV), k8.to(DEV), v8.to(DEV), sl.to(DEV), d ** -0.5, 0.5, 0.25,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = 0.25 * oracle.default().e4m3(torch.arange(256, dtype=torch.uint8)).reshape(H_kv, d)
+    got = out[0].double().cpu().numpy().reshape(H_kv, H_q // H_kv, d)
+    for j in range(H_q // H_kv):
+        assert np.array_equal(got[:, j], want, equal_nan=True)
+
+
+SHAPES = [
+    # B, H_q, H_kv, d, T_max, lo   (ragged lengths U[lo, T_max])
+    (1, 8, 2, 64, 128, None),
+    (3, 8, 8, 64, 300, 1),           # MHA, d = 64
+    (2, 32, 8, 128, 1000, 200),      # Llama-3-8B grouping
+    (2, 64, 8, 128, 777, 1),         # G = 8
+    (2, 16, 1, 128, 520, 33),        # MQA, G = 16
+    (2, 32, 1, 128, 600, 100),       # MQA, G = 32
+    (1, 64, 1, 128, 450, None),      # G = 64
+    (2, 12, 4, 128, 333, 10),        # G = 3
+    (2, 48, 1, 64, 300, 7),          # G = 48, d = 64
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_Hq%d_Hkv%d_d%d_T%d" % s[:5])
+@pytest.mark.parametrize("chunk", [0, 256])
+def test_fp8_small(shape, chunk):
+    B, hq, hkv, d, T, lo = shape
+    x = small(B, hq, hkv, d, T, seed=sum(shape[:5]) * 13 + chunk, lo=lo)
+    check(x, chunk_tokens=chunk, label="fp8")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 192])
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+@pytest.mark.parametrize("tiles", [1, 2, 4])
+def test_fp8_forced_spans_merges_tiles(chunk, merge, tiles):
+    x = small(4, 32, 8, 128, 500, seed=chunk + tiles, lens=[1, 17, 255, 500])
+    check(x, chunk_tokens=chunk, merge=merge, tiles=tiles, label="fp8-span")
+
+
+def test_fp8_edges():
+    """Empty sequences, one token, lengths around multiples of 16, and lengths
+    beyond the capacity (clamped)."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 0, 319, 320, 1000]
+    x = small(len(lens), 16, 4, 128, 320, seed=11, lens=lens)
+    out = check(x, label="fp8-edges")
+    assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[8]) == 0
+    check(x, chunk_tokens=64, merge="kernel", label="fp8-edges-span")
+
+
+def test_fp8_uniform_codes_and_scales():
+    """Caches of uniformly drawn finite codes (every magnitude from the
+    subnormals to 448), with scales far from 1."""
+    B, H_q, H_kv, d, T = 3, 32, 8, 128, 257
+    g = torch.Generator().manual_seed(19)
+    codes = torch.randint(0, 254, (2, B, H_kv, T, d), generator=g)
+    codes = codes + (codes >= 0x7F).long()                      # skip the NaN code 0x7F (0xFF is out of range)
+    x = {"q": torch.randn(B, H_q, d, generator=g).to(torch.bfloat16), "k": codes[0].to(torch.uint8),
+         "v": codes[1].to(torch.uint8), "seq_lens": torch.tensor([257, 100, 33], dtype=torch.int32),
+         "scale": d ** -0.5, "k_scale": 1.0 / 448.0, "v_scale": 3.0e-3}
+    check(x, label="fp8-uniform-codes")
+
+
+def test_fp8_repeats_bitwise():
+    x = small(4, 32, 8, 128, 1000, seed=31, lo=100)
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    args = (xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], x["k_scale"], x["v_scale"])
+    a = gqa.decode_fp8(*args, out_dtype=torch.float32)
+    b = gqa.decode_fp8(*args, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def full_fp8(name, sample):
+    w = workloads.WORKLOADS[name]
+    note("full-fp8", w.name, "generate")
+    x = workloads.to_e4m3(workloads.generate(w, DEV, poison_padding=True))
+    note("full-fp8", w.name, "decode")
+    args = (x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], x["k_scale"], x["v_scale"])
+    o32 = gqa.decode_fp8(*args, out_dtype=torch.float32)
+    o16 = gqa.decode_fp8(*args, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert bool(torch.isfinite(o32).all())
+    g = torch.Generator().manual_seed(78)
+    heads = sorted(set(torch.randperm(w.B * w.H_q, generator=g)[:sample].tolist()) | {0, w.B * w.H_q - 1})
+    note("full-fp8", w.name, "oracle on %d sampled heads" % len(heads))
+    e = 0.0
+    for hid in heads:
+        b, i = divmod(hid, w.H_q)
+        gi = i // w.G
+        n = int(x["seq_lens"][b])
+        ref = oracle.default().decode_fp8(x["q"][b:b + 1, i:i + 1].cpu(), x["k"][b:b + 1, gi:gi + 1, :n].cpu(),
+                                          x["v"][b:b + 1, gi:gi + 1, :n].cpu(), torch.tensor([n], dtype=torch.int32),
+                                          w.scale, x["k_scale"], x["v_scale"])[0, 0]
+        e = max(e, float(np.abs(o32[b, i].double().cpu().numpy() - ref).max()))
+    note("full-fp8", w.name, "max err %.3e" % e)
+    assert e <= TOL
+
+
+@pytest.mark.timeout(600)
+def test_full_llama3_8b_layer_fp8():
+    full_fp8("llama3-8b-layer", 64)
+
+
+@pytest.mark.timeout(600)
+def test_full_70b_ragged_layer_fp8():
+    full_fp8("llama-70b-ragged-layer", 64)
