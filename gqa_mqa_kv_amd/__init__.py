@@ -12,14 +12,15 @@ arguments.  See include/gqa_decode.h for the ABI.
 append_rope is the step before a decode step: it turns the new token's
 queries and keys by the rotary position embedding of section 4 of the same
 page and appends its key and value to the cache.  decode_paged reads a cache
-held in fixed-size pages of a pool through a per-sequence table of page ids.
+held in fixed-size pages of a pool through a per-sequence table of page ids
+(append_rope_paged appends to such a cache).
 decode_fp8 reads a cache of one-byte E4M3 elements with one scale for the
 keys and one for the values (the bytes-per-element term of section 1 of the
 same page, halved).
 """
-from ._binding import (GqaDims, GqaError, Prepared, append_rope, decode, decode_fp8, decode_layers, decode_paged,
-                       default_workspace, lib, make_dims, plan, prepare, prepare_append, prepare_fp8, prepare_paged,
-                       status_string, workspace_bytes)
+from ._binding import (GqaDims, GqaError, Prepared, append_rope, append_rope_paged, decode, decode_fp8,
+                       decode_layers, decode_paged, default_workspace, lib, make_dims, plan, prepare, prepare_append,
+                       prepare_fp8, prepare_paged, status_string, workspace_bytes)
 
-__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "decode_paged", "decode_fp8", "append_rope", "default_workspace",
+__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "decode_paged", "decode_fp8", "append_rope", "append_rope_paged", "default_workspace",
            "lib", "make_dims", "plan", "prepare_append", "prepare_fp8", "prepare_paged", "status_string", "workspace_bytes"]

@@ -20,7 +20,7 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
-SYMBOLS = ("gqa_append_rope", "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_paged",
+SYMBOLS = ("gqa_append_rope", "gqa_append_rope_paged", "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_paged",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
 
 
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode_plan.argtypes = [dims_p, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.gqa_append_rope.restype = ctypes.c_int
         L.gqa_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp]
+        L.gqa_append_rope_paged.restype = ctypes.c_int
+        L.gqa_append_rope_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, ctypes.c_float, vp, dims_p, vp]
         L.gqa_status_string.restype = ctypes.c_char_p
         L.gqa_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -353,6 +355,46 @@ def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k
     _check(lib().gqa_append_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets),
                                  _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), _ptr(q_out),
                                  ctypes.byref(dims), s))
+    return q_out, new_seq_lens
+
+
+def append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
+                      max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None):
+    """append_rope for a cache held in pages of a pool (the layout of
+    decode_paged): k_pool/v_pool [num_pages,H_kv,page,d], block_table int32
+    [B,max_pages]; the new token of sequence b goes to row seq_lens[b] % page
+    of page block_table[b, seq_lens[b] // page].  max_seq_len (the capacity)
+    defaults to max_pages * page.  Returns (q_out, new_seq_lens)."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool"),
+                 (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k_new.dim() != 3 or v_new.shape != k_new.shape:
+        raise ValueError("expected q [B,H_q,d] and k_new/v_new [B,H_kv,d]")
+    B, H_q, d = q.shape
+    H_kv = k_new.shape[1]
+    if k_new.shape[0] != B or k_new.shape[2] != d or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("shape mismatch between q, k_new/v_new and seq_lens")
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or k_pool.shape[1] != H_kv or k_pool.shape[3] != d:
+        raise ValueError("pools must be [num_pages,H_kv,page,d]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32 [B,max_pages]")
+    for t in (k_new, v_new, k_pool, v_pool):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k_new, v_new and the pools must share one dtype")
+    page, max_pages = k_pool.shape[2], block_table.shape[1]
+    dims = make_dims(B, H_q, H_kv, d, max_pages * page if max_seq_len is None else int(max_seq_len), q.dtype)
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    new_seq_lens = torch.empty_like(seq_lens) if new_seq_lens is None else new_seq_lens
+    _require(q_out, "q_out", dev)
+    _require(new_seq_lens, "new_seq_lens", dev)
+    if q_out.shape != q.shape or q_out.dtype != q.dtype or new_seq_lens.shape != (B,) or \
+            new_seq_lens.dtype != torch.int32:
+        raise ValueError("q_out must match q and new_seq_lens be int32 [B]")
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _check(lib().gqa_append_rope_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(block_table), int(max_pages), int(page), _ptr(seq_lens),
+                                       _ptr(new_seq_lens), float(rope_base), _ptr(q_out), ctypes.byref(dims), s))
     return q_out, new_seq_lens
 
 

@@ -374,9 +374,11 @@ gqa_status gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cach
   return launch(1, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
 }
 
-gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                           const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
-                           float rope_base, void* q_out, const gqa_dims* dims, void* stream) {
+namespace {
+gqa_status append_launch(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         const int64_t* kv_offsets, const int32_t* block_table, int32_t max_pages, int32_t page,
+                         const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, void* q_out,
+                         const gqa_dims* dims, void* stream) {
   gqa_status st = check_dims(dims, 1);
   if (st != GQA_OK) return st;
   if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return GQA_ERR_INVALID_ARG;
@@ -385,7 +387,7 @@ gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, 
   const uintptr_t e = dims->dtype == GQA_DTYPE_F32 ? 4 : 2;
   if (!aligned(q, e) || !aligned(k_new, e) || !aligned(v_new, e) || !aligned(k_cache, e) || !aligned(v_cache, e) ||
       !aligned(q_out, e) || !aligned(seq_lens, 4) || (new_seq_lens && !aligned(new_seq_lens, 4)) ||
-      (kv_offsets && !aligned(kv_offsets, 8)))
+      (kv_offsets && !aligned(kv_offsets, 8)) || (block_table && !aligned(block_table, 4)))
     return GQA_ERR_INVALID_ARG;
   gqa::RopeProblem p;
   p.q = q;
@@ -395,6 +397,9 @@ gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, 
   p.v_cache = v_cache;
   p.q_out = q_out;
   p.kv_offsets = kv_offsets;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.page = page;
   p.seq_lens = seq_lens;
   p.new_seq_lens = new_seq_lens;
   p.B = dims->batch;
@@ -413,6 +418,25 @@ gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, 
                       static_cast<hipStream_t>(stream)) != hipSuccess)
     return GQA_ERR_LAUNCH;
   return GQA_OK;
+}
+}  // namespace
+
+gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                           float rope_base, void* q_out, const gqa_dims* dims, void* stream) {
+  return append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, nullptr, 0, 0, seq_lens, new_seq_lens, rope_base,
+                       q_out, dims, stream);
+}
+
+gqa_status gqa_append_rope_paged(const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                 const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                                 const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, void* q_out,
+                                 const gqa_dims* dims, void* stream) {
+  if (page_size <= 0 || page_size % 16 != 0 || max_pages <= 0) return GQA_ERR_INVALID_ARG;
+  if (dims && (int64_t)max_pages * page_size < dims->max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (dims && dims->batch > 0 && !block_table) return GQA_ERR_INVALID_ARG;
+  return append_launch(q, k_new, v_new, k_pool, v_pool, nullptr, block_table, max_pages, page_size, seq_lens,
+                       new_seq_lens, rope_base, q_out, dims, stream);
 }
 
 const char* gqa_status_string(gqa_status s) {

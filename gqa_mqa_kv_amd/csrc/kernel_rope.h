@@ -24,6 +24,8 @@ struct RopeProblem {
   void* v_cache;
   void* q_out;
   const int64_t* kv_offsets;   // [B+1] or nullptr (dense [B][H_kv][T_max][D])
+  const int32_t* block_table;  // paged pool [num_pages][H_kv][page][D]: [B][max_pages] page ids, or nullptr
+  int32_t max_pages, page;
   const int32_t* seq_lens;     // [B]
   int32_t* new_seq_lens;       // [B] or nullptr (may equal seq_lens)
   int32_t B, H_q, H_kv, T_max;
@@ -67,8 +69,14 @@ __global__ __launch_bounds__(256) void gqa_append_rope(RopeProblem p) {
 
   // rows of this token: q and out [B][H_q][D], k_new/v_new [B][H_kv][D]
   const int64_t qrow = (int64_t)b * p.H_q, krow = (int64_t)b * p.H_kv;
-  int64_t crow0, cstride;   // cache row of KV head g: crow0 + g * cstride
-  if (p.kv_offsets) {
+  int64_t crow0 = 0, cstride = 0;   // cache row of KV head g: crow0 + g * cstride
+  if (p.block_table) {
+    if (append) {   // the page holding position m (read only when m < capacity <= max_pages * page)
+      const int64_t pid = p.block_table[(int64_t)b * p.max_pages + m / p.page];
+      crow0 = pid * p.H_kv * p.page + m % p.page;
+      cstride = p.page;
+    }
+  } else if (p.kv_offsets) {
     crow0 = p.kv_offsets[b] * p.H_kv + m;
     cstride = cap;
   } else {

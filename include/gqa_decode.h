@@ -272,6 +272,22 @@ gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, 
                            const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
                            float rope_base, void* q_out, const gqa_dims* dims, void* stream);
 
+/*
+ * The same step for a cache held in pages of a pool (the layout of
+ * gqa_decode_paged): the rotated key and the value of sequence b's new token
+ * go to row m % page_size of page block_table[b][m / page_size] of each KV
+ * head, m = max(seq_lens[b], 0).  The capacity of a sequence is
+ * dims->max_seq_len (<= max_pages * page_size); a full sequence is not
+ * appended.  The table entry of position m must name a page of the pool when
+ * m < dims->max_seq_len (the caller allocates the page first); it is the only
+ * entry read.  page_size: a positive multiple of 16; block_table 4-byte
+ * aligned.  Everything else, and the errors, as for gqa_append_rope.
+ */
+gqa_status gqa_append_rope_paged(const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                 const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                                 const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, void* q_out,
+                                 const gqa_dims* dims, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* gqa_status_string(gqa_status status);
 

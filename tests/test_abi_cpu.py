@@ -265,6 +265,24 @@ def test_decode_fp8_validation():
     assert call_fp8(dims(B=0), [None] * 5) == OK
 
 
+def test_append_rope_paged_validation():
+    """The paged append checks the page size, the capacity and the table
+    before touching the device."""
+    d = dims(T_max=1024)
+    call = lambda dd=d, bt=FAKE, mp=64, pg=16, base=10000.0: gqa.lib().gqa_append_rope_paged(
+        FAKE, FAKE, FAKE, FAKE, FAKE, bt, mp, pg, FAKE, None, base, FAKE, ctypes.byref(dd) if dd else None, None)
+    for pg in (0, -16, 8, 24):
+        assert call(pg=pg) == INVALID, pg
+    assert call(mp=0) == INVALID
+    assert call(mp=63) == INVALID                    # 63 * 16 < max_seq_len
+    assert call(bt=None) == INVALID
+    assert call(bt=FAKE + 2) == INVALID              # table not 4-byte aligned
+    assert call(base=0.0) == INVALID
+    assert call(dd=dims(d=96)) == UNSUPPORTED
+    assert call(dd=None) == INVALID
+    assert call(dd=dims(B=0), bt=None) == OK
+
+
 def test_library_missing_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding._build, "LIB_PATH", str(tmp_path / "absent.so"))

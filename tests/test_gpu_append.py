@@ -173,3 +173,75 @@ def test_append_then_decode(dtype):
     tol = 1e-5 if dtype == torch.float32 else 2e-3
     err = float(np.abs(out.double().cpu().numpy() - ref).max())
     assert err <= tol, err
+
+
+def paged_for_append(x, page, seed):
+    """Pool and table for the dense cache of ``x`` with a page allocated for
+    position seq_lens[b] too (where the append writes), when it is inside T."""
+    T = x["k"].shape[2]
+    alloc = dict(x, seq_lens=(x["seq_lens"] + 1).clamp(max=T))
+    return workloads.to_pages(alloc, page, seed=seed)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("page", [16, 48])
+def test_append_paged_matches_oracle(dtype, page):
+    """The paged append writes the rotated key and the value at row m % page
+    of page table[b][m // page] of every KV head, and nothing else."""
+    B, H_q, H_kv, d, T = 6, 32, 8, 128, 192
+    lens = [0, 15, 16, 47, 191, 192]                       # page boundaries, last row, full
+    x = make(B, H_q, H_kv, d, T, dtype, seed=40 + page, lens=lens)
+    kp, vp, table = paged_for_append({k: x[k] for k in ("k", "v", "seq_lens")}, page, seed=page)
+    kd, vd, td = kp.to(DEV), vp.to(DEV), table.to(DEV)
+    note("append paged", dtype, page)
+    q_out, nl = gqa.append_rope_paged(x["q"].to(DEV), x["k_new"].to(DEV), x["v_new"].to(DEV), kd, vd, td,
+                                      x["seq_lens"].to(DEV), 10000.0, max_seq_len=T)
+    torch.cuda.synchronize()
+    orc = oracle.default()
+    pos = torch.tensor(lens)
+    assert rot_err_ok(q_out, orc.rope(x["q"], pos.view(B, 1), 10000.0), dtype)
+    k_rot = orc.rope(x["k_new"], pos.view(B, 1), 10000.0)
+    k_after, v_after = kd.cpu(), vd.cpu()
+    written = torch.zeros(kp.shape[:3], dtype=torch.bool)
+    for b in range(B):
+        m = lens[b]
+        if m < T:
+            pid = int(table[b, m // page])
+            written[pid, :, m % page] = True
+            assert rot_err_ok(k_after[pid, :, m % page], k_rot[b], dtype)
+            assert torch.equal(v_after[pid, :, m % page], x["v_new"][b])
+            assert int(nl[b]) == m + 1
+        else:
+            assert int(nl[b]) == m
+    keep = ~written
+    assert torch.equal(k_after[keep].view(-1).view(torch.int8), kp[keep].view(-1).view(torch.int8))
+    assert torch.equal(v_after[keep].view(-1).view(torch.int8), vp[keep].view(-1).view(torch.int8))
+
+
+def test_append_then_decode_paged():
+    """A whole decode step on a paged cache: append with rotation, then
+    attend, against the oracle's rotation of every position and its
+    attention."""
+    B, H_q, H_kv, d, T, page = 3, 32, 8, 128, 700, 32
+    g = torch.Generator().manual_seed(78)
+    lens = torch.tensor([0, 350, 699], dtype=torch.int32)
+    raw_k = torch.randn(B, H_kv, T, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H_kv, T, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, H_q, d, generator=g).to(torch.bfloat16)
+    base = 10000.0
+    orc = oracle.default()
+    rot_k = torch.from_numpy(orc.rope(raw_k, torch.arange(T).view(1, 1, T), base)).to(torch.bfloat16)
+    kp, vp, table = paged_for_append({"k": rot_k, "v": v, "seq_lens": lens}, page, seed=5)
+    m = lens.long()
+    kn, vn = raw_k[torch.arange(B), :, m], v[torch.arange(B), :, m]
+    note("append then decode, paged")
+    kd, vd, td = kp.to(DEV), vp.to(DEV), table.to(DEV)
+    q_rot, nl = gqa.append_rope_paged(q.to(DEV), kn.contiguous().to(DEV), vn.contiguous().to(DEV), kd, vd, td,
+                                      lens.to(DEV), base, max_seq_len=T)
+    out = gqa.decode_paged(q_rot, kd, vd, td, nl, d ** -0.5, out_dtype=torch.float32, max_seq_len=T)
+    torch.cuda.synchronize()
+    ref_q = torch.from_numpy(orc.rope(q.double(), m.view(B, 1), base))
+    ref_k = torch.from_numpy(orc.rope(raw_k.double(), torch.arange(T).view(1, 1, T), base))
+    ref = orc.decode(ref_q, ref_k, v.double(), (lens + 1).tolist(), d ** -0.5)
+    err = float(np.abs(out.double().cpu().numpy() - ref).max())
+    assert err <= 2e-3, err
