@@ -194,10 +194,10 @@ def to_pages(inputs: dict, page: int, seed: int, spare: int = 3, share_first_pag
     Sequence b (its length clamped to [0, T]) gets ceil(len / page) pages,
     taken in the order of a seeded permutation of the pool (in pool order
     when ``shuffle`` is false), which has ``spare`` pages more than the
-    sequences use.  Spare pages and the rows of
-    a last page past the sequence's length are NaN; table entries past a
-    sequence's last page name the last page of the permutation, which is spare
-    (spare >= 1).  ``share_first_page`` points sequence 1's first entry at
+    sequences use.  Spare pages and the rows of a last page past the
+    sequence's length are NaN (the E4M3 NaN code 0x7F for uint8 caches);
+    table entries past a sequence's last page name the last page of the
+    permutation, which is spare (spare >= 1).  ``share_first_page`` points sequence 1's first entry at
     sequence 0's first page (a shared prefix), when sequence 0 fills that page
     and sequence 1 uses a page.
     """
@@ -211,8 +211,9 @@ def to_pages(inputs: dict, page: int, seed: int, spare: int = 3, share_first_pag
     total = sum(used) + spare
     perm = (torch.randperm(total, generator=torch.Generator().manual_seed(seed)) if shuffle
             else torch.arange(total)).tolist()
-    k_pool = torch.full((total, H_kv, page, d), float("nan"), dtype=k.dtype, device=dev)
-    v_pool = torch.full_like(k_pool, float("nan"))
+    pad = float("nan") if k.dtype.is_floating_point else 0x7F   # NaN, or the E4M3 NaN code for byte caches
+    k_pool = torch.full((total, H_kv, page, d), pad, dtype=k.dtype, device=dev)
+    v_pool = torch.full_like(k_pool, pad)
     table = torch.full((B, -(-T // page)), perm[-1], dtype=torch.int32)
     o = 0
     for b in range(B):
@@ -222,7 +223,7 @@ def to_pages(inputs: dict, page: int, seed: int, spare: int = 3, share_first_pag
         ids = perm[o:o + u]
         o += u
         for src, pool in ((k, k_pool), (v, v_pool)):
-            rows = torch.full((H_kv, u * page, d), float("nan"), dtype=k.dtype, device=dev)
+            rows = torch.full((H_kv, u * page, d), pad, dtype=k.dtype, device=dev)
             rows[:, :lens[b]] = src[b, :, :lens[b]]
             pool[torch.tensor(ids, device=dev)] = rows.view(H_kv, u, page, d).permute(1, 0, 2, 3)
         table[b, :u] = torch.tensor(ids, dtype=torch.int32)

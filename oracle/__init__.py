@@ -16,7 +16,8 @@ Contents
 * :meth:`Oracle.decode_fp8` -- the same attention over a cache of one-byte
   OCP E4M3 elements with one scale for the keys and one for the values (the
   bytes-per-element term of section 1, "KV Cache Memory Footprint", below
-  two); :meth:`Oracle.e4m3` decodes such bytes.
+  two); :meth:`Oracle.e4m3` decodes such bytes, and
+  :meth:`Oracle.decode_paged_fp8` reads such a cache from pages of a pool.
 * :meth:`Oracle.rope` -- fp64 rotary position embedding (section 4 of the
   same page, "Rotary Position Embeddings (RoPE) Interaction"), for the step
   that appends the new token's keys and values.
@@ -84,6 +85,9 @@ class Oracle:
         lib.oracle_gqa_decode_fp8.restype = ctypes.c_int
         lib.oracle_gqa_decode_fp8.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp, dbl, dbl, dbl,
                                               i64, vp, vp]
+        lib.oracle_gqa_decode_paged_fp8.restype = ctypes.c_int
+        lib.oracle_gqa_decode_paged_fp8.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, i64, i64, vp,
+                                                    dbl, dbl, dbl, i64, vp, vp]
         lib.oracle_e4m3_decode.restype = ctypes.c_int
         lib.oracle_e4m3_decode.argtypes = [i64, vp, vp]
         lib.oracle_rope.restype = ctypes.c_int
@@ -194,6 +198,37 @@ class Oracle:
                                                v_pool.data_ptr(), bt.ctypes.data, bt.shape[1], int(page),
                                                sl.ctypes.data, float(np.float32(scale)), B * H_q, None,
                                                out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return out
+
+    def decode_paged_fp8(self, q, k_pool, v_pool, block_table, page: int, seq_lens, scale: float, k_scale: float,
+                         v_scale: float) -> np.ndarray:
+        """decode_fp8 with the E4M3 cache held in pages of a pool (uint8 or
+        float8_e4m3fn pools [num_pages, H_kv, page, d] and a block table, as
+        in :meth:`decode_paged`)."""
+        if q.dtype not in _DTYPE_CODE:
+            raise TypeError("oracle takes float32, bfloat16 or float64 queries")
+        q = q.detach().to("cpu").contiguous()
+        k_pool = k_pool.detach().to("cpu").contiguous().view(torch.uint8)
+        v_pool = v_pool.detach().to("cpu").contiguous().view(torch.uint8)
+        B, H_q, d = q.shape
+        if k_pool.dim() != 4 or k_pool.shape[2] != page or k_pool.shape[3] != d or v_pool.shape != k_pool.shape:
+            raise ValueError("pools must be [num_pages, H_kv, page, d]")
+        bt = np.ascontiguousarray(np.asarray(
+            block_table.cpu() if isinstance(block_table, torch.Tensor) else block_table, dtype=np.int32))
+        if bt.ndim != 2 or bt.shape[0] != B:
+            raise ValueError("block_table must be [B, max_pages]")
+        if bt.size and (bt.min() < 0 or bt.max() >= k_pool.shape[0]):
+            raise ValueError("page id out of the pool")
+        sl = np.ascontiguousarray(np.asarray(
+            seq_lens.cpu() if isinstance(seq_lens, torch.Tensor) else seq_lens, dtype=np.int32))
+        out = np.zeros((B, H_q, d), dtype=np.float64)
+        f32 = lambda x: float(np.float32(x))
+        rc = self._lib.oracle_gqa_decode_paged_fp8(B, H_q, k_pool.shape[1], d, _DTYPE_CODE[q.dtype], q.data_ptr(),
+                                                   k_pool.data_ptr(), v_pool.data_ptr(), bt.ctypes.data, bt.shape[1],
+                                                   int(page), sl.ctypes.data, f32(scale), f32(k_scale), f32(v_scale),
+                                                   B * H_q, None, out.ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
         return out

@@ -256,6 +256,20 @@ int oracle_gqa_decode_fp8(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int d
   return decode_heads(B, H_q, H_kv, d, dtype, q, &K, &V, &L, seq_lens, scale, n_heads, head_ids, out);
 }
 
+/* The E4M3 cache of oracle_gqa_decode_fp8 held in pages of a pool, as in
+ * oracle_gqa_decode_paged. */
+int oracle_gqa_decode_paged_fp8(int64_t B, int64_t H_q, int64_t H_kv, int64_t d, int dtype,
+                                const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_table, int64_t max_pages, int64_t page,
+                                const int32_t* seq_lens, double scale, double k_scale, double v_scale,
+                                int64_t n_heads, const int64_t* head_ids, double* out) {
+  if (!block_table || max_pages < 0 || page <= 0) return -1;
+  if (!isfinite(k_scale) || !isfinite(v_scale)) return -1;
+  cache_layout L = {NULL, block_table, max_pages, page, H_kv};
+  const kv_array K = {k_pool, ORACLE_E4M3, k_scale}, V = {v_pool, ORACLE_E4M3, v_scale};
+  return decode_heads(B, H_q, H_kv, d, dtype, q, &K, &V, &L, seq_lens, scale, n_heads, head_ids, out);
+}
+
 /* The values of n OCP E4M3 bytes (the decoder the fp8 attention uses). */
 int oracle_e4m3_decode(int64_t n, const uint8_t* codes, double* out) {
   for (int64_t j = 0; j < n; ++j) out[j] = e4m3_value(codes[j]);

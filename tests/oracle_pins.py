@@ -332,6 +332,19 @@ def pin_fp8_attention_is_dequantised_attention(orc):
         assert np.isfinite(got).all() and np.abs(got - want).max() <= 1e-12, shape
 
 
+def pin_fp8_paged_layout(orc):
+    """An E4M3 cache held in shuffled pages (spare pages and page tails hold
+    the NaN code) gives bitwise the dense E4M3 cache's result."""
+    x = case(3, 8, 2, 64, 48, 161, dtype=torch.bfloat16, lo=1, poison=True)
+    x8 = workloads.to_e4m3(x)
+    dense = orc.decode_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], x8["k_scale"], x8["v_scale"])
+    for page in (16, 48):
+        kp, vp, table = workloads.to_pages(x8, page, seed=page)
+        got = orc.decode_paged_fp8(x["q"], kp, vp, table, page, x["seq_lens"], x["scale"], x8["k_scale"],
+                                   x8["v_scale"])
+        assert np.array_equal(got, dense), page
+
+
 def pin_fp8_scale_placement(orc):
     """k_scale multiplies the scores and v_scale the output: with powers of
     two every product stays exact, so trading k_scale against ``scale`` and
