@@ -193,8 +193,8 @@ def main():
         print("--paged takes a single-layer bf16 workload and a page that is a multiple of 16", file=sys.stderr)
         sys.exit(2)
     fp8 = args.kv == "fp8"
-    if fp8 and (w.layers != 1 or w.packed or w.dtype != torch.bfloat16 or args.paged):
-        print("--kv fp8 takes a single-layer bf16 workload in the dense layout", file=sys.stderr)
+    if fp8 and (w.layers != 1 or w.packed or w.dtype != torch.bfloat16):
+        print("--kv fp8 takes a single-layer bf16 workload (dense, or paged with --paged)", file=sys.stderr)
         sys.exit(2)
     out_dtype = {None: w.dtype, "bf16": torch.bfloat16, "fp32": torch.float32}[args.out_dtype]
     seq_lens = workloads.seq_lens_for(w)
@@ -216,8 +216,15 @@ def main():
         if fp8:
             x8 = workloads.to_e4m3(x)
             del x["k"], x["v"]   # the E4M3 copy holds the cache now
-            launchers.append(gqa.prepare_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], x8["k_scale"],
-                                             x8["v_scale"], out_dtype=out_dtype, chunk_tokens=args.chunk_tokens))
+            if args.paged:
+                kp, vp, table = workloads.to_pages(x8, args.paged, seed=1000 + r, spare=1)
+                del x8["k"], x8["v"]
+                launchers.append(gqa.prepare_paged_fp8(x["q"], kp, vp, table, x["seq_lens"], x["scale"],
+                                                       x8["k_scale"], x8["v_scale"], max_seq_len=w.T_max,
+                                                       out_dtype=out_dtype, chunk_tokens=args.chunk_tokens))
+            else:
+                launchers.append(gqa.prepare_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], x8["k_scale"],
+                                                 x8["v_scale"], out_dtype=out_dtype, chunk_tokens=args.chunk_tokens))
             continue
         if args.paged:
             kp, vp, table = workloads.to_pages(x, args.paged, seed=1000 + r, spare=1)

@@ -20,7 +20,8 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
-SYMBOLS = ("gqa_append_rope", "gqa_append_rope_paged", "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_paged",
+SYMBOLS = ("gqa_append_rope", "gqa_append_rope_paged", "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers",
+           "gqa_decode_paged", "gqa_decode_paged_fp8",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
 
 
@@ -59,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode_layers.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_paged.restype = ctypes.c_int
         L.gqa_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_paged_fp8.restype = ctypes.c_int
+        L.gqa_decode_paged_fp8.argtypes = [vp, vp, vp, vp, i32, i32, vp, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_fp8.restype = ctypes.c_int
         L.gqa_decode_fp8.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, dims_p, vp,
                                      sz, vp]
@@ -170,7 +174,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
 
 
 def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype, max_seq_len, chunk_tokens,
-                seq_len_hint, workspace, stream, tiles, merge, per_cu):
+                seq_len_hint, workspace, stream, tiles, merge, per_cu, scales=None):
     dev = q.device
     for t, n in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"), (block_table, "block_table"),
                  (seq_lens, "seq_lens")):
@@ -183,8 +187,11 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype,
     if (k_pool.shape[3] != d or block_table.shape[0] != B or block_table.dtype != torch.int32
             or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32):
         raise ValueError("shape mismatch between q, pools, block_table and seq_lens")
-    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+    if scales is None and (k_pool.dtype != q.dtype or v_pool.dtype != q.dtype):
         raise TypeError("q, k_pool and v_pool must share one dtype")
+    if scales is not None and (q.dtype != torch.bfloat16 or k_pool.dtype not in E4M3_DTYPES
+                               or v_pool.dtype not in E4M3_DTYPES):
+        raise TypeError("expected bf16 q and one-byte E4M3 pools (uint8 or float8_e4m3fn)")
     T = max_pages * page if max_seq_len is None else int(max_seq_len)
     dims = make_dims(B, H_q, H_kv, d, T, q.dtype, out_dtype, seq_len_hint, chunk_tokens, "mfma", 0, tiles, merge,
                      per_cu)
@@ -195,9 +202,9 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype,
         raise ValueError("out must be [B,H_q,d] of the output dtype")
     ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages), int(page), _ptr(seq_lens),
-            float(scale), _ptr(out), ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-            s)
+    sc = (float(scale),) if scales is None else (float(scale), float(scales[0]), float(scales[1]))
+    args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages), int(page), _ptr(seq_lens)) + \
+        sc + (_ptr(out), ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
     return args, (out, q, k_pool, v_pool, block_table, seq_lens, ws, dims)
 
 
@@ -255,6 +262,18 @@ def decode_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_sc
     args, keep = _fp8_args(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, out, out_dtype, chunk_tokens,
                            seq_len_hint, workspace, stream, tiles, merge, per_cu)
     _check(lib().gqa_decode_fp8(*args))
+    return keep[0]
+
+
+def decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, scale: float, k_scale: float, v_scale: float,
+                     out=None, out_dtype=None, max_seq_len: Optional[int] = None, chunk_tokens: int = 0,
+                     seq_len_hint: int = 0, workspace=None, stream=None, tiles: int = 0, merge: str = "auto",
+                     per_cu: int = 0):
+    """decode_paged over pools of one-byte OCP E4M3 elements (uint8 or
+    float8_e4m3fn [num_pages,H_kv,page,d]) with the scales of decode_fp8."""
+    args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype, max_seq_len,
+                             chunk_tokens, seq_len_hint, workspace, stream, tiles, merge, per_cu, (k_scale, v_scale))
+    _check(lib().gqa_decode_paged_fp8(*args))
     return keep[0]
 
 
@@ -492,5 +511,16 @@ def prepare_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_s
     args, keep = _fp8_args(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, None, out_dtype, chunk_tokens,
                            seq_len_hint, None, stream, tiles, merge, per_cu)
     pr = Prepared(lib().gqa_decode_fp8, args, keep)
+    pr()
+    return pr
+
+
+def prepare_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, scale: float, k_scale: float, v_scale: float,
+                      out_dtype=None, max_seq_len=None, chunk_tokens: int = 0, seq_len_hint: int = 0, stream=None,
+                      tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """As prepare, for gqa_decode_paged_fp8."""
+    args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, None, out_dtype, max_seq_len,
+                             chunk_tokens, seq_len_hint, None, stream, tiles, merge, per_cu, (k_scale, v_scale))
+    pr = Prepared(lib().gqa_decode_paged_fp8, args, keep)
     pr()
     return pr

@@ -199,7 +199,7 @@ struct CacheArgs {
   const int64_t* kv_offsets = nullptr;   // packed layout, else dense
   const int32_t* block_table = nullptr;  // paged layout (one layer; page a multiple of 16)
   int32_t max_pages = 0, page = 0;
-  bool e4m3 = false;                     // one-byte OCP E4M3 elements (dense layout)
+  bool e4m3 = false;                     // one-byte OCP E4M3 elements
   float k_scale = 1.f, v_scale = 1.f;    // E4M3: what each key / value element is multiplied by
 };
 
@@ -207,6 +207,9 @@ kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan, const CacheArgs& ca) 
   const int G = d->num_q_heads / d->num_kv_heads;
   if (plan.mfma) {
     const int hb = (G + 15) / 16;
+    if (ca.e4m3 && ca.block_table)
+      return d->head_dim == 128 ? mfma_kernel<128, true, true>(hb, plan.waves, plan.tiles)
+                                : mfma_kernel<64, true, true>(hb, plan.waves, plan.tiles);
     if (ca.e4m3)
       return d->head_dim == 128 ? mfma_kernel<128, false, true>(hb, plan.waves, plan.tiles)
                                 : mfma_kernel<64, false, true>(hb, plan.waves, plan.tiles);
@@ -357,6 +360,28 @@ gqa_status gqa_decode_paged(const void* q, const void* k_pool, const void* v_poo
   ca.block_table = block_table;
   ca.max_pages = max_pages;
   ca.page = page_size;
+  return launch(1, q, k_pool, v_pool, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                                int32_t max_pages, int32_t page_size, const int32_t* seq_lens, float scale,
+                                float k_scale, float v_scale, void* out, const gqa_dims* dims, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  gqa_status st = check_dims(dims, 1);
+  if (st != GQA_OK) return st;
+  if (page_size <= 0 || page_size % 16 != 0 || max_pages <= 0) return GQA_ERR_INVALID_ARG;
+  if ((int64_t)max_pages * page_size < dims->max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (dims->dtype != GQA_DTYPE_BF16 || !use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // matrix-core kernel only
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale)) return GQA_ERR_INVALID_ARG;
+  if (dims->batch == 0) return GQA_OK;
+  if (!block_table || !aligned(block_table, 4)) return GQA_ERR_INVALID_ARG;
+  CacheArgs ca;
+  ca.block_table = block_table;
+  ca.max_pages = max_pages;
+  ca.page = page_size;
+  ca.e4m3 = true;
+  ca.k_scale = k_scale;
+  ca.v_scale = v_scale;
   return launch(1, q, k_pool, v_pool, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
 }
 

@@ -1,4 +1,7 @@
-// Matrix-core GQA decode kernel for bf16 caches, D = 64 or 128, G <= 16*HB*HG.
+// Matrix-core GQA decode kernel for bf16 queries, D = 64 or 128,
+// G <= 16*HB*HG; caches of bf16 elements (dense, packed or paged) or of
+// one-byte E4M3 elements (dense or paged), which are widened to bf16 exactly
+// before the products.
 //
 // Work split ("token split", see common.h): the valid tokens of all units
 // form one stream cut into equal spans, one per workgroup (one per CU),
@@ -224,19 +227,29 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   auto load_tile = [&](tile_t& T, const Ctx& c, int t0, int64_t tr) __attribute__((always_inline)) {
     if constexpr (KV8) {
       typedef typename std::remove_reference<decltype(T.v[0])>::type vraw_t;
-      const int last = c.c1 - 1;
-      const bool full = t0 + TILE <= c.c1;
-      // full tile: rows tr .. tr+15; ragged tail: rows past the piece are
-      // clamped to its last valid row (in bounds), their weights forced to 0
-      const kv_t* kb = PAGED ? c.kg + (tr - t0) * D : c.kg;
-      const kv_t* vb = PAGED ? c.vg + (tr - t0) * D : c.vg;
-      const kv_t* kt = full ? c.kg + tr * D + koff : kb + (int64_t)min(t0 + m16, last) * D + q4 * (D / 4);
+      if (t0 + TILE <= c.c1) {
+        // full tile: one base address per lane, the rest are immediate offsets
+        const kv_t* kt = c.kg + tr * D + koff;
+        const kv_t* vt = c.vg + tr * D + voff;
 #pragma unroll
-      for (int s = 0; s < D / 64; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 16 * s));
+        for (int s = 0; s < D / 64; ++s)
+          T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 16 * s));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const kv_t* vr = full ? c.vg + tr * D + voff + i * D : vb + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16;
-        T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vraw_t*>(vr));
+        for (int i = 0; i < 4; ++i) T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vraw_t*>(vt + i * D));
+      } else {
+        // ragged tail: rows past the piece are clamped to its last valid row
+        // (in bounds), their weights forced to 0 below
+        const int last = c.c1 - 1;
+        const kv_t* kb = PAGED ? c.kg + (tr - t0) * D : c.kg;
+        const kv_t* vb = PAGED ? c.vg + (tr - t0) * D : c.vg;
+        const kv_t* kt = kb + (int64_t)min(t0 + m16, last) * D + q4 * (D / 4);
+#pragma unroll
+        for (int s = 0; s < D / 64; ++s)
+          T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 16 * s));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          T.v[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const vraw_t*>(vb + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
       }
     } else if (t0 + TILE <= c.c1) {
       // full tile: one base address per lane, the rest are immediate offsets

@@ -30,7 +30,8 @@
  *               seq_len_hint if set, max_seq_len)].
  *   q, k_cache, v_cache and out must be 16-byte aligned; out must not
  *   overlap any input.
- * Types.  q, k_cache and v_cache share dims->dtype (fp32 or bf16); out has
+ * Types.  q, k_cache and v_cache share dims->dtype (fp32 or bf16), except
+ *   in gqa_decode_fp8, whose caches hold one-byte E4M3 elements; out has
  *   dims->out_dtype.  Products, softmax and sums are accumulated in fp32; a
  *   bf16 output is rounded to nearest-even.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
@@ -212,6 +213,18 @@ gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_ca
 gqa_status gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, float scale,
                           float k_scale, float v_scale, void* out, const gqa_dims* dims, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_decode_fp8 with the cache held in pages of a pool: the pools are one
+ * byte per element, in the layout of gqa_decode_paged ([num_pages][H_kv]
+ * [page_size][d], 16-byte aligned), read through block_table as there, each
+ * element standing for k_scale or v_scale times its E4M3 value as in
+ * gqa_decode_fp8.  Every argument rule and error of those two calls applies.
+ */
+gqa_status gqa_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                                int32_t max_pages, int32_t page_size, const int32_t* seq_lens, float scale,
+                                float k_scale, float v_scale, void* out, const gqa_dims* dims, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * One decode step of one layer whose cache is held in pages of a pool.

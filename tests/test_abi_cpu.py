@@ -265,6 +265,23 @@ def test_decode_fp8_validation():
     assert call_fp8(dims(B=0), [None] * 5) == OK
 
 
+def test_decode_paged_fp8_validation():
+    """The paged E4M3 entry point applies the rules of both parents."""
+    d = dims(T_max=1024)
+    call = lambda dd=d, bt=FAKE, mp=64, pg=16, ks=0.01, ptrs=None: gqa.lib().gqa_decode_paged_fp8(
+        *(ptrs or [FAKE] * 3), bt, mp, pg, FAKE, 0.125, ks, 0.02, FAKE, ctypes.byref(dd), None, 0, None)
+    assert call() == WORKSPACE                                          # valid: only the workspace is missing
+    for pg in (0, 8, 24):
+        assert call(pg=pg) == INVALID, pg
+    assert call(mp=63) == INVALID
+    assert call(bt=None) == INVALID and call(bt=FAKE + 2) == INVALID
+    assert call(ks=float("nan")) == INVALID
+    assert call(dd=dims(dtype=torch.float32)) == UNSUPPORTED
+    assert call(dd=dims(path="valu")) == UNSUPPORTED
+    assert call(ptrs=[FAKE, FAKE + 8, FAKE]) == INVALID                # pools must be 16-byte aligned
+    assert call(dd=dims(B=0), bt=None) == OK
+
+
 def test_append_rope_paged_validation():
     """The paged append checks the page size, the capacity and the table
     before touching the device."""

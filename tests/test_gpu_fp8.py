@@ -176,3 +176,84 @@ def test_full_llama3_8b_layer_fp8():
 @pytest.mark.timeout(600)
 def test_full_70b_ragged_layer_fp8():
     full_fp8("llama-70b-ragged-layer", 64)
+
+
+# ------------------------------------------------ E4M3 caches in pages --
+def check_paged(x, page, seed=0, label="", **kw):
+    """gqa_decode_paged_fp8 on the E4M3 codes of ``x`` laid out in shuffled
+    pages (spare pages and page tails hold the NaN code), against the oracle
+    on the same pool."""
+    T = x["k"].shape[2]
+    clamped = x["seq_lens"].clamp(0, T)
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    kp, vp, table = workloads.to_pages(xd, page, seed=seed)
+    note(label, tuple(x["q"].shape), tuple(x["k"].shape), "page", page, kw)
+    ref = oracle.default().decode_paged_fp8(x["q"], kp.cpu(), vp.cpu(), table.cpu(), page, clamped, x["scale"],
+                                            x["k_scale"], x["v_scale"])
+    args = (xd["q"], kp, vp, table, xd["seq_lens"], x["scale"], x["k_scale"], x["v_scale"])
+    o32 = gqa.decode_paged_fp8(*args, out_dtype=torch.float32, max_seq_len=T, **kw)
+    o16 = gqa.decode_paged_fp8(*args, out_dtype=torch.bfloat16, max_seq_len=T, **kw)
+    torch.cuda.synchronize()
+    o = o32.double().cpu().numpy()
+    assert np.isfinite(o).all(), "non-finite output"
+    e = float(np.abs(o - ref).max())
+    assert e <= TOL, "%s: max err %.3e" % (label, e)
+    assert torch.equal(o16.cpu(), o32.cpu().to(torch.bfloat16)), "bf16 out is not RNE(fp32 out)"
+    return o32
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_Hq%d_Hkv%d_d%d_T%d" % s[:5])
+@pytest.mark.parametrize("page", [16, 64])
+def test_fp8_paged_small(shape, page):
+    B, hq, hkv, d, T, lo = shape
+    x = small(B, hq, hkv, d, T, seed=sum(shape[:5]) * 17 + page, lo=lo)
+    check_paged(x, page, seed=page, label="fp8-paged")
+
+
+@pytest.mark.parametrize("chunk", [64, 192])
+@pytest.mark.parametrize("merge", ["fused", "kernel"])
+@pytest.mark.parametrize("tiles", [1, 2, 4])
+def test_fp8_paged_spans_merges_tiles(chunk, merge, tiles):
+    x = small(4, 32, 8, 128, 500, seed=chunk + tiles + 7, lens=[1, 17, 255, 500])
+    check_paged(x, 48, seed=2, chunk_tokens=chunk, merge=merge, tiles=tiles, label="fp8-paged-span")
+
+
+def test_fp8_paged_edges():
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 0, 319, 320, 1000]
+    x = small(len(lens), 16, 4, 128, 320, seed=12, lens=lens)
+    out = check_paged(x, 32, seed=5, label="fp8-paged-edges")
+    assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[8]) == 0
+
+
+@pytest.mark.timeout(600)
+def test_full_llama3_8b_layer_paged_fp8():
+    """The full 8B layer as E4M3 codes in shuffled pages of 16 tokens, on
+    sampled heads (each against the dense E4M3 oracle on its sequence's
+    rows gathered from its own pages)."""
+    w = workloads.WORKLOADS["llama3-8b-layer"]
+    page = 16
+    note("full-fp8-paged", w.name, "generate")
+    x = workloads.to_e4m3(workloads.generate(w, DEV, poison_padding=True))
+    kp, vp, table = workloads.to_pages(x, page, seed=page)
+    note("full-fp8-paged", w.name, "decode")
+    args = (x["q"], kp, vp, table, x["seq_lens"], x["scale"], x["k_scale"], x["v_scale"])
+    o32 = gqa.decode_paged_fp8(*args, out_dtype=torch.float32, max_seq_len=w.T_max)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o32).all())
+    g = torch.Generator().manual_seed(79)
+    heads = sorted(set(torch.randperm(w.B * w.H_q, generator=g)[:48].tolist()) | {0, w.B * w.H_q - 1})
+    tab = table.cpu()
+    e = 0.0
+    for hid in heads:
+        b, i = divmod(hid, w.H_q)
+        gi = i // w.G
+        n = int(x["seq_lens"][b])
+        u = -(-n // page)
+        ids = tab[b, :u].long().to(DEV)
+        k1 = kp[ids, gi].reshape(1, 1, u * page, w.d)[:, :, :n].cpu()
+        v1 = vp[ids, gi].reshape(1, 1, u * page, w.d)[:, :, :n].cpu()
+        ref = oracle.default().decode_fp8(x["q"][b:b + 1, i:i + 1].cpu(), k1, v1, torch.tensor([n], dtype=torch.int32),
+                                          w.scale, x["k_scale"], x["v_scale"])[0, 0]
+        e = max(e, float(np.abs(o32[b, i].double().cpu().numpy() - ref).max()))
+    note("full-fp8-paged", w.name, "max err %.3e" % e)
+    assert e <= TOL
