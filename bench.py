@@ -109,8 +109,32 @@ def cpu_baseline(w, budget_s: float = 10.0):
     per_step = el / n
     nbytes = algorithmic_bytes(w, x["seq_lens"], 2 if str(w.dtype).endswith("bfloat16") else 4)
     return {"value": round(nbytes / per_step / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
-            "kind": "oracle", "us_per_step": round(per_step * 1e6, 1),
+            "kind": "oracle", "us_per_step": round(per_step * 1e6, 1), "cpu_model": cpu_model(),
             "sample": "%d whole steps of %s (fp64 C oracle, OpenMP), %.1f s" % (n, w.name, el)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def step_percentiles(torch, step, stream, n: int, start: int):
+    """Per-step times (µs) of n more steps, each bracketed by its own events
+    (a pass after the timed region, so the events do not touch it)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(start + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    pick = lambda f: round(t[min(len(t) - 1, int(f * len(t)))], 2)
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "steps": n}
 
 
 def copy_calibration(torch, dev, nbytes: int, launches: int) -> None:
@@ -123,6 +147,32 @@ def copy_calibration(torch, dev, nbytes: int, launches: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"copy_kernel": "elementwise neg, fp32", "bytes_read_per_launch": nbytes,
                       "bytes_written_per_launch": nbytes, "launches": launches}), flush=True)
+
+
+def time_layers_one_by_one(torch, gqa, workloads, w, x, stream, out_dtype, reps: int = 3):
+    """The same step as L launches of one layer each (gqa_decode_layers with
+    L = 1 on each layer's slice), as a model that computes layer l's queries
+    from layer l-1 would issue it."""
+    launchers = []
+    for l in range(w.layers):
+        xl = workloads.layer_view(x, l)
+        extra = dict(kv_offsets=x["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if w.packed else {}
+        launchers.append(gqa.prepare(xl["q"][None], xl["k"], xl["v"], x["seq_lens"], x["scale"], out_dtype=out_dtype,
+                                     **extra))
+    for f in launchers:
+        f()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for f in launchers:
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e3
+        best = t if best is None else min(best, t)
+    return {"us_per_step": round(best, 1), "launches": w.layers, "best_of": reps}
 
 
 def time_append(torch, gqa, w, x, stream, steps: int, warmup: int):
@@ -306,6 +356,10 @@ def main():
         "cpu_baseline": None,
         "context": {"h100_sxm5_hbm_TBps": 3.35, "h100_sxm5_dense_bf16_TFLOPs": 989, "h100_I_sat_FLOP_per_B": 295.2},
     }
+    result["per_step_us"] = step_percentiles(torch, step, stream, min(args.steps, 100), args.steps)
+    if w.layers > 1:
+        result["sequential_single_layer_launches"] = time_layers_one_by_one(torch, gqa, workloads, w, batches[0],
+                                                                            stream, out_dtype)
     if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged and not fp8:
         result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:
