@@ -88,6 +88,8 @@ class Oracle:
         lib.oracle_gqa_decode_paged_fp8.restype = ctypes.c_int
         lib.oracle_gqa_decode_paged_fp8.argtypes = [i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, i64, i64, vp,
                                                     dbl, dbl, dbl, i64, vp, vp]
+        lib.oracle_e4m3_encode.restype = ctypes.c_int
+        lib.oracle_e4m3_encode.argtypes = [i64, vp, vp]
         lib.oracle_e4m3_decode.restype = ctypes.c_int
         lib.oracle_e4m3_decode.argtypes = [i64, vp, vp]
         lib.oracle_rope.restype = ctypes.c_int
@@ -231,6 +233,15 @@ class Oracle:
                                                    B * H_q, None, out.ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
+        return out
+
+    def e4m3_encode(self, x) -> np.ndarray:
+        """OCP E4M3 bytes of ``x`` (any shape; widened to fp64): nearest value,
+        ties to even, saturating at +-448, NaN to 0x7F."""
+        v = np.ascontiguousarray(np.asarray(x.detach().cpu().double() if isinstance(x, torch.Tensor) else x,
+                                            dtype=np.float64))
+        out = np.zeros(v.shape, dtype=np.uint8)
+        self._lib.oracle_e4m3_encode(v.size, v.ctypes.data, out.ctypes.data)
         return out
 
     def e4m3(self, codes) -> np.ndarray:

@@ -270,6 +270,34 @@ int oracle_gqa_decode_paged_fp8(int64_t B, int64_t H_q, int64_t H_kv, int64_t d,
   return decode_heads(B, H_q, H_kv, d, dtype, q, &K, &V, &L, seq_lens, scale, n_heads, head_ids, out);
 }
 
+/* The OCP E4M3 byte of x: the nearest E4M3 value, ties to the even
+ * mantissa, saturating at +-448 (a cached element stays finite; infinities
+ * saturate too); NaN gives the NaN code 0x7F.  Written from the format's
+ * definition: below 2^-6 the grid is m * 2^-9 (m = 0 .. 8, where m = 8 is the
+ * smallest normal), above it (1 + m/8) * 2^e with e in [-6, 8]. */
+static uint8_t e4m3_code(double x) {
+  if (isnan(x)) return 0x7F;
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  const double a = fabs(x);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) return sign | (uint8_t)nearbyint(ldexp(a, 9));   /* m * 2^-9, m <= 8 */
+  int e = (int)floor(log2(a));
+  if (ldexp(1.0, e) > a) e -= 1;          /* guard the floor of log2 against rounding */
+  if (ldexp(1.0, e + 1) <= a) e += 1;
+  int m = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+  if (m == 8) {
+    m = 0;
+    e += 1;
+  }
+  return sign | (uint8_t)(((e + 7) << 3) | m);
+}
+
+/* The E4M3 bytes of n doubles (the encoder the quantising append follows). */
+int oracle_e4m3_encode(int64_t n, const double* x, uint8_t* out) {
+  for (int64_t j = 0; j < n; ++j) out[j] = e4m3_code(x[j]);
+  return 0;
+}
+
 /* The values of n OCP E4M3 bytes (the decoder the fp8 attention uses). */
 int oracle_e4m3_decode(int64_t n, const uint8_t* codes, double* out) {
   for (int64_t j = 0; j < n; ++j) out[j] = e4m3_value(codes[j]);

@@ -332,6 +332,34 @@ def pin_fp8_attention_is_dequantised_attention(orc):
         assert np.isfinite(got).all() and np.abs(got - want).max() <= 1e-12, shape
 
 
+def pin_e4m3_encode(orc):
+    """The encoder the quantising append follows: every finite code
+    re-encodes to itself; float32 values across the whole range, every
+    midpoint between neighbouring codes (ties go to the even mantissa) and
+    the float32 neighbours of those midpoints agree with torch's
+    float8_e4m3fn conversion (a library routine) below 448; beyond it the
+    encoder saturates (448, infinities), and NaN gives 0x7F."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    vals = orc.e4m3(codes)
+    fin = np.isfinite(vals)
+    assert np.array_equal(orc.e4m3_encode(vals[fin]), codes.numpy()[fin])
+    pos = np.sort(vals[(vals >= 0) & fin & ~np.signbit(vals)])
+    mids = (pos[:-1] + pos[1:]) / 2                       # exact in float32 (4 significant bits)
+    m32 = torch.tensor(mids, dtype=torch.float32)
+    around = torch.cat([m32, torch.nextafter(m32, torch.tensor(np.inf, dtype=torch.float32)),
+                        torch.nextafter(m32, torch.tensor(-np.inf, dtype=torch.float32))])
+    g = torch.Generator().manual_seed(31)
+    rnd = torch.randn(100000, generator=g) * torch.exp(torch.empty(100000).uniform_(-14, 6, generator=g))
+    x = torch.cat([around, -around, rnd])
+    x = x[x.abs() < 448]
+    lib = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.e4m3_encode(x.double()), lib)
+    # ties: 1 + 1/16 -> 1, 1 + 3/16 -> 1.25, 2^-10 -> 0, 3 * 2^-11 -> 2^-9
+    assert orc.e4m3_encode([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -11]).tolist() == [0x38, 0x3A, 0x00, 0x01]
+    sat = orc.e4m3_encode([448.0, 460.0, 1e9, np.inf, -1e9, -np.inf, np.nan, -0.0])
+    assert sat.tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x80]
+
+
 def pin_fp8_paged_layout(orc):
     """An E4M3 cache held in shuffled pages (spare pages and page tails hold
     the NaN code) gives bitwise the dense E4M3 cache's result."""

@@ -54,6 +54,13 @@ MUTANTS = {
     # E4M3 cache: the key and value scales swapped
     "fp8_scales_swapped": ("const kv_array K = {k8, ORACLE_E4M3, k_scale}, V = {v8, ORACLE_E4M3, v_scale};",
                            "const kv_array K = {k8, ORACLE_E4M3, v_scale}, V = {v8, ORACLE_E4M3, k_scale};"),
+    # E4M3 encoder: ties away from zero instead of to even
+    "e4m3_encode_ties_away": ("int m = (int)nearbyint((ldexp(a, -e) - 1.0) * 8.0);",
+                              "int m = (int)round((ldexp(a, -e) - 1.0) * 8.0);"),
+    # E4M3 encoder: overflow to NaN instead of saturating
+    "e4m3_encode_no_saturation": ("if (a >= 448.0) return sign | 0x7E;", "if (a > 464.0) return 0x7F;"),
+    # E4M3 encoder: subnormal grid of 2^-8 instead of 2^-9
+    "e4m3_encode_subnormal_grid": ("(uint8_t)nearbyint(ldexp(a, 9))", "(uint8_t)nearbyint(ldexp(a, 8))"),
     # rotary embedding: turning the other way
     "rope_orientation": ("out[v * d + 2 * j] = x0 * c - x1 * s;", "out[v * d + 2 * j] = x0 * c + x1 * s;"),
     # rotary embedding: pairs (j, j + d/2) instead of consecutive elements
