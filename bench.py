@@ -218,6 +218,9 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps: no per-step percentiles, single-layer launches or append timing "
+                         "(for kernel traces that should hold one kind of launch)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain N-MiB device copy (counter calibration kernel)")
@@ -356,11 +359,12 @@ def main():
         "cpu_baseline": None,
         "context": {"h100_sxm5_hbm_TBps": 3.35, "h100_sxm5_dense_bf16_TFLOPs": 989, "h100_I_sat_FLOP_per_B": 295.2},
     }
-    result["per_step_us"] = step_percentiles(torch, step, stream, min(args.steps, 100), args.steps)
-    if w.layers > 1:
+    if not args.no_extras:
+        result["per_step_us"] = step_percentiles(torch, step, stream, min(args.steps, 100), args.steps)
+    if w.layers > 1 and not args.no_extras:
         result["sequential_single_layer_launches"] = time_layers_one_by_one(torch, gqa, workloads, w, batches[0],
                                                                             stream, out_dtype)
-    if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged and not fp8:
+    if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged and not fp8 and not args.no_extras:
         result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

@@ -20,8 +20,8 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
-SYMBOLS = ("gqa_append_rope", "gqa_append_rope_paged", "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers",
-           "gqa_decode_paged", "gqa_decode_paged_fp8",
+SYMBOLS = ("gqa_append_rope", "gqa_append_rope_fp8", "gqa_append_rope_paged", "gqa_append_rope_paged_fp8",
+           "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_paged", "gqa_decode_paged_fp8",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
 
 
@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
         L.gqa_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp]
         L.gqa_append_rope_paged.restype = ctypes.c_int
         L.gqa_append_rope_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, ctypes.c_float, vp, dims_p, vp]
+        f32 = ctypes.c_float
+        L.gqa_append_rope_fp8.restype = ctypes.c_int
+        L.gqa_append_rope_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, dims_p, vp]
+        L.gqa_append_rope_paged_fp8.restype = ctypes.c_int
+        L.gqa_append_rope_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, f32, f32, f32, vp, dims_p, vp]
         L.gqa_status_string.restype = ctypes.c_char_p
         L.gqa_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -325,7 +330,7 @@ def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, 
 
 
 def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
-                max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None):
+                max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None, scales=None):
     """Append each sequence's new token to one layer's cache with rotary
     position embedding at position seq_lens[b] (see gqa_append_rope in
     include/gqa_decode.h).  q [B,H_q,d]; k_new/v_new [B,H_kv,d]; caches dense
@@ -356,9 +361,11 @@ def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k
         if v_cache.numel() != k_cache.numel() or k_cache.numel() % (H_kv * d):
             raise ValueError("packed cache size mismatch")
         T_max = max_seq_len
-    for t in (k_new, v_new, k_cache, v_cache):
+    for t in (k_new, v_new) + (() if scales else (k_cache, v_cache)):
         if t.dtype != q.dtype:
             raise TypeError("q, k_new, v_new and the caches must share one dtype")
+    if scales and (k_cache.dtype not in E4M3_DTYPES or v_cache.dtype not in E4M3_DTYPES):
+        raise TypeError("E4M3 caches are uint8 or float8_e4m3fn")
     dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype)
     if q_out is None:
         q_out = torch.empty_like(q)
@@ -371,14 +378,28 @@ def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k
     if new_seq_lens.shape != (B,) or new_seq_lens.dtype != torch.int32:
         raise ValueError("new_seq_lens must be int32 [B]")
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    _check(lib().gqa_append_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets),
-                                 _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), _ptr(q_out),
-                                 ctypes.byref(dims), s))
+    head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
+            _ptr(new_seq_lens), float(rope_base))
+    if scales:
+        _check(lib().gqa_append_rope_fp8(*head, float(scales[0]), float(scales[1]), _ptr(q_out), ctypes.byref(dims), s))
+    else:
+        _check(lib().gqa_append_rope(*head, _ptr(q_out), ctypes.byref(dims), s))
     return q_out, new_seq_lens
 
 
+def append_rope_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k_scale: float, v_scale: float,
+                    kv_offsets=None, max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None):
+    """append_rope into caches of one-byte E4M3 codes (uint8 or float8_e4m3fn;
+    dense or packed): the rotated key is stored as the code of key / k_scale,
+    the value as the code of value / v_scale (nearest, ties to even,
+    saturating at +-448)."""
+    return append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets=kv_offsets,
+                       max_seq_len=max_seq_len, q_out=q_out, new_seq_lens=new_seq_lens, stream=stream,
+                       scales=(k_scale, v_scale))
+
+
 def append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
-                      max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None):
+                      max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None, scales=None):
     """append_rope for a cache held in pages of a pool (the layout of
     decode_paged): k_pool/v_pool [num_pages,H_kv,page,d], block_table int32
     [B,max_pages]; the new token of sequence b goes to row seq_lens[b] % page
@@ -398,9 +419,11 @@ def append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, ro
         raise ValueError("pools must be [num_pages,H_kv,page,d]")
     if block_table.dim() != 2 or block_table.shape[0] != B or block_table.dtype != torch.int32:
         raise ValueError("block_table must be int32 [B,max_pages]")
-    for t in (k_new, v_new, k_pool, v_pool):
+    for t in (k_new, v_new) + (() if scales else (k_pool, v_pool)):
         if t.dtype != q.dtype:
             raise TypeError("q, k_new, v_new and the pools must share one dtype")
+    if scales and (k_pool.dtype not in E4M3_DTYPES or v_pool.dtype not in E4M3_DTYPES):
+        raise TypeError("E4M3 pools are uint8 or float8_e4m3fn")
     page, max_pages = k_pool.shape[2], block_table.shape[1]
     dims = make_dims(B, H_q, H_kv, d, max_pages * page if max_seq_len is None else int(max_seq_len), q.dtype)
     q_out = torch.empty_like(q) if q_out is None else q_out
@@ -411,10 +434,24 @@ def append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, ro
             new_seq_lens.dtype != torch.int32:
         raise ValueError("q_out must match q and new_seq_lens be int32 [B]")
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    _check(lib().gqa_append_rope_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
-                                       _ptr(block_table), int(max_pages), int(page), _ptr(seq_lens),
-                                       _ptr(new_seq_lens), float(rope_base), _ptr(q_out), ctypes.byref(dims), s))
+    head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages),
+            int(page), _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base))
+    if scales:
+        _check(lib().gqa_append_rope_paged_fp8(*head, float(scales[0]), float(scales[1]), _ptr(q_out),
+                                               ctypes.byref(dims), s))
+    else:
+        _check(lib().gqa_append_rope_paged(*head, _ptr(q_out), ctypes.byref(dims), s))
     return q_out, new_seq_lens
+
+
+def append_rope_paged_fp8(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float, k_scale: float,
+                          v_scale: float, max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None,
+                          stream=None):
+    """append_rope_paged into pools of one-byte E4M3 codes, quantised as in
+    append_rope_fp8."""
+    return append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base,
+                             max_seq_len=max_seq_len, q_out=q_out, new_seq_lens=new_seq_lens, stream=stream,
+                             scales=(k_scale, v_scale))
 
 
 def prepare_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,

@@ -400,17 +400,22 @@ gqa_status gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cach
 }
 
 namespace {
+// e4m3: the caches hold one-byte E4M3 codes of key / k_scale and value / v_scale.
 gqa_status append_launch(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int64_t* kv_offsets, const int32_t* block_table, int32_t max_pages, int32_t page,
                          const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, void* q_out,
-                         const gqa_dims* dims, void* stream) {
+                         const gqa_dims* dims, void* stream, bool e4m3 = false, float k_scale = 1.f,
+                         float v_scale = 1.f) {
   gqa_status st = check_dims(dims, 1);
   if (st != GQA_OK) return st;
   if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return GQA_ERR_INVALID_ARG;
+  if (e4m3 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) || !(v_scale > 0.f)))
+    return GQA_ERR_INVALID_ARG;
   if (dims->batch == 0) return GQA_OK;
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !seq_lens || !q_out) return GQA_ERR_INVALID_ARG;
   const uintptr_t e = dims->dtype == GQA_DTYPE_F32 ? 4 : 2;
-  if (!aligned(q, e) || !aligned(k_new, e) || !aligned(v_new, e) || !aligned(k_cache, e) || !aligned(v_cache, e) ||
+  const uintptr_t ec = e4m3 ? 1 : e;   // cache element size
+  if (!aligned(q, e) || !aligned(k_new, e) || !aligned(v_new, e) || !aligned(k_cache, ec) || !aligned(v_cache, ec) ||
       !aligned(q_out, e) || !aligned(seq_lens, 4) || (new_seq_lens && !aligned(new_seq_lens, 4)) ||
       (kv_offsets && !aligned(kv_offsets, 8)) || (block_table && !aligned(block_table, 4)))
     return GQA_ERR_INVALID_ARG;
@@ -432,12 +437,21 @@ gqa_status append_launch(const void* q, const void* k_new, const void* v_new, vo
   p.H_kv = dims->num_kv_heads;
   p.T_max = dims->max_seq_len;
   p.base = (double)rope_base;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   typedef void (*rope_fn)(gqa::RopeProblem);
   rope_fn k;
-  if (dims->dtype == GQA_DTYPE_F32)
-    k = dims->head_dim == 128 ? gqa::gqa_append_rope<float, 128> : gqa::gqa_append_rope<float, 64>;
-  else
-    k = dims->head_dim == 128 ? gqa::gqa_append_rope<uint16_t, 128> : gqa::gqa_append_rope<uint16_t, 64>;
+  const bool d128 = dims->head_dim == 128;
+  if (e4m3) {
+    if (dims->dtype == GQA_DTYPE_F32)
+      k = d128 ? gqa::gqa_append_rope<float, 128, true> : gqa::gqa_append_rope<float, 64, true>;
+    else
+      k = d128 ? gqa::gqa_append_rope<uint16_t, 128, true> : gqa::gqa_append_rope<uint16_t, 64, true>;
+  } else if (dims->dtype == GQA_DTYPE_F32) {
+    k = d128 ? gqa::gqa_append_rope<float, 128, false> : gqa::gqa_append_rope<float, 64, false>;
+  } else {
+    k = d128 ? gqa::gqa_append_rope<uint16_t, 128, false> : gqa::gqa_append_rope<uint16_t, 64, false>;
+  }
   void* args[] = {&p};
   if (hipLaunchKernel(reinterpret_cast<const void*>(k), dim3((unsigned)dims->batch), dim3(256), args, 0,
                       static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -462,6 +476,25 @@ gqa_status gqa_append_rope_paged(const void* q, const void* k_new, const void* v
   if (dims && dims->batch > 0 && !block_table) return GQA_ERR_INVALID_ARG;
   return append_launch(q, k_new, v_new, k_pool, v_pool, nullptr, block_table, max_pages, page_size, seq_lens,
                        new_seq_lens, rope_base, q_out, dims, stream);
+}
+
+gqa_status gqa_append_rope_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                               float rope_base, float k_scale, float v_scale, void* q_out, const gqa_dims* dims,
+                               void* stream) {
+  return append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, nullptr, 0, 0, seq_lens, new_seq_lens, rope_base,
+                       q_out, dims, stream, true, k_scale, v_scale);
+}
+
+gqa_status gqa_append_rope_paged_fp8(const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                                     const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, float k_scale,
+                                     float v_scale, void* q_out, const gqa_dims* dims, void* stream) {
+  if (page_size <= 0 || page_size % 16 != 0 || max_pages <= 0) return GQA_ERR_INVALID_ARG;
+  if (dims && (int64_t)max_pages * page_size < dims->max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (dims && dims->batch > 0 && !block_table) return GQA_ERR_INVALID_ARG;
+  return append_launch(q, k_new, v_new, k_pool, v_pool, nullptr, block_table, max_pages, page_size, seq_lens,
+                       new_seq_lens, rope_base, q_out, dims, stream, true, k_scale, v_scale);
 }
 
 const char* gqa_status_string(gqa_status s) {

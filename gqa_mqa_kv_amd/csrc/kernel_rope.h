@@ -10,6 +10,10 @@
 // once, in double precision (m * theta_j reaches 1e5 radians), and shared
 // through LDS as single-precision cosine and sine; each thread then turns
 // element pairs of the queries and keys.
+//
+// KV8: the cache holds one-byte OCP E4M3 elements; the rotated key and the
+// value are stored as the codes of key / k_scale and value / v_scale (nearest
+// E4M3 value, ties to the even mantissa, saturating at +-448, NaN to 0x7F).
 #pragma once
 
 #include "common.h"
@@ -30,7 +34,26 @@ struct RopeProblem {
   int32_t* new_seq_lens;       // [B] or nullptr (may equal seq_lens)
   int32_t B, H_q, H_kv, T_max;
   double base;
+  float k_scale, v_scale;      // KV8: what a key / value code is multiplied by
 };
+
+// The E4M3 byte of y, from the format's definition: |y| >= 448 saturates; below
+// 2^-6 the grid is m * 2^-9 (m = 0 .. 8, m = 8 being the smallest normal);
+// above, three mantissa bits rounded to nearest even, a carry moving into the
+// exponent.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7Fu;                 // NaN
+  if (a >= 0x43e00000u) return sign | 0x7Eu;         // |y| >= 448 (and infinities)
+  if (a < 0x3c800000u) return sign | (uint32_t)rintf(__uint_as_float(a) * 512.f);   // |y| < 2^-6
+  const uint32_t e = (a >> 23) - 127u + 7u;          // biased E4M3 exponent, 1 .. 15
+  const uint32_t m = a & 0x7fffffu;
+  const uint32_t rem = m & 0xfffffu;
+  const uint32_t q = (m >> 20) + ((rem > 0x80000u || (rem == 0x80000u && ((m >> 20) & 1u))) ? 1u : 0u);
+  return sign | ((e << 3) + q);
+}
 
 template <typename T>
 struct RopeElem;
@@ -49,7 +72,7 @@ struct RopeElem<uint16_t> {
   }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool KV8>
 __global__ __launch_bounds__(256) void gqa_append_rope(RopeProblem p) {
   constexpr int NT = 256, P = D / 2;
   __shared__ float sm_cos[P], sm_sin[P];
@@ -96,11 +119,21 @@ __global__ __launch_bounds__(256) void gqa_append_rope(RopeProblem p) {
       const int g = (e - nq) / P;
       const int64_t i0 = (krow + g) * D + 2 * j, o0 = (crow0 + g * cstride) * D + 2 * j;
       const float x0 = RopeElem<T>::get(p.k_new, i0), x1 = RopeElem<T>::get(p.k_new, i0 + 1);
-      RopeElem<T>::put(p.k_cache, o0, x0 * c - x1 * s);
-      RopeElem<T>::put(p.k_cache, o0 + 1, x0 * s + x1 * c);
-      // the value row is stored as it is
-      RopeElem<T>::put(p.v_cache, o0, RopeElem<T>::get(p.v_new, i0));
-      RopeElem<T>::put(p.v_cache, o0 + 1, RopeElem<T>::get(p.v_new, i0 + 1));
+      const float k0 = x0 * c - x1 * s, k1 = x0 * s + x1 * c;
+      if constexpr (KV8) {
+        uint8_t* kc = static_cast<uint8_t*>(p.k_cache);
+        uint8_t* vc = static_cast<uint8_t*>(p.v_cache);
+        kc[o0] = (uint8_t)e4m3_encode(k0 / p.k_scale);
+        kc[o0 + 1] = (uint8_t)e4m3_encode(k1 / p.k_scale);
+        vc[o0] = (uint8_t)e4m3_encode(RopeElem<T>::get(p.v_new, i0) / p.v_scale);
+        vc[o0 + 1] = (uint8_t)e4m3_encode(RopeElem<T>::get(p.v_new, i0 + 1) / p.v_scale);
+      } else {
+        RopeElem<T>::put(p.k_cache, o0, k0);
+        RopeElem<T>::put(p.k_cache, o0 + 1, k1);
+        // the value row is stored as it is
+        RopeElem<T>::put(p.v_cache, o0, RopeElem<T>::get(p.v_new, i0));
+        RopeElem<T>::put(p.v_cache, o0 + 1, RopeElem<T>::get(p.v_new, i0 + 1));
+      }
     }
   }
   if (p.new_seq_lens) {

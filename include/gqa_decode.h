@@ -301,6 +301,27 @@ gqa_status gqa_append_rope_paged(const void* q, const void* k_new, const void* v
                                  const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, void* q_out,
                                  const gqa_dims* dims, void* stream);
 
+/*
+ * The append step for caches of one-byte OCP E4M3 elements (the caches of
+ * gqa_decode_fp8 and gqa_decode_paged_fp8).  The pages give no rule for
+ * turning a value into such a byte; here the rotated key is stored as the
+ * code of key / k_scale and the value as the code of value / v_scale: the
+ * nearest E4M3 value, ties to the even mantissa, saturating at +-448 (a cached
+ * element stays finite), NaN to 0x7F.  The division and the rotation run in
+ * fp32.  k_scale and v_scale: finite and > 0 (GQA_ERR_INVALID_ARG otherwise).
+ * q, k_new, v_new and q_out are fp32 or bf16 (dims->dtype); the caches need
+ * no alignment.  Everything else as for gqa_append_rope (dense or packed
+ * caches) and gqa_append_rope_paged (paged pools).
+ */
+gqa_status gqa_append_rope_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                               float rope_base, float k_scale, float v_scale, void* q_out, const gqa_dims* dims,
+                               void* stream);
+gqa_status gqa_append_rope_paged_fp8(const void* q, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages, int32_t page_size,
+                                     const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, float k_scale,
+                                     float v_scale, void* q_out, const gqa_dims* dims, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* gqa_status_string(gqa_status status);
 

@@ -300,6 +300,21 @@ def test_append_rope_paged_validation():
     assert call(dd=dims(B=0), bt=None) == OK
 
 
+def test_append_rope_fp8_validation():
+    """The quantising appends check their scales on top of their parents'
+    rules, before touching the device; E4M3 caches need no alignment."""
+    d = dims(T_max=1024)
+    dense = lambda dd=d, ks=0.01, vs=0.02, cache=FAKE + 1: gqa.lib().gqa_append_rope_fp8(
+        FAKE, FAKE, FAKE, cache, cache, None, FAKE, None, 10000.0, ks, vs, FAKE, ctypes.byref(dd), None)
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert dense(ks=bad) == INVALID and dense(vs=bad) == INVALID
+    assert dense(dd=dims(d=96)) == UNSUPPORTED
+    assert dense(dd=dims(B=0)) == OK
+    paged = lambda pg=16, mp=64, bt=FAKE: gqa.lib().gqa_append_rope_paged_fp8(
+        FAKE, FAKE, FAKE, FAKE, FAKE, bt, mp, pg, FAKE, None, 10000.0, 0.01, 0.02, FAKE, ctypes.byref(d), None)
+    assert paged(pg=24) == INVALID and paged(mp=63) == INVALID and paged(bt=None) == INVALID
+
+
 def test_library_missing_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding._build, "LIB_PATH", str(tmp_path / "absent.so"))

@@ -245,3 +245,153 @@ def test_append_then_decode_paged():
     ref = orc.decode(ref_q, ref_k, v.double(), (lens + 1).tolist(), d ** -0.5)
     err = float(np.abs(out.double().cpu().numpy() - ref).max())
     assert err <= 2e-3, err
+
+
+# ------------------------------------------------ quantising append (E4M3) --
+def codes_within(gpu_codes, y, eps):
+    """Each code decodes to a value the E4M3 encoder gives for some point of
+    [y - eps, y + eps] (the encoder is monotone): the GPU's fp32 rotation and
+    division may move y by eps, which only matters next to a rounding
+    boundary.  Away from boundaries this is exact equality."""
+    orc = oracle.default()
+    got = orc.e4m3(gpu_codes)
+    lo = orc.e4m3(orc.e4m3_encode(y - eps))
+    hi = orc.e4m3(orc.e4m3_encode(y + eps))
+    return bool(((got >= lo) & (got <= hi)).all())
+
+
+def e4m3_cache(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    c = torch.randint(0, 0x7E, shape, generator=g, dtype=torch.uint8)
+    return c | (torch.randint(0, 2, shape, generator=g, dtype=torch.uint8) << 7)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("paged", [False, True], ids=["dense", "paged"])
+def test_append_fp8_matches_oracle(dtype, paged):
+    """Rotated keys and values written as E4M3 codes of key / k_scale and
+    value / v_scale (nearest, ties to even, saturating), every other byte
+    unchanged; sequence 3's new token is large enough to saturate."""
+    B, H_q, H_kv, d, T, page = 6, 32, 8, 128, 192, 32
+    lens = [0, 15, 16, 47, 191, 192]
+    x = make(B, H_q, H_kv, d, T, dtype, seed=61, lens=lens)
+    x["k_new"][3] *= 40
+    x["v_new"][3] *= 40
+    ks, vs = 0.03125, 0.0125
+    kc, vc = e4m3_cache((B, H_kv, T, d), 1), e4m3_cache((B, H_kv, T, d), 2)
+    note("append fp8", dtype, "paged" if paged else "dense")
+    args = (x["q"].to(DEV), x["k_new"].to(DEV), x["v_new"].to(DEV))
+    if paged:
+        pk, pv, table = paged_for_append({"k": kc, "v": vc, "seq_lens": x["seq_lens"]}, page, seed=8)
+        kd, vd = pk.to(DEV), pv.to(DEV)
+        q_out, nl = gqa.append_rope_paged_fp8(*args, kd, vd, table.to(DEV), x["seq_lens"].to(DEV), 10000.0, ks, vs,
+                                              max_seq_len=T)
+        row = lambda t, b, m: t[int(table[b, m // page]), :, m % page]
+        before_k, before_v = pk, pv
+    else:
+        kd, vd = kc.to(DEV), vc.to(DEV)
+        q_out, nl = gqa.append_rope_fp8(*args, kd, vd, x["seq_lens"].to(DEV), 10000.0, ks, vs)
+        row = lambda t, b, m: t[b, :, m]
+        before_k, before_v = kc, vc
+    torch.cuda.synchronize()
+    orc = oracle.default()
+    pos = torch.tensor(lens)
+    assert rot_err_ok(q_out, orc.rope(x["q"], pos.view(B, 1), 10000.0), dtype)
+    k_rot = orc.rope(x["k_new"], pos.view(B, 1), 10000.0)                  # fp64 [B, H_kv, d]
+    k_after, v_after = kd.cpu(), vd.cpu()
+    written_k, written_v = before_k.clone(), before_v.clone()
+    for b in range(B):
+        m = lens[b]
+        if m >= T:
+            assert int(nl[b]) == m
+            continue
+        assert int(nl[b]) == m + 1
+        xk = x["k_new"][b].double().numpy()
+        pair_mag = np.abs(xk.reshape(H_kv, d // 2, 2)).sum(-1).repeat(2, -1)   # |x0| + |x1| of each element's pair
+        yk = k_rot[b] / ks
+        assert codes_within(row(k_after, b, m), yk, 4 * 2.0 ** -23 * pair_mag / ks + 2.0 ** -22 * np.abs(yk))
+        yv = x["v_new"][b].double().numpy() / vs
+        assert codes_within(row(v_after, b, m), yv, 2.0 ** -22 * np.abs(yv))
+        row(written_k, b, m)[...] = row(k_after, b, m)
+        row(written_v, b, m)[...] = row(v_after, b, m)
+    assert torch.equal(k_after, written_k) and torch.equal(v_after, written_v)   # nothing else changed
+    assert (row(k_after, 3, lens[3]).numpy() & 0x7F).max() == 0x7E                 # the large token saturates
+
+
+def test_append_then_decode_fp8():
+    """A whole decode step on an E4M3 cache: the quantising append, then the
+    E4M3 decode, against the oracle's rotation, encoder and E4M3 attention."""
+    B, H_q, H_kv, d, T = 3, 32, 8, 128, 700
+    g = torch.Generator().manual_seed(79)
+    lens = torch.tensor([0, 350, 699], dtype=torch.int32)
+    raw_k = torch.randn(B, H_kv, T, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H_kv, T, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, H_q, d, generator=g).to(torch.bfloat16)
+    base, ks, vs = 10000.0, 4.0 / 448, 4.0 / 448
+    orc = oracle.default()
+    rot_k = orc.rope(raw_k, torch.arange(T).view(1, 1, T), base)
+    k8 = torch.from_numpy(orc.e4m3_encode(rot_k / float(np.float32(ks))))          # the cache earlier appends left
+    v8 = torch.from_numpy(orc.e4m3_encode(v.double() / float(np.float32(vs))))
+    m = lens.long()
+    kn, vn = raw_k[torch.arange(B), :, m], v[torch.arange(B), :, m]
+    note("append then decode, E4M3")
+    kd, vd = k8.clone().to(DEV), v8.clone().to(DEV)
+    q_rot, nl = gqa.append_rope_fp8(q.to(DEV), kn.contiguous().to(DEV), vn.contiguous().to(DEV), kd, vd, lens.to(DEV),
+                                    base, ks, vs)
+    out = gqa.decode_fp8(q_rot, kd, vd, nl, d ** -0.5, ks, vs, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_q = torch.from_numpy(orc.rope(q.double(), m.view(B, 1), base))
+    ref_k8, ref_v8 = k8.clone(), v8.clone()                                     # the oracle's own append
+    for b in range(B):
+        ref_k8[b, :, int(m[b])] = torch.from_numpy(orc.e4m3_encode(orc.rope(kn[b], int(m[b]), base)
+                                                                   / float(np.float32(ks))))
+        ref_v8[b, :, int(m[b])] = torch.from_numpy(orc.e4m3_encode(vn[b].double() / float(np.float32(vs))))
+    ref = orc.decode_fp8(ref_q, ref_k8, ref_v8, (lens + 1).tolist(), d ** -0.5, ks, vs)
+    err = float(np.abs(out.double().cpu().numpy() - ref).max())
+    assert err <= 2e-3, err
+
+
+def test_e4m3_encoder_exact():
+    """The kernel's E4M3 encoder, exactly: with scales of 1 it sees the
+    values themselves, so every value code must equal the oracle encoder's.
+    Keys are turned at position 0 (cos 1, sin 0): x0 - x1 * 0 is x0 exactly
+    unless the partner x1 is infinite or NaN (inf * 0) or x0 is a zero (whose
+    sign the subtraction may flip), so key codes are compared where neither
+    happens.  Inputs:
+    every midpoint between neighbouring codes and its two float32
+    neighbours (ties and near-ties, both signs), values across the whole
+    range, and the saturating and special values."""
+    orc = oracle.default()
+    vals = orc.e4m3(torch.arange(256, dtype=torch.uint8))
+    pos = np.sort(vals[np.isfinite(vals) & (vals >= 0) & ~np.signbit(vals)])
+    mids = torch.tensor((pos[:-1] + pos[1:]) / 2, dtype=torch.float32)
+    up = torch.nextafter(mids, torch.tensor(np.inf, dtype=torch.float32))
+    dn = torch.nextafter(mids, torch.tensor(-np.inf, dtype=torch.float32))
+    g = torch.Generator().manual_seed(5)
+    rnd = torch.randn(60000, generator=g) * torch.exp(torch.empty(60000).uniform_(-16, 8, generator=g))
+    special = torch.tensor([0.0, -0.0, 448.0, -448.0, 447.9, 464.0, 465.0, 1e9, -1e9, float("inf"), float("-inf"),
+                            float("nan"), 2.0 ** -6, 2.0 ** -7, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 1e-30])
+    x = torch.cat([mids, up, dn, -mids, -up, -dn, torch.from_numpy(pos).float(), rnd, special])
+    H_kv, d = 8, 128
+    per = H_kv * d
+    B = -(-x.numel() // per)
+    x = torch.cat([x, torch.zeros(B * per - x.numel())]).view(B, H_kv, d)
+    q = torch.zeros(B, 8, d)
+    kc = torch.zeros(B, H_kv, 1, d, dtype=torch.uint8)
+    vc = torch.zeros(B, H_kv, 1, d, dtype=torch.uint8)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    note("E4M3 encoder exact", B * per, "values")
+    gqa.append_rope_fp8(q.to(DEV), x.to(DEV), x.to(DEV), kd, vd, torch.zeros(B, dtype=torch.int32, device=DEV),
+                        10000.0, 1.0, 1.0)
+    torch.cuda.synchronize()
+    want = orc.e4m3_encode(x.double())
+    got_v, got_k = vd.cpu()[:, :, 0].numpy(), kd.cpu()[:, :, 0].numpy()
+    bad = np.argwhere(got_v != want)
+    assert len(bad) == 0, ("value codes differ", [(float(x[tuple(i)]), int(got_v[tuple(i)]), int(want[tuple(i)]))
+                                                  for i in bad[:8]])
+    xv = x.numpy()
+    partner = xv.reshape(B, H_kv, d // 2, 2)[..., ::-1].reshape(B, H_kv, d)
+    ok = np.isfinite(partner) & (xv != 0)
+    bad = np.argwhere((got_k != want) & ok)
+    assert len(bad) == 0, ("key codes differ", [(float(x[tuple(i)]), int(got_k[tuple(i)]), int(want[tuple(i)]))
+                                                for i in bad[:8]])
