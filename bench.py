@@ -149,6 +149,25 @@ def copy_calibration(torch, dev, nbytes: int, launches: int) -> None:
                       "bytes_written_per_launch": nbytes, "launches": launches}), flush=True)
 
 
+def copy_probe(torch, dev, stream, nbytes: int = 1 << 30, launches: int = 10):
+    """Achievable HBM rate of a plain device copy (an elementwise fp32 kernel
+    reading nbytes and writing nbytes): context for the step's rate."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        torch.neg(src, out=dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    del src, dst
+    return {"GB/s": round(2 * nbytes / (us * 1e-6) / 1e9, 1), "us_per_launch": round(us, 1),
+            "bytes_read_and_written": 2 * nbytes}
+
+
 def time_layers_one_by_one(torch, gqa, workloads, w, x, stream, out_dtype, reps: int = 3):
     """The same step as L launches of one layer each (gqa_decode_layers with
     L = 1 on each layer's slice), as a model that computes layer l's queries
@@ -361,6 +380,12 @@ def main():
     }
     if not args.no_extras:
         result["per_step_us"] = step_percentiles(torch, step, stream, min(args.steps, 100), args.steps)
+        # the same step repeated on one input batch: whatever of it fits stays in the caches
+        result["warm_one_batch_us_per_step"] = step_percentiles(
+            torch, lambda i: launchers[0](), stream, min(args.steps, 50), 0)["p50"]
+        probe = copy_probe(torch, dev, stream)
+        probe["step_rate_as_fraction"] = round(gbps / probe["GB/s"], 4)
+        result["hbm_copy_probe"] = probe
     if w.layers > 1 and not args.no_extras:
         result["sequential_single_layer_launches"] = time_layers_one_by_one(torch, gqa, workloads, w, batches[0],
                                                                             stream, out_dtype)
