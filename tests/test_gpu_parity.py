@@ -439,3 +439,33 @@ def test_full_32_layer_stack():
     assert e <= 2e-3
     del x
     torch.cuda.empty_cache()
+
+
+# -------------------------------------------------------- largest batches --
+@pytest.mark.timeout(300)
+def test_batch_at_the_matrix_core_limit():
+    """4096 sequences (the most whose prefix sums the matrix-core path keeps
+    in LDS: 16 per thread), lengths 0 .. 40, dense and paged; 4097 sequences
+    on the automatic path run on the vector path, which has no such limit."""
+    g = torch.Generator().manual_seed(4096)
+    for B, path, expect_mfma in ((4096, "auto", True), (4097, "auto", False)):
+        x = small(B, 8, 2, 64, 40, seed=B)
+        x["seq_lens"] = torch.randint(0, 41, (B,), generator=g, dtype=torch.int32)
+        for b, n in enumerate(x["seq_lens"].tolist()):
+            x["k"][b, :, n:] = float("nan")
+            x["v"][b, :, n:] = float("nan")
+        d = gqa.make_dims(B, 8, 2, 64, 40, torch.bfloat16, path=path)
+        chunk, n = gqa.plan(d)
+        assert (chunk == 0) == expect_mfma, (B, chunk, n)   # the matrix-core split reports no chunk size
+        check(x, label="B=%d %s" % (B, path))
+        if B == 4096:
+            xd = to_dev(x)
+            kp, vp, tb = workloads.to_pages(xd, 16, seed=1)
+            out = gqa.decode_paged(xd["q"], kp, vp, tb, xd["seq_lens"], x["scale"], out_dtype=torch.float32,
+                                   max_seq_len=40)
+            torch.cuda.synchronize()
+            ref = oracle.default().decode_paged(x["q"], kp.cpu(), vp.cpu(), tb.cpu(), 16, x["seq_lens"], x["scale"])
+            assert err(out, ref) <= 2e-3
+    with pytest.raises(gqa.GqaError):   # forcing the matrix-core path beyond its limit is refused
+        xd = to_dev(small(4097, 8, 2, 64, 16, seed=1))
+        gqa.decode(xd["q"], xd["k"], xd["v"], xd["seq_lens"], xd["scale"], path="mfma")
