@@ -29,6 +29,11 @@ def build(verbose: bool = False) -> str:
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-shared", "-fPIC",
            # packed fp32 VALU forms are kept out of the generated code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # matrix-core accumulators in ordinary VGPRs: the decode kernel's
+           # O accumulators are also scaled on the vector ALU, and with them
+           # in accumulation registers every such pass costs two copies per
+           # element (and the two-head-block variants spill)
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-I", INCLUDE, "-I", CSRC] + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -179,7 +179,7 @@ int max_waves(int) { return 4; }
 // so the one-block E4M3 variant loads two per batch by default (measured:
 // 10-20 % faster than one on every workload; four, on request, gain 3 % on
 // very long units and lose 10 % on the 8B and ragged 70B layers).
-int max_tiles(int hb, bool kv8) { return hb == 1 ? (kv8 ? 4 : 2) : 1; }
+int max_tiles(int hb, bool kv8) { return hb == 1 ? (kv8 ? 4 : 2) : hb == 2 ? 2 : 1; }
 int default_tiles(int hb, bool kv8) { return kv8 && hb == 1 ? 2 : 1; }
 
 template <int D, bool PAGED = false, bool KV8 = false>
@@ -189,7 +189,8 @@ kernel_fn mfma_kernel(int hb, int, int tiles) {
       if (KV8 && tiles == 4) return gqa::gqa_decode_mfma<D, 1, 1, 4, KV8 ? 4 : 2, PAGED, KV8>;
       return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, PAGED, KV8>
                         : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, PAGED, KV8>;
-    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1, PAGED, KV8>;
+    case 2:
+      return tiles == 2 ? gqa::gqa_decode_mfma<D, 2, 1, 4, 2, PAGED, KV8> : gqa::gqa_decode_mfma<D, 2, 1, 4, 1, PAGED, KV8>;
     default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, PAGED, KV8>;
   }
 }

@@ -27,15 +27,19 @@
 // 4*q4 .. 4*q4+3: exactly the B operand the P.V product needs from that lane,
 // so the softmax weights never move between lanes.
 //
-// P.V: O^T[col][head] += V^T P^T on v_mfma_f32_16x16x16_bf16 (K = 16 tokens),
-// A = V^T.  Lane (m, q4) holds rows 4*q4 .. 4*q4+3 of the tile, D/16
-// consecutive columns each (16 lanes cover a row, so each load instruction
-// reads 4 complete rows); column r of that run becomes the A operand of
-// column block r after a half-word repack (block r holds columns D/16*m + r).
+// P.V: O^T[col][head] += V^T P^T, A = V^T.  Lane (m, q4) holds rows
+// 4*q4 .. 4*q4+3 of the tile, D/16 consecutive columns each (16 lanes cover a
+// row, so each load instruction reads 4 complete rows); column r of that run
+// becomes the A operand of column block r after a half-word repack (block r
+// holds columns D/16*m + r).
 //
 // Softmax weights enter the bf16 product as a two-term split p = hi + lo
 // (hi = bf16(p), lo = bf16(p - hi)), so their rounding error stays near
-// 2^-17 of p instead of 2^-9; the normaliser l sums the fp32 p.  The running
+// 2^-17 of p instead of 2^-9; the normaliser l sums the fp32 p.  Both terms
+// go through one v_mfma_f32_16x16x32_bf16: its 32-long reduction runs over
+// the 16 tokens twice, the lane's four tokens with their hi weights and then
+// the same four with their lo weights (A repeats the lane's V values), so the
+// split costs no second product.  The running
 // maximum is only moved (and O, l rescaled) on tiles where it grows for some
 // head of the wavefront; otherwise the rescale factor would be exactly 1.
 #pragma once
@@ -46,7 +50,6 @@
 
 namespace gqa {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -66,15 +69,34 @@ __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
-// D(16x16) += A(16x16) B(16x16), bf16 inputs, fp32 accumulate.
-__device__ __forceinline__ f32x4 mfma_k16(u32x2 a, u32x2 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
-                                                   0, 0);
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// How far (in base-2 exponent) a score may exceed the running reference
+// before O and l are rescaled to a new one.
+constexpr float kRescaleSlack = 8.f;
+
+// 2^x on the hardware instruction alone (v_exp_f32, 1 ulp).  Results below
+// 2^-126 come out as 0 instead of subnormals: a softmax weight that small,
+// next to the weight 1 of the running maximum, is below every rounding of
+// the sums it enters.  2^-inf = 0.
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum of x over the four lanes m, m + 16, m + 32, m + 48 (the lanes of
+// one row index m in the wavefront's four 16-lane rows), in every one of
+// them.  Two lane swaps on the vector ALU: rows 0/1 and 2/3, then the two
+// halves.  Each swap of a value with itself leaves the row's partner value
+// in one result and its own in the other.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Low (hi = false) or high halves of two words, packed: {x0.half, x1.half}.
@@ -174,6 +196,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   // product takes columns q4*D/4 + 8s .. +7 of K and of q alike).
   const uint32_t koff = KV8 ? (uint32_t)(m16 * D + q4 * (D / 4)) : (uint32_t)(m16 * D + 8 * q4);
   const uint32_t voff = (uint32_t)(4 * q4 * D + VW * m16);
+  const uint32_t koff_b = koff * (uint32_t)sizeof(kv_t), voff_b = voff * (uint32_t)sizeof(kv_t);   // in bytes
 
   // One piece: the part [c0, c1) of a unit that lies in this span.
   struct Ctx {
@@ -228,9 +251,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     if constexpr (KV8) {
       typedef typename std::remove_reference<decltype(T.v[0])>::type vraw_t;
       if (t0 + TILE <= c.c1) {
-        // full tile: one base address per lane, the rest are immediate offsets
-        const kv_t* kt = c.kg + tr * D + koff;
-        const kv_t* vt = c.vg + tr * D + voff;
+        // full tile: a wave-uniform base, the lane's 32-bit offset, immediates
+        const char* kt = reinterpret_cast<const char*>(c.kg + tr * D) + koff_b;
+        const char* vt = reinterpret_cast<const char*>(c.vg + tr * D) + voff_b;
 #pragma unroll
         for (int s = 0; s < D / 64; ++s)
           T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 16 * s));
@@ -252,13 +275,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
               reinterpret_cast<const vraw_t*>(vb + (int64_t)min(t0 + 4 * q4 + i, last) * D + VW * m16));
       }
     } else if (t0 + TILE <= c.c1) {
-      // full tile: one base address per lane, the rest are immediate offsets
-      const uint16_t* kt = c.kg + tr * D + koff;
-      const uint16_t* vt = c.vg + tr * D + voff;
+      // full tile: a wave-uniform base, the lane's 32-bit offset, immediates
+      const char* kt = reinterpret_cast<const char*>(c.kg + tr * D) + koff_b;
+      const char* vt = reinterpret_cast<const char*>(c.vg + tr * D) + voff_b;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 32 * s));
+      for (int s = 0; s < KS; ++s) T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 64 * s));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vrow_t*>(vt + i * D));
+      for (int i = 0; i < 4; ++i)
+        T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vrow_t*>(vt + i * D * 2));
     } else {
       // ragged tail: rows past the piece are clamped to its last valid row
       // (in bounds and finite); their weights are forced to 0 below
@@ -337,11 +361,16 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
           if (t0 + 4 * q4 + i >= c1) x[i] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__any(mx > m_run[hb])) {   // wave-uniform: some head's maximum grew
+      mx = max_over_rows(mx);
+      // The reference m_run moves only when some head's maximum passes it by
+      // more than kRescaleSlack (wave-uniform test): until then the weights
+      // 2^(x - m_run) stay below 2^kRescaleSlack, which fp32 sums and the
+      // two-term bf16 split carry at full relative precision, and O and l
+      // need no rescaling.  Every state keeps the m_run its weights were
+      // taken against, so merges combine them exactly as before.
+      if (__any(mx > m_run[hb] + kRescaleSlack)) {
         const float m_new = fmaxf(m_run[hb], mx);
-        const float alpha = exp2f(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
+        const float alpha = exp2_raw(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
         m_run[hb] = m_new;
         l_run[hb] *= alpha;
 #pragma unroll
@@ -350,7 +379,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = exp2f(x[i] - m_run[hb]);
+        pv[i] = exp2_raw(x[i] - m_run[hb]);
         l_run[hb] += pv[i];
       }
       const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
@@ -367,11 +396,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         va = u32x2{pack_halves<true>(T.v[0][w], T.v[1][w]), pack_halves<true>(T.v[2][w], T.v[3][w])};
       else
         va = u32x2{pack_halves<false>(T.v[0][w], T.v[1][w]), pack_halves<false>(T.v[2][w], T.v[3][w])};
+      const u32x4 vv = u32x4{va[0], va[1], va[0], va[1]};
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        oacc[r][hb] = mfma_k16(va, phi[hb], oacc[r][hb]);
-        oacc[r][hb] = mfma_k16(va, plo[hb], oacc[r][hb]);
-      }
+      for (int hb = 0; hb < HB; ++hb)
+        oacc[r][hb] = mfma_k32(vv, u32x4{phi[hb][0], phi[hb][1], plo[hb][0], plo[hb][1]}, oacc[r][hb]);
     }
   };
   auto compute_batch = [&](const tile_t (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
@@ -562,6 +590,17 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     return true;
   };
   for (;;) {
+    // Steady state: while the piece has two more batches, neither step ends
+    // it, and this loop carries only the running softmax state.
+    while (j + 2 * NL * TPW < pc.ntiles) {
+      load_batch(TB, pc, j + NL * TPW, pid);
+      fetch_pages(pid, pc, j + 2 * NL * TPW);
+      compute_batch(TA, pc, j);
+      load_batch(TA, pc, j + 2 * NL * TPW, pid);
+      fetch_pages(pid, pc, j + 3 * NL * TPW);
+      compute_batch(TB, pc, j + NL * TPW);
+      j += 2 * NL * TPW;
+    }
     if (!step(TA, TB)) {
       compute_batch(TA, pc, j);
       break;
