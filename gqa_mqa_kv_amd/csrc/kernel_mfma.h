@@ -75,6 +75,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two weights as packed bf16 pairs hi = bf16(p), lo = bf16(p - hi).
+__device__ __forceinline__ void split_weights(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(p0, p1);
+  lo = pack_bf16x2(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xffff0000u));
+}
+
 // How far (in base-2 exponent) a score may exceed the running reference
 // before O and l are rescaled to a new one.
 constexpr float kRescaleSlack = 8.f;
@@ -131,19 +137,49 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0), e4m3x2_to_bf16x2<false>(w1),
                e4m3x2_to_bf16x2<true>(w1)};
 }
+// An E4M3 tile with its keys widened to bf16 (the score product's A
+// operands); the values stay bytes until they become P.V operands.
 template <int D>
-__device__ __forceinline__ Tile16<D> widen(const Tile16F8<D>& t) {
-  Tile16<D> w;
+struct Tile16K8 {
+  u32x4 k[D / 32];
+  typename std::conditional<D == 128, u32x2, uint32_t>::type v[4];
+};
+template <int D>
+__device__ __forceinline__ Tile16K8<D> widen(const Tile16F8<D>& t) {
+  Tile16K8<D> w;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) w.k[s] = e4m3x8_to_bf16x8(t.k[s / 2][2 * (s % 2)], t.k[s / 2][2 * (s % 2) + 1]);
 #pragma unroll
+  for (int i = 0; i < 4; ++i) w.v[i] = t.v[i];
+  return w;
+}
+
+// A operand of P.V column block r (the lane's V rows 4*q4 .. 4*q4+3 at column
+// D/16*m + r, as two bf16 pairs).  bf16 tiles: a half-word repack of two row
+// slices per pair.  E4M3 tiles: one byte permutation gathers rows (0, 1) (or
+// (2, 3)) of columns r and r + 1 (r even) and one conversion widens the pair
+// of column r or of column r + 1, so the permutation serves two blocks.
+template <int D>
+__device__ __forceinline__ u32x2 v_operand(const Tile16<D>& T, int r) {
+  const int w = r >> 1;
+  if (r & 1) return u32x2{pack_halves<true>(T.v[0][w], T.v[1][w]), pack_halves<true>(T.v[2][w], T.v[3][w])};
+  return u32x2{pack_halves<false>(T.v[0][w], T.v[1][w]), pack_halves<false>(T.v[2][w], T.v[3][w])};
+}
+template <int D>
+__device__ __forceinline__ u32x2 v_operand(const Tile16K8<D>& T, int r) {
+  const int k = r & 3;   // byte of the row word holding column r
+  const uint32_t sel = (k & 2) ? 0x07030602u : 0x05010400u;   // {x0.b, x1.b, x0.b+1, x1.b+1}, b = k & ~1
+  uint32_t x[4];
+#pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (D == 128)
-      w.v[i] = e4m3x8_to_bf16x8(t.v[i][0], t.v[i][1]);
+      x[i] = T.v[i][r >> 2];
     else
-      w.v[i] = u32x2{e4m3x2_to_bf16x2<false>(t.v[i]), e4m3x2_to_bf16x2<true>(t.v[i])};
+      x[i] = T.v[i];
   }
-  return w;
+  const uint32_t p01 = __builtin_amdgcn_perm(x[1], x[0], sel), p23 = __builtin_amdgcn_perm(x[3], x[2], sel);
+  if (k & 1) return u32x2{e4m3x2_to_bf16x2<true>(p01), e4m3x2_to_bf16x2<true>(p23)};
+  return u32x2{e4m3x2_to_bf16x2<false>(p01), e4m3x2_to_bf16x2<false>(p23)};
 }
 
 // Heads: each wavefront serves HB blocks of 16 query heads; the wavefronts
@@ -345,7 +381,36 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     }
   };
 
-  auto compute_tile = [&](const Tile16<D>& T, int t0, int c1) __attribute__((always_inline)) {
+  // The reference m_run moves only when some head's maximum (mx, over the
+  // head's lanes) passes it by more than kRescaleSlack (wave-uniform test):
+  // until then the weights 2^(x - m_run) stay below 2^kRescaleSlack, which
+  // fp32 sums and the two-term bf16 split carry at full relative precision,
+  // and O and l need no rescaling.  Every state keeps the m_run its weights
+  // were taken against, so merges combine them exactly as before.
+  auto rebase = [&](int hb, float mx) __attribute__((always_inline)) {
+    if (__any(mx > m_run[hb] + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run[hb], mx);
+      const float alpha = exp2_raw(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
+      m_run[hb] = m_new;
+      l_run[hb] *= alpha;
+#pragma unroll
+      for (int r = 0; r < VW; ++r) oacc[r][hb] *= alpha;
+    }
+  };
+  // Scores of one tile for head block hb, in base 2, with tokens at or past
+  // c1 masked.
+  auto tile_scores = [&](float (&x)[4], const f32x4& sc, int t0, int c1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = sc[i] * sl2;
+    if (t0 + TILE > c1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (t0 + 4 * q4 + i >= c1) x[i] = -INFINITY;
+    }
+  };
+
+  // T: a Tile16 (bf16 cache) or a Tile16K8 (E4M3 cache, keys widened).
+  auto compute_tile = [&](const auto& T, int t0, int c1) __attribute__((always_inline)) {
     u32x2 phi[HB], plo[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -353,49 +418,25 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) sc = mfma_k32(T.k[s], qf[hb][s], sc);
       float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = sc[i] * sl2;
-      if (t0 + TILE > c1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 4 * q4 + i >= c1) x[i] = -INFINITY;
-      }
+      tile_scores(x, sc, t0, c1);
       float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mx = max_over_rows(mx);
-      // The reference m_run moves only when some head's maximum passes it by
-      // more than kRescaleSlack (wave-uniform test): until then the weights
-      // 2^(x - m_run) stay below 2^kRescaleSlack, which fp32 sums and the
-      // two-term bf16 split carry at full relative precision, and O and l
-      // need no rescaling.  Every state keeps the m_run its weights were
-      // taken against, so merges combine them exactly as before.
-      if (__any(mx > m_run[hb] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run[hb], mx);
-        const float alpha = exp2_raw(m_run[hb] - m_new);   // 0 on the first tile, 1 where nothing grew
-        m_run[hb] = m_new;
-        l_run[hb] *= alpha;
-#pragma unroll
-        for (int r = 0; r < VW; ++r) oacc[r][hb] *= alpha;
-      }
+      rebase(hb, mx);
       float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pv[i] = exp2_raw(x[i] - m_run[hb]);
         l_run[hb] += pv[i];
       }
-      const uint32_t h01 = pack_bf16x2(pv[0], pv[1]), h23 = pack_bf16x2(pv[2], pv[3]);
-      const uint32_t l01 = pack_bf16x2(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xffff0000u));
-      const uint32_t l23 = pack_bf16x2(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xffff0000u));
+      uint32_t h01, h23, l01, l23;
+      split_weights(pv[0], pv[1], h01, l01);
+      split_weights(pv[2], pv[3], h23, l23);
       phi[hb] = u32x2{h01, h23};
       plo[hb] = u32x2{l01, l23};
     }
 #pragma unroll
     for (int r = 0; r < VW; ++r) {
-      const int w = r >> 1;
-      u32x2 va;
-      if (r & 1)
-        va = u32x2{pack_halves<true>(T.v[0][w], T.v[1][w]), pack_halves<true>(T.v[2][w], T.v[3][w])};
-      else
-        va = u32x2{pack_halves<false>(T.v[0][w], T.v[1][w]), pack_halves<false>(T.v[2][w], T.v[3][w])};
+      const u32x2 va = v_operand<D>(T, r);
       const u32x4 vv = u32x4{va[0], va[1], va[0], va[1]};
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
