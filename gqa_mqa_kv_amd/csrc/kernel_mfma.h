@@ -119,8 +119,9 @@ struct Tile16 {
 };
 
 // A tile of one-byte E4M3 elements as loaded: lane (q4, m16) holds bytes
-// q4*D/4 .. q4*D/4 + D/4 - 1 of K row m16 (the A operands of every score
-// step, see load_q) and bytes D/16*m16 .. of V rows 4*q4 + i.
+// 64*h + 16*q4 .. +15 of K row m16 for h < D/64 (the A operands of every
+// score step, see load_q: each load instruction reads 64 contiguous bytes of
+// 16 rows) and bytes D/16*m16 .. of V rows 4*q4 + i.
 template <int D>
 struct Tile16F8 {
   u32x4 k[D / 64];
@@ -228,9 +229,9 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   if (s0 >= s1) return;   // no tokens for this workgroup (uniform)
 
   // Per-lane element offsets inside a tile (relative to the tile's first row).
-  // E4M3 keys: the lane's D/4 columns are contiguous (step s of the score
-  // product takes columns q4*D/4 + 8s .. +7 of K and of q alike).
-  const uint32_t koff = KV8 ? (uint32_t)(m16 * D + q4 * (D / 4)) : (uint32_t)(m16 * D + 8 * q4);
+  // E4M3 keys: the lane holds columns 64h + 16q4 .. +15 (step s of the score
+  // product takes columns 64(s/2) + 16q4 + 8(s%2) .. +7 of K and of q alike).
+  const uint32_t koff = KV8 ? (uint32_t)(m16 * D + 16 * q4) : (uint32_t)(m16 * D + 8 * q4);
   const uint32_t voff = (uint32_t)(4 * q4 * D + VW * m16);
   const uint32_t koff_b = koff * (uint32_t)sizeof(kv_t), voff_b = voff * (uint32_t)sizeof(kv_t);   // in bytes
 
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       const uint16_t* qg = reinterpret_cast<const uint16_t*>(p.q) + (c.orow + h) * D;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int col = KV8 ? q4 * (D / 4) + 8 * s : 32 * s + 8 * q4;   // the columns K's step s holds
+        const int col = KV8 ? 64 * (s >> 1) + 16 * q4 + 8 * (s & 1) : 32 * s + 8 * q4;   // the columns K's step s holds
         qf[hb][s] = (h < G) ? *reinterpret_cast<const u32x4*>(qg + col) : u32x4{0, 0, 0, 0};
       }
     }
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         const char* vt = reinterpret_cast<const char*>(c.vg + tr * D) + voff_b;
 #pragma unroll
         for (int s = 0; s < D / 64; ++s)
-          T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 16 * s));
+          T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 64 * s));
 #pragma unroll
         for (int i = 0; i < 4; ++i) T.v[i] = __builtin_nontemporal_load(reinterpret_cast<const vraw_t*>(vt + i * D));
       } else {
@@ -301,10 +302,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         const int last = c.c1 - 1;
         const kv_t* kb = PAGED ? c.kg + (tr - t0) * D : c.kg;
         const kv_t* vb = PAGED ? c.vg + (tr - t0) * D : c.vg;
-        const kv_t* kt = kb + (int64_t)min(t0 + m16, last) * D + q4 * (D / 4);
+        const kv_t* kt = kb + (int64_t)min(t0 + m16, last) * D + 16 * q4;
 #pragma unroll
         for (int s = 0; s < D / 64; ++s)
-          T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 16 * s));
+          T.k[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + 64 * s));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           T.v[i] = __builtin_nontemporal_load(
