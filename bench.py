@@ -53,10 +53,14 @@ def traffic_profile(key: str) -> str:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode kernels' sources with comments and layout removed,
+    so that it changes with the code and not with its comments."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gqa_mqa_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gqa_mqa_kv_amd", "csrc", f)) as fh:
+            t = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
     return h.hexdigest()[:16]
 
 

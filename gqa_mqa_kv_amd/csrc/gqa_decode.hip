@@ -173,7 +173,8 @@ typedef void (*kernel_fn)(gqa::Problem);
 // one block of 16 heads (G <= 16) or two (G <= 64); beyond 32 heads the four
 // wavefronts form two head groups.  Each wavefront holds two tile batches in
 // registers (the one it computes and the next one, loading), which leaves
-// room for one wavefront per SIMD; two tiles per batch fit for G <= 16 only.
+// room for one wavefront per SIMD; two tiles per batch fit up to G = 32 (the
+// two-block variant then holds 502 of its 512 registers).
 int max_waves(int) { return 4; }
 // One-byte tiles hold half the registers and half the bytes of bf16 ones,
 // so the one-block E4M3 variant loads two per batch by default (measured:

@@ -130,9 +130,10 @@ typedef struct gqa_dims {
                               load batch of each wavefront of the matrix-core
                               kernel.  A wavefront computes one batch while
                               the next one loads.  bf16 caches: default 1,
-                              at most 2 for G <= 16, else 1.  E4M3 caches
+                              at most 2 for G <= 32, else 1.  E4M3 caches
                               (gqa_decode_fp8): default 2 and at most 4
-                              for G <= 16, else 1.  Larger requests run at the
+                              for G <= 16; default 1 and at most 2 for
+                              G <= 32; else 1.  Larger requests run at the
                               variant's limit. */
   int32_t merge;           /* gqa_merge */
   int32_t workgroups_per_cu; /* 0: default (1); else matrix-core workgroups
