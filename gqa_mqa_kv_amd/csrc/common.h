@@ -312,26 +312,51 @@ __device__ __forceinline__ f32x2 load2_coherent(Rsrc r, int idx) {
   return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, idx * 4, 0, kPolicySc1));
 }
 
-// Combined output columns c .. c+3 (c a multiple of 4) of head hd of a split
-// unit: the pieces of workgroups w0 .. w_last (w0's in slot first_slot,
-// workgroup w's in slot 2w) merged in piece order,
+// Partial merge state of output columns c .. c+3 of one head: the running
+// maximum M, the denominator sum_k 2^(m_k - M) l_k and the numerator
+// sum_k 2^(m_k - M) O_k.  Empty: M = -inf, den = 0, num = 0.
+struct MergeAcc {
+  float M, den;
+  f32x4 num;
+};
+// Two partial states combined (commutative: a + b and b + a round alike, so
+// both lanes of a butterfly obtain the same bits).
+__device__ __forceinline__ MergeAcc merge_combine(const MergeAcc& x, const MergeAcc& y) {
+  MergeAcc r;
+  r.M = fmaxf(x.M, y.M);
+  const float a = x.M == -INFINITY ? 0.f : exp2f(x.M - r.M);
+  const float b = y.M == -INFINITY ? 0.f : exp2f(y.M - r.M);
+  r.den = x.den * a + y.den * b;
+  r.num = x.num * a + y.num * b;
+  return r;
+}
+// The normalised output of a complete state (0 when no token contributed).
+__device__ __forceinline__ f32x4 merge_finish(const Problem& p, const MergeAcc& s) {
+  const float inv = s.den > 0.f ? p.out_mul / s.den : 0.f;
+  return s.num * inv;
+}
+
+// Merge state of output columns c .. c+3 (c a multiple of 4) of head hd of a
+// split unit over the pieces of workgroups w_first, w_first + stride, ...
+// up to w_last (workgroup w0's piece is in slot first_slot, workgroup w's in
+// slot 2w), in that order:
 //   M = max_k m_k,  out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k,
 // with a running maximum.  The loads of kMergeBatch pieces are issued
-// together (indices past the last piece are clamped to it and their values
-// unused).  COHERENT: the pieces were published with the sc1 stores above.
+// together (indices past the last piece are clamped to an in-bounds piece and
+// their values unused).  COHERENT: the pieces were published with the sc1
+// stores above.
 constexpr int kMergeBatch = 8;
 template <bool COHERENT>
-__device__ __forceinline__ f32x4 merge_pieces(const Problem& p, int64_t w0, int64_t w_last, int64_t first_slot, int hd,
-                                              int c, int D) {
+__device__ __forceinline__ MergeAcc merge_pieces(const Problem& p, int64_t w0, int64_t w_first, int64_t w_last,
+                                                 int stride, int64_t first_slot, int hd, int c, int D) {
   const int G = p.G;
-  float M = -INFINITY, den = 0.f;
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t wb = w0; wb <= w_last; wb += kMergeBatch) {
+  MergeAcc acc{-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int64_t wb = w_first; wb <= w_last; wb += (int64_t)kMergeBatch * stride) {
     f32x2 ml[kMergeBatch];
     f32x4 ok[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int64_t w = min(wb + u, w_last);
+      const int64_t w = min(wb + (int64_t)u * stride, w_last);
       const int64_t slot = w == w0 ? first_slot : 2 * w;
       if (COHERENT) {
         ml[u] = load2_coherent(slot_rsrc(p.ws_ml + slot * G * 2, G * 2), 2 * hd);
@@ -345,17 +370,16 @@ __device__ __forceinline__ f32x4 merge_pieces(const Problem& p, int64_t w0, int6
     // branch: a branch would let the compiler sink each load to its use.
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const bool real = wb + u <= w_last;
-      const float Mn = real ? fmaxf(M, ml[u][0]) : M;
-      const float a = real ? exp2f(M - Mn) : 1.f;   // M = -inf on the first piece: a = 0
+      const bool real = wb + (int64_t)u * stride <= w_last;
+      const float Mn = real ? fmaxf(acc.M, ml[u][0]) : acc.M;
+      const float a = real ? exp2f(acc.M - Mn) : 1.f;   // M = -inf on the first piece: a = 0
       const float f = real ? exp2f(ml[u][0] - Mn) : 0.f;
-      num = num * a + f * ok[u];
-      den = den * a + f * ml[u][1];
-      M = Mn;
+      acc.num = acc.num * a + f * ok[u];
+      acc.den = acc.den * a + f * ml[u][1];
+      acc.M = Mn;
     }
   }
-  const float inv = den > 0.f ? p.out_mul / den : 0.f;
-  return num * inv;
+  return acc;
 }
 
 // Final store of four consecutive output columns.
@@ -396,7 +420,8 @@ __device__ __forceinline__ void fused_merge(const Problem& p, int64_t w0, int64_
   // four columns per thread
   const int nq = G * D / 4;
   for (int q = threadIdx.x; q < nq; q += NT)
-    store_out4(p, orow + 4 * q / D, 4 * q % D, D, merge_pieces<true>(p, w0, w_last, first_slot, 4 * q / D, 4 * q % D, D));
+    store_out4(p, orow + 4 * q / D, 4 * q % D, D,
+               merge_finish(p, merge_pieces<true>(p, w0, w0, w_last, 1, first_slot, 4 * q / D, 4 * q % D, D)));
   if (threadIdx.x == 0) __hip_atomic_store(p.ws_cnt + w0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -440,10 +465,27 @@ __global__ __launch_bounds__(256) void gqa_merge_spans(Problem p) {
   const int nq = p.G * D / 4;
   const int H = (int)(w_last - w0), h = (int)(m - w0 - 1);
   const int per = (nq + H - 1) / H;
-  const int q1 = min(nq, (h + 1) * per);
-  for (int q = h * per + (int)threadIdx.x; q < q1; q += NT) {
-    const f32x4 v = merge_pieces<false>(p, w0, w_last, first_slot, 4 * q / D, 4 * q % D, D);
-    store_out4(p, orow + 4 * q / D, 4 * q % D, D, v);
+  const int q0 = h * per, q1 = min(nq, (h + 1) * per);
+  // S lanes (adjacent, a power of two up to 16) share each group of four
+  // columns: lane k of the S merges pieces w0 + k, w0 + k + S, ..., then a
+  // butterfly over the S lanes combines their states, so a unit of many
+  // pieces needs few dependent load rounds per lane.
+  int S = 1;
+  while (S < 16 && 2 * S * (q1 - q0) <= NT) S *= 2;
+  const int sub = (int)threadIdx.x % S;
+  const int groups = NT / S;
+  for (int qb = q0; qb < q1; qb += groups) {   // uniform trip count: every lane reaches the shuffles
+    const int q = min(qb + (int)threadIdx.x / S, q1 - 1);
+    MergeAcc acc = merge_pieces<false>(p, w0, w0 + sub, w_last, S, first_slot, 4 * q / D, 4 * q % D, D);
+    for (int o = 1; o < S; o *= 2) {
+      MergeAcc y;
+      y.M = __shfl_xor(acc.M, o);
+      y.den = __shfl_xor(acc.den, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y.num[e] = __shfl_xor(acc.num[e], o);
+      acc = merge_combine(acc, y);
+    }
+    if (sub == 0 && qb + (int)threadIdx.x / S < q1) store_out4(p, orow + 4 * q / D, 4 * q % D, D, merge_finish(p, acc));
   }
 }
 
