@@ -197,6 +197,53 @@ def test_workgroups_per_cu(per_cu, merge):
         check(x, path="mfma", per_cu=per_cu, merge=merge, label="per_cu %d %s" % (per_cu, merge))
 
 
+@pytest.mark.parametrize("rate", [0.5, 4.0, 7.9, 8.1, 20.0])
+def test_growing_scores_move_the_reference(rate):
+    """Scores that grow by `rate` (base-2 units) per 16-token tile, so the
+    running maximum moves on every tile: below the kernel's rescale slack
+    (8) the reference stays put and the weights grow up to 2^8, above it the
+    state is rescaled on each tile.  Each head of a group grows at its own
+    rate, and spans of 64 tokens split units across workgroups whose states
+    then differ by many powers of two."""
+    B, H_q, H_kv, d, T = 2, 32, 8, 128, 700
+    x = small(B, H_q, H_kv, d, T, seed=int(rate * 10) + 5)
+    x["seq_lens"] = torch.tensor([700, 523], dtype=torch.int32)
+    G = H_q // H_kv
+    gen = torch.Generator().manual_seed(77)
+    u = torch.zeros(d)
+    u[3] = 1.0
+    step = rate / 16 / (x["scale"] * np.log2(np.e))     # score growth per token, in K units
+    t = torch.arange(T, dtype=torch.float32)
+    for b in range(B):
+        for g in range(H_kv):
+            kk = step * t[:, None] * u[None, :] + 0.01 * torch.randn(T, d, generator=gen)
+            x["k"][b, g] = kk.to(x["k"].dtype)
+        for i in range(H_q):
+            x["q"][b, i] = (u * (1.0 + (i % G) / G)).to(x["q"].dtype)
+    for b, n in enumerate(x["seq_lens"].tolist()):
+        x["k"][b, :, n:] = float("nan")
+        x["v"][b, :, n:] = float("nan")
+    for path, span, merge in (("mfma", 0, "auto"), ("mfma", 64, "fused"), ("mfma", 64, "kernel"), ("valu", 64, "auto")):
+        check(x, path=path, chunk_tokens=span, merge=merge, label="growth %.1f %s span %d %s" % (rate, path, span, merge))
+
+
+@pytest.mark.parametrize("shape", [(2, 32, 1, 128, 16000), (2, 16, 2, 128, 9000)], ids=["G32", "G8"])
+@pytest.mark.parametrize("span", [64, 192])
+def test_merge_of_many_pieces(shape, span):
+    """Units split into up to 250 pieces (spans of 64 and 192 tokens): the
+    merge kernel's lanes each take several load rounds of their strided
+    pieces before the butterfly combines them; the fused merge reads them all
+    in one workgroup."""
+    B, H_q, H_kv, d, T = shape
+    x = small(B, H_q, H_kv, d, T, seed=span + H_kv)
+    x["seq_lens"] = torch.tensor([T, T * 2 // 3 + 1], dtype=torch.int32)
+    for b, n in enumerate(x["seq_lens"].tolist()):
+        x["k"][b, :, n:] = float("nan")
+        x["v"][b, :, n:] = float("nan")
+    for merge in ("kernel", "fused"):
+        check(x, path="mfma", chunk_tokens=span, merge=merge, label="many pieces span %d %s" % (span, merge))
+
+
 def test_token_split_with_empty_and_tiny_sequences():
     """Sequences of 0, 1, 15, 16, 17 and many tokens in one batch: the token
     stream skips empty sequences (their outputs are zero) and spans cross
