@@ -235,25 +235,15 @@ struct Piece {
   int npad;        // stream positions of the unit (n, rounded up to 16 for a paged cache)
 };
 
-// The unit holding stream position x (0 <= x < total).
+// The piece of unit (l, b, g) that starts at its token t, at stream
+// position start + t.
 template <bool PAGED>
-__device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, const int32_t* sm_N,
-                                        const TokenSpace& ts, int64_t x) {
+__device__ __forceinline__ Piece fill_piece(const Problem& p, const int32_t* sm_P, const int32_t* sm_N, int l, int b,
+                                            int g, int t, int64_t start) {
   Piece pc;
-  const int l = (int)(x / ts.per_layer);
-  const int64_t r = x - (int64_t)l * ts.per_layer;
-  int lo = 0, hi = p.B - 1;   // largest b with H_kv * P[b] <= r (such b holds tokens)
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)p.H_kv * uniform(sm_P[mid]) <= r) lo = mid; else hi = mid - 1;
-  }
-  const int b = lo;
-  const int32_t pb = uniform(sm_P[b]);
-  const int v = uniform(sm_P[b + 1]) - pb;   // stream positions of each unit of sequence b
-  const int64_t r2 = r - (int64_t)p.H_kv * pb;
-  const int g = (int)(r2 / v);
-  pc.t = (int)(r2 - (int64_t)g * v);
-  pc.start = x - pc.t;
+  const int v = uniform(sm_P[b + 1]) - uniform(sm_P[b]);   // stream positions of each unit of sequence b
+  pc.t = t;
+  pc.start = start;
   pc.npad = v;
   pc.ui.l = l;
   pc.ui.b = b;
@@ -271,6 +261,48 @@ __device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, c
     pc.ui.row0 = ((int64_t)(l * p.B + b) * p.H_kv + g) * p.T_max;
   }
   return pc;
+}
+
+// The unit holding stream position x (0 <= x < total): a binary search over
+// the prefix sums.
+template <bool PAGED>
+__device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, const int32_t* sm_N,
+                                        const TokenSpace& ts, int64_t x) {
+  const int l = (int)(x / ts.per_layer);
+  const int64_t r = x - (int64_t)l * ts.per_layer;
+  int lo = 0, hi = p.B - 1;   // largest b with H_kv * P[b] <= r (such b holds tokens)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)p.H_kv * uniform(sm_P[mid]) <= r) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int32_t pb = uniform(sm_P[b]);
+  const int v = uniform(sm_P[b + 1]) - pb;
+  const int64_t r2 = r - (int64_t)p.H_kv * pb;
+  const int g = (int)(r2 / v);
+  const int t = (int)(r2 - (int64_t)g * v);
+  return fill_piece<PAGED>(p, sm_P, sm_N, l, b, g, t, x - t);
+}
+
+// The unit after pc's in the stream, from its token 0 (the caller knows one
+// exists): the next KV head of the same sequence, else the next sequence
+// with tokens, else the first such sequence of the next layer.  No division
+// and no search: a piece boundary costs a few LDS reads.
+template <bool PAGED>
+__device__ __forceinline__ Piece next_unit(const Problem& p, const int32_t* sm_P, const int32_t* sm_N,
+                                           const Piece& pc) {
+  int l = pc.ui.l, b = pc.ui.b, g = pc.ui.g + 1;
+  if (g == p.H_kv) {
+    g = 0;
+    for (int k = 0; k < p.L * p.B; ++k) {   // sequences without tokens hold no stream positions
+      if (++b == p.B) {
+        b = 0;
+        ++l;
+      }
+      if (uniform(sm_P[b + 1]) != uniform(sm_P[b])) break;
+    }
+  }
+  return fill_piece<PAGED>(p, sm_P, sm_N, l, b, g, 0, pc.start + pc.npad);
 }
 
 // Zero the outputs of sequences with no valid token (every layer), spread

@@ -105,6 +105,17 @@ __device__ __forceinline__ float max_over_rows(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Sum of x over the same four lanes, in every one of them (rows 0 + 1 and
+// 2 + 3 first, then the two halves: every lane adds in the same order).
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Low (hi = false) or high halves of two words, packed: {x0.half, x1.half}.
 template <bool HI>
 __device__ __forceinline__ uint32_t pack_halves(uint32_t x0, uint32_t x1) {
@@ -204,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   typedef typename std::conditional<KV8, uint8_t, uint16_t>::type kv_t;   // one cache element
   typedef typename std::conditional<KV8, Tile16F8<D>, Tile16<D>>::type tile_t;
 
-  __shared__ float sm_slot[(NL > 1 ? HG * (NL / 2) : 1) * SLOT];
+  __shared__ float sm_slot[(NL > 1 ? HG * (NL - 1) : 1) * SLOT];
   __shared__ float sm_wm[NW][HP], sm_wl[NW][HP];
   __shared__ int32_t sm_P[kMaxBatch + 1];
   __shared__ int32_t sm_N[PAGED ? kMaxBatch : 1];
@@ -248,10 +259,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     int c0, c1, ntiles;
     bool whole;
     int slot_id;      // only the first and the last piece of a span can be partial
+    Piece at;         // the unit and the piece's first token
   };
-  auto open_piece = [&](int64_t x) __attribute__((always_inline)) {
-    const Piece pc = locate<PAGED>(p, sm_P, sm_N, ts, x);
+  // The piece of the span that starts at stream position x, located as pc.
+  auto open_at = [&](const Piece& pc, int64_t x) __attribute__((always_inline)) {
     Ctx c;
+    c.at = pc;
     c.x = x;
     c.start = pc.start;
     c.c0 = pc.t;
@@ -261,12 +274,17 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     c.ntiles = (c.c1 - c.c0 + TILE - 1) / TILE;
     c.whole = c.c0 == 0 && c.c1 == pc.ui.n;
     c.slot_id = x == s0 ? 0 : 1;
-    c.w0 = pc.start / ts.span;
-    c.w_last = (pc.start + pc.ui.n - 1) / ts.span;
+    // the workgroups holding the unit's first and last token (a split unit's
+    // merge only)
+    c.w0 = c.whole ? 0 : pc.start / ts.span;
+    c.w_last = c.whole ? 0 : (pc.start + pc.ui.n - 1) / ts.span;
     c.kg = reinterpret_cast<const kv_t*>(p.k) + pc.ui.row0 * D;
     c.vg = reinterpret_cast<const kv_t*>(p.v) + pc.ui.row0 * D;
     c.orow = out_row0(p, pc.ui);
     return c;
+  };
+  auto open_piece = [&](int64_t x) __attribute__((always_inline)) {
+    return open_at(locate<PAGED>(p, sm_P, sm_N, ts, x), x);
   };
   // B operands of the score product: query head head0 + 16 hb, columns 32s + 8q4 .. +7.
   auto load_q = [&](u32x4 (&qf)[HB][KS], const Ctx& c) __attribute__((always_inline)) {
@@ -462,9 +480,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   auto end_piece = [&](const Ctx& c) __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      float lt = l_run[hb];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = sum_over_rows(l_run[hb]);
       if (q4 == 0) {
         sm_wm[wave][hb * 16 + m16] = m_run[hb];
         sm_wl[wave][hb * 16 + m16] = lt;
@@ -490,12 +506,14 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 #pragma unroll
       for (int r = 0; r < VW; ++r) oacc[r][hb] *= f;
     }
-    // Tree over the tile lanes of each head group: in each round the upper
-    // half hands its O to the lower half.
-#pragma unroll
-    for (int s = NL / 2; s >= 1; s /= 2) {
-      if (tl >= s && tl < 2 * s) {
-        float* dst = sm_slot + (hg * (NL / 2) + (tl - s)) * SLOT + lane;
+    // One round: every tile lane of a head group but the first leaves its O
+    // in an LDS slot of its own, and the first adds them in lane order.  The
+    // other lanes go straight on to the next piece; the slots are rewritten
+    // only after the next piece's first barrier, which the first lane reaches
+    // after its reads.
+    if constexpr (NL > 1) {
+      if (tl > 0) {
+        float* dst = sm_slot + (hg * (NL - 1) + (tl - 1)) * SLOT + lane;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -504,16 +522,18 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
             for (int i = 0; i < 4; ++i) dst[((hb * VW + r) * 4 + i) * 64] = oacc[r][hb][i];
       }
       __syncthreads();
-      if (tl < s) {
-        const float* src = sm_slot + (hg * (NL / 2) + tl) * SLOT + lane;
+      if (tl == 0) {
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+        for (int k = 0; k < NL - 1; ++k) {
+          const float* src = sm_slot + (hg * (NL - 1) + k) * SLOT + lane;
 #pragma unroll
-          for (int r = 0; r < VW; ++r)
+          for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) oacc[r][hb][i] += src[((hb * VW + r) * 4 + i) * 64];
+            for (int r = 0; r < VW; ++r)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) oacc[r][hb][i] += src[((hb * VW + r) * 4 + i) * 64];
+        }
       }
-      __syncthreads();
     }
 
     // Lane (q4, m16) holds head head0 + 16 hb of each block, columns D/16*(4*q4+i) + r.
@@ -613,7 +633,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     const int64_t xn = PAGED ? pc.next : pc.x + (pc.c1 - pc.c0);
     if (piece_done && xn >= s1) return false;
     if (piece_done) {
-      const Ctx pn = open_piece(xn);
+      // the piece ran to its unit's end: the next one starts the next unit
+      const Ctx pn = open_at(next_unit<PAGED>(p, sm_P, sm_N, pc.at), xn);
       fetch_pages(pid, pn, tl);
       load_batch(nxt, pn, tl, pid);
       fetch_pages(pid, pn, tl + NL * TPW);
