@@ -426,6 +426,41 @@ def test_full_llama3_8b_layer():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("layout", ["dense", "paged", "e4m3"])
+@pytest.mark.parametrize("B,lo,hi", [(1024, 64, 64), (2048, 1, 100), (256, 256, 256)])
+def test_many_short_units_every_head(B, lo, hi, layout):
+    """Many short units in the planner's launch (one workgroup per CU): each
+    span holds tens of whole units, so the incremental step to the next unit
+    and the per-piece combine run thousands of times; every head against the
+    oracle, for the plain cache, the same cache in shuffled pages of 16 and
+    as E4M3 codes."""
+    w = workloads.Workload("short-units", B, 32, 8, 128, lo, hi, torch.bfloat16, 1234 + B + hi)
+    x = workloads.generate(w, "cpu", poison_padding=True)
+    xd = to_dev(x)
+    note("short units", B, lo, hi, layout)
+    orc = oracle.default()
+    if layout == "dense":
+        run = lambda dt: gqa.decode(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], out_dtype=dt)
+        ref = orc.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+    elif layout == "paged":
+        kp, vp, tb = workloads.to_pages(x, 16, seed=B)
+        kpd, vpd, tbd = kp.to(DEV), vp.to(DEV), tb.to(DEV)
+        run = lambda dt: gqa.decode_paged(xd["q"], kpd, vpd, tbd, xd["seq_lens"], x["scale"], out_dtype=dt,
+                                          max_seq_len=hi)
+        ref = orc.decode_paged(x["q"], kp, vp, tb, 16, x["seq_lens"], x["scale"])
+    else:
+        x8 = workloads.to_e4m3(x)
+        k8, v8 = x8["k"].to(DEV), x8["v"].to(DEV)
+        run = lambda dt: gqa.decode_fp8(xd["q"], k8, v8, xd["seq_lens"], x["scale"], x8["k_scale"], x8["v_scale"],
+                                        out_dtype=dt)
+        ref = orc.decode_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"], x8["k_scale"], x8["v_scale"])
+    out32, out16 = run(torch.float32), run(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out32.to(torch.bfloat16))
+    assert err(out32, ref) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.timeout(600)
 def test_full_llama3_8b_layer_fp32_inputs():
     """fp32 copy of the same shape at the fp32 bar: one dropped token at
     T = 4096 moves an output by ~1e-3, two orders above 1e-5."""
