@@ -172,14 +172,20 @@ def copy_probe(torch, dev, stream, nbytes: int = 1 << 30, launches: int = 10):
             "bytes_read_and_written": 2 * nbytes}
 
 
-def time_layers_one_by_one(torch, gqa, workloads, w, x, stream, out_dtype, reps: int = 3):
-    """The same step as L launches of one layer each (gqa_decode_layers with
-    L = 1 on each layer's slice), as a model that computes layer l's queries
-    from layer l-1 would issue it."""
+def time_layers_one_by_one(torch, gqa, workloads, w, x, stream, out_dtype, reps: int = 3, fp8: bool = False):
+    """The same step as L launches of one layer each (gqa_decode_layers, or
+    gqa_decode_layers_fp8, with L = 1 on each layer's slice), as a model that
+    computes layer l's queries from layer l-1 would issue it."""
     launchers = []
     for l in range(w.layers):
         xl = workloads.layer_view(x, l)
         extra = dict(kv_offsets=x["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if w.packed else {}
+        if fp8:
+            launchers.append(gqa.prepare_layers_fp8(xl["q"][None], xl["k"][None] if not w.packed else xl["k"],
+                                                    xl["v"][None] if not w.packed else xl["v"], x["seq_lens"],
+                                                    x["scale"], x["k_scale"], x["v_scale"], out_dtype=out_dtype,
+                                                    **extra))
+            continue
         launchers.append(gqa.prepare(xl["q"][None], xl["k"], xl["v"], x["seq_lens"], x["scale"], out_dtype=out_dtype,
                                      **extra))
     for f in launchers:
@@ -269,8 +275,8 @@ def main():
         print("--paged takes a single-layer bf16 workload and a page that is a multiple of 16", file=sys.stderr)
         sys.exit(2)
     fp8 = args.kv == "fp8"
-    if fp8 and (w.layers != 1 or w.packed or w.dtype != torch.bfloat16):
-        print("--kv fp8 takes a single-layer bf16 workload (dense, or paged with --paged)", file=sys.stderr)
+    if fp8 and w.dtype != torch.bfloat16:
+        print("--kv fp8 takes a bf16 workload", file=sys.stderr)
         sys.exit(2)
     out_dtype = {None: w.dtype, "bf16": torch.bfloat16, "fp32": torch.float32}[args.out_dtype]
     seq_lens = workloads.seq_lens_for(w)
@@ -290,9 +296,14 @@ def main():
     launchers = []
     for r, x in enumerate(batches):
         if fp8:
-            x8 = workloads.to_e4m3(x)
-            del x["k"], x["v"]   # the E4M3 copy holds the cache now
-            if args.paged:
+            x8 = workloads.to_e4m3(x, release=True)   # the E4M3 copy holds the cache now
+            batches[r] = x8
+            if w.layers > 1:
+                extra = dict(kv_offsets=x["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if w.packed else {}
+                launchers.append(gqa.prepare_layers_fp8(x["q"], x8["k"], x8["v"], x["seq_lens"], x["scale"],
+                                                        x8["k_scale"], x8["v_scale"], out_dtype=out_dtype,
+                                                        chunk_tokens=args.chunk_tokens, **extra))
+            elif args.paged:
                 kp, vp, table = workloads.to_pages(x8, args.paged, seed=1000 + r, spare=1)
                 del x8["k"], x8["v"]
                 launchers.append(gqa.prepare_paged_fp8(x["q"], kp, vp, table, x["seq_lens"], x["scale"],
@@ -392,7 +403,7 @@ def main():
         result["hbm_copy_probe"] = probe
     if w.layers > 1 and not args.no_extras:
         result["sequential_single_layer_launches"] = time_layers_one_by_one(torch, gqa, workloads, w, batches[0],
-                                                                            stream, out_dtype)
+                                                                            stream, out_dtype, fp8=fp8)
     if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged and not fp8 and not args.no_extras:
         result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:

@@ -16,12 +16,16 @@ held in fixed-size pages of a pool through a per-sequence table of page ids
 (append_rope_paged appends to such a cache).
 decode_fp8 reads a cache of one-byte E4M3 elements with one scale for the
 keys and one for the values (the bytes-per-element term of section 1 of the
-same page, halved).
+same page, halved); decode_layers_fp8 does the same for the layer-batched
+call.
 """
 from ._binding import (GqaDims, GqaError, Prepared, append_rope, append_rope_fp8, append_rope_paged,
-                       append_rope_paged_fp8, decode, decode_fp8,
-                       decode_layers, decode_paged, decode_paged_fp8, default_workspace, lib, make_dims, plan, prepare,
-                       prepare_append, prepare_fp8, prepare_paged, prepare_paged_fp8, status_string, workspace_bytes)
+                       append_rope_paged_fp8, decode, decode_fp8, decode_layers, decode_layers_fp8, decode_paged,
+                       decode_paged_fp8, default_workspace, lib, make_dims, plan, prepare, prepare_append,
+                       prepare_fp8, prepare_layers_fp8, prepare_paged, prepare_paged_fp8, status_string,
+                       workspace_bytes)
 
-__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "decode_paged", "decode_fp8", "decode_paged_fp8", "append_rope", "append_rope_fp8", "append_rope_paged", "append_rope_paged_fp8", "default_workspace",
-           "lib", "make_dims", "plan", "prepare_append", "prepare_fp8", "prepare_paged", "prepare_paged_fp8", "status_string", "workspace_bytes"]
+__all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_layers", "decode_layers_fp8",
+           "decode_paged", "decode_fp8", "decode_paged_fp8", "append_rope", "append_rope_fp8", "append_rope_paged",
+           "append_rope_paged_fp8", "default_workspace", "lib", "make_dims", "plan", "prepare_append", "prepare_fp8",
+           "prepare_layers_fp8", "prepare_paged", "prepare_paged_fp8", "status_string", "workspace_bytes"]

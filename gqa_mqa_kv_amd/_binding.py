@@ -21,7 +21,8 @@ MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
 SYMBOLS = ("gqa_append_rope", "gqa_append_rope_fp8", "gqa_append_rope_paged", "gqa_append_rope_paged_fp8",
-           "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_paged", "gqa_decode_paged_fp8",
+           "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8", "gqa_decode_paged",
+           "gqa_decode_paged_fp8",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
 
 
@@ -58,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_layers.restype = ctypes.c_int
         L.gqa_decode_layers.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_layers_fp8.restype = ctypes.c_int
+        L.gqa_decode_layers_fp8.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                            vp, dims_p, vp, sz, vp]
         L.gqa_decode_paged.restype = ctypes.c_int
         L.gqa_decode_paged.argtypes = [vp, vp, vp, vp, i32, i32, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_paged_fp8.restype = ctypes.c_int
@@ -282,15 +286,10 @@ def decode_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, scale: float, k_s
     return keep[0]
 
 
-def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len: Optional[int] = None,
-                  num_kv_heads: Optional[int] = None, out=None, out_dtype=None, chunk_tokens: int = 0,
-                  path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
-           tiles: int = 0, merge: str = "auto", per_cu: int = 0):
-    """One decode step of L independent layers in one launch.  q [L,B,H_q,d].
-    Dense caches are [L,B,H_kv,T_max,d]; with ``kv_offsets`` (int64 [B+1] on
-    the device) the caches are packed (any shape holding L*kv_offsets[B]*H_kv*d
-    elements), and ``max_seq_len`` (the largest capacity) and ``num_kv_heads``
-    must be given."""
+def _layers_args(q, k_cache, v_cache, seq_lens, scale, kv_offsets, max_seq_len, num_kv_heads, out, out_dtype,
+                 chunk_tokens, path, seq_len_hint, workspace, stream, waves, tiles, merge, per_cu, scales=None):
+    """Validated arguments of gqa_decode_layers, or of gqa_decode_layers_fp8
+    when ``scales`` = (k_scale, v_scale)."""
     dev = q.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
         _require(t, n, dev)
@@ -312,21 +311,54 @@ def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, 
         H_kv, T_max = num_kv_heads, max_seq_len
     if seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be int32 [B]")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise TypeError("q, k_cache and v_cache must share one dtype")
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge, per_cu)
+    if scales is None:
+        if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+            raise TypeError("q, k_cache and v_cache must share one dtype")
+    elif q.dtype != torch.bfloat16 or k_cache.dtype not in E4M3_DTYPES or v_cache.dtype not in E4M3_DTYPES:
+        raise TypeError("expected bf16 q and one-byte E4M3 caches (uint8 or float8_e4m3fn)")
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge,
+                     per_cu)
     if out is None:
         out = torch.empty(L, B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
     _require(out, "out", dev)
     if out.shape != (L, B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [L,B,H_q,d] of the output dtype")
-    need = workspace_bytes(dims, L)
-    ws = default_workspace(need, dev) if workspace is None else workspace
+    ws = default_workspace(workspace_bytes(dims, L), dev) if workspace is None else workspace
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    _check(lib().gqa_decode_layers(int(L), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
-                                   float(scale), _ptr(out), ctypes.byref(dims), _ptr(ws),
-                                   0 if ws is None else ws.numel() * ws.element_size(), s))
-    return out
+    sc = () if scales is None else (float(scales[0]), float(scales[1]))
+    args = (int(L), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens), float(scale)) + sc + (
+        _ptr(out), ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
+    return args, (out, q, k_cache, v_cache, kv_offsets, seq_lens, ws, dims)
+
+
+def decode_layers(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len: Optional[int] = None,
+                  num_kv_heads: Optional[int] = None, out=None, out_dtype=None, chunk_tokens: int = 0,
+                  path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
+                  tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """One decode step of L independent layers in one launch.  q [L,B,H_q,d].
+    Dense caches are [L,B,H_kv,T_max,d]; with ``kv_offsets`` (int64 [B+1] on
+    the device) the caches are packed (any shape holding L*kv_offsets[B]*H_kv*d
+    elements), and ``max_seq_len`` (the largest capacity) and ``num_kv_heads``
+    must be given."""
+    args, keep = _layers_args(q, k_cache, v_cache, seq_lens, scale, kv_offsets, max_seq_len, num_kv_heads, out,
+                              out_dtype, chunk_tokens, path, seq_len_hint, workspace, stream, waves, tiles, merge,
+                              per_cu)
+    _check(lib().gqa_decode_layers(*args))
+    return keep[0]
+
+
+def decode_layers_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_scale: float, kv_offsets=None,
+                      max_seq_len: Optional[int] = None, num_kv_heads: Optional[int] = None, out=None,
+                      out_dtype=None, chunk_tokens: int = 0, seq_len_hint: int = 0, workspace=None, stream=None,
+                      tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """decode_layers over one-byte OCP E4M3 caches (uint8 or float8_e4m3fn, in
+    the dense or packed layout), with the scales of decode_fp8 shared by every
+    layer.  q bf16 [L,B,H_q,d]."""
+    args, keep = _layers_args(q, k_cache, v_cache, seq_lens, scale, kv_offsets, max_seq_len, num_kv_heads, out,
+                              out_dtype, chunk_tokens, "mfma", seq_len_hint, workspace, stream, 0, tiles, merge, per_cu,
+                              (k_scale, v_scale))
+    _check(lib().gqa_decode_layers_fp8(*args))
+    return keep[0]
 
 
 def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
@@ -548,6 +580,18 @@ def prepare_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_s
     args, keep = _fp8_args(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, None, out_dtype, chunk_tokens,
                            seq_len_hint, None, stream, tiles, merge, per_cu)
     pr = Prepared(lib().gqa_decode_fp8, args, keep)
+    pr()
+    return pr
+
+
+def prepare_layers_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_scale: float, kv_offsets=None,
+                       max_seq_len=None, num_kv_heads=None, out_dtype=None, chunk_tokens: int = 0,
+                       seq_len_hint: int = 0, stream=None, tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """As prepare, for gqa_decode_layers_fp8."""
+    args, keep = _layers_args(q, k_cache, v_cache, seq_lens, scale, kv_offsets, max_seq_len, num_kv_heads, None,
+                              out_dtype, chunk_tokens, "mfma", seq_len_hint, None, stream, 0, tiles, merge, per_cu,
+                              (k_scale, v_scale))
+    pr = Prepared(lib().gqa_decode_layers_fp8, args, keep)
     pr()
     return pr
 

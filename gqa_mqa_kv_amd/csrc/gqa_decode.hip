@@ -403,6 +403,22 @@ gqa_status gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cach
 
 namespace {
 // e4m3: the caches hold one-byte E4M3 codes of key / k_scale and value / v_scale.
+gqa_status gqa_decode_layers_fp8(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
+                                 const int64_t* kv_offsets, const int32_t* seq_lens, float scale, float k_scale,
+                                 float v_scale, void* out, const gqa_dims* dims, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  gqa_status st = check_dims(dims, num_layers);
+  if (st != GQA_OK) return st;
+  if (dims->dtype != GQA_DTYPE_BF16 || !use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // matrix-core kernel only
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale)) return GQA_ERR_INVALID_ARG;
+  CacheArgs ca;
+  ca.kv_offsets = kv_offsets;
+  ca.e4m3 = true;
+  ca.k_scale = k_scale;
+  ca.v_scale = v_scale;
+  return launch(num_layers, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+}
+
 gqa_status append_launch(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int64_t* kv_offsets, const int32_t* block_table, int32_t max_pages, int32_t page,
                          const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, void* q_out,

@@ -235,23 +235,41 @@ def to_pages(inputs: dict, page: int, seed: int, spare: int = 3, share_first_pag
 E4M3_MAX = 448.0   # largest finite OCP E4M3 value
 
 
+_E4M3_CHUNK = 1 << 26   # elements converted at a time (bounds the float32 temporaries)
+
+
 def quantize_e4m3(x: torch.Tensor):
     """``x`` as one-byte OCP E4M3 codes and one scale: scale = max|x| / 448
     over the finite elements (a float32 value), codes = torch's
     round-to-nearest-even conversion of x / scale to float8_e4m3fn, as uint8.
-    Non-finite elements become NaN codes.  Returns (codes, scale)."""
-    xf = x.float()
-    fin = torch.isfinite(xf)
-    amax = float(xf[fin].abs().max()) if bool(fin.any()) else 0.0
+    Non-finite elements become NaN codes.  Returns (codes, scale).  Works
+    through x in slices, so a cache of any size needs only its codes as
+    extra memory."""
+    flat = x.reshape(-1)
+    amax = 0.0
+    for i in range(0, flat.numel(), _E4M3_CHUNK):
+        xf = flat[i:i + _E4M3_CHUNK].float()
+        fin = torch.isfinite(xf)
+        if bool(fin.any()):
+            amax = max(amax, float(xf[fin].abs().max()))
     scale = float(torch.tensor(amax / E4M3_MAX if amax > 0 else 1.0, dtype=torch.float32))
-    y = torch.where(fin, xf / scale, torch.full_like(xf, float("nan")))
-    return y.to(torch.float8_e4m3fn).view(torch.uint8), scale
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    cf = codes.view(-1)
+    for i in range(0, flat.numel(), _E4M3_CHUNK):
+        xf = flat[i:i + _E4M3_CHUNK].float()
+        y = torch.where(torch.isfinite(xf), xf / scale, torch.full_like(xf, float("nan")))
+        cf[i:i + _E4M3_CHUNK] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
 
 
-def to_e4m3(inputs: dict) -> dict:
+def to_e4m3(inputs: dict, release: bool = False) -> dict:
     """A copy of ``inputs`` whose k and v are E4M3 codes (uint8, same layout)
-    with their scales k_scale and v_scale; NaN padding stays NaN."""
+    with their scales k_scale and v_scale; NaN padding stays NaN.  release:
+    drop ``inputs``' k (v) as soon as its codes exist, so that a cache near
+    the device's capacity is never held twice."""
     out = dict(inputs)
-    out["k"], out["k_scale"] = quantize_e4m3(inputs["k"])
-    out["v"], out["v_scale"] = quantize_e4m3(inputs["v"])
+    for name in ("k", "v"):
+        out[name], out[name + "_scale"] = quantize_e4m3(inputs[name])
+        if release:
+            inputs[name] = None
     return out

@@ -31,7 +31,7 @@
  *   q, k_cache, v_cache and out must be 16-byte aligned; out must not
  *   overlap any input.
  * Types.  q, k_cache and v_cache share dims->dtype (fp32 or bf16), except
- *   in gqa_decode_fp8, whose caches hold one-byte E4M3 elements; out has
+ *   in the *_fp8 decode calls, whose caches hold one-byte E4M3 elements; out has
  *   dims->out_dtype.  Products, softmax and sums are accumulated in fp32; a
  *   bf16 output is rounded to nearest-even.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
@@ -214,6 +214,21 @@ gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_ca
 gqa_status gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, float scale,
                           float k_scale, float v_scale, void* out, const gqa_dims* dims, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_decode_layers over caches of one-byte E4M3 elements: the dense
+ * [L][B][H_kv][T_max][d] or packed (kv_offsets) layouts of gqa_decode_layers,
+ * counted in bytes, with the element format and scales of gqa_decode_fp8.
+ * One k_scale and one v_scale hold for every layer of the call (layers with
+ * scales of their own are separate calls).  q, out: [L][B][H_q][d], q bf16.
+ * Matrix-core path only (GQA_ERR_UNSUPPORTED otherwise); workspace
+ * gqa_decode_workspace_bytes(dims, num_layers).  The result equals
+ * num_layers separate gqa_decode_fp8 calls on the layers' caches.
+ */
+gqa_status gqa_decode_layers_fp8(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
+                                 const int64_t* kv_offsets, const int32_t* seq_lens, float scale, float k_scale,
+                                 float v_scale, void* out, const gqa_dims* dims, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * gqa_decode_fp8 with the cache held in pages of a pool: the pools are one

@@ -265,6 +265,30 @@ def test_decode_fp8_validation():
     assert call_fp8(dims(B=0), [None] * 5) == OK
 
 
+def test_decode_layers_fp8_validation():
+    """The layer-batched E4M3 entry point: the checks of gqa_decode_fp8, a
+    positive layer count, and the packed layout's offsets aligned."""
+    d = dims()
+    call = lambda dd=d, L=3, offs=None, ptrs=None, scale=0.125, ks=0.01, vs=0.02: gqa.lib().gqa_decode_layers_fp8(
+        L, *(ptrs or [FAKE] * 5)[:3], offs, FAKE if ptrs is None else ptrs[3], scale, ks, vs,
+        FAKE if ptrs is None else ptrs[4], ctypes.byref(dd), None, 0, None)
+    assert call() == WORKSPACE                                          # dense layers: only the workspace is missing
+    assert call(offs=FAKE) == WORKSPACE                                 # packed
+    assert call(offs=FAKE + 4) == INVALID                               # offsets not 8-byte aligned
+    assert call(L=0) == INVALID
+    assert call(dims(dtype=torch.float32)) == UNSUPPORTED
+    assert call(dims(path="valu")) == UNSUPPORTED
+    for bad in (float("nan"), float("inf")):
+        assert call(ks=bad) == INVALID
+        assert call(vs=bad) == INVALID
+        assert call(scale=bad) == INVALID
+    for pos in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[pos] = None
+        assert call(ptrs=ptrs) == INVALID, pos
+    assert call(dims(B=0), ptrs=[None] * 5) == OK
+
+
 def test_decode_paged_fp8_validation():
     """The paged E4M3 entry point applies the rules of both parents."""
     d = dims(T_max=1024)

@@ -257,3 +257,79 @@ def test_full_llama3_8b_layer_paged_fp8():
         e = max(e, float(np.abs(o32[b, i].double().cpu().numpy() - ref).max()))
     note("full-fp8-paged", w.name, "max err %.3e" % e)
     assert e <= TOL
+
+
+# ------------------------------------------------------------ layer batches --
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("H_kv", [8, 1])
+@pytest.mark.parametrize("span,merge", [(0, "auto"), (192, "fused"), (192, "kernel")])
+def test_layers_fp8(packed, H_kv, span, merge):
+    """gqa_decode_layers_fp8: four layers of E4M3 caches (one scale pair for
+    all of them), dense and packed, G = 4 and G = 32, the planner's split
+    and forced spans with both merges; each layer against the oracle on the
+    same bytes."""
+    w = workloads.Workload("layers-fp8", 3, 32, H_kv, 128, 100, 900, torch.bfloat16, 61 + H_kv, layers=4,
+                           packed=packed)
+    x8 = workloads.to_e4m3(workloads.generate(w, "cpu", poison_padding=True))
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x8.items()}
+    note("layers fp8", packed, H_kv, span, merge)
+    kw = dict(kv_offsets=xd["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if packed else {}
+    run = lambda dt: gqa.decode_layers_fp8(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x8["scale"], x8["k_scale"],
+                                           x8["v_scale"], out_dtype=dt, chunk_tokens=span, merge=merge, **kw)
+    out32, out16 = run(torch.float32), run(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out16.cpu(), out32.cpu().to(torch.bfloat16)), "bf16 out is not RNE(fp32 out)"
+    orc = oracle.default()
+    for l in range(w.layers):
+        xl = workloads.layer_view(x8, l)
+        ref = orc.decode_fp8(xl["q"], xl["k"], xl["v"], x8["seq_lens"], x8["scale"], x8["k_scale"], x8["v_scale"],
+                             kv_offsets=x8["kv_offsets"].numpy() if packed else None, num_kv_heads=w.H_kv)
+        e = float(np.abs(out32[l].double().cpu().numpy() - ref).max())
+        assert e <= TOL, "layer %d: max err %.3e" % (l, e)
+
+
+@pytest.mark.timeout(900)
+def test_full_32_layer_stack_fp8():
+    """The 32-layer packed stack with its cache as E4M3 codes (about 77 GB),
+    one launch; outputs checked on sampled (layer, sequence, head) triples
+    against the oracle on the same bytes."""
+    w = workloads.WORKLOADS["llama3-8b-32-layer-stack"]
+    torch.cuda.empty_cache()
+    free, total = torch.cuda.mem_get_info(DEV)
+    sl = workloads.seq_lens_for(w)
+    need = 2 * w.layers * int(sl.sum()) * w.H_kv * w.d * 2 + w.layers * int(sl.sum()) * w.H_kv * w.d
+    if need > free - (8 << 30):
+        pytest.skip("needs %.1f GB of device memory, %.1f free" % (need / 1e9, free / 1e9))
+    note("full fp8", w.name, "generate")
+    x = workloads.generate(w, DEV)
+    x8 = workloads.to_e4m3(x, release=True)
+    del x
+    torch.cuda.empty_cache()
+    note("full fp8", w.name, "decode")
+    out = gqa.decode_layers_fp8(x8["q"], x8["k"], x8["v"], x8["seq_lens"], x8["scale"], x8["k_scale"],
+                                x8["v_scale"], kv_offsets=x8["kv_offsets"], max_seq_len=w.T_max,
+                                num_kv_heads=w.H_kv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    off = x8["kv_offsets"].cpu()
+    rows_per_layer = int(off[-1]) * w.H_kv
+    g = torch.Generator().manual_seed(6)
+    orc = oracle.default()
+    e = 0.0
+    for _ in range(24):
+        l = int(torch.randint(w.layers, (1,), generator=g))
+        b = int(torch.randint(w.B, (1,), generator=g))
+        i = int(torch.randint(w.H_q, (1,), generator=g))
+        kv = i // w.G
+        n = int(x8["seq_lens"][b])
+        cap = int(off[b + 1] - off[b])
+        r0 = l * rows_per_layer + int(off[b]) * w.H_kv + kv * cap
+        k1 = x8["k"][r0:r0 + n].cpu().view(1, 1, n, w.d)
+        v1 = x8["v"][r0:r0 + n].cpu().view(1, 1, n, w.d)
+        q1 = x8["q"][l, b:b + 1, i:i + 1].cpu()
+        ref = orc.decode_fp8(q1, k1, v1, torch.tensor([n], dtype=torch.int32), w.scale, x8["k_scale"],
+                             x8["v_scale"])[0, 0]
+        e = max(e, float(np.abs(out[l, b, i].double().cpu().numpy() - ref).max()))
+    note("full fp8", w.name, "max err %.3e" % e)
+    assert e <= TOL
+    del x8
+    torch.cuda.empty_cache()
