@@ -232,6 +232,44 @@ def time_append(torch, gqa, w, x, stream, steps: int, warmup: int):
             "bound": "launch latency (the call moves %d bytes)" % nbytes, "rope_base": 500000.0}
 
 
+def time_fused_append(torch, gqa, w, batches, stream, steps: int, warmup: int):
+    """One decode step including its append: gqa_append_rope then gqa_decode
+    (two launches) against gqa_decode_append_rope (one), over the rotated
+    input batches.  Every sequence holds T_max - 1 tokens and appends one, so
+    the attention covers as many tokens as the plain step.  Both sides rewrite
+    the same cache rows with the same values at every step."""
+    two, one = [], []
+    for x in batches:
+        g = torch.Generator(device=x["q"].device).manual_seed(w.seed + 19)
+        kn = torch.randn(w.B, w.H_kv, w.d, device=x["q"].device, generator=g).to(w.dtype)
+        vn = torch.randn(w.B, w.H_kv, w.d, device=x["q"].device, generator=g).to(w.dtype)
+        lens = torch.full((w.B,), w.T_max - 1, dtype=torch.int32, device=x["q"].device)
+        new_lens = torch.empty_like(lens)
+        q_out = torch.empty_like(x["q"])
+        app = gqa.prepare_append(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, q_out=q_out, new_seq_lens=new_lens)
+        dec = gqa.prepare(q_out, x["k"], x["v"], new_lens, x["scale"])
+        two.append((app, dec))
+        one.append(gqa.prepare_decode_append(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, x["scale"]))
+
+    def run(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+
+    n = len(batches)
+    sep = run(lambda i: (two[i % n][0](), two[i % n][1]()))
+    fused = run(lambda i: one[i % n]())
+    return {"append_then_decode_us_per_step": sep, "fused_us_per_step": fused,
+            "launches": {"append_then_decode": 2, "fused": 1}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +444,8 @@ def main():
                                                                             stream, out_dtype, fp8=fp8)
     if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged and not fp8 and not args.no_extras:
         result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
+        result["step_with_append"] = time_fused_append(torch, gqa, w, batches, stream, min(args.steps, 100),
+                                                       args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

@@ -21,7 +21,8 @@ MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
 SYMBOLS = ("gqa_append_rope", "gqa_append_rope_fp8", "gqa_append_rope_paged", "gqa_append_rope_paged_fp8",
-           "gqa_decode", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8", "gqa_decode_paged",
+           "gqa_decode", "gqa_decode_append_rope", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8",
+           "gqa_decode_paged",
            "gqa_decode_paged_fp8",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
 
@@ -59,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_layers.restype = ctypes.c_int
         L.gqa_decode_layers.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_append_rope.restype = ctypes.c_int
+        L.gqa_decode_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp,
+                                             dims_p, vp, sz, vp]
         L.gqa_decode_layers_fp8.restype = ctypes.c_int
         L.gqa_decode_layers_fp8.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                             vp, dims_p, vp, sz, vp]
@@ -419,6 +423,84 @@ def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k
     return q_out, new_seq_lens
 
 
+def _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets, max_seq_len, q_out,
+                        new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream, tiles, merge, per_cu):
+    dev = q.device
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k_new.dim() != 3 or v_new.shape != k_new.shape:
+        raise ValueError("expected q [B,H_q,d] and k_new/v_new [B,H_kv,d]")
+    B, H_q, d = q.shape
+    H_kv = k_new.shape[1]
+    if k_new.shape[0] != B or k_new.shape[2] != d or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("shape mismatch between q, k_new/v_new and seq_lens")
+    if kv_offsets is None:
+        if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.shape[:2] != (B, H_kv) or \
+                k_cache.shape[3] != d:
+            raise ValueError("dense caches must be [B,H_kv,T_max,d]")
+        T_max = k_cache.shape[2]
+    else:
+        _require(kv_offsets, "kv_offsets", dev)
+        if kv_offsets.dtype != torch.int64 or kv_offsets.shape != (B + 1,) or max_seq_len is None:
+            raise ValueError("packed caches need kv_offsets int64 [B+1] and max_seq_len")
+        if v_cache.numel() != k_cache.numel() or k_cache.numel() % (H_kv * d):
+            raise ValueError("packed cache size mismatch")
+        T_max = max_seq_len
+    for t in (k_new, v_new, k_cache, v_cache):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k_new, v_new and the caches must share one dtype")
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, 0, chunk_tokens, "mfma", 0, tiles, merge, per_cu)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if new_seq_lens is None:
+        new_seq_lens = torch.empty_like(seq_lens)
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
+    for t, n in ((q_out, "q_out"), (new_seq_lens, "new_seq_lens"), (out, "out")):
+        _require(t, n, dev)
+    if q_out.shape != q.shape or q_out.dtype != q.dtype or new_seq_lens.shape != (B,) or \
+            new_seq_lens.dtype != torch.int32:
+        raise ValueError("q_out must match q and new_seq_lens seq_lens")
+    if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
+        raise ValueError("out must be [B,H_q,d] of the output dtype")
+    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
+            _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out), ctypes.byref(dims), _ptr(ws),
+            0 if ws is None else ws.numel() * ws.element_size(), s)
+    return args, (out, q_out, new_seq_lens, q, k_new, v_new, k_cache, v_cache, kv_offsets, seq_lens, ws, dims)
+
+
+def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, scale: float, kv_offsets=None,
+                       max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, out=None, out_dtype=None,
+                       chunk_tokens: int = 0, workspace=None, stream=None, tiles: int = 0, merge: str = "auto",
+                       per_cu: int = 0):
+    """append_rope followed by decode in one launch (gqa_decode_append_rope):
+    bf16 q [B,H_q,d], k_new/v_new [B,H_kv,d], a plain [B,H_kv,T_max,d] or
+    packed (``kv_offsets``, ``max_seq_len``) cache written in place.  Returns
+    (out, q_out, new_seq_lens); q_out and new_seq_lens are new tensors unless
+    given (they may not be q and seq_lens)."""
+    args, keep = _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets,
+                                     max_seq_len, q_out, new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream,
+                                     tiles, merge, per_cu)
+    _check(lib().gqa_decode_append_rope(*args))
+    return keep[0], keep[1], keep[2]
+
+
+def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, scale: float,
+                          kv_offsets=None, max_seq_len=None, out_dtype=None, chunk_tokens: int = 0, stream=None,
+                          tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """As prepare, for gqa_decode_append_rope (each call appends again: the
+    new token overwrites the same cache rows with the same values)."""
+    args, keep = _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets,
+                                     max_seq_len, None, None, None, out_dtype, chunk_tokens, None, stream, tiles, merge,
+                                     per_cu)
+    pr = Prepared(lib().gqa_decode_append_rope, args, keep)
+    pr()
+    return pr
+
+
 def append_rope_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k_scale: float, v_scale: float,
                     kv_offsets=None, max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None):
     """append_rope into caches of one-byte E4M3 codes (uint8 or float8_e4m3fn;
@@ -487,13 +569,13 @@ def append_rope_paged_fp8(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens
 
 
 def prepare_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
-                   max_seq_len: Optional[int] = None, stream=None):
+                   max_seq_len: Optional[int] = None, stream=None, q_out=None, new_seq_lens=None):
     """Validate (by running it once) and return a callable that enqueues the
     same append_rope call again (for timing loops); it returns the rotated
-    queries.  The new lengths go to a tensor of their own, so every call
-    appends at the same rows."""
+    queries.  The new lengths go to a tensor of their own (``new_seq_lens``
+    if given), so every call appends at the same rows."""
     q_out, new_lens = append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets=kv_offsets,
-                                  max_seq_len=max_seq_len, stream=stream)
+                                  max_seq_len=max_seq_len, stream=stream, q_out=q_out, new_seq_lens=new_seq_lens)
     B, H_q, d = q.shape
     T_max = k_cache.shape[2] if kv_offsets is None else max_seq_len
     dims = make_dims(B, H_q, k_new.shape[1], d, T_max, q.dtype)

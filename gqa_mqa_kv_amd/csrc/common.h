@@ -56,6 +56,15 @@ struct Problem {
   const int32_t* block_table; // paged cache: [B][max_pages] page ids, or nullptr
   int32_t max_pages, page;    // paged cache: table entries per sequence, tokens per page (a multiple of 16)
   float out_mul;              // factor of every normalised output (the value scale of an E4M3 cache, else 1)
+  // Decode with the append of the new token (one layer, plain or packed bf16
+  // cache): sequence b's token at position m = max(seq_lens[b], 0) is turned
+  // by the rotary embedding and written to cache row m (when m < capacity),
+  // and the attention covers it.
+  const void* k_new;          // [B][H_kv][D] keys before the rotation
+  const void* v_new;          // [B][H_kv][D]
+  void* q_out;                // [B][H_q][D] turned queries
+  int32_t* new_seq_lens;      // [B] or nullptr
+  double rope_base;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -66,6 +75,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// Rotary embedding ("Grouped-Query Attention (GQA) and Multi-Query
+// Attention (MQA): ...", section 4): the cosine and sine of pair j's angle
+// m * base^(-2j/D) (computed in double precision, as m * theta_j reaches
+// 1e5 radians, then rounded to float), and the turn of the pair (x0, x1) by
+// it.  The turn is written with explicit fused multiply-adds so that every
+// kernel that uses it rounds alike.
+__device__ __forceinline__ void rope_angle(double base, int64_t m, int j, int D, float& c, float& s) {
+  const double a = (double)m * pow(base, -2.0 * (double)j / (double)D);
+  double sd, cd;
+  sincos(a, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+__device__ __forceinline__ void rope_turn(float x0, float x1, float c, float s, float& y0, float& y1) {
+  y0 = fmaf(x0, c, -(x1 * s));
+  y1 = fmaf(x0, s, x1 * c);
 }
 
 struct UnitInfo {
@@ -161,8 +188,11 @@ __global__ __launch_bounds__(256) void gqa_merge_chunks(Problem p) {
 // to a multiple of 16, so that every 16-token tile of a unit starts at a
 // multiple of 16 and lies in one page, and the clamped counts go to
 // sm_N[0..B).  sm_wave holds NT/64 ints.
-template <int NT, bool PAGED>
-__device__ __forceinline__ void build_prefix(const Problem& p, int32_t* sm_P, int32_t* sm_N, int32_t* sm_wave) {
+// APPEND: sm_M[b] receives the new token's position m and the length counts
+// it when the cache has room (m < capacity).
+template <int NT, bool PAGED, bool APPEND = false>
+__device__ __forceinline__ void build_prefix(const Problem& p, int32_t* sm_P, int32_t* sm_N, int32_t* sm_wave,
+                                             int32_t* sm_M = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = p.B;
   const int E = (B + NT - 1) / NT;   // entries per thread, contiguous
@@ -170,8 +200,13 @@ __device__ __forceinline__ void build_prefix(const Problem& p, int32_t* sm_P, in
   int local = 0;
   for (int b = b0; b < b0 + E && b < B; ++b) {
     int64_t cap = p.kv_offsets ? p.kv_offsets[b + 1] - p.kv_offsets[b] : (int64_t)p.T_max;
-    if (cap > p.T_cap) cap = p.T_cap;
     int64_t n = p.seq_lens[b];
+    if constexpr (APPEND) {
+      n = n < 0 ? 0 : n;
+      sm_M[b] = (int32_t)n;
+      n = n < cap ? n + 1 : cap;
+    }
+    if (cap > p.T_cap) cap = p.T_cap;
     n = n < 0 ? 0 : (n > cap ? cap : n);
     if constexpr (PAGED) {
       sm_N[b] = (int32_t)n;
@@ -314,6 +349,36 @@ __device__ __forceinline__ void zero_empty_sequences(const Problem& p, const int
     if (sm_P[b + 1] != sm_P[b]) continue;
     const int64_t row = (int64_t)lb * p.H_q;
     for (int e = threadIdx.x; e < p.H_q * D; e += NT) store_out(p, row + e / D, e % D, D, 0.f);
+  }
+}
+
+// The fused append's outputs that no decode piece writes (one layer):
+// new_seq_lens (workgroup 0; the length grows by the appended token, a full
+// cache keeps the length given), and the turned queries of sequences without
+// any token to attend to (spread over the workgroups).
+template <int D, int NT>
+__device__ __forceinline__ void append_side_outputs(const Problem& p, const int32_t* sm_P, const int32_t* sm_M,
+                                                    int wg, int n_wg) {
+  if (wg == 0 && p.new_seq_lens) {
+    for (int b = threadIdx.x; b < p.B; b += NT) {
+      const int64_t cap = p.kv_offsets ? p.kv_offsets[b + 1] - p.kv_offsets[b] : (int64_t)p.T_max;
+      const int32_t m = sm_M[b];
+      p.new_seq_lens[b] = m < cap ? m + 1 : p.seq_lens[b];
+    }
+  }
+  for (int b = wg; b < p.B; b += n_wg) {
+    if (sm_P[b + 1] != sm_P[b]) continue;
+    const int64_t row = (int64_t)b * p.H_q;
+    for (int e = threadIdx.x; e < p.H_q * (D / 2); e += NT) {
+      const int h = e / (D / 2), j = e % (D / 2);
+      float c, s, y0, y1;
+      rope_angle(p.rope_base, sm_M[b], j, D, c, s);
+      const uint16_t* qi = static_cast<const uint16_t*>(p.q) + (row + h) * D + 2 * j;
+      rope_turn(bf16_to_f32(qi[0]), bf16_to_f32(qi[1]), c, s, y0, y1);
+      uint16_t* qo = static_cast<uint16_t*>(p.q_out) + (row + h) * D + 2 * j;
+      qo[0] = (uint16_t)f32_to_bf16_rne(y0);
+      qo[1] = (uint16_t)f32_to_bf16_rne(y1);
+    }
   }
 }
 

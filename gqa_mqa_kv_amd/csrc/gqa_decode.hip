@@ -196,6 +196,19 @@ kernel_fn mfma_kernel(int hb, int, int tiles) {
   }
 }
 
+// The decode fused with the append (bf16, plain or packed cache): two
+// tiles per batch for one head block, one otherwise.
+template <int D>
+kernel_fn mfma_append_kernel(int hb, int tiles) {
+  switch (hb) {
+    case 1:
+      return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, false, false, true>
+                        : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, false, false, true>;
+    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1, false, false, true>;
+    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, false, false, true>;
+  }
+}
+
 // Where the cache of a call lives and what its elements are.
 struct CacheArgs {
   const int64_t* kv_offsets = nullptr;   // packed layout, else dense
@@ -203,12 +216,20 @@ struct CacheArgs {
   int32_t max_pages = 0, page = 0;
   bool e4m3 = false;                     // one-byte OCP E4M3 elements
   float k_scale = 1.f, v_scale = 1.f;    // E4M3: what each key / value element is multiplied by
+  // the decode fused with the append of each sequence's new token
+  const void* k_new = nullptr;           // non-null: fused append
+  const void* v_new = nullptr;
+  void* q_out = nullptr;
+  int32_t* new_seq_lens = nullptr;
+  double rope_base = 0.0;
 };
 
 kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan, const CacheArgs& ca) {
   const int G = d->num_q_heads / d->num_kv_heads;
   if (plan.mfma) {
     const int hb = (G + 15) / 16;
+    if (ca.k_new)
+      return d->head_dim == 128 ? mfma_append_kernel<128>(hb, plan.tiles) : mfma_append_kernel<64>(hb, plan.tiles);
     if (ca.e4m3 && ca.block_table)
       return d->head_dim == 128 ? mfma_kernel<128, true, true>(hb, plan.waves, plan.tiles)
                                 : mfma_kernel<64, true, true>(hb, plan.waves, plan.tiles);
@@ -292,6 +313,11 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   p.scale_log2 = ca.e4m3 ? (float)((double)scale * (double)ca.k_scale * 1.4426950408889634)
                          : scale * 1.4426950408889634f;
   p.out_mul = ca.e4m3 ? ca.v_scale : 1.f;
+  p.k_new = ca.k_new;
+  p.v_new = ca.v_new;
+  p.q_out = ca.q_out;
+  p.new_seq_lens = ca.new_seq_lens;
+  p.rope_base = ca.rope_base;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* args[] = {&p};
@@ -417,6 +443,32 @@ gqa_status gqa_decode_layers_fp8(int32_t num_layers, const void* q, const void* 
   ca.k_scale = k_scale;
   ca.v_scale = v_scale;
   return launch(num_layers, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                  float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  gqa_status st = check_dims(dims, 1);
+  if (st != GQA_OK) return st;
+  if (dims->dtype != GQA_DTYPE_BF16 || !use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // matrix-core kernel only
+  if (dims->seq_len_hint != 0) return GQA_ERR_INVALID_ARG;   // the lengths grow inside the call
+  if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return GQA_ERR_INVALID_ARG;
+  if (dims->batch == 0) return GQA_OK;
+  if (!k_new || !v_new || !q_out) return GQA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q_out, 16)) return GQA_ERR_INVALID_ARG;
+  // every workgroup reads q and seq_lens while others write q_out and new_seq_lens
+  if (q_out == q || static_cast<const void*>(new_seq_lens) == static_cast<const void*>(seq_lens))
+    return GQA_ERR_INVALID_ARG;
+  if (new_seq_lens && !aligned(new_seq_lens, 4)) return GQA_ERR_INVALID_ARG;
+  CacheArgs ca;
+  ca.kv_offsets = kv_offsets;
+  ca.k_new = k_new;
+  ca.v_new = v_new;
+  ca.q_out = q_out;
+  ca.new_seq_lens = new_seq_lens;
+  ca.rope_base = (double)rope_base;
+  return launch(1, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
 }
 
 gqa_status append_launch(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

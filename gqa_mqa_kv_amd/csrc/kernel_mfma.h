@@ -204,8 +204,16 @@ __device__ __forceinline__ u32x2 v_operand(const Tile16K8<D>& T, int r) {
 // KV8: cache elements are one-byte E4M3 values (bf16 queries).  Tiles move
 // as bytes and are widened to bf16, exactly, just before the products; the
 // key scale is folded into p.scale_log2 and the value scale into p.out_mul.
-template <int D, int HB, int HG, int NW, int TPW, bool PAGED, bool KV8>
+// APPEND (plain or packed bf16 cache): the decode step fused with the append
+// of each sequence's new token.  The token's position m comes from
+// seq_lens[b]; its queries are turned by the rotary embedding in registers
+// at the first tile of every piece (and written to q_out by the unit's
+// first piece), and the attention covers the new token: the wavefront whose
+// tile holds row m takes the turned key and the value from k_new / v_new
+// instead of the cache and writes them to cache row m.
+template <int D, int HB, int HG, int NW, int TPW, bool PAGED, bool KV8, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
+  static_assert(!APPEND || (!PAGED && !KV8), "the fused append takes a plain or packed bf16 cache");
   static_assert(NW % HG == 0, "head groups must divide the wavefronts");
   constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
   constexpr int NL = NW / HG;             // tile lanes
@@ -221,6 +229,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   __shared__ int32_t sm_N[PAGED ? kMaxBatch : 1];
   __shared__ int32_t sm_wave[NW];
   __shared__ int sm_flag;
+  __shared__ int32_t sm_M[APPEND ? kMaxBatch : 1];        // APPEND: new token positions
+  __shared__ float sm_cs[APPEND ? NW : 1][2][2][D / 2];  // APPEND: each wavefront's cosines and sines, two tables
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);   // wavefront index, in a scalar register (everything derived from it is too)
@@ -230,9 +240,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   const int head0 = hg * HP + m16;      // this lane's query head of block 0 (block hb: head0 + 16 hb)
   const float sl2 = p.scale_log2;
 
-  build_prefix<NT, PAGED>(p, sm_P, sm_N, sm_wave);
+  build_prefix<NT, PAGED, APPEND>(p, sm_P, sm_N, sm_wave, sm_M);
   const TokenSpace ts = token_space(p, sm_P);
   zero_empty_sequences<D, NT>(p, sm_P, blockIdx.x, gridDim.x);
+  if constexpr (APPEND) append_side_outputs<D, NT>(p, sm_P, sm_M, blockIdx.x, gridDim.x);
   if (!p.fused) write_merge_desc<PAGED>(p, sm_P, sm_N, ts, blockIdx.x);
   const int64_t s0 = (int64_t)blockIdx.x * ts.span;
   const int64_t s1 = min(s0 + ts.span, ts.total);
@@ -260,7 +271,15 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     bool whole;
     int slot_id;      // only the first and the last piece of a span can be partial
     Piece at;         // the unit and the piece's first token
+    // APPEND: the new token's position, its index in the unit when this piece
+    // holds it (else -1), and its key (turned at the piece's first tile) and
+    // value, the lane's columns of each
+    int32_t m, mnew;
+    int tab;          // the wavefront's angle table of the piece (tables alternate by piece)
+    u32x4 knew[KS];
+    vrow_t vnew;
   };
+  int tab_next = 0;
   // The piece of the span that starts at stream position x, located as pc.
   auto open_at = [&](const Piece& pc, int64_t x) __attribute__((always_inline)) {
     Ctx c;
@@ -281,6 +300,26 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     c.kg = reinterpret_cast<const kv_t*>(p.k) + pc.ui.row0 * D;
     c.vg = reinterpret_cast<const kv_t*>(p.v) + pc.ui.row0 * D;
     c.orow = out_row0(p, pc.ui);
+    if constexpr (APPEND) {
+      c.m = uniform(sm_M[pc.ui.b]);
+      // the piece holds the new token when it reaches the end of a unit that
+      // grew by it (the unit then has m + 1 tokens)
+      c.mnew = (c.c1 == pc.ui.n && pc.ui.n == c.m + 1) ? c.m : -1;
+      // lane j < D/2 computes pair j's cosine and sine into the wavefront's
+      // table for this piece (the previous piece may still read the other)
+      c.tab = tab_next;
+      tab_next ^= 1;
+      float* tab = &sm_cs[wave][c.tab][0][0];
+      if (lane < D / 2) rope_angle(p.rope_base, c.m, lane, D, tab[lane], tab[D / 2 + lane]);
+      // the lane's columns of the new key and value (loaded for every piece:
+      // an unconditional load keeps the wait counts exact)
+      const int64_t nrow = ((int64_t)pc.ui.b * p.H_kv + pc.ui.g) * D;
+      const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + nrow;
+      const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + nrow;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) c.knew[s] = *reinterpret_cast<const u32x4*>(kn + 32 * s + 8 * q4);
+      c.vnew = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
+    }
     return c;
   };
   auto open_piece = [&](int64_t x) __attribute__((always_inline)) {
@@ -429,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   };
 
   // T: a Tile16 (bf16 cache) or a Tile16K8 (E4M3 cache, keys widened).
-  auto compute_tile = [&](const auto& T, int t0, int c1) __attribute__((always_inline)) {
+  auto compute_core = [&](const auto& T, int t0, int c1) __attribute__((always_inline)) {
     u32x2 phi[HB], plo[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -462,14 +501,98 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         oacc[r][hb] = mfma_k32(vv, u32x4{phi[hb][0], phi[hb][1], plo[hb][0], plo[hb][1]}, oacc[r][hb]);
     }
   };
+  // APPEND: the tile that holds the new token (row m of the unit, in
+  // registers from the cache's stale row) takes the turned key and the value
+  // in the lanes holding that row (the tail's clamped rows too), and the
+  // lanes holding it exactly write it to cache row m.
+  auto compute_tile = [&](const auto& T, const Ctx& c, int t0) __attribute__((always_inline)) {
+    if constexpr (APPEND) {
+      if (c.mnew >= t0 && c.mnew < t0 + TILE) {   // wave-uniform
+        Tile16<D> U = T;
+        const int mn = c.mnew, last = c.c1 - 1;
+        if (min(t0 + m16, last) == mn) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) U.k[s] = c.knew[s];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (min(t0 + 4 * q4 + i, last) == mn) U.v[i] = c.vnew;
+        uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + (int64_t)mn * D;
+        uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + (int64_t)mn * D;
+        if (t0 + m16 == mn) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(kc + 32 * s + 8 * q4) = c.knew[s];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 4 * q4 + i == mn) *reinterpret_cast<vrow_t*>(vc + VW * m16) = c.vnew;
+        compute_core(U, t0, c.c1);
+        return;
+      }
+    }
+    compute_core(T, t0, c.c1);
+  };
+  // APPEND: the queries (and the new key) of the current piece are turned at
+  // its first tile, once their loads have long landed, with the angle table
+  // the piece's opening filled; a lane's columns 32s + 8q4 .. +7 are pairs
+  // 16s + 4q4 .. +3.  The unit's first piece writes the turned queries of its
+  // heads to q_out.
+  bool turn_pending = false;
+  auto turn_words = [&](const u32x4& w, const float (&cc)[4], const float (&ss)[4]) __attribute__((always_inline)) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float y0, y1;
+      rope_turn(bf16_to_f32(w[k] & 0xffffu), bf16_to_f32(w[k] >> 16), cc[k], ss[k], y0, y1);
+      r[k] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+    }
+    return r;
+  };
+  auto turn_piece = [&](Ctx& c) __attribute__((always_inline)) {
+    if constexpr (APPEND) {
+      const float* tab = &sm_cs[wave][c.tab][0][0];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float cc[4], ss[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          cc[k] = tab[16 * s + 4 * q4 + k];
+          ss[k] = tab[D / 2 + 16 * s + 4 * q4 + k];
+        }
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) qf[hb][s] = turn_words(qf[hb][s], cc, ss);
+        c.knew[s] = turn_words(c.knew[s], cc, ss);
+      }
+      if (c.c0 == 0 && tl == 0) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const int h = head0 + 16 * hb;
+          if (h >= G) continue;
+          uint16_t* qo = reinterpret_cast<uint16_t*>(p.q_out) + (c.orow + h) * D;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(qo + 32 * s + 8 * q4) = qf[hb][s];
+        }
+      }
+    }
+  };
+  // Called before any batch that may be a piece's first (never inside the
+  // steady-state loop, which a piece enters only after its first batch).
+  auto turn_if_pending = [&](Ctx& c) __attribute__((always_inline)) {
+    if constexpr (APPEND) {
+      if (turn_pending) {
+        turn_piece(c);
+        turn_pending = false;
+      }
+    }
+  };
   auto compute_batch = [&](const tile_t (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (j + NL * u < c.ntiles) {
         if constexpr (KV8)
-          compute_tile(widen(T[u]), c.c0 + (j + NL * u) * TILE, c.c1);
+          compute_tile(widen(T[u]), c, c.c0 + (j + NL * u) * TILE);
         else
-          compute_tile(T[u], c.c0 + (j + NL * u) * TILE, c.c1);
+          compute_tile(T[u], c, c.c0 + (j + NL * u) * TILE);
       }
     }
   };
@@ -622,6 +745,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   int32_t pid[TPW];   // paged: page ids of the next batch to load
   fetch_pages(pid, pc, j);
   load_q(qf, pc);
+  turn_pending = APPEND;
   reset_state();
   tile_t TA[TPW], TB[TPW];
   load_batch(TA, pc, j, pid);
@@ -629,6 +753,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   // One step with `cur` loaded: false if it is the span's last batch (left
   // for the caller), else load the next batch into `nxt` and compute `cur`.
   auto step = [&](const tile_t (&cur)[TPW], tile_t (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
+    turn_if_pending(pc);
     const bool piece_done = j + NL * TPW >= pc.ntiles;
     const int64_t xn = PAGED ? pc.next : pc.x + (pc.c1 - pc.c0);
     if (piece_done && xn >= s1) return false;
@@ -643,6 +768,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       end_piece(pc);
       reset_state();
       pc = pn;
+      turn_pending = APPEND;
       j = tl;
     } else {
       load_batch(nxt, pc, j + NL * TPW, pid);
@@ -655,6 +781,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   for (;;) {
     // Steady state: while the piece has two more batches, neither step ends
     // it, and this loop carries only the running softmax state.
+    turn_if_pending(pc);
     while (j + 2 * NL * TPW < pc.ntiles) {
       load_batch(TB, pc, j + NL * TPW, pid);
       fetch_pages(pid, pc, j + 2 * NL * TPW);

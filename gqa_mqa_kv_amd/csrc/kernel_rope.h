@@ -81,13 +81,7 @@ __global__ __launch_bounds__(256) void gqa_append_rope(RopeProblem p) {
   const int32_t len = p.seq_lens[b];
   const int64_t m = len < 0 ? 0 : len;     // the new token's position
   const bool append = m < cap;             // a full cache is left as it is
-  for (int j = tid; j < P; j += NT) {
-    const double a = (double)m * pow(p.base, -2.0 * (double)j / (double)D);
-    double s, c;
-    sincos(a, &s, &c);
-    sm_cos[j] = (float)c;
-    sm_sin[j] = (float)s;
-  }
+  for (int j = tid; j < P; j += NT) rope_angle(p.base, m, j, D, sm_cos[j], sm_sin[j]);
   __syncthreads();
 
   // rows of this token: q and out [B][H_q][D], k_new/v_new [B][H_kv][D]
@@ -113,13 +107,16 @@ __global__ __launch_bounds__(256) void gqa_append_rope(RopeProblem p) {
     if (e < nq) {
       const int64_t i0 = (qrow + e / P) * D + 2 * j;
       const float x0 = RopeElem<T>::get(p.q, i0), x1 = RopeElem<T>::get(p.q, i0 + 1);
-      RopeElem<T>::put(p.q_out, i0, x0 * c - x1 * s);
-      RopeElem<T>::put(p.q_out, i0 + 1, x0 * s + x1 * c);
+      float y0, y1;
+      rope_turn(x0, x1, c, s, y0, y1);
+      RopeElem<T>::put(p.q_out, i0, y0);
+      RopeElem<T>::put(p.q_out, i0 + 1, y1);
     } else if (append) {
       const int g = (e - nq) / P;
       const int64_t i0 = (krow + g) * D + 2 * j, o0 = (crow0 + g * cstride) * D + 2 * j;
       const float x0 = RopeElem<T>::get(p.k_new, i0), x1 = RopeElem<T>::get(p.k_new, i0 + 1);
-      const float k0 = x0 * c - x1 * s, k1 = x0 * s + x1 * c;
+      float k0, k1;
+      rope_turn(x0, x1, c, s, k0, k1);
       if constexpr (KV8) {
         uint8_t* kc = static_cast<uint8_t*>(p.k_cache);
         uint8_t* vc = static_cast<uint8_t*>(p.v_cache);

@@ -302,6 +302,30 @@ gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, 
                            float rope_base, void* q_out, const gqa_dims* dims, void* stream);
 
 /*
+ * gqa_append_rope followed by gqa_decode, in one launch (bf16, matrix-core
+ * path): sequence b's new token at position m = max(seq_lens[b], 0) is
+ * turned and appended exactly as gqa_append_rope does (cache row m of every
+ * KV head when m < capacity, q_out, new_seq_lens), and out is the attention
+ * of the turned queries over the cache including that token, as gqa_decode
+ * computes it on the updated cache and lengths.  Results equal the two calls
+ * in sequence, bit for bit.
+ *   q, k_new, v_new, k_cache, v_cache, kv_offsets, rope_base : as for
+ *                  gqa_append_rope (q, k_new, v_new and q_out 16-byte
+ *                  aligned); the cache is plain or packed, one layer
+ *   q_out        : [B][H_q][d], required, and must not be q (workgroups
+ *                  read q while others write q_out)
+ *   new_seq_lens : [B] or NULL, and must not be seq_lens (same reason)
+ *   scale, out, dims, workspace, stream : as for gqa_decode;
+ *                  dims->seq_len_hint must be 0 (GQA_ERR_INVALID_ARG)
+ * For callers that run a decode step right after the append: the append's
+ * launch (and its read of q) disappears into the decode kernel.
+ */
+gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                  float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The same step for a cache held in pages of a pool (the layout of
  * gqa_decode_paged): the rotated key and the value of sequence b's new token
  * go to row m % page_size of page block_table[b][m / page_size] of each KV

@@ -289,6 +289,31 @@ def test_decode_layers_fp8_validation():
     assert call(dims(B=0), ptrs=[None] * 5) == OK
 
 
+def test_decode_append_rope_validation():
+    """The fused append-and-decode entry point checks its arguments before
+    touching the device: bf16 on the matrix-core path, no length hint, a
+    finite positive base, q_out present and distinct from q, new lengths
+    distinct from the lengths read, 16-byte aligned new rows."""
+    d = dims()
+    Q, KN, VN, KC, VC, SL, NL, QO, OUT = (FAKE + 0x1000 * i for i in range(9))
+    call = lambda dd=d, q=Q, kn=KN, vn=VN, sl=SL, nl=NL, base=10000.0, qo=QO, offs=None: \
+        gqa.lib().gqa_decode_append_rope(q, kn, vn, KC, VC, offs, sl, nl, base, 0.125, qo, OUT, ctypes.byref(dd), None,
+                                         0, None)
+    assert call() == WORKSPACE                                          # valid: only the workspace is missing
+    assert call(nl=None) == WORKSPACE                                   # new lengths are optional
+    assert call(dims(dtype=torch.float32)) == UNSUPPORTED
+    assert call(dims(path="valu")) == UNSUPPORTED
+    assert call(dims(seq_len_hint=100)) == INVALID
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(base=bad) == INVALID
+    assert call(qo=None) == INVALID
+    assert call(qo=Q) == INVALID                                        # q_out may not be q
+    assert call(nl=SL) == INVALID                                       # new lengths may not be the lengths
+    for kw in (dict(kn=None), dict(vn=None), dict(kn=KN + 8), dict(vn=VN + 8), dict(qo=QO + 8), dict(nl=NL + 2)):
+        assert call(**kw) == INVALID, kw
+    assert call(dims(B=0), q=None, kn=None, vn=None, sl=None, nl=None, qo=None) == OK
+
+
 def test_decode_paged_fp8_validation():
     """The paged E4M3 entry point applies the rules of both parents."""
     d = dims(T_max=1024)

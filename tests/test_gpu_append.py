@@ -395,3 +395,86 @@ def test_e4m3_encoder_exact():
     bad = np.argwhere((got_k != want) & ok)
     assert len(bad) == 0, ("key codes differ", [(float(x[tuple(i)]), int(got_k[tuple(i)]), int(want[tuple(i)]))
                                                 for i in bad[:8]])
+
+
+# ------------------------------------------------------ append fused into decode --
+FUSED_CASES = [
+    # B, H_q, H_kv, d, T_max, lengths before the append (T_max = full: not appended; negative: position 0)
+    (6, 32, 8, 128, 300, [0, 15, 16, 17, 299, 300]),     # G = 4, tile edges and a full cache
+    (3, 64, 8, 128, 777, [776, 1, 500]),                 # G = 8
+    (2, 32, 1, 128, 1000, [999, 313]),                   # G = 32 (two head blocks)
+    (2, 64, 1, 64, 257, [256, 100]),                     # G = 64 (two head groups), d = 64
+    (3, 12, 4, 128, 200, [-3, 31, 150]),                 # G = 3, a negative length
+]
+
+
+def fused_vs_pipeline(x, base, scale, packed=None, **kw):
+    """The fused call and append_rope + decode on copies of the same inputs:
+    outputs, turned queries, caches and lengths bitwise equal.  Returns the
+    pipeline's (out, caches, new lengths)."""
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    ka, va, kb, vb = xd["k"].clone(), xd["v"].clone(), xd["k"].clone(), xd["v"].clone()
+    ext = dict(kv_offsets=packed[0].to(DEV), max_seq_len=packed[1]) if packed else {}
+    qo, nl = gqa.append_rope(xd["q"], xd["k_new"], xd["v_new"], ka, va, xd["seq_lens"], base, **ext)
+    if packed:
+        ref = gqa.decode_layers(qo[None], ka, va, nl, scale, kv_offsets=ext["kv_offsets"], max_seq_len=packed[1],
+                                num_kv_heads=x["k_new"].shape[1], out_dtype=torch.float32, **kw)[0]
+    else:
+        ref = gqa.decode(qo, ka, va, nl, scale, out_dtype=torch.float32, **kw)
+    out, qf, nlf = gqa.decode_append_rope(xd["q"], xd["k_new"], xd["v_new"], kb, vb, xd["seq_lens"], base, scale,
+                                          out_dtype=torch.float32, **ext, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(qf, qo), "turned queries differ"
+    assert torch.equal(nlf, nl), "new lengths differ"
+    assert torch.equal(kb, ka) and torch.equal(vb, va), "caches differ"
+    assert torch.equal(out, ref), "outputs differ: max %.3e" % float((out - ref).abs().max())
+    return ref, ka, va, nl
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d_T%d" % c[:5])
+@pytest.mark.parametrize("span,merge,tiles", [(0, "auto", 0), (64, "fused", 0), (64, "kernel", 0), (128, "auto", 2)])
+def test_decode_append_rope_equals_the_two_calls(case, span, merge, tiles):
+    """gqa_decode_append_rope against gqa_append_rope followed by gqa_decode
+    (plain cache): every output bitwise, with the planner's split and with
+    forced spans that cut units into pieces (the new token then lies in a
+    unit's last piece, its queries' first piece another workgroup), both
+    merges and two tiles per batch; and the attention against the oracle on
+    the updated cache."""
+    B, H_q, H_kv, d, T, lens = case
+    x = make(B, H_q, H_kv, d, T, torch.bfloat16, 91 + B + d, lens)
+    note("fused append", case, span, merge, tiles)
+    scale = d ** -0.5
+    ref, ka, va, nl = fused_vs_pipeline(x, 10000.0, scale, chunk_tokens=span, merge=merge, tiles=tiles)
+    qo, _ = gqa.append_rope(x["q"].to(DEV), x["k_new"].to(DEV), x["v_new"].to(DEV), x["k"].to(DEV).clone(),
+                            x["v"].to(DEV).clone(), x["seq_lens"].to(DEV), 10000.0)
+    want = oracle.decode(qo.cpu(), ka.cpu(), va.cpu(), nl.cpu(), scale)
+    assert float(np.abs(ref.double().cpu().numpy() - want).max()) <= 2e-3
+
+
+def test_decode_append_rope_packed_cache():
+    """The fused call on the packed layout (capacities of their own, one of
+    them full, one empty), against the two calls."""
+    g = torch.Generator().manual_seed(5)
+    caps = [40, 0, 17, 300]
+    lens = [12, 0, 17, 299]
+    H_q, H_kv, d = 32, 8, 128
+    offs = torch.tensor([0] + list(np.cumsum(caps)), dtype=torch.int64)
+    rows = int(offs[-1]) * H_kv
+    r = lambda *s: torch.randn(*s, generator=g).to(torch.bfloat16)
+    x = dict(q=r(4, H_q, d), k_new=r(4, H_kv, d), v_new=r(4, H_kv, d), k=r(rows, d), v=r(rows, d),
+             seq_lens=torch.tensor(lens, dtype=torch.int32))
+    for span in (0, 64):
+        fused_vs_pipeline(x, 500000.0, d ** -0.5, packed=(offs, max(caps)), chunk_tokens=span)
+
+
+def test_decode_append_rope_full_8b_layer():
+    """The Llama-3-8B-shaped layer (16 x 4096 cached tokens, one appended
+    each: 4097 attended), fused against the two calls, bitwise."""
+    w = workloads.WORKLOADS["llama3-8b-layer"]
+    g = torch.Generator().manual_seed(8)
+    T = w.T_max + 64
+    r = lambda *s: torch.randn(*s, generator=g).to(torch.bfloat16)
+    x = dict(q=r(w.B, w.H_q, w.d), k_new=r(w.B, w.H_kv, w.d), v_new=r(w.B, w.H_kv, w.d),
+             k=r(w.B, w.H_kv, T, w.d), v=r(w.B, w.H_kv, T, w.d),
+             seq_lens=torch.full((w.B,), w.T_max, dtype=torch.int32))
+    fused_vs_pipeline(x, 500000.0, w.scale)
