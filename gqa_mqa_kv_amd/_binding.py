@@ -453,14 +453,16 @@ def _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, 
     dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, 0, chunk_tokens, "mfma", 0, tiles, merge, per_cu)
     if q_out is None:
         q_out = torch.empty_like(q)
-    if new_seq_lens is None:
-        new_seq_lens = torch.empty_like(seq_lens)
+    lens_out = new_seq_lens is not False   # False: the grown lengths are not written
+    if new_seq_lens is None or new_seq_lens is False:
+        new_seq_lens = torch.empty_like(seq_lens) if lens_out else None
     if out is None:
         out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
     for t, n in ((q_out, "q_out"), (new_seq_lens, "new_seq_lens"), (out, "out")):
-        _require(t, n, dev)
-    if q_out.shape != q.shape or q_out.dtype != q.dtype or new_seq_lens.shape != (B,) or \
-            new_seq_lens.dtype != torch.int32:
+        if t is not None:
+            _require(t, n, dev)
+    if q_out.shape != q.shape or q_out.dtype != q.dtype or \
+            (lens_out and (new_seq_lens.shape != (B,) or new_seq_lens.dtype != torch.int32)):
         raise ValueError("q_out must match q and new_seq_lens seq_lens")
     if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [B,H_q,d] of the output dtype")
@@ -476,11 +478,13 @@ def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: f
                        max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, out=None, out_dtype=None,
                        chunk_tokens: int = 0, workspace=None, stream=None, tiles: int = 0, merge: str = "auto",
                        per_cu: int = 0):
-    """append_rope followed by decode in one launch (gqa_decode_append_rope):
-    bf16 q [B,H_q,d], k_new/v_new [B,H_kv,d], a plain [B,H_kv,T_max,d] or
-    packed (``kv_offsets``, ``max_seq_len``) cache written in place.  Returns
-    (out, q_out, new_seq_lens); q_out and new_seq_lens are new tensors unless
-    given (they may not be q and seq_lens)."""
+    """append_rope followed by decode (gqa_decode_append_rope): bf16 q
+    [B,H_q,d], k_new/v_new [B,H_kv,d], a plain [B,H_kv,T_max,d] or packed
+    (``kv_offsets``, ``max_seq_len``) cache written in place.  Returns (out,
+    q_out, new_seq_lens); q_out and new_seq_lens are new tensors unless given
+    (they may not be q and seq_lens).  ``new_seq_lens=False`` writes no
+    lengths (returned as None); the call is then one kernel at every G (with
+    lengths and G > 16 it is the append kernel and the decode)."""
     args, keep = _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets,
                                      max_seq_len, q_out, new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream,
                                      tiles, merge, per_cu)

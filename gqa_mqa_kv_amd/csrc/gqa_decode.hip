@@ -427,7 +427,6 @@ gqa_status gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cach
   return launch(1, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
 }
 
-namespace {
 // e4m3: the caches hold one-byte E4M3 codes of key / k_scale and value / v_scale.
 gqa_status gqa_decode_layers_fp8(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
                                  const int64_t* kv_offsets, const int32_t* seq_lens, float scale, float k_scale,
@@ -445,32 +444,7 @@ gqa_status gqa_decode_layers_fp8(int32_t num_layers, const void* q, const void* 
   return launch(num_layers, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
 }
 
-gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                                  const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
-                                  float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
-  gqa_status st = check_dims(dims, 1);
-  if (st != GQA_OK) return st;
-  if (dims->dtype != GQA_DTYPE_BF16 || !use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // matrix-core kernel only
-  if (dims->seq_len_hint != 0) return GQA_ERR_INVALID_ARG;   // the lengths grow inside the call
-  if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return GQA_ERR_INVALID_ARG;
-  if (dims->batch == 0) return GQA_OK;
-  if (!k_new || !v_new || !q_out) return GQA_ERR_INVALID_ARG;
-  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q_out, 16)) return GQA_ERR_INVALID_ARG;
-  // every workgroup reads q and seq_lens while others write q_out and new_seq_lens
-  if (q_out == q || static_cast<const void*>(new_seq_lens) == static_cast<const void*>(seq_lens))
-    return GQA_ERR_INVALID_ARG;
-  if (new_seq_lens && !aligned(new_seq_lens, 4)) return GQA_ERR_INVALID_ARG;
-  CacheArgs ca;
-  ca.kv_offsets = kv_offsets;
-  ca.k_new = k_new;
-  ca.v_new = v_new;
-  ca.q_out = q_out;
-  ca.new_seq_lens = new_seq_lens;
-  ca.rope_base = (double)rope_base;
-  return launch(1, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
-}
-
+namespace {
 gqa_status append_launch(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const int64_t* kv_offsets, const int32_t* block_table, int32_t max_pages, int32_t page,
                          const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, void* q_out,
@@ -529,6 +503,45 @@ gqa_status append_launch(const void* q, const void* k_new, const void* v_new, vo
   return GQA_OK;
 }
 }  // namespace
+
+gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                  float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  gqa_status st = check_dims(dims, 1);
+  if (st != GQA_OK) return st;
+  if (dims->dtype != GQA_DTYPE_BF16 || !use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // matrix-core kernel only
+  if (dims->seq_len_hint != 0) return GQA_ERR_INVALID_ARG;   // the lengths grow inside the call
+  if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return GQA_ERR_INVALID_ARG;
+  if (dims->batch == 0) return GQA_OK;
+  if (!k_new || !v_new || !q_out) return GQA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q_out, 16)) return GQA_ERR_INVALID_ARG;
+  // every workgroup reads q and seq_lens while others write q_out and new_seq_lens
+  if (q_out == q || static_cast<const void*>(new_seq_lens) == static_cast<const void*>(seq_lens))
+    return GQA_ERR_INVALID_ARG;
+  if (new_seq_lens && !aligned(new_seq_lens, 4)) return GQA_ERR_INVALID_ARG;
+  const int64_t G = dims->num_q_heads / dims->num_kv_heads;
+  if (G > 16 && new_seq_lens) {
+    // Two head blocks: there the fused kernel needs more registers than a
+    // SIMD holds and spills at every piece end, and the append kernel followed
+    // by the decode of the grown cache is faster, with the same results (both
+    // turn, round and substitute alike).
+    st = append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, nullptr, 0, 0, seq_lens, new_seq_lens,
+                       rope_base, q_out, dims, stream);
+    if (st != GQA_OK) return st;
+    CacheArgs cb;
+    cb.kv_offsets = kv_offsets;
+    return launch(1, q_out, k_cache, v_cache, cb, new_seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+  }
+  CacheArgs ca;
+  ca.kv_offsets = kv_offsets;
+  ca.k_new = k_new;
+  ca.v_new = v_new;
+  ca.q_out = q_out;
+  ca.new_seq_lens = new_seq_lens;
+  ca.rope_base = (double)rope_base;
+  return launch(1, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+}
 
 gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                            const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,

@@ -231,6 +231,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   __shared__ int sm_flag;
   __shared__ int32_t sm_M[APPEND ? kMaxBatch : 1];        // APPEND: new token positions
   __shared__ float sm_cs[APPEND ? NW : 1][2][2][D / 2];  // APPEND: each wavefront's cosines and sines, two tables
+  // APPEND: each wavefront's turned new key and new value, one row each per table
+  __shared__ __align__(16) uint16_t sm_kvn[APPEND ? NW : 1][2][2][D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);   // wavefront index, in a scalar register (everything derived from it is too)
@@ -271,13 +273,10 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     bool whole;
     int slot_id;      // only the first and the last piece of a span can be partial
     Piece at;         // the unit and the piece's first token
-    // APPEND: the new token's position, its index in the unit when this piece
-    // holds it (else -1), and its key (turned at the piece's first tile) and
-    // value, the lane's columns of each
+    // APPEND: the new token's position and its index in the unit when this
+    // piece holds it (else -1)
     int32_t m, mnew;
     int tab;          // the wavefront's angle table of the piece (tables alternate by piece)
-    u32x4 knew[KS];
-    vrow_t vnew;
   };
   int tab_next = 0;
   // The piece of the span that starts at stream position x, located as pc.
@@ -305,20 +304,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       // the piece holds the new token when it reaches the end of a unit that
       // grew by it (the unit then has m + 1 tokens)
       c.mnew = (c.c1 == pc.ui.n && pc.ui.n == c.m + 1) ? c.m : -1;
-      // lane j < D/2 computes pair j's cosine and sine into the wavefront's
-      // table for this piece (the previous piece may still read the other)
-      c.tab = tab_next;
+      c.tab = tab_next;   // the piece's angle table (filled by fill_angles)
       tab_next ^= 1;
-      float* tab = &sm_cs[wave][c.tab][0][0];
-      if (lane < D / 2) rope_angle(p.rope_base, c.m, lane, D, tab[lane], tab[D / 2 + lane]);
-      // the lane's columns of the new key and value (loaded for every piece:
-      // an unconditional load keeps the wait counts exact)
-      const int64_t nrow = ((int64_t)pc.ui.b * p.H_kv + pc.ui.g) * D;
-      const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + nrow;
-      const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + nrow;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) c.knew[s] = *reinterpret_cast<const u32x4*>(kn + 32 * s + 8 * q4);
-      c.vnew = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
     }
     return c;
   };
@@ -503,41 +490,34 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   };
   // APPEND: the tile that holds the new token (row m of the unit, in
   // registers from the cache's stale row) takes the turned key and the value
-  // in the lanes holding that row (the tail's clamped rows too), and the
-  // lanes holding it exactly write it to cache row m.
-  auto compute_tile = [&](const auto& T, const Ctx& c, int t0) __attribute__((always_inline)) {
-    if constexpr (APPEND) {
+  // from LDS in the lanes holding that row (the tail's clamped rows too).
+  auto compute_tile = [&](const auto& T, const Ctx& c, int t0, auto may_hold_new) __attribute__((always_inline)) {
+    if constexpr (APPEND && decltype(may_hold_new)::value) {
+      // one product either way: only the substitution is conditional
+      Tile16<D> U = T;
       if (c.mnew >= t0 && c.mnew < t0 + TILE) {   // wave-uniform
-        Tile16<D> U = T;
         const int mn = c.mnew, last = c.c1 - 1;
+        const uint16_t* kn = &sm_kvn[wave][c.tab][0][0];
+        const uint16_t* vn = &sm_kvn[wave][c.tab][1][0];
         if (min(t0 + m16, last) == mn) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) U.k[s] = c.knew[s];
+          for (int s = 0; s < KS; ++s) U.k[s] = *reinterpret_cast<const u32x4*>(kn + 32 * s + 8 * q4);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (min(t0 + 4 * q4 + i, last) == mn) U.v[i] = c.vnew;
-        uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + (int64_t)mn * D;
-        uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + (int64_t)mn * D;
-        if (t0 + m16 == mn) {
-#pragma unroll
-          for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(kc + 32 * s + 8 * q4) = c.knew[s];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t0 + 4 * q4 + i == mn) *reinterpret_cast<vrow_t*>(vc + VW * m16) = c.vnew;
-        compute_core(U, t0, c.c1);
-        return;
+          if (min(t0 + 4 * q4 + i, last) == mn) U.v[i] = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
       }
+      compute_core(U, t0, c.c1);
+    } else {
+      compute_core(T, t0, c.c1);
     }
-    compute_core(T, t0, c.c1);
   };
-  // APPEND: the queries (and the new key) of the current piece are turned at
-  // its first tile, once their loads have long landed, with the angle table
-  // the piece's opening filled; a lane's columns 32s + 8q4 .. +7 are pairs
-  // 16s + 4q4 .. +3.  The unit's first piece writes the turned queries of its
-  // heads to q_out.
-  bool turn_pending = false;
+  // APPEND: the queries (and the new key) of a piece are turned when the
+  // piece becomes current: after the prologue's loads, or after the previous
+  // piece's end (its tiles and accumulators are then free, only the next
+  // batch is in flight), with the angle table the piece's opening filled; a
+  // lane's columns 32s + 8q4 .. +7 are pairs 16s + 4q4 .. +3.  The unit's
+  // first piece writes the turned queries of its heads to q_out.
   auto turn_words = [&](const u32x4& w, const float (&cc)[4], const float (&ss)[4]) __attribute__((always_inline)) {
     u32x4 r;
 #pragma unroll
@@ -551,17 +531,58 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   auto turn_piece = [&](Ctx& c) __attribute__((always_inline)) {
     if constexpr (APPEND) {
       const float* tab = &sm_cs[wave][c.tab][0][0];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        float cc[4], ss[4];
+      // the cosines and sines of the lane's pairs 16s + 4q4 .. +3
+      auto angles = [&](int s, float (&cc)[4], float (&ss)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           cc[k] = tab[16 * s + 4 * q4 + k];
           ss[k] = tab[D / 2 + 16 * s + 4 * q4 + k];
         }
+      };
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float cc[4], ss[4];
+        angles(s, cc, ss);
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) qf[hb][s] = turn_words(qf[hb][s], cc, ss);
-        c.knew[s] = turn_words(c.knew[s], cc, ss);
+      }
+      // Only the piece that ends a grown unit needs the new row: its key and
+      // value are loaded here (a wait of one load latency, once per unit), the
+      // key turned, both kept in the wavefront's slot for the tile that holds
+      // the row (lanes of one m16 hold the whole key, lanes of one q4 the
+      // whole value), and wavefront 0 writes them to cache row m (no other
+      // workgroup reads that row, and this piece's tile holding it takes the
+      // slot's copy whatever it loaded).
+      if (c.mnew >= 0) {   // wave-uniform
+        const int64_t nrow = ((int64_t)c.at.ui.b * p.H_kv + c.at.ui.g) * D;
+        const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + nrow;
+        const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + nrow;
+        u32x4 knew[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) knew[s] = *reinterpret_cast<const u32x4*>(kn + 32 * s + 8 * q4);
+        const vrow_t vnew = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          float cc[4], ss[4];
+          angles(s, cc, ss);
+          knew[s] = turn_words(knew[s], cc, ss);
+        }
+        uint16_t* ks = &sm_kvn[wave][c.tab][0][0];
+        uint16_t* vs = &sm_kvn[wave][c.tab][1][0];
+        if (m16 == 0) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(ks + 32 * s + 8 * q4) = knew[s];
+        }
+        if (q4 == 0) *reinterpret_cast<vrow_t*>(vs + VW * m16) = vnew;
+        if (wave == 0) {
+          uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + (int64_t)c.mnew * D;
+          uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + (int64_t)c.mnew * D;
+          if (m16 == 0) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(kc + 32 * s + 8 * q4) = knew[s];
+          }
+          if (q4 == 0) *reinterpret_cast<vrow_t*>(vc + VW * m16) = vnew;
+        }
       }
       if (c.c0 == 0 && tl == 0) {
 #pragma unroll
@@ -575,24 +596,27 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       }
     }
   };
-  // Called before any batch that may be a piece's first (never inside the
-  // steady-state loop, which a piece enters only after its first batch).
-  auto turn_if_pending = [&](Ctx& c) __attribute__((always_inline)) {
+  // APPEND: lane j < D/2 computes pair j's cosine and sine for the piece's
+  // position into the wavefront's table of the piece (the previous piece may
+  // still read the other one).  Called right after the piece's first loads
+  // are issued, so that this arithmetic overlaps their latency.
+  auto fill_angles = [&](const Ctx& c) __attribute__((always_inline)) {
     if constexpr (APPEND) {
-      if (turn_pending) {
-        turn_piece(c);
-        turn_pending = false;
-      }
+      float* tab = &sm_cs[wave][c.tab][0][0];
+      if (lane < D / 2) rope_angle(p.rope_base, c.m, lane, D, tab[lane], tab[D / 2 + lane]);
     }
   };
-  auto compute_batch = [&](const tile_t (&T)[TPW], const Ctx& c, int j) __attribute__((always_inline)) {
+  // may_hold_new: std::true_type unless the batch is known not to hold the
+  // piece's last tile (the only one that can hold an appended token)
+  auto compute_batch = [&](const tile_t (&T)[TPW], const Ctx& c, int j,
+                           auto may_hold_new) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       if (j + NL * u < c.ntiles) {
         if constexpr (KV8)
-          compute_tile(widen(T[u]), c, c.c0 + (j + NL * u) * TILE);
+          compute_tile(widen(T[u]), c, c.c0 + (j + NL * u) * TILE, may_hold_new);
         else
-          compute_tile(T[u], c, c.c0 + (j + NL * u) * TILE);
+          compute_tile(T[u], c, c.c0 + (j + NL * u) * TILE, may_hold_new);
       }
     }
   };
@@ -745,58 +769,61 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   int32_t pid[TPW];   // paged: page ids of the next batch to load
   fetch_pages(pid, pc, j);
   load_q(qf, pc);
-  turn_pending = APPEND;
   reset_state();
   tile_t TA[TPW], TB[TPW];
   load_batch(TA, pc, j, pid);
   fetch_pages(pid, pc, j + NL * TPW);
+  fill_angles(pc);
+  turn_piece(pc);
   // One step with `cur` loaded: false if it is the span's last batch (left
   // for the caller), else load the next batch into `nxt` and compute `cur`.
   auto step = [&](const tile_t (&cur)[TPW], tile_t (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
-    turn_if_pending(pc);
     const bool piece_done = j + NL * TPW >= pc.ntiles;
     const int64_t xn = PAGED ? pc.next : pc.x + (pc.c1 - pc.c0);
-    if (piece_done && xn >= s1) return false;
+    if (piece_done && xn >= s1) {
+      return false;
+    }
     if (piece_done) {
       // the piece ran to its unit's end: the next one starts the next unit
       const Ctx pn = open_at(next_unit<PAGED>(p, sm_P, sm_N, pc.at), xn);
       fetch_pages(pid, pn, tl);
       load_batch(nxt, pn, tl, pid);
       fetch_pages(pid, pn, tl + NL * TPW);
-      compute_batch(cur, pc, j);
+      compute_batch(cur, pc, j, std::true_type{});
       load_q(qf, pn);   // the next piece's queries: their latency overlaps end_piece
       end_piece(pc);
       reset_state();
       pc = pn;
-      turn_pending = APPEND;
+      fill_angles(pc);
+      turn_piece(pc);
       j = tl;
     } else {
       load_batch(nxt, pc, j + NL * TPW, pid);
       fetch_pages(pid, pc, j + 2 * NL * TPW);
-      compute_batch(cur, pc, j);
+      compute_batch(cur, pc, j, std::true_type{});
       j += NL * TPW;
     }
     return true;
   };
   for (;;) {
     // Steady state: while the piece has two more batches, neither step ends
-    // it, and this loop carries only the running softmax state.
-    turn_if_pending(pc);
+    // it, and this loop carries only the running softmax state.  Its tiles
+    // all lie below j + 2 NL TPW <= ntiles - 1, so none is the piece's last.
     while (j + 2 * NL * TPW < pc.ntiles) {
       load_batch(TB, pc, j + NL * TPW, pid);
       fetch_pages(pid, pc, j + 2 * NL * TPW);
-      compute_batch(TA, pc, j);
+      compute_batch(TA, pc, j, std::false_type{});
       load_batch(TA, pc, j + 2 * NL * TPW, pid);
       fetch_pages(pid, pc, j + 3 * NL * TPW);
-      compute_batch(TB, pc, j + NL * TPW);
+      compute_batch(TB, pc, j + NL * TPW, std::false_type{});
       j += 2 * NL * TPW;
     }
     if (!step(TA, TB)) {
-      compute_batch(TA, pc, j);
+      compute_batch(TA, pc, j, std::true_type{});
       break;
     }
     if (!step(TB, TA)) {
-      compute_batch(TB, pc, j);
+      compute_batch(TB, pc, j, std::true_type{});
       break;
     }
   }

@@ -302,8 +302,8 @@ gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, 
                            float rope_base, void* q_out, const gqa_dims* dims, void* stream);
 
 /*
- * gqa_append_rope followed by gqa_decode, in one launch (bf16, matrix-core
- * path): sequence b's new token at position m = max(seq_lens[b], 0) is
+ * gqa_append_rope followed by gqa_decode (bf16, matrix-core path), in one
+ * launch up to G = 16 query heads per KV head: sequence b's new token at position m = max(seq_lens[b], 0) is
  * turned and appended exactly as gqa_append_rope does (cache row m of every
  * KV head when m < capacity, q_out, new_seq_lens), and out is the attention
  * of the turned queries over the cache including that token, as gqa_decode
@@ -318,7 +318,11 @@ gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, 
  *   scale, out, dims, workspace, stream : as for gqa_decode;
  *                  dims->seq_len_hint must be 0 (GQA_ERR_INVALID_ARG)
  * For callers that run a decode step right after the append: the append's
- * launch (and its read of q) disappears into the decode kernel.
+ * launch (and its read of q) disappears into the decode kernel.  For G > 16
+ * with new_seq_lens given, the call enqueues the append kernel and then the
+ * decode of the grown cache (the fused kernel spills registers there and is
+ * slower); with new_seq_lens NULL it is one kernel at every G.  The results
+ * are the same either way.
  */
 gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                   const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,

@@ -408,10 +408,11 @@ FUSED_CASES = [
 ]
 
 
-def fused_vs_pipeline(x, base, scale, packed=None, **kw):
+def fused_vs_pipeline(x, base, scale, packed=None, lens_out=True, **kw):
     """The fused call and append_rope + decode on copies of the same inputs:
-    outputs, turned queries, caches and lengths bitwise equal.  Returns the
-    pipeline's (out, caches, new lengths)."""
+    outputs, turned queries, caches and lengths bitwise equal (lens_out
+    False: the fused call writes no lengths, and is then one kernel at every
+    G).  Returns the pipeline's (out, caches, new lengths)."""
     xd = {k: v.to(DEV) for k, v in x.items()}
     ka, va, kb, vb = xd["k"].clone(), xd["v"].clone(), xd["k"].clone(), xd["v"].clone()
     ext = dict(kv_offsets=packed[0].to(DEV), max_seq_len=packed[1]) if packed else {}
@@ -422,10 +423,11 @@ def fused_vs_pipeline(x, base, scale, packed=None, **kw):
     else:
         ref = gqa.decode(qo, ka, va, nl, scale, out_dtype=torch.float32, **kw)
     out, qf, nlf = gqa.decode_append_rope(xd["q"], xd["k_new"], xd["v_new"], kb, vb, xd["seq_lens"], base, scale,
-                                          out_dtype=torch.float32, **ext, **kw)
+                                          out_dtype=torch.float32, new_seq_lens=None if lens_out else False,
+                                          **ext, **kw)
     torch.cuda.synchronize()
     assert torch.equal(qf, qo), "turned queries differ"
-    assert torch.equal(nlf, nl), "new lengths differ"
+    assert (nlf is None) if not lens_out else torch.equal(nlf, nl), "new lengths differ"
     assert torch.equal(kb, ka) and torch.equal(vb, va), "caches differ"
     assert torch.equal(out, ref), "outputs differ: max %.3e" % float((out - ref).abs().max())
     return ref, ka, va, nl
@@ -449,6 +451,18 @@ def test_decode_append_rope_equals_the_two_calls(case, span, merge, tiles):
                             x["v"].to(DEV).clone(), x["seq_lens"].to(DEV), 10000.0)
     want = oracle.decode(qo.cpu(), ka.cpu(), va.cpu(), nl.cpu(), scale)
     assert float(np.abs(ref.double().cpu().numpy() - want).max()) <= 2e-3
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d_T%d" % c[:5])
+@pytest.mark.parametrize("span,merge", [(0, "auto"), (64, "fused"), (64, "kernel")])
+def test_decode_append_rope_one_kernel_without_lengths(case, span, merge):
+    """With no lengths to write the call is the fused kernel at every G (with
+    lengths, G > 16 runs as the append kernel and the decode): bitwise equal
+    to the two calls."""
+    B, H_q, H_kv, d, T, lens = case
+    x = make(B, H_q, H_kv, d, T, torch.bfloat16, 93 + B + d, lens)
+    note("fused append without lengths", case, span, merge)
+    fused_vs_pipeline(x, 10000.0, d ** -0.5, lens_out=False, chunk_tokens=span, merge=merge)
 
 
 def test_decode_append_rope_packed_cache():
