@@ -21,7 +21,7 @@ MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
           4: "GQA_ERR_LAUNCH"}
 SYMBOLS = ("gqa_append_rope", "gqa_append_rope_fp8", "gqa_append_rope_paged", "gqa_append_rope_paged_fp8",
-           "gqa_decode", "gqa_decode_append_rope", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8",
+           "gqa_decode", "gqa_decode_append_rope", "gqa_decode_append_rope_paged", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8",
            "gqa_decode_paged",
            "gqa_decode_paged_fp8",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode_append_rope.restype = ctypes.c_int
         L.gqa_decode_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp,
                                              dims_p, vp, sz, vp]
+        L.gqa_decode_append_rope_paged.restype = ctypes.c_int
+        L.gqa_decode_append_rope_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, ctypes.c_float,
+                                                   ctypes.c_float, vp, vp, dims_p, vp, sz, vp]
         L.gqa_decode_layers_fp8.restype = ctypes.c_int
         L.gqa_decode_layers_fp8.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                             vp, dims_p, vp, sz, vp]
@@ -490,6 +493,58 @@ def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: f
                                      tiles, merge, per_cu)
     _check(lib().gqa_decode_append_rope(*args))
     return keep[0], keep[1], keep[2]
+
+
+def decode_append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float, scale: float,
+                             max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, out=None,
+                             out_dtype=None, chunk_tokens: int = 0, workspace=None, stream=None, tiles: int = 0,
+                             merge: str = "auto", per_cu: int = 0):
+    """append_rope_paged followed by decode_paged (gqa_decode_append_rope_paged):
+    bf16 q [B,H_q,d], k_new/v_new [B,H_kv,d], pools [num_pages,H_kv,page,d]
+    written in place, block_table int32 [B,max_pages] (only read).  Returns
+    (out, q_out, new_seq_lens) as decode_append_rope does (new_seq_lens=False:
+    no lengths written, None returned)."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool"),
+                 (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k_new.dim() != 3 or v_new.shape != k_new.shape or k_pool.dim() != 4 or \
+            v_pool.shape != k_pool.shape or block_table.dim() != 2:
+        raise ValueError("expected q [B,H_q,d], k_new/v_new [B,H_kv,d], pools [num_pages,H_kv,page,d] and "
+                         "block_table [B,max_pages]")
+    B, H_q, d = q.shape
+    _, H_kv, page, _ = k_pool.shape
+    max_pages = block_table.shape[1]
+    if k_new.shape != (B, H_kv, d) or k_pool.shape[3] != d or block_table.shape[0] != B or \
+            block_table.dtype != torch.int32 or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("shape mismatch between q, k_new/v_new, pools, block_table and seq_lens")
+    for t in (k_new, v_new, k_pool, v_pool):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k_new, v_new and the pools must share one dtype")
+    T = max_pages * page if max_seq_len is None else int(max_seq_len)
+    dims = make_dims(B, H_q, H_kv, d, T, q.dtype, out_dtype, 0, chunk_tokens, "mfma", 0, tiles, merge, per_cu)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    lens_out = new_seq_lens is not False
+    if new_seq_lens is None or new_seq_lens is False:
+        new_seq_lens = torch.empty_like(seq_lens) if lens_out else None
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
+    for t, n in ((q_out, "q_out"), (new_seq_lens, "new_seq_lens"), (out, "out")):
+        if t is not None:
+            _require(t, n, dev)
+    if q_out.shape != q.shape or q_out.dtype != q.dtype or \
+            (lens_out and (new_seq_lens.shape != (B,) or new_seq_lens.dtype != torch.int32)):
+        raise ValueError("q_out must match q and new_seq_lens seq_lens")
+    if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
+        raise ValueError("out must be [B,H_q,d] of the output dtype")
+    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _check(lib().gqa_decode_append_rope_paged(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages), int(page),
+        _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out),
+        ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s))
+    return out, q_out, new_seq_lens
 
 
 def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, scale: float,

@@ -196,16 +196,16 @@ kernel_fn mfma_kernel(int hb, int, int tiles) {
   }
 }
 
-// The decode fused with the append (bf16, plain or packed cache): two
+// The decode fused with the append (bf16 cache: plain, packed or paged): two
 // tiles per batch for one head block, one otherwise.
-template <int D>
+template <int D, bool PAGED = false>
 kernel_fn mfma_append_kernel(int hb, int tiles) {
   switch (hb) {
     case 1:
-      return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, false, false, true>
-                        : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, false, false, true>;
-    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1, false, false, true>;
-    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, false, false, true>;
+      return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, PAGED, false, true>
+                        : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, PAGED, false, true>;
+    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1, PAGED, false, true>;
+    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, PAGED, false, true>;
   }
 }
 
@@ -228,6 +228,9 @@ kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan, const CacheArgs& ca) 
   const int G = d->num_q_heads / d->num_kv_heads;
   if (plan.mfma) {
     const int hb = (G + 15) / 16;
+    if (ca.k_new && ca.block_table)
+      return d->head_dim == 128 ? mfma_append_kernel<128, true>(hb, plan.tiles)
+                                : mfma_append_kernel<64, true>(hb, plan.tiles);
     if (ca.k_new)
       return d->head_dim == 128 ? mfma_append_kernel<128>(hb, plan.tiles) : mfma_append_kernel<64>(hb, plan.tiles);
     if (ca.e4m3 && ca.block_table)
@@ -504,10 +507,14 @@ gqa_status append_launch(const void* q, const void* k_new, const void* v_new, vo
 }
 }  // namespace
 
-gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                                  const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
-                                  float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// The fused append and decode on a plain or packed cache (block_table null)
+// or on a paged pool.
+gqa_status decode_append_launch(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                const int64_t* kv_offsets, const int32_t* block_table, int32_t max_pages,
+                                int32_t page, const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base,
+                                float scale, void* q_out, void* out, const gqa_dims* dims, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   gqa_status st = check_dims(dims, 1);
   if (st != GQA_OK) return st;
   if (dims->dtype != GQA_DTYPE_BF16 || !use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // matrix-core kernel only
@@ -520,27 +527,50 @@ gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* 
   if (q_out == q || static_cast<const void*>(new_seq_lens) == static_cast<const void*>(seq_lens))
     return GQA_ERR_INVALID_ARG;
   if (new_seq_lens && !aligned(new_seq_lens, 4)) return GQA_ERR_INVALID_ARG;
+  CacheArgs cb;
+  cb.kv_offsets = kv_offsets;
+  cb.block_table = block_table;
+  cb.max_pages = max_pages;
+  cb.page = page;
   const int64_t G = dims->num_q_heads / dims->num_kv_heads;
   if (G > 16 && new_seq_lens) {
     // Two head blocks: there the fused kernel needs more registers than a
     // SIMD holds and spills at every piece end, and the append kernel followed
     // by the decode of the grown cache is faster, with the same results (both
     // turn, round and substitute alike).
-    st = append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, nullptr, 0, 0, seq_lens, new_seq_lens,
-                       rope_base, q_out, dims, stream);
+    st = append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, block_table, max_pages, page, seq_lens,
+                       new_seq_lens, rope_base, q_out, dims, stream);
     if (st != GQA_OK) return st;
-    CacheArgs cb;
-    cb.kv_offsets = kv_offsets;
     return launch(1, q_out, k_cache, v_cache, cb, new_seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
   }
-  CacheArgs ca;
-  ca.kv_offsets = kv_offsets;
+  CacheArgs ca = cb;
   ca.k_new = k_new;
   ca.v_new = v_new;
   ca.q_out = q_out;
   ca.new_seq_lens = new_seq_lens;
   ca.rope_base = (double)rope_base;
   return launch(1, q, k_cache, v_cache, ca, seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
+}
+}  // namespace
+
+gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int64_t* kv_offsets, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                  float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, nullptr, 0, 0, seq_lens, new_seq_lens,
+                              rope_base, scale, q_out, out, dims, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_append_rope_paged(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                        void* v_pool, const int32_t* block_table, int32_t max_pages,
+                                        int32_t page_size, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                        float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (page_size <= 0 || page_size % 16 != 0 || max_pages <= 0) return GQA_ERR_INVALID_ARG;
+  if (dims && (int64_t)max_pages * page_size < dims->max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (!block_table || !aligned(block_table, 4)) return GQA_ERR_INVALID_ARG;
+  return decode_append_launch(q, k_new, v_new, k_pool, v_pool, nullptr, block_table, max_pages, page_size, seq_lens,
+                              new_seq_lens, rope_base, scale, q_out, out, dims, workspace, workspace_bytes, stream);
 }
 
 gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

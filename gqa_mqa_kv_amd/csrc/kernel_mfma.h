@@ -204,16 +204,17 @@ __device__ __forceinline__ u32x2 v_operand(const Tile16K8<D>& T, int r) {
 // KV8: cache elements are one-byte E4M3 values (bf16 queries).  Tiles move
 // as bytes and are widened to bf16, exactly, just before the products; the
 // key scale is folded into p.scale_log2 and the value scale into p.out_mul.
-// APPEND (plain or packed bf16 cache): the decode step fused with the append
-// of each sequence's new token.  The token's position m comes from
-// seq_lens[b]; its queries are turned by the rotary embedding in registers
-// at the first tile of every piece (and written to q_out by the unit's
-// first piece), and the attention covers the new token: the wavefront whose
-// tile holds row m takes the turned key and the value from k_new / v_new
-// instead of the cache and writes them to cache row m.
+// APPEND (bf16 cache: plain, packed or paged): the decode step fused with
+// the append of each sequence's new token.  The token's position m comes
+// from seq_lens[b]; the queries are turned by the rotary embedding in
+// registers when a piece becomes current (and written to q_out by the
+// unit's first piece), and the attention covers the new token: the piece
+// that ends a grown unit turns the new key, its tile holding row m takes
+// the turned key and the value instead of the cache's row, and wavefront 0
+// writes them to cache row m.
 template <int D, int HB, int HG, int NW, int TPW, bool PAGED, bool KV8, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
-  static_assert(!APPEND || (!PAGED && !KV8), "the fused append takes a plain or packed bf16 cache");
+  static_assert(!APPEND || !KV8, "the fused append takes a bf16 cache");
   static_assert(NW % HG == 0, "head groups must divide the wavefronts");
   constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
   constexpr int NL = NW / HG;             // tile lanes
@@ -575,8 +576,12 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         }
         if (q4 == 0) *reinterpret_cast<vrow_t*>(vs + VW * m16) = vnew;
         if (wave == 0) {
-          uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + (int64_t)c.mnew * D;
-          uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + (int64_t)c.mnew * D;
+          // cache row m: the unit's row m, or row m % page of the page the
+          // sequence's table names for it (within the pool shifted to head g)
+          int64_t crow = c.mnew;
+          if constexpr (PAGED) crow = (int64_t)c.pages[c.mnew / p.page] * p.H_kv * p.page + c.mnew % p.page;
+          uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + crow * D;
+          uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + crow * D;
           if (m16 == 0) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(kc + 32 * s + 8 * q4) = knew[s];

@@ -330,6 +330,22 @@ gqa_status gqa_decode_append_rope(const void* q, const void* k_new, const void* 
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same fused step on a cache held in pages of a pool: gqa_append_rope_paged
+ * followed by gqa_decode_paged, bit for bit (one launch up to G = 16, or with
+ * new_seq_lens NULL; else the two kernels).  The new token of sequence b goes
+ * to row m % page_size of page block_table[b][m / page_size] of each KV head,
+ * m = max(seq_lens[b], 0), when m < dims->max_seq_len; that table entry must
+ * name a page of the pool (the caller allocates it first).  k_pool, v_pool,
+ * block_table, max_pages, page_size: as for gqa_decode_paged; everything else
+ * as for gqa_decode_append_rope.  The table is only read.
+ */
+gqa_status gqa_decode_append_rope_paged(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                        void* v_pool, const int32_t* block_table, int32_t max_pages,
+                                        int32_t page_size, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                        float rope_base, float scale, void* q_out, void* out, const gqa_dims* dims,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The same step for a cache held in pages of a pool (the layout of
  * gqa_decode_paged): the rotated key and the value of sequence b's new token
  * go to row m % page_size of page block_table[b][m / page_size] of each KV

@@ -314,6 +314,29 @@ def test_decode_append_rope_validation():
     assert call(dims(B=0), q=None, kn=None, vn=None, sl=None, nl=None, qo=None) == OK
 
 
+def test_decode_append_rope_paged_validation():
+    """The paged fused entry point applies the page rules of gqa_decode_paged
+    and the rules of the fused call."""
+    d = dims(T_max=1024)
+    Q, KN, VN, KP, VP, SL, NL, QO, OUT = (FAKE + 0x1000 * i for i in range(9))
+    call = lambda dd=d, bt=FAKE, mp=64, pg=16, qo=QO, nl=NL, base=10000.0: gqa.lib().gqa_decode_append_rope_paged(
+        Q, KN, VN, KP, VP, bt, mp, pg, SL, nl, base, 0.125, qo, OUT, ctypes.byref(dd), None, 0, None)
+    assert call() == WORKSPACE                                          # valid: only the workspace is missing
+    assert call(nl=None) == WORKSPACE                                   # new lengths are optional
+    for pg in (0, 8, 24, -16):
+        assert call(pg=pg) == INVALID, pg                               # a positive multiple of 16
+    assert call(mp=0) == INVALID
+    assert call(mp=63) == INVALID                                       # max_pages * page_size < max_seq_len
+    assert call(bt=None) == INVALID
+    assert call(bt=FAKE + 2) == INVALID                                 # table 4-byte aligned
+    assert call(dims(T_max=1024, dtype=torch.float32)) == UNSUPPORTED
+    assert call(dims(T_max=1024, seq_len_hint=100)) == INVALID
+    assert call(qo=None) == INVALID
+    assert call(qo=Q) == INVALID
+    assert call(nl=SL) == INVALID
+    assert call(base=float("nan")) == INVALID
+
+
 def test_decode_paged_fp8_validation():
     """The paged E4M3 entry point applies the rules of both parents."""
     d = dims(T_max=1024)

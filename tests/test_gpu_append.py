@@ -492,3 +492,35 @@ def test_decode_append_rope_full_8b_layer():
              k=r(w.B, w.H_kv, T, w.d), v=r(w.B, w.H_kv, T, w.d),
              seq_lens=torch.full((w.B,), w.T_max, dtype=torch.int32))
     fused_vs_pipeline(x, 500000.0, w.scale)
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d_T%d" % c[:5])
+@pytest.mark.parametrize("page", [16, 48])
+@pytest.mark.parametrize("span,merge,lens_out", [(0, "auto", True), (0, "auto", False), (64, "fused", False),
+                                                 (64, "kernel", True)])
+def test_decode_append_rope_paged_equals_the_two_calls(case, page, span, merge, lens_out):
+    """gqa_decode_append_rope_paged against gqa_append_rope_paged followed by
+    gqa_decode_paged on copies of one shuffled pool: outputs, turned queries,
+    pools and lengths bitwise equal (the new token's page is allocated, also
+    for a negative length, whose token goes to position 0)."""
+    B, H_q, H_kv, d, T, lens = case
+    x = make(B, H_q, H_kv, d, T, torch.bfloat16, 97 + B + d + page, lens)
+    note("fused paged append", case, page, span, merge, lens_out)
+    alloc = dict(x, seq_lens=(x["seq_lens"].clamp(min=0) + 1).clamp(max=T))
+    kp, vp, table = workloads.to_pages(alloc, page, seed=11 + page)
+    kp, vp, table = kp.to(DEV), vp.to(DEV), table.to(DEV)
+    ka, va, kb, vb = kp.clone(), vp.clone(), kp.clone(), vp.clone()
+    q, kn, vn, sl = (x[n].to(DEV) for n in ("q", "k_new", "v_new", "seq_lens"))
+    scale, base = d ** -0.5, 10000.0
+    kw = dict(chunk_tokens=span, merge=merge, max_seq_len=T)
+    qo, nl = gqa.append_rope_paged(q, kn, vn, ka, va, table, sl, base, max_seq_len=T)
+    ref = gqa.decode_paged(qo, ka, va, table, nl, scale, out_dtype=torch.float32, **kw)
+    out, qf, nlf = gqa.decode_append_rope_paged(q, kn, vn, kb, vb, table, sl, base, scale, out_dtype=torch.float32,
+                                                new_seq_lens=None if lens_out else False, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(qf, qo), "turned queries differ"
+    assert (nlf is None) if not lens_out else torch.equal(nlf, nl), "new lengths differ"
+    # the pools hold NaN in unused rows: compare bit patterns
+    assert torch.equal(kb.view(torch.int16), ka.view(torch.int16)), "key pools differ"
+    assert torch.equal(vb.view(torch.int16), va.view(torch.int16)), "value pools differ"
+    assert torch.equal(out, ref), "outputs differ: max %.3e" % float((out - ref).abs().max())
