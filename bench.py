@@ -246,10 +246,19 @@ def time_fused_append(torch, gqa, w, batches, stream, steps: int, warmup: int):
         lens = (x["seq_lens"] - 1).clamp(min=0).to(torch.int32)
         new_lens = torch.empty_like(lens)
         q_out = torch.empty_like(x["q"])
-        app = gqa.prepare_append(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, q_out=q_out, new_seq_lens=new_lens)
-        dec = gqa.prepare(q_out, x["k"], x["v"], new_lens, x["scale"])
+        if "pool" in x:   # paged: the pool and table of the plain step (every appended row has its page)
+            kp, vp, table = x["pool"]
+            app = gqa.prepare_append_paged(x["q"], kn, vn, kp, vp, table, lens, 500000.0, max_seq_len=w.T_max,
+                                           q_out=q_out, new_seq_lens=new_lens)
+            dec = gqa.prepare_paged(q_out, kp, vp, table, new_lens, x["scale"], max_seq_len=w.T_max)
+            one.append(gqa.prepare_decode_append_paged(x["q"], kn, vn, kp, vp, table, lens, 500000.0, x["scale"],
+                                                       max_seq_len=w.T_max))
+        else:
+            app = gqa.prepare_append(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, q_out=q_out,
+                                     new_seq_lens=new_lens)
+            dec = gqa.prepare(q_out, x["k"], x["v"], new_lens, x["scale"])
+            one.append(gqa.prepare_decode_append(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, x["scale"]))
         two.append((app, dec))
-        one.append(gqa.prepare_decode_append(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, x["scale"]))
 
     def run(fn):
         for i in range(warmup):
@@ -354,6 +363,7 @@ def main():
         if args.paged:
             kp, vp, table = workloads.to_pages(x, args.paged, seed=1000 + r, spare=1)
             del x["k"], x["v"]   # the pool holds the cache now
+            x["pool"] = (kp, vp, table)
             launchers.append(gqa.prepare_paged(x["q"], kp, vp, table, x["seq_lens"], x["scale"],
                                                max_seq_len=w.T_max, out_dtype=out_dtype,
                                                chunk_tokens=args.chunk_tokens))
@@ -442,8 +452,9 @@ def main():
     if w.layers > 1 and not args.no_extras:
         result["sequential_single_layer_launches"] = time_layers_one_by_one(torch, gqa, workloads, w, batches[0],
                                                                             stream, out_dtype, fp8=fp8)
-    if w.layers == 1 and w.dtype == torch.bfloat16 and not args.paged and not fp8 and not args.no_extras:
-        result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
+    if w.layers == 1 and w.dtype == torch.bfloat16 and not fp8 and not args.no_extras:
+        if not args.paged:
+            result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
         result["step_with_append"] = time_fused_append(torch, gqa, w, batches, stream, min(args.steps, 100),
                                                        args.warmup)
     if not args.no_cpu_baseline and w.layers == 1:

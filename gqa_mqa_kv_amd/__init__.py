@@ -22,10 +22,10 @@ call.
 from ._binding import (GqaDims, GqaError, Prepared, append_rope, append_rope_fp8, append_rope_paged,
                        append_rope_paged_fp8, decode, decode_append_rope, decode_append_rope_paged, decode_fp8, decode_layers, decode_layers_fp8, decode_paged,
                        decode_paged_fp8, default_workspace, lib, make_dims, plan, prepare, prepare_append,
-                       prepare_decode_append, prepare_fp8, prepare_layers_fp8, prepare_paged, prepare_paged_fp8, status_string,
+                       prepare_decode_append, prepare_decode_append_paged, prepare_append_paged, prepare_fp8, prepare_layers_fp8, prepare_paged, prepare_paged_fp8, status_string,
                        workspace_bytes)
 
 __all__ = ["GqaDims", "GqaError", "Prepared", "prepare", "decode", "decode_append_rope", "decode_append_rope_paged", "decode_layers", "decode_layers_fp8",
            "decode_paged", "decode_fp8", "decode_paged_fp8", "append_rope", "append_rope_fp8", "append_rope_paged",
-           "append_rope_paged_fp8", "default_workspace", "lib", "make_dims", "plan", "prepare_append", "prepare_decode_append", "prepare_fp8",
+           "append_rope_paged_fp8", "default_workspace", "lib", "make_dims", "plan", "prepare_append", "prepare_decode_append", "prepare_decode_append_paged", "prepare_append_paged", "prepare_fp8",
            "prepare_layers_fp8", "prepare_paged", "prepare_paged_fp8", "status_string", "workspace_bytes"]

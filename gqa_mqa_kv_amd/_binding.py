@@ -495,15 +495,9 @@ def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: f
     return keep[0], keep[1], keep[2]
 
 
-def decode_append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float, scale: float,
-                             max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, out=None,
-                             out_dtype=None, chunk_tokens: int = 0, workspace=None, stream=None, tiles: int = 0,
-                             merge: str = "auto", per_cu: int = 0):
-    """append_rope_paged followed by decode_paged (gqa_decode_append_rope_paged):
-    bf16 q [B,H_q,d], k_new/v_new [B,H_kv,d], pools [num_pages,H_kv,page,d]
-    written in place, block_table int32 [B,max_pages] (only read).  Returns
-    (out, q_out, new_seq_lens) as decode_append_rope does (new_seq_lens=False:
-    no lengths written, None returned)."""
+def _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, scale, max_seq_len,
+                              q_out, new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream, tiles, merge,
+                              per_cu):
     dev = q.device
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool"),
                  (block_table, "block_table"), (seq_lens, "seq_lens")):
@@ -540,11 +534,63 @@ def decode_append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_l
         raise ValueError("out must be [B,H_q,d] of the output dtype")
     ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    _check(lib().gqa_decode_append_rope_paged(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages), int(page),
-        _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out),
-        ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s))
-    return out, q_out, new_seq_lens
+    args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages),
+            int(page), _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out),
+            ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
+    return args, (out, q_out, new_seq_lens, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, ws, dims)
+
+
+def decode_append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float, scale: float,
+                             max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, out=None,
+                             out_dtype=None, chunk_tokens: int = 0, workspace=None, stream=None, tiles: int = 0,
+                             merge: str = "auto", per_cu: int = 0):
+    """append_rope_paged followed by decode_paged (gqa_decode_append_rope_paged):
+    bf16 q [B,H_q,d], k_new/v_new [B,H_kv,d], pools [num_pages,H_kv,page,d]
+    written in place, block_table int32 [B,max_pages] (only read).  Returns
+    (out, q_out, new_seq_lens) as decode_append_rope does (new_seq_lens=False:
+    no lengths written, None returned)."""
+    args, keep = _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, scale,
+                                           max_seq_len, q_out, new_seq_lens, out, out_dtype, chunk_tokens, workspace,
+                                           stream, tiles, merge, per_cu)
+    _check(lib().gqa_decode_append_rope_paged(*args))
+    return keep[0], keep[1], keep[2]
+
+
+def prepare_decode_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
+                                scale: float, max_seq_len=None, out_dtype=None, chunk_tokens: int = 0, stream=None,
+                                tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """As prepare, for gqa_decode_append_rope_paged (each call appends again:
+    the new token overwrites the same pool rows with the same values)."""
+    args, keep = _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, scale,
+                                           max_seq_len, None, None, None, out_dtype, chunk_tokens, None, stream, tiles,
+                                           merge, per_cu)
+    pr = Prepared(lib().gqa_decode_append_rope_paged, args, keep)
+    pr()
+    return pr
+
+
+def prepare_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
+                         max_seq_len: Optional[int] = None, stream=None, q_out=None, new_seq_lens=None):
+    """As prepare_append, for append_rope_paged: validates by running it once
+    and returns a callable that enqueues the same call again."""
+    q_out, new_lens = append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base,
+                                        max_seq_len=max_seq_len, stream=stream, q_out=q_out,
+                                        new_seq_lens=new_seq_lens)
+    B, H_q, d = q.shape
+    _, H_kv, page, _ = k_pool.shape
+    max_pages = block_table.shape[1]
+    T = max_pages * page if max_seq_len is None else int(max_seq_len)
+    dims = make_dims(B, H_q, H_kv, d, T, q.dtype)
+    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages),
+            int(page), _ptr(seq_lens), _ptr(new_lens), float(rope_base), _ptr(q_out), ctypes.byref(dims), s)
+    fn = lib().gqa_append_rope_paged
+    keep = (q_out, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, new_lens, dims)
+
+    def call():
+        _check(fn(*args))
+        return keep[0]
+    return call
 
 
 def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, scale: float,
