@@ -524,3 +524,32 @@ def test_decode_append_rope_paged_equals_the_two_calls(case, page, span, merge, 
     assert torch.equal(kb.view(torch.int16), ka.view(torch.int16)), "key pools differ"
     assert torch.equal(vb.view(torch.int16), va.view(torch.int16)), "value pools differ"
     assert torch.equal(out, ref), "outputs differ: max %.3e" % float((out - ref).abs().max())
+
+
+def test_prepared_paged_calls_repeat_the_direct_ones():
+    """prepare_decode_append_paged and prepare_append_paged (the timing
+    loops' callables) enqueue the same calls as the direct ones: a repeated
+    call rewrites the same rows with the same values and gives the same
+    outputs, bitwise."""
+    B, H_q, H_kv, d, T, page = 4, 32, 8, 128, 600, 32
+    x = make(B, H_q, H_kv, d, T, torch.bfloat16, 131, [100, 599, 0, 345])
+    note("prepared paged calls")
+    alloc = dict(x, seq_lens=(x["seq_lens"].clamp(min=0) + 1).clamp(max=T))
+    kp, vp, table = (t.to(DEV) for t in workloads.to_pages(alloc, page, seed=17))
+    q, kn, vn, sl = (x[n].to(DEV) for n in ("q", "k_new", "v_new", "seq_lens"))
+    scale, base = d ** -0.5, 10000.0
+    ka, va, kb, vb = kp.clone(), vp.clone(), kp.clone(), vp.clone()
+    out, qo, nl = gqa.decode_append_rope_paged(q, kn, vn, ka, va, table, sl, base, scale, max_seq_len=T)
+    pr = gqa.prepare_decode_append_paged(q, kn, vn, kb, vb, table, sl, base, scale, max_seq_len=T)
+    again = pr().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(again, out)
+    assert torch.equal(kb.view(torch.int16), ka.view(torch.int16))
+    assert torch.equal(vb.view(torch.int16), va.view(torch.int16))
+    kc, vc = kp.clone(), vp.clone()
+    app = gqa.prepare_append_paged(q, kn, vn, kc, vc, table, sl, base, max_seq_len=T)
+    q2 = app().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(q2, qo)
+    assert torch.equal(kc.view(torch.int16), ka.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), va.view(torch.int16))
