@@ -19,11 +19,12 @@ GQA_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 MERGES = {"auto": 0, "fused": 1, "kernel": 2}
 STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "GQA_ERR_WORKSPACE",
-          4: "GQA_ERR_LAUNCH"}
+          4: "GQA_ERR_LAUNCH", 5: "GQA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # GQA_NOALLOC_SCRATCH_BYTES
 SYMBOLS = ("gqa_append_rope", "gqa_append_rope_fp8", "gqa_append_rope_paged", "gqa_append_rope_paged_fp8",
            "gqa_decode", "gqa_decode_append_rope", "gqa_decode_append_rope_paged", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8",
            "gqa_decode_paged",
-           "gqa_decode_paged_fp8",
+           "gqa_decode_paged_fp8", "gqa_decode_noalloc",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
 
 
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
         dims_p = ctypes.POINTER(GqaDims)
         L.gqa_decode.restype = ctypes.c_int
         L.gqa_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.gqa_decode_noalloc.restype = ctypes.c_int
+        L.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp]
         L.gqa_decode_layers.restype = ctypes.c_int
         L.gqa_decode_layers.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.gqa_decode_append_rope.restype = ctypes.c_int
@@ -186,6 +189,38 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
     _check(lib().gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out),
                             ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                             s))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None, chunk_tokens: int = 0,
+                   path: str = "auto", seq_len_hint: int = 0, stream=None, waves: int = 0, tiles: int = 0,
+                   merge: str = "auto", per_cu: int = 0):
+    """decode through gqa_decode_noalloc: the partial states live in the
+    library's static device buffer (GQA_NOALLOC_SCRATCH_BYTES per GPU), so
+    the call allocates nothing on the device beyond ``out`` when ``out`` is
+    None (pass ``out`` to allocate nothing at all).  Calls that may overlap in
+    time on one GPU race on that buffer."""
+    dev = q.device
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _require(t, n, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,H_q,d] and k/v [B,H_kv,T_max,d]")
+    B, H_q, d = q.shape
+    _, H_kv, T_max, _ = k_cache.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != d or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles,
+                     merge, per_cu)
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
+    _require(out, "out", dev)
+    if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
+        raise ValueError("out must be [B,H_q,d] of the output dtype")
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    _check(lib().gqa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out),
+                                    ctypes.byref(dims), s))
     return out
 
 

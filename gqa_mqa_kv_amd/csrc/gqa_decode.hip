@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kernel_mfma.h"
 #include "kernel_rope.h"
@@ -610,6 +611,81 @@ gqa_status gqa_append_rope_paged_fp8(const void* q, const void* k_new, const voi
                        new_seq_lens, rope_base, q_out, dims, stream, true, k_scale, v_scale);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// gqa_decode_noalloc: the partial states of gqa_decode in a static device
+// buffer instead of a caller workspace, for callers that cannot allocate.
+// In host code `scratch` names a host-side stand-in of the array, not its
+// device address: the address of each device's copy is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// pointer is ever passed to a kernel.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[GQA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;   // device address of this device's copy of `scratch`
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+__global__ __launch_bounds__(256) void zero_words(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
+// The device address of `scratch` on the device `stream` runs on (the
+// current device), or nullptr when the runtime cannot give it.
+void* scratch_ptr(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return;   // slot.ptr stays null: every call on this device reports GQA_ERR_LAUNCH
+    }
+    // The arrival counters must start at zero.  The array is zero when the
+    // code object is loaded; clear the counter region once more on the
+    // caller's stream, except inside a graph capture, where the clear would
+    // only run at replay.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+      void* args[] = {&p, nullptr};
+      int64_t n = (int64_t)(kCounterBytes / 4);
+      args[1] = &n;
+      if (hipLaunchKernel(reinterpret_cast<const void*>(zero_words), dim3(256), dim3(256), args, 0, stream) !=
+          hipSuccess) {
+        (void)hipGetLastError();
+        return;
+      }
+    }
+    slot.ptr = p;
+  });
+  return slot.ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                              float scale, void* out, const gqa_dims* dims, void* stream) {
+  gqa_status st = check_dims(dims, 1);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  if (dims->batch == 0) return GQA_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return GQA_ERR_INVALID_ARG;
+  if (make_plan(dims, 1).ws_bytes > GQA_NOALLOC_SCRATCH_BYTES) return GQA_ERR_SCRATCH;
+  void* ws = scratch_ptr(static_cast<hipStream_t>(stream));
+  if (!ws) return GQA_ERR_LAUNCH;
+  return launch(1, q, k_cache, v_cache, CacheArgs{}, seq_lens, scale, out, dims, ws, GQA_NOALLOC_SCRATCH_BYTES,
+                stream);
+}
+
 const char* gqa_status_string(gqa_status s) {
   switch (s) {
     case GQA_OK: return "GQA_OK";
@@ -617,6 +693,7 @@ const char* gqa_status_string(gqa_status s) {
     case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: unsupported shape, dtype or path";
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
     case GQA_ERR_LAUNCH: return "GQA_ERR_LAUNCH: kernel launch failed";
+    case GQA_ERR_SCRATCH: return "GQA_ERR_SCRATCH: the call needs more scratch than the static buffer holds";
   }
   return "unknown gqa_status";
 }

@@ -21,7 +21,9 @@
  * ---------------------------------------
  * Memory.  Every tensor pointer is a device pointer owned by the caller; the
  *   library allocates nothing, keeps no pointer after the call returns and
- *   has no mutable global state.  All tensors are dense and row-major.
+ *   has no mutable global state (apart from the static buffer that
+ *   gqa_decode_noalloc uses in place of a workspace).  All tensors are dense
+ *   and row-major.
  *   q, out    : [B][H_q][d]           (per layer, see gqa_decode_layers)
  *   k_cache,
  *   v_cache   : [B][H_kv][T_max][d]   (dense layout)
@@ -80,7 +82,9 @@ typedef enum gqa_status {
   GQA_ERR_UNSUPPORTED = 2,  /* head_dim not 64/128, G > 64, dtype/path pairing, more than
                                4096 sequences on the matrix-core path */
   GQA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
-  GQA_ERR_LAUNCH = 4        /* the HIP runtime refused the launch */
+  GQA_ERR_LAUNCH = 4,       /* the HIP runtime refused the launch */
+  GQA_ERR_SCRATCH = 5       /* gqa_decode_noalloc only: the call needs more partial-state
+                               memory than the library's static buffer holds */
 } gqa_status;
 
 /* Which kernel family runs the step.  AUTO picks the matrix-core kernel for
@@ -381,6 +385,33 @@ gqa_status gqa_append_rope_paged_fp8(const void* q, const void* k_new, const voi
                                      const int32_t* block_table, int32_t max_pages, int32_t page_size,
                                      const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base, float k_scale,
                                      float v_scale, void* q_out, const gqa_dims* dims, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * gqa_decode with its partial states kept in a static device buffer of the
+ * library instead of a caller workspace: GQA_NOALLOC_SCRATCH_BYTES on each
+ * GPU the call runs on, held from the first call on that GPU until the
+ * process ends.  The call allocates and frees nothing.
+ *   Limit: a call whose plan needs more than GQA_NOALLOC_SCRATCH_BYTES of
+ *   partial states (gqa_decode_workspace_bytes(dims, 1) bounds what it
+ *   needs) returns GQA_ERR_SCRATCH before enqueueing anything.  32 MiB holds
+ *   every split up to G = 64 at one workgroup per CU on a 256-CU part.
+ *   Sharing: every call on one GPU uses that GPU's one buffer, and it keeps
+ *   the last call's contents.  Calls ordered on one stream may follow each
+ *   other freely (each completed call leaves the arrival counters at zero);
+ *   calls that may overlap in time on one GPU (other streams, other host
+ *   threads) race and must not be issued.
+ *   First call on a device: the buffer's device address is looked up, and
+ *   its counter region is zero-filled by a kernel on `stream` (skipped while
+ *   the stream is capturing a graph; the buffer is zero when the library is
+ *   loaded).  `stream` runs on the current device (NULL: its default stream).
+ * q, k_cache, v_cache, seq_lens, scale, out, dims, stream and every other
+ * error as for gqa_decode; the results equal gqa_decode's bit for bit.
+ */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                              float scale, void* out, const gqa_dims* dims, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* gqa_status_string(gqa_status status);

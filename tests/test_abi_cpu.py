@@ -424,3 +424,22 @@ def test_page_layout_of_the_input_generator():
     spare = [p for p in range(kp.shape[0]) if p not in seen]
     assert len(spare) == 2 and all(bool(torch.isnan(kp[p]).all()) for p in spare)
     assert bool(torch.isnan(kp[int(table[1, 1]), :, 1:]).all())   # tail of sequence 1's last page
+
+
+def test_noalloc_validates_and_refuses_plans_beyond_its_buffer():
+    """gqa_decode_noalloc checks its arguments like gqa_decode and refuses, on
+    the host, a plan whose partial states exceed the static buffer."""
+    lib = gqa.lib()
+    d = dims()
+    assert lib.gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None) == INVALID
+    assert lib.gqa_decode_noalloc(None, FAKE, FAKE, FAKE, 0.1, FAKE, ctypes.byref(d), None) == INVALID
+    assert lib.gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, ctypes.byref(d), None) == INVALID
+    assert lib.gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, ctypes.byref(dims(d=96)), None) == UNSUPPORTED
+    empty = dims(B=0)
+    assert lib.gqa_decode_noalloc(None, None, None, None, 0.1, None, ctypes.byref(empty), None) == OK
+    big = dims(B=64, H_q=64, H_kv=1, d=128, T_max=32768, chunk_tokens=64)
+    assert gqa.workspace_bytes(big) > _binding.NOALLOC_SCRATCH_BYTES
+    assert lib.gqa_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, ctypes.byref(big), None) == 5   # GQA_ERR_SCRATCH
+    src = open(HEADER).read()
+    assert "#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in src
+    assert _binding.NOALLOC_SCRATCH_BYTES == 32 << 20
