@@ -247,6 +247,42 @@ def test_append_then_decode_paged():
     assert err <= 2e-3, err
 
 
+@pytest.mark.parametrize("H_q,H_kv", [(32, 8), (64, 8), (32, 1)], ids=["G4", "G8", "G32"])
+@pytest.mark.parametrize("span", [0, 64])
+def test_decode_append_rope_paged_matches_oracle(H_q, H_kv, span):
+    """The fused paged step (gqa_decode_append_rope_paged) against the oracle
+    directly: its rotation of the queries and of every cached key at its own
+    position (the new token's at m = seq_lens[b]), then its attention over
+    the cache including the new token.  G = 32 with lengths runs as the
+    append kernel and the decode; spans of 64 tokens cut units into pieces,
+    so the new token lies in a unit's last piece."""
+    B, d, T, page = 3, 128, 700, 32
+    g = torch.Generator().manual_seed(79 + H_q + H_kv + span)
+    lens = torch.tensor([0, 350, 699], dtype=torch.int32)
+    raw_k = torch.randn(B, H_kv, T, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H_kv, T, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, H_q, d, generator=g).to(torch.bfloat16)
+    base, scale = 10000.0, d ** -0.5
+    orc = oracle.default()
+    rot_k = torch.from_numpy(orc.rope(raw_k, torch.arange(T).view(1, 1, T), base)).to(torch.bfloat16)
+    kp, vp, table = paged_for_append({"k": rot_k, "v": v, "seq_lens": lens}, page, seed=6 + span)
+    m = lens.long()
+    kn, vn = raw_k[torch.arange(B), :, m], v[torch.arange(B), :, m]
+    note("fused paged append vs oracle", H_q, H_kv, span)
+    kd, vd, td = kp.to(DEV), vp.to(DEV), table.to(DEV)
+    out, q_rot, nl = gqa.decode_append_rope_paged(q.to(DEV), kn.contiguous().to(DEV), vn.contiguous().to(DEV), kd,
+                                                  vd, td, lens.to(DEV), base, scale, out_dtype=torch.float32,
+                                                  max_seq_len=T, chunk_tokens=span)
+    torch.cuda.synchronize()
+    ref_q = orc.rope(q.double(), m.view(B, 1), base)
+    assert rot_err_ok(q_rot, ref_q, torch.bfloat16)
+    assert nl.cpu().tolist() == (lens + 1).tolist()
+    ref_k = torch.from_numpy(orc.rope(raw_k.double(), torch.arange(T).view(1, 1, T), base))
+    ref = orc.decode(torch.from_numpy(ref_q), ref_k, v.double(), (lens + 1).tolist(), scale)
+    err = float(np.abs(out.double().cpu().numpy() - ref).max())
+    assert err <= 2e-3, err
+
+
 # ------------------------------------------------ quantising append (E4M3) --
 def codes_within(gpu_codes, y, eps):
     """Each code decodes to a value the E4M3 encoder gives for some point of
@@ -541,6 +577,9 @@ def test_prepared_paged_calls_repeat_the_direct_ones():
     ka, va, kb, vb = kp.clone(), vp.clone(), kp.clone(), vp.clone()
     out, qo, nl = gqa.decode_append_rope_paged(q, kn, vn, ka, va, table, sl, base, scale, max_seq_len=T)
     pr = gqa.prepare_decode_append_paged(q, kn, vn, kb, vb, table, sl, base, scale, max_seq_len=T)
+    torch.cuda.synchronize()
+    assert torch.equal(kb.view(torch.int16), kp.view(torch.int16))   # preparing enqueues nothing
+    pr()
     again = pr().clone()
     torch.cuda.synchronize()
     assert torch.equal(again, out)
@@ -548,6 +587,7 @@ def test_prepared_paged_calls_repeat_the_direct_ones():
     assert torch.equal(vb.view(torch.int16), va.view(torch.int16))
     kc, vc = kp.clone(), vp.clone()
     app = gqa.prepare_append_paged(q, kn, vn, kc, vc, table, sl, base, max_seq_len=T)
+    app()
     q2 = app().clone()
     torch.cuda.synchronize()
     assert torch.equal(q2, qo)

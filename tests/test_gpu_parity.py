@@ -475,18 +475,27 @@ def test_full_70b_ragged_layer():
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["grouping-sweep-mha", "grouping-sweep-gqa", "grouping-sweep-mqa"])
 def test_full_grouping_sweep(name):
-    full_check(name, sample=48)
+    """Every output of the three grouping-sweep runs (8 x 32 heads over
+    32768 tokens each) against the oracle."""
+    full_check(name)
 
 
 @pytest.mark.timeout(600)
-def test_full_grouping_sweep_mqa_fp32_inputs():
-    full_check("grouping-sweep-mqa", sample=24, dtype=torch.float32, path="valu")
+@pytest.mark.parametrize("name", ["llama-70b-ragged-layer", "grouping-sweep-mha", "grouping-sweep-gqa",
+                                  "grouping-sweep-mqa"])
+def test_full_size_fp32_inputs(name):
+    """fp32 copies of the ragged 70B layer and of the grouping sweep, every
+    output at the fp32 bar (vector path): one dropped or doubled token among
+    32768 moves an output by ~1.5e-4, fifteen times the bar."""
+    full_check(name, dtype=torch.float32, path="valu")
 
 
 @pytest.mark.timeout(900)
 def test_full_32_layer_stack():
-    """The 32-layer packed stack at full size (about 155 GB of cache), one
-    launch; outputs checked on sampled (layer, sequence, head) triples."""
+    """The 32-layer packed stack at full size (about 160 GB of cache), one
+    launch: every output of every layer against the oracle, layer by layer
+    (each layer's cache copied to the host), and the bf16 output bitwise the
+    rounding of the fp32 one."""
     w = workloads.WORKLOADS["llama3-8b-32-layer-stack"]
     torch.cuda.empty_cache()
     free, total = torch.cuda.mem_get_info(DEV)
@@ -497,30 +506,107 @@ def test_full_32_layer_stack():
     note("full", w.name, "generate %.1f GB" % (need / 1e9))
     x = workloads.generate(w, DEV)
     note("full", w.name, "decode")
-    out = gqa.decode_layers(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], kv_offsets=x["kv_offsets"],
-                            max_seq_len=w.T_max, num_kv_heads=w.H_kv, out_dtype=torch.float32)
+    kw = dict(kv_offsets=x["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv)
+    out = gqa.decode_layers(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], out_dtype=torch.float32, **kw)
+    out16 = gqa.decode_layers(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], out_dtype=torch.bfloat16, **kw)
     torch.cuda.synchronize()
-    off = x["kv_offsets"].cpu()
-    rows_per_layer = int(off[-1]) * w.H_kv
-    g = torch.Generator().manual_seed(5)
+    assert torch.equal(out16, out.to(torch.bfloat16))
+    offs = x["kv_offsets"].cpu().numpy()
+    sl = x["seq_lens"].cpu()
     e = 0.0
-    for _ in range(24):
-        l = int(torch.randint(w.layers, (1,), generator=g))
-        b = int(torch.randint(w.B, (1,), generator=g))
-        i = int(torch.randint(w.H_q, (1,), generator=g))
-        kv = i // w.G
-        n = int(x["seq_lens"][b])
-        cap = int(off[b + 1] - off[b])
-        r0 = l * rows_per_layer + int(off[b]) * w.H_kv + kv * cap
-        k1 = x["k"][r0:r0 + n].cpu().view(1, 1, n, w.d)
-        v1 = x["v"][r0:r0 + n].cpu().view(1, 1, n, w.d)
-        q1 = x["q"][l, b:b + 1, i:i + 1].cpu()
-        ref = oracle.decode(q1, k1, v1, torch.tensor([n], dtype=torch.int32), w.scale)[0, 0]
-        e = max(e, err(out[l, b, i], ref))
-    note("full", w.name, "max err %.3e" % e)
+    for l in range(w.layers):
+        xl = workloads.layer_view(x, l)
+        ref = oracle.decode(xl["q"].cpu(), xl["k"].cpu(), xl["v"].cpu(), sl, w.scale, kv_offsets=offs,
+                            num_kv_heads=w.H_kv)
+        el = err(out[l], ref)
+        note("full", w.name, "layer %d: max err %.3e" % (l, el))
+        e = max(e, el)
     assert e <= 2e-3
     del x
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------ cuts of the planner's own split --
+def planner_cuts(B, H_q, H_kv, d, T_max, lens):
+    """Stream positions where the planner's even token split cuts the
+    (sequence, KV head, token) stream of one layer: every workgroup owns
+    span = ceil(total / workgroups) positions rounded up to a multiple of 16
+    (the split the header describes, with the workgroup count the library
+    reports), as (b, g, t) with t the first token of the later piece."""
+    _, groups = gqa.plan(gqa.make_dims(B, H_q, H_kv, d, T_max, torch.bfloat16))
+    total = H_kv * sum(lens)
+    span = max(16, -(-(-(-total // groups)) // 16) * 16)
+    starts = []   # (stream position of the unit's token 0, b, g, n)
+    pos = 0
+    for b, n in enumerate(lens):
+        for g in range(H_kv):
+            if n > 0:
+                starts.append((pos, b, g, n))
+            pos += n
+    cuts, u = [], 0
+    for w in range(1, groups):
+        x = w * span
+        if x >= total:
+            break
+        while u + 1 < len(starts) and starts[u + 1][0] <= x:
+            u += 1
+        p0, b, g, n = starts[u]
+        cuts.append((b, g, x - p0, u))
+    return cuts, starts
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["llama3-8b-layer", "llama-70b-ragged-layer"])
+def test_spikes_at_the_planners_cuts(name):
+    """Full-size layers under the planner's own split (no forced span): every
+    cache token on either side of each cut, and the tiles around it, gets an
+    equal, overwhelming score (a "spike"), so each head's output is the plain
+    mean of its unit's spike values.  A token dropped or doubled at a cut
+    moves that mean by O(0.1), ten thousand times the fp32-output bar here;
+    units the split does not cut get one spike.  Also checked against the
+    oracle on the same inputs."""
+    w = workloads.WORKLOADS[name]
+    x = workloads.generate(w, DEV, poison_padding=True)
+    lens = x["seq_lens"].cpu().tolist()
+    cuts, starts = planner_cuts(w.B, w.H_q, w.H_kv, w.d, w.T_max, lens)
+    spikes = {}   # unit index -> token positions
+    for b, g, t, u in cuts:
+        n = lens[b]
+        if t == 0:   # a cut between units: the previous unit's last token and this one's first
+            spikes.setdefault(u - 1, set()).add(starts[u - 1][3] - 1)
+            spikes.setdefault(u, set()).add(0)
+            continue
+        for tt in (t - 16, t - 1, t, t + 15):
+            if 0 <= tt < n:
+                spikes.setdefault(u, set()).add(tt)
+    gen = torch.Generator().manual_seed(11)
+    for u, (_, b, g, n) in enumerate(starts):
+        if u not in spikes:
+            spikes[u] = {int(torch.randint(n, (1,), generator=gen))}
+    note("planner cuts", name, "%d cuts, %d units" % (len(cuts), len(starts)))
+    x["q"].zero_()
+    x["q"][..., 0] = 8.0
+    for u, ts in spikes.items():
+        _, b, g, n = starts[u]
+        idx = torch.tensor(sorted(ts), device=DEV)
+        row = torch.zeros(w.d, dtype=x["k"].dtype, device=DEV)
+        row[0] = 64.0                      # score 8 * 64 / sqrt(128) = 45 against |score| < 4 elsewhere
+        x["k"][b, g, idx] = row
+    out = gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], out_dtype=torch.float32)
+    out16 = gqa.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out.to(torch.bfloat16))
+    o = out.double().cpu()
+    e = 0.0
+    for u, ts in spikes.items():
+        _, b, g, n = starts[u]
+        want = x["v"][b, g, torch.tensor(sorted(ts), device=DEV)].double().mean(0).cpu()
+        e = max(e, float((o[b, g * w.G:(g + 1) * w.G] - want).abs().max()))
+    note("planner cuts", name, "max |out - spike mean| %.3e" % e)
+    assert e <= 1e-5
+    xc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    ref = oracle.decode(xc["q"], xc["k"], xc["v"], xc["seq_lens"], w.scale)
+    assert err(out, ref) <= 2e-3
 
 
 # -------------------------------------------------------- largest batches --
