@@ -5,13 +5,17 @@
 One step = one decode step of the workload (every split-KV piece and the
 merge of the pieces: one kernel launch when the merge is fused into the
 decode kernel, else the decode kernel and a small merge kernel) over one
-batch of synthetic inputs that are already resident in HBM.  Steps rotate over enough independent input batches
-(``--replicas``) that the working set exceeds the 256 MB last-level
-(Infinity) cache, so every step streams its K/V from HBM.  ``--paged PAGE`` lays each batch's
-cache out in pages of PAGE tokens (shuffled in a pool, read through a block
-table) and times gqa_decode_paged instead.  ``--kv fp8`` stores each batch's
-cache as one-byte E4M3 codes with one scale per array and times
-gqa_decode_fp8 (the bytes per cached element halve).
+batch of synthetic inputs that are already resident in HBM.  The default
+workload is the 32-layer stack (B 64, H_q 32, H_kv 8, d 128, lengths
+U[4096, 32768] shared by the layers, about 160 GB of packed bf16 cache): the
+largest configuration, one launch of gqa_decode_layers per step.  Steps
+rotate over enough independent input batches (``--replicas``) that the
+working set exceeds the 256 MB last-level (Infinity) cache, so every step
+streams its K/V from HBM.  ``--paged PAGE`` lays each batch's cache out in
+pages of PAGE tokens (shuffled in a pool, read through a block table) and
+times gqa_decode_paged instead.  ``--kv fp8`` stores each batch's cache as
+one-byte E4M3 codes with one scale per array and times gqa_decode_fp8 (the
+bytes per cached element halve).
 
 Metric: (K + V bytes of the valid tokens + q bytes + out bytes) / time, the
 KV traffic formula of "Grouped-Query Attention (GQA) and Multi-Query
@@ -19,12 +23,18 @@ Attention (MQA): ...", section 1 ("KV Cache Memory Footprint"), per step.
 
 The single JSON line also carries
   * roofline: the decode kernel's achieved algorithmic GB/s (HIP events
-    around the timed region on the launch stream, per launch) against the
-    MI355X HBM3E peak of 8 TB/s,
-    and the HBM traffic the rocprofv3 counters recorded (profiles/), if they
-    were taken on the current kernel source;
-  * cpu_baseline: the fp64 CPU oracle timed on this host over whole steps of
-    the same workload (about ten seconds of work);
+    around the timed region on the launch stream, divided by the launches)
+    against the MI355X HBM3E peak of 8 TB/s, and the HBM traffic the
+    rocprofv3 counters recorded (profiles/), if they were taken on the
+    current kernel source;
+  * cpu_baseline: the fp64 CPU oracle timed on this host on a sample of the
+    same workload (whole steps of a single-layer workload; a few layers of a
+    layer-batched one, scaled to the whole step), about ten seconds of work;
+  * read_probe: a plain read of the step's K/V tensors by the library's
+    read-probe kernel, the rate a step that reads those bytes can approach;
+  * per_step_us: percentiles of the steps of the timed region (long steps)
+    or of a pass after it (short steps); for long steps also the first ten
+    steps' rate and a sustained pass of more than a second;
   * context: the H100 roofline figures printed on that page (3.35 TB/s,
     989 TFLOP/s, I_sat ~ 295 FLOP/B), hardware context only.
 """
@@ -43,8 +53,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "GQA decode effective HBM GB/s (% of MI355X peak) + µs/step"
-DEFAULT_WORKLOAD = "llama3-8b-layer"
+DEFAULT_WORKLOAD = "llama3-8b-32-layer-stack"
 KERNEL_SOURCES = ["common.h", "kernel_mfma.h", "kernel_valu.h", "gqa_decode.hip"]
+LONG_STEP_MS = 0.5   # steps at least this long carry events of their own inside the timed region
 
 
 def traffic_profile(key: str) -> str:
@@ -92,29 +103,57 @@ def read_traffic(workload_name: str, launches_bytes: int):
         return None
 
 
-def cpu_baseline(w, budget_s: float = 10.0):
-    """Time the fp64 oracle on whole steps of the workload on this host."""
+def cpu_baseline(w, budget_s: float = 10.0, x=None):
+    """Time the fp64 oracle on this host on a sample of the workload.
+
+    Single-layer workloads: whole steps, repeated for about ``budget_s``.
+    Layer-batched workloads: the layers are independent and the oracle runs
+    layer by layer (each layer's K/V copied to the host first, outside the
+    timing), on layers 0, 1, ... until ``budget_s`` is spent; the step's time
+    is the mean per-layer time times the number of layers.  ``x``: the
+    step's inputs (any device) for a layer-batched workload."""
     import oracle
     from gqa_mqa_kv_amd import workloads
 
     orc = oracle.default()
-    x = workloads.generate(w, "cpu") if w.layers == 1 else None
-    if x is None:
-        raise RuntimeError("cpu baseline is defined for single-layer workloads")
-    args = (x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
-    orc.decode(*args)   # warm
-    n, t0 = 0, time.perf_counter()
-    while True:
-        orc.decode(*args)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 1000:
-            break
-    per_step = el / n
-    nbytes = algorithmic_bytes(w, x["seq_lens"], 2 if str(w.dtype).endswith("bfloat16") else 4)
+    out_bytes = 2 if str(w.dtype).endswith("bfloat16") else 4
+    if w.layers == 1:
+        x = workloads.generate(w, "cpu")
+        args = (x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+        orc.decode(*args)   # warm
+        n, t0 = 0, time.perf_counter()
+        while True:
+            orc.decode(*args)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 1000:
+                break
+        per_step = el / n
+        sample = "%d whole steps of %s (fp64 C oracle, OpenMP), %.1f s" % (n, w.name, el)
+        sl = x["seq_lens"]
+    else:
+        if x is None:
+            x = workloads.generate(w, "cpu")
+        sl = x["seq_lens"].cpu()
+        offs = x["kv_offsets"].cpu().numpy() if w.packed else None
+        spent, n = 0.0, 0
+        for l in range(w.layers):
+            xl = workloads.layer_view(x, l)
+            q, k, v = xl["q"].cpu(), xl["k"].cpu(), xl["v"].cpu()
+            t0 = time.perf_counter()
+            orc.decode(q, k, v, sl, x["scale"], kv_offsets=offs, num_kv_heads=w.H_kv)
+            spent += time.perf_counter() - t0
+            n += 1
+            del q, k, v
+            if spent >= budget_s:
+                break
+        per_step = spent / n * w.layers
+        sample = ("%d of %d layers of %s (fp64 C oracle, OpenMP, each layer's K/V copied to the host first, "
+                  "untimed), %.1f s; step time = mean layer time x %d" % (n, w.layers, w.name, spent, w.layers))
+    nbytes = algorithmic_bytes(w, sl, out_bytes)
     return {"value": round(nbytes / per_step / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle", "us_per_step": round(per_step * 1e6, 1), "cpu_model": cpu_model(),
-            "sample": "%d whole steps of %s (fp64 C oracle, OpenMP), %.1f s" % (n, w.name, el)}
+            "sample": sample}
 
 
 def cpu_model() -> str:
@@ -153,23 +192,61 @@ def copy_calibration(torch, dev, nbytes: int, launches: int) -> None:
                       "bytes_written_per_launch": nbytes, "launches": launches}), flush=True)
 
 
-def copy_probe(torch, dev, stream, nbytes: int = 1 << 30, launches: int = 10):
-    """Achievable HBM rate of a plain device copy (an elementwise fp32 kernel
-    reading nbytes and writing nbytes): context for the step's rate."""
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    torch.neg(src, out=dst)
+def read_probe(torch, gqa, pairs, stream, launches: int = 0, sustained_s: float = 0.0):
+    """The library's read-probe kernel over ``pairs`` (the (K, V) tensors of
+    each input batch, in the order the steps use them): one launch reads a
+    batch's K and then its V, as a decode step does; a pass reads every
+    batch once.  Tries 1, 2, 4 and 8 workgroups per CU and reports the best
+    rate, each shape's rate, and (``sustained_s``) the first and last ten
+    passes of a run of about that many seconds at the best shape."""
+    dev = pairs[0][0].device
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = sum(t.numel() * t.element_size() for kv in pairs for t in kv)
+
+    def one_pass(wpc):
+        for k, v in pairs:
+            gqa.hbm_read_probe(k, wpc, sink, stream.cuda_stream, b=v)
+
+    rates = {}
+    for wpc in (1, 2, 4, 8):
+        one_pass(wpc)
+        torch.cuda.synchronize()
+        reps = launches or max(3, min(200, int(2e9 // max(nbytes, 1))))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            one_pass(wpc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        rates[wpc] = (round(nbytes / (us * 1e-6) / 1e9, 1), round(us, 2))
+    best = max(rates, key=lambda k: rates[k][0])
+    res = {"GB/s": rates[best][0], "us_per_pass": rates[best][1], "bytes_per_pass": nbytes,
+           "launches_per_pass": len(pairs), "workgroups_per_cu": best,
+           "GB/s_by_workgroups_per_cu": {str(k): v[0] for k, v in rates.items()},
+           "kernel": "gqa_hbm_read_probe: 16-byte non-temporal loads, 8 in flight per thread, one span per workgroup"}
+    if sustained_s > 0:
+        res["sustained"] = sustained_rates(torch, lambda i: one_pass(best), stream, nbytes,
+                                           max(20, int(sustained_s * 1e6 / rates[best][1])))
+    return res
+
+
+def sustained_rates(torch, step, stream, nbytes: int, n: int):
+    """n back-to-back steps, each bracketed by events: the rate of the first
+    ten, of the last ten, and of all of them (GB/s), and how long the run
+    streamed."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(launches):
-        torch.neg(src, out=dst)
-    e1.record(stream)
+    evs[0].record(stream)
+    for i in range(n):
+        step(i)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / launches
-    del src, dst
-    return {"GB/s": round(2 * nbytes / (us * 1e-6) / 1e9, 1), "us_per_launch": round(us, 1),
-            "bytes_read_and_written": 2 * nbytes}
+    t = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)]
+    rate = lambda ts: round(nbytes * len(ts) / (sum(ts) * 1e-6) / 1e9, 1)
+    return {"steps": n, "seconds": round(sum(t) * 1e-6, 3), "first_10_GB/s": rate(t[:10]),
+            "last_10_GB/s": rate(t[-10:]), "all_GB/s": rate(t), "first_10_us": round(sum(t[:10]) / 10, 1),
+            "last_10_us": round(sum(t[-10:]) / 10, 1)}
 
 
 def time_layers_one_by_one(torch, gqa, workloads, w, x, stream, out_dtype, reps: int = 3, fp8: bool = False):
@@ -282,8 +359,8 @@ def time_fused_append(torch, gqa, w, batches, stream, steps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--replicas", type=int, default=0, help="input batches rotated over (0: enough for >= 2 GiB)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
@@ -298,6 +375,8 @@ def main():
                     help="only the timed steps: no per-step percentiles, single-layer launches or append timing "
                          "(for kernel traces that should hold one kind of launch)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--sustained-s", type=float, default=1.5,
+                    help="long steps: seconds of back-to-back steps (and of probe reads) in the sustained pass")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain N-MiB device copy (counter calibration kernel)")
     args = ap.parse_args()
@@ -352,7 +431,8 @@ def main():
                                                         chunk_tokens=args.chunk_tokens, **extra))
             elif args.paged:
                 kp, vp, table = workloads.to_pages(x8, args.paged, seed=1000 + r, spare=1)
-                del x8["k"], x8["v"]
+                del x8["k"], x8["v"]   # the pool holds the cache now
+                x8["pool"] = (kp, vp, table)
                 launchers.append(gqa.prepare_paged_fp8(x["q"], kp, vp, table, x["seq_lens"], x["scale"],
                                                        x8["k_scale"], x8["v_scale"], max_seq_len=w.T_max,
                                                        out_dtype=out_dtype, chunk_tokens=args.chunk_tokens))
@@ -374,30 +454,42 @@ def main():
     def step(i):
         return launchers[i % reps]()
 
+    we0, we1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    we0.record(stream)
     for i in range(args.warmup):
         step(i)
+    we1.record(stream)
     torch.cuda.synchronize()
+    warm_ms = we0.elapsed_time(we1) / max(args.warmup, 1)
+    # Long steps carry an event of their own at every step boundary inside the
+    # timed region (a marker between launches that are milliseconds long);
+    # short steps are timed as one block, and their percentiles come from a
+    # pass after it.
+    long_steps = args.warmup > 0 and warm_ms >= LONG_STEP_MS
     # timed region: exactly K steps, synchronised on both sides
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1 if long_steps else 2)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     for i in range(args.steps):
         step(i)
-    ev1.record(stream)
+        if long_steps:
+            evs[i + 1].record(stream)
+    if not long_steps:
+        evs[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = ev0.elapsed_time(ev1)
+    total_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = total_ms / args.steps
+    step_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)] if long_steps else None
     nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4, args.paged, 1 if fp8 else 0)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
-    # The decode kernel's duration per launch: the HIP events above bracket the
-    # timed region on the launch stream; a step is one launch when the merge
-    # is fused into the decode kernel (else the decode kernel plus a small
-    # merge kernel, and this is their sum).
-    kern_ms = ms_per_step
-    achieved = nbytes / (kern_ms * 1e-3) / 1e9
-
+    # The decode kernel's average launch duration: HIP events bracket the
+    # timed region on the launch stream, divided by its launches (one per
+    # step when the merge is fused into the decode kernel; with the merge
+    # kernel a step is two launches and this figure covers both).
+    achieved = gbps
     d = gqa.make_dims(w.B, w.H_q, w.H_kv, w.d, w.T_max, w.dtype, out_dtype, chunk_tokens=args.chunk_tokens,
                       path=args.path)
     a, b = gqa.plan(d, w.layers)
@@ -436,19 +528,38 @@ def main():
                    "wall_s_timed_region": round(wall, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel_ms_avg": round(kern_ms, 5), "algorithmic_bytes_per_launch": nbytes,
-                     "kernel_source_hash": kernel_source_hash()},
+                     "launch_us_avg": round(ms_per_step * 1e3, 2),
+                     "launch_us_avg_source": "HIP events around the timed region on the launch stream / steps "
+                                             "(one launch per step with the fused merge)",
+                     "algorithmic_bytes_per_launch": nbytes, "kernel_source_hash": kernel_source_hash()},
         "cpu_baseline": None,
         "context": {"h100_sxm5_hbm_TBps": 3.35, "h100_sxm5_dense_bf16_TFLOPs": 989, "h100_I_sat_FLOP_per_B": 295.2},
     }
+    if long_steps:
+        # every step of the timed region, and the first ten steps alone
+        t = sorted(step_us)
+        pick = lambda f: round(t[min(len(t) - 1, int(f * len(t)))], 2)
+        result["per_step_us"] = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "steps": len(t),
+                                 "source": "the timed region's steps"}
+        first = step_us[:10]
+        result["first_10_steps"] = {"us_per_step": round(sum(first) / len(first), 1),
+                                    "GB/s": round(nbytes * len(first) / (sum(first) * 1e-6) / 1e9, 1)}
     if not args.no_extras:
-        result["per_step_us"] = step_percentiles(torch, step, stream, min(args.steps, 100), args.steps)
-        # the same step repeated on one input batch: whatever of it fits stays in the caches
-        result["warm_one_batch_us_per_step"] = step_percentiles(
-            torch, lambda i: launchers[0](), stream, min(args.steps, 50), 0)["p50"]
-        probe = copy_probe(torch, dev, stream)
+        if not long_steps:
+            result["per_step_us"] = dict(step_percentiles(torch, step, stream, min(args.steps, 100), args.steps),
+                                         source="a pass of events per step after the timed region")
+            # the same step repeated on one input batch: whatever of it fits stays in the caches
+            result["warm_one_batch_us_per_step"] = step_percentiles(
+                torch, lambda i: launchers[0](), stream, min(args.steps, 50), 0)["p50"]
+        else:
+            # more than a second of back-to-back steps: the part's sustained rate
+            result["sustained_steps"] = sustained_rates(torch, step, stream, nbytes,
+                                                        max(20, int(args.sustained_s * 1e3 / ms_per_step)))
+        # a plain read of the same K/V tensors (rotated like the steps)
+        kv = [(x["pool"][0], x["pool"][1]) if "pool" in x else (x["k"], x["v"]) for x in batches]
+        probe = read_probe(torch, gqa, kv, stream, sustained_s=args.sustained_s if long_steps else 0.0)
         probe["step_rate_as_fraction"] = round(gbps / probe["GB/s"], 4)
-        result["hbm_copy_probe"] = probe
+        result["read_probe"] = probe
     if w.layers > 1 and not args.no_extras:
         result["sequential_single_layer_launches"] = time_layers_one_by_one(torch, gqa, workloads, w, batches[0],
                                                                             stream, out_dtype, fp8=fp8)
@@ -457,9 +568,9 @@ def main():
             result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
         result["step_with_append"] = time_fused_append(torch, gqa, w, batches, stream, min(args.steps, 100),
                                                        args.warmup)
-    if not args.no_cpu_baseline and w.layers == 1:
+    if not args.no_cpu_baseline and not fp8 and not args.paged:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, batches[0] if w.layers > 1 else None)
     print(json.dumps(result), flush=True)
 
 

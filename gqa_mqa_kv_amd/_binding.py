@@ -25,7 +25,8 @@ SYMBOLS = ("gqa_append_rope", "gqa_append_rope_fp8", "gqa_append_rope_paged", "g
            "gqa_decode", "gqa_decode_append_rope", "gqa_decode_append_rope_paged", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8",
            "gqa_decode_paged",
            "gqa_decode_paged_fp8", "gqa_decode_noalloc",
-           "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string")
+           "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string",
+           "gqa_hbm_read_probe")
 
 
 class GqaDims(ctypes.Structure):
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.gqa_append_rope_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, dims_p, vp]
         L.gqa_append_rope_paged_fp8.restype = ctypes.c_int
         L.gqa_append_rope_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, f32, f32, f32, vp, dims_p, vp]
+        L.gqa_hbm_read_probe.restype = ctypes.c_int
+        L.gqa_hbm_read_probe.argtypes = [vp, sz, vp, sz, i32, vp, vp]
         L.gqa_status_string.restype = ctypes.c_char_p
         L.gqa_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -130,20 +133,40 @@ def plan(dims: GqaDims, num_layers: int = 1):
     return c.value, n.value
 
 
-_workspaces = {}
+_workspaces = {}   # (device type, device index, stream handle) -> zero-filled workspace
+_retired = []      # workspaces replaced by larger ones: kept alive for the life of the process
 
 
-def default_workspace(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
+def _stream_handle(device: torch.device, stream) -> int:
+    return int(torch.cuda.current_stream(device).cuda_stream if stream is None else stream)
+
+
+def default_workspace(nbytes: int, device: torch.device, stream=None) -> Optional[torch.Tensor]:
     """A zero-filled device buffer of at least ``nbytes`` (256-byte aligned),
-    cached per device.  The library leaves its arrival counters at zero after
-    each call, so the buffer is shared as is by calls ordered on one stream."""
+    cached per (device, stream): calls on one stream are ordered, so they may
+    share it (the library leaves its arrival counters at zero after each
+    call), while calls on different streams, which may overlap in time, get
+    buffers of their own.  ``stream``: a hipStream_t handle (None: the
+    current stream).  A buffer is zero-filled on the stream that uses it.  A
+    buffer replaced by a larger one is never freed: a kernel still running on
+    that stream, or a captured graph, may hold its address.  Sizes are
+    rounded up to a power of two, so a stream replaces its buffer a few
+    times at most."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
+    s = _stream_handle(device, stream)
+    key = (device.type, device.index, s)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+        size = 1 << (int(nbytes) - 1).bit_length()
+        if s == int(torch.cuda.current_stream(device).cuda_stream):
+            new = torch.zeros(size, dtype=torch.uint8, device=device)
+        else:
+            with torch.cuda.stream(torch.cuda.ExternalStream(s, device=device)):
+                new = torch.zeros(size, dtype=torch.uint8, device=device)
+        if ws is not None:
+            _retired.append(ws)
+        _workspaces[key] = ws = new
     return ws
 
 
@@ -160,12 +183,9 @@ def _require(t: torch.Tensor, name: str, device: torch.device):
         raise ValueError("%s must be contiguous" % name)
 
 
-def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None, chunk_tokens: int = 0,
-           path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
-           tiles: int = 0, merge: str = "auto", per_cu: int = 0):
-    """One decode step of one layer.  q [B,H_q,d]; k_cache/v_cache
-    [B,H_kv,T_max,d]; seq_lens int32 [B] on the same device.  Returns out
-    [B,H_q,d] (dtype ``out_dtype``, default q's)."""
+def _decode_args(q, k_cache, v_cache, seq_lens, scale, out, out_dtype, chunk_tokens, path, seq_len_hint, workspace,
+                 stream, waves, tiles, merge, per_cu):
+    """Validated arguments of gqa_decode (nothing is enqueued)."""
     dev = q.device
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
         _require(t, n, dev)
@@ -177,19 +197,30 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None
         raise ValueError("shape mismatch between q, caches and seq_lens")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache and v_cache must share one dtype")
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge, per_cu)
+    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge,
+                     per_cu)
     if out is None:
         out = torch.empty(B, H_q, d, dtype=out_dtype or q.dtype, device=dev)
     _require(out, "out", dev)
     if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [B,H_q,d] of the output dtype")
-    need = workspace_bytes(dims)
-    ws = default_workspace(need, dev) if workspace is None else workspace
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    _check(lib().gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out),
-                            ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                            s))
-    return out
+    s = _stream_handle(dev, stream)
+    ws = default_workspace(workspace_bytes(dims), dev, s) if workspace is None else workspace
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out), ctypes.byref(dims),
+            _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
+    return args, (out, q, k_cache, v_cache, seq_lens, ws, dims)
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None, chunk_tokens: int = 0,
+           path: str = "auto", seq_len_hint: int = 0, workspace=None, stream=None, waves: int = 0,
+           tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """One decode step of one layer.  q [B,H_q,d]; k_cache/v_cache
+    [B,H_kv,T_max,d]; seq_lens int32 [B] on the same device.  Returns out
+    [B,H_q,d] (dtype ``out_dtype``, default q's)."""
+    args, keep = _decode_args(q, k_cache, v_cache, seq_lens, scale, out, out_dtype, chunk_tokens, path, seq_len_hint,
+                              workspace, stream, waves, tiles, merge, per_cu)
+    _check(lib().gqa_decode(*args))
+    return keep[0]
 
 
 def decode_noalloc(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dtype=None, chunk_tokens: int = 0,
@@ -224,6 +255,24 @@ def decode_noalloc(q, k_cache, v_cache, seq_lens, scale: float, out=None, out_dt
     return out
 
 
+def hbm_read_probe(a: torch.Tensor, workgroups_per_cu: int, sink: torch.Tensor, stream=None, b=None):
+    """Enqueue gqa_hbm_read_probe: one plain read of tensor ``a`` and then of
+    tensor ``b`` (optional), contiguous device tensors, in one launch, with
+    ``workgroups_per_cu`` workgroups per CU; ``sink`` is a one-element int32
+    device tensor the kernel folds what it reads into.  Measurement only."""
+    dev = a.device
+    _require(a, "a", dev)
+    _require(sink, "sink", dev)
+    if b is not None:
+        _require(b, "b", dev)
+    if sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("sink must be an int32 device tensor")
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    nb = 0 if b is None else b.numel() * b.element_size()
+    _check(lib().gqa_hbm_read_probe(_ptr(a), a.numel() * a.element_size(), _ptr(b), nb, int(workgroups_per_cu),
+                                    _ptr(sink), s))
+
+
 def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype, max_seq_len, chunk_tokens,
                 seq_len_hint, workspace, stream, tiles, merge, per_cu, scales=None):
     dev = q.device
@@ -251,8 +300,8 @@ def _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, out, out_dtype,
     _require(out, "out", dev)
     if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [B,H_q,d] of the output dtype")
-    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    s = _stream_handle(dev, stream)
+    ws = default_workspace(workspace_bytes(dims), dev, s) if workspace is None else workspace
     sc = (float(scale),) if scales is None else (float(scale), float(scales[0]), float(scales[1]))
     args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages), int(page), _ptr(seq_lens)) + \
         sc + (_ptr(out), ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
@@ -296,8 +345,8 @@ def _fp8_args(q, k8, v8, seq_lens, scale, k_scale, v_scale, out, out_dtype, chun
     _require(out, "out", dev)
     if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [B,H_q,d] of the output dtype")
-    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    s = _stream_handle(dev, stream)
+    ws = default_workspace(workspace_bytes(dims), dev, s) if workspace is None else workspace
     args = (_ptr(q), _ptr(k8), _ptr(v8), _ptr(seq_lens), float(scale), float(k_scale), float(v_scale), _ptr(out),
             ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
     return args, (out, q, k8, v8, seq_lens, ws, dims)
@@ -365,8 +414,8 @@ def _layers_args(q, k_cache, v_cache, seq_lens, scale, kv_offsets, max_seq_len, 
     _require(out, "out", dev)
     if out.shape != (L, B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [L,B,H_q,d] of the output dtype")
-    ws = default_workspace(workspace_bytes(dims, L), dev) if workspace is None else workspace
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    s = _stream_handle(dev, stream)
+    ws = default_workspace(workspace_bytes(dims, L), dev, s) if workspace is None else workspace
     sc = () if scales is None else (float(scales[0]), float(scales[1]))
     args = (int(L), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens), float(scale)) + sc + (
         _ptr(out), ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
@@ -403,16 +452,10 @@ def decode_layers_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: floa
     return keep[0]
 
 
-def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
-                max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None, scales=None):
-    """Append each sequence's new token to one layer's cache with rotary
-    position embedding at position seq_lens[b] (see gqa_append_rope in
-    include/gqa_decode.h).  q [B,H_q,d]; k_new/v_new [B,H_kv,d]; caches dense
-    [B,H_kv,T_max,d], or packed with ``kv_offsets`` (int64 [B+1]) and
-    ``max_seq_len``.  Writes the caches in place; returns (q_out,
-    new_seq_lens): the rotated queries (a new tensor unless ``q_out`` is
-    given, which may be q itself) and the lengths after the append (a new
-    int32 tensor unless ``new_seq_lens`` is given, which may be seq_lens)."""
+def _append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets, max_seq_len, q_out,
+                 new_seq_lens, stream, scales):
+    """Validated (function, arguments, tensors kept) of gqa_append_rope, or of
+    gqa_append_rope_fp8 with ``scales`` (nothing is enqueued)."""
     dev = q.device
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (seq_lens, "seq_lens")):
@@ -451,14 +494,31 @@ def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k
     _require(new_seq_lens, "new_seq_lens", dev)
     if new_seq_lens.shape != (B,) or new_seq_lens.dtype != torch.int32:
         raise ValueError("new_seq_lens must be int32 [B]")
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    s = _stream_handle(dev, stream)
     head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
             _ptr(new_seq_lens), float(rope_base))
     if scales:
-        _check(lib().gqa_append_rope_fp8(*head, float(scales[0]), float(scales[1]), _ptr(q_out), ctypes.byref(dims), s))
+        fn, args = lib().gqa_append_rope_fp8, head + (float(scales[0]), float(scales[1]), _ptr(q_out),
+                                                      ctypes.byref(dims), s)
     else:
-        _check(lib().gqa_append_rope(*head, _ptr(q_out), ctypes.byref(dims), s))
-    return q_out, new_seq_lens
+        fn, args = lib().gqa_append_rope, head + (_ptr(q_out), ctypes.byref(dims), s)
+    return fn, args, (q_out, new_seq_lens, q, k_new, v_new, k_cache, v_cache, seq_lens, kv_offsets, dims)
+
+
+def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
+                max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None, scales=None):
+    """Append each sequence's new token to one layer's cache with rotary
+    position embedding at position seq_lens[b] (see gqa_append_rope in
+    include/gqa_decode.h).  q [B,H_q,d]; k_new/v_new [B,H_kv,d]; caches dense
+    [B,H_kv,T_max,d], or packed with ``kv_offsets`` (int64 [B+1]) and
+    ``max_seq_len``.  Writes the caches in place; returns (q_out,
+    new_seq_lens): the rotated queries (a new tensor unless ``q_out`` is
+    given, which may be q itself) and the lengths after the append (a new
+    int32 tensor unless ``new_seq_lens`` is given, which may be seq_lens)."""
+    fn, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets, max_seq_len,
+                                  q_out, new_seq_lens, stream, scales)
+    _check(fn(*args))
+    return keep[0], keep[1]
 
 
 def _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets, max_seq_len, q_out,
@@ -504,8 +564,8 @@ def _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, 
         raise ValueError("q_out must match q and new_seq_lens seq_lens")
     if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [B,H_q,d] of the output dtype")
-    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    s = _stream_handle(dev, stream)
+    ws = default_workspace(workspace_bytes(dims), dev, s) if workspace is None else workspace
     args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
             _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out), ctypes.byref(dims), _ptr(ws),
             0 if ws is None else ws.numel() * ws.element_size(), s)
@@ -567,8 +627,8 @@ def _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_
         raise ValueError("q_out must match q and new_seq_lens seq_lens")
     if out.shape != (B, H_q, d) or GQA_DTYPE.get(out.dtype) != dims.out_dtype:
         raise ValueError("out must be [B,H_q,d] of the output dtype")
-    ws = default_workspace(workspace_bytes(dims), dev) if workspace is None else workspace
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    s = _stream_handle(dev, stream)
+    ws = default_workspace(workspace_bytes(dims), dev, s) if workspace is None else workspace
     args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages),
             int(page), _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out),
             ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
@@ -595,50 +655,32 @@ def prepare_decode_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, se
                                 scale: float, max_seq_len=None, out_dtype=None, chunk_tokens: int = 0, stream=None,
                                 tiles: int = 0, merge: str = "auto", per_cu: int = 0):
     """As prepare, for gqa_decode_append_rope_paged (each call appends again:
-    the new token overwrites the same pool rows with the same values)."""
+    the new token overwrites the same pool rows with the same values; the
+    first call is the first append)."""
     args, keep = _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, scale,
                                            max_seq_len, None, None, None, out_dtype, chunk_tokens, None, stream, tiles,
                                            merge, per_cu)
-    pr = Prepared(lib().gqa_decode_append_rope_paged, args, keep)
-    pr()
-    return pr
+    return Prepared(lib().gqa_decode_append_rope_paged, args, keep)
 
 
 def prepare_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
                          max_seq_len: Optional[int] = None, stream=None, q_out=None, new_seq_lens=None):
-    """As prepare_append, for append_rope_paged: validates by running it once
-    and returns a callable that enqueues the same call again."""
-    q_out, new_lens = append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base,
-                                        max_seq_len=max_seq_len, stream=stream, q_out=q_out,
-                                        new_seq_lens=new_seq_lens)
-    B, H_q, d = q.shape
-    _, H_kv, page, _ = k_pool.shape
-    max_pages = block_table.shape[1]
-    T = max_pages * page if max_seq_len is None else int(max_seq_len)
-    dims = make_dims(B, H_q, H_kv, d, T, q.dtype)
-    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-    args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages),
-            int(page), _ptr(seq_lens), _ptr(new_lens), float(rope_base), _ptr(q_out), ctypes.byref(dims), s)
-    fn = lib().gqa_append_rope_paged
-    keep = (q_out, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, new_lens, dims)
-
-    def call():
-        _check(fn(*args))
-        return keep[0]
-    return call
+    """As prepare_append, for append_rope_paged."""
+    fn, args, keep = _append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base,
+                                        max_seq_len, q_out, new_seq_lens, stream, None)
+    return Prepared(fn, args, keep)
 
 
 def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, scale: float,
                           kv_offsets=None, max_seq_len=None, out_dtype=None, chunk_tokens: int = 0, stream=None,
                           tiles: int = 0, merge: str = "auto", per_cu: int = 0):
     """As prepare, for gqa_decode_append_rope (each call appends again: the
-    new token overwrites the same cache rows with the same values)."""
+    new token overwrites the same cache rows with the same values; the first
+    call is the first append)."""
     args, keep = _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets,
                                      max_seq_len, None, None, None, out_dtype, chunk_tokens, None, stream, tiles, merge,
                                      per_cu)
-    pr = Prepared(lib().gqa_decode_append_rope, args, keep)
-    pr()
-    return pr
+    return Prepared(lib().gqa_decode_append_rope, args, keep)
 
 
 def append_rope_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k_scale: float, v_scale: float,
@@ -652,13 +694,10 @@ def append_rope_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: floa
                        scales=(k_scale, v_scale))
 
 
-def append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
-                      max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None, scales=None):
-    """append_rope for a cache held in pages of a pool (the layout of
-    decode_paged): k_pool/v_pool [num_pages,H_kv,page,d], block_table int32
-    [B,max_pages]; the new token of sequence b goes to row seq_lens[b] % page
-    of page block_table[b, seq_lens[b] // page].  max_seq_len (the capacity)
-    defaults to max_pages * page.  Returns (q_out, new_seq_lens)."""
+def _append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, max_seq_len, q_out,
+                       new_seq_lens, stream, scales):
+    """Validated (function, arguments, tensors kept) of gqa_append_rope_paged,
+    or of gqa_append_rope_paged_fp8 with ``scales`` (nothing is enqueued)."""
     dev = q.device
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool"),
                  (block_table, "block_table"), (seq_lens, "seq_lens")):
@@ -687,15 +726,30 @@ def append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, ro
     if q_out.shape != q.shape or q_out.dtype != q.dtype or new_seq_lens.shape != (B,) or \
             new_seq_lens.dtype != torch.int32:
         raise ValueError("q_out must match q and new_seq_lens be int32 [B]")
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+    s = _stream_handle(dev, stream)
     head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages),
             int(page), _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base))
     if scales:
-        _check(lib().gqa_append_rope_paged_fp8(*head, float(scales[0]), float(scales[1]), _ptr(q_out),
-                                               ctypes.byref(dims), s))
+        fn, args = lib().gqa_append_rope_paged_fp8, head + (float(scales[0]), float(scales[1]), _ptr(q_out),
+                                                            ctypes.byref(dims), s)
     else:
-        _check(lib().gqa_append_rope_paged(*head, _ptr(q_out), ctypes.byref(dims), s))
-    return q_out, new_seq_lens
+        fn, args = lib().gqa_append_rope_paged, head + (_ptr(q_out), ctypes.byref(dims), s)
+    return fn, args, (q_out, new_seq_lens, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, dims)
+
+
+
+
+def append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
+                      max_seq_len: Optional[int] = None, q_out=None, new_seq_lens=None, stream=None, scales=None):
+    """append_rope for a cache held in pages of a pool (the layout of
+    decode_paged): k_pool/v_pool [num_pages,H_kv,page,d], block_table int32
+    [B,max_pages]; the new token of sequence b goes to row seq_lens[b] % page
+    of page block_table[b, seq_lens[b] // page].  max_seq_len (the capacity)
+    defaults to max_pages * page.  Returns (q_out, new_seq_lens)."""
+    fn, args, keep = _append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base,
+                                        max_seq_len, q_out, new_seq_lens, stream, scales)
+    _check(fn(*args))
+    return keep[0], keep[1]
 
 
 def append_rope_paged_fp8(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float, k_scale: float,
@@ -710,34 +764,26 @@ def append_rope_paged_fp8(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens
 
 def prepare_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, kv_offsets=None,
                    max_seq_len: Optional[int] = None, stream=None, q_out=None, new_seq_lens=None):
-    """Validate (by running it once) and return a callable that enqueues the
-    same append_rope call again (for timing loops); it returns the rotated
-    queries.  The new lengths go to a tensor of their own (``new_seq_lens``
-    if given), so every call appends at the same rows."""
-    q_out, new_lens = append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets=kv_offsets,
-                                  max_seq_len=max_seq_len, stream=stream, q_out=q_out, new_seq_lens=new_seq_lens)
-    B, H_q, d = q.shape
-    T_max = k_cache.shape[2] if kv_offsets is None else max_seq_len
-    dims = make_dims(B, H_q, k_new.shape[1], d, T_max, q.dtype)
-    s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-    args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
-            _ptr(new_lens), float(rope_base), _ptr(q_out), ctypes.byref(dims), s)
-    fn = lib().gqa_append_rope
-    keep = (q_out, q, k_new, v_new, k_cache, v_cache, seq_lens, new_lens, kv_offsets, dims)
-
-    def call():
-        _check(fn(*args))
-        return keep[0]
-    return call
+    """A callable that enqueues append_rope with these arguments (for timing
+    loops); it returns the rotated queries.  The arguments are checked on the
+    host here and nothing is enqueued until the first call, which is the
+    first append.  The new lengths go to a tensor of their own
+    (``new_seq_lens`` if given, else a new one), so every call appends at the
+    same rows."""
+    fn, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets, max_seq_len,
+                                  q_out, new_seq_lens, stream, None)
+    return Prepared(fn, args, keep)
 
 
 class Prepared:
-    """A decode call with every argument marshalled once; calling it only
-    enqueues the launch (for timing loops where per-call argument checks
-    would cost more host time than the kernel takes)."""
+    """A call of the library with every argument marshalled and checked on the
+    host once; calling it only enqueues the launch (for timing loops and
+    graph capture, where per-call argument checks would cost more host time
+    than the kernel takes).  Construction enqueues nothing; argument errors
+    the library itself detects surface at the first call."""
 
-    def __init__(self, layers, args: tuple, keep: tuple):
-        self._fn = layers if callable(layers) else (lib().gqa_decode_layers if layers else lib().gqa_decode)
+    def __init__(self, fn, args: tuple, keep: tuple):
+        self._fn = fn
         self._args = args
         self._keep = keep   # tensors whose memory the pointers refer to
 
@@ -749,39 +795,17 @@ class Prepared:
 def prepare(q, k_cache, v_cache, seq_lens, scale: float, kv_offsets=None, max_seq_len=None, num_kv_heads=None,
             out_dtype=None, chunk_tokens: int = 0, path: str = "auto", seq_len_hint: int = 0, stream=None,
             waves: int = 0, tiles: int = 0, merge: str = "auto", per_cu: int = 0):
-    """Validate (by running the call once) and return a Prepared launcher
-    writing into a fresh output tensor, which each call returns.  q [B,H_q,d]
-    selects gqa_decode, q [L,B,H_q,d] selects gqa_decode_layers."""
-    dev = q.device
-    layers = q.dim() == 4
-    out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
-    if layers:
-        decode_layers(q, k_cache, v_cache, seq_lens, scale, kv_offsets=kv_offsets, max_seq_len=max_seq_len,
-                      num_kv_heads=num_kv_heads, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
-                      path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge, per_cu=per_cu)
-        L, B, H_q, d = q.shape
-        if kv_offsets is None:
-            H_kv, T_max = k_cache.shape[2], k_cache.shape[3]
-        else:
-            H_kv, T_max = num_kv_heads, max_seq_len
-    else:
-        decode(q, k_cache, v_cache, seq_lens, scale, out=out, out_dtype=out_dtype, chunk_tokens=chunk_tokens,
-               path=path, seq_len_hint=seq_len_hint, stream=stream, waves=waves, tiles=tiles, merge=merge, per_cu=per_cu)
-        B, H_q, d = q.shape
-        H_kv, T_max = k_cache.shape[1], k_cache.shape[2]
-        L = 1
-    dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, seq_len_hint, chunk_tokens, path, waves, tiles, merge, per_cu)
-    ws = default_workspace(workspace_bytes(dims, L), dev)
-    nbytes = 0 if ws is None else ws.numel()
-    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
-    dref = ctypes.byref(dims)
-    if layers:
-        args = (int(L), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens), float(scale),
-                _ptr(out), dref, _ptr(ws), nbytes, s)
-    else:
-        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), float(scale), _ptr(out), dref, _ptr(ws),
-                nbytes, s)
-    return Prepared(layers, args, (out, q, k_cache, v_cache, seq_lens, kv_offsets, ws, dims))
+    """A Prepared launcher writing into a fresh output tensor, which each call
+    returns.  q [B,H_q,d] selects gqa_decode, q [L,B,H_q,d] selects
+    gqa_decode_layers."""
+    if q.dim() == 4:
+        args, keep = _layers_args(q, k_cache, v_cache, seq_lens, scale, kv_offsets, max_seq_len, num_kv_heads, None,
+                                  out_dtype, chunk_tokens, path, seq_len_hint, None, stream, waves, tiles, merge,
+                                  per_cu)
+        return Prepared(lib().gqa_decode_layers, args, keep)
+    args, keep = _decode_args(q, k_cache, v_cache, seq_lens, scale, None, out_dtype, chunk_tokens, path, seq_len_hint,
+                              None, stream, waves, tiles, merge, per_cu)
+    return Prepared(lib().gqa_decode, args, keep)
 
 
 def prepare_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float, out_dtype=None, max_seq_len=None,
@@ -790,9 +814,7 @@ def prepare_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float, out_dt
     """As prepare, for gqa_decode_paged."""
     args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, None, out_dtype, max_seq_len,
                              chunk_tokens, seq_len_hint, None, stream, tiles, merge, per_cu)
-    pr = Prepared(lib().gqa_decode_paged, args, keep)
-    pr()
-    return pr
+    return Prepared(lib().gqa_decode_paged, args, keep)
 
 
 def prepare_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_scale: float, out_dtype=None,
@@ -801,9 +823,7 @@ def prepare_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_s
     """As prepare, for gqa_decode_fp8."""
     args, keep = _fp8_args(q, k_cache, v_cache, seq_lens, scale, k_scale, v_scale, None, out_dtype, chunk_tokens,
                            seq_len_hint, None, stream, tiles, merge, per_cu)
-    pr = Prepared(lib().gqa_decode_fp8, args, keep)
-    pr()
-    return pr
+    return Prepared(lib().gqa_decode_fp8, args, keep)
 
 
 def prepare_layers_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: float, v_scale: float, kv_offsets=None,
@@ -813,9 +833,7 @@ def prepare_layers_fp8(q, k_cache, v_cache, seq_lens, scale: float, k_scale: flo
     args, keep = _layers_args(q, k_cache, v_cache, seq_lens, scale, kv_offsets, max_seq_len, num_kv_heads, None,
                               out_dtype, chunk_tokens, "mfma", seq_len_hint, None, stream, 0, tiles, merge, per_cu,
                               (k_scale, v_scale))
-    pr = Prepared(lib().gqa_decode_layers_fp8, args, keep)
-    pr()
-    return pr
+    return Prepared(lib().gqa_decode_layers_fp8, args, keep)
 
 
 def prepare_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, scale: float, k_scale: float, v_scale: float,
@@ -824,6 +842,4 @@ def prepare_paged_fp8(q, k_pool, v_pool, block_table, seq_lens, scale: float, k_
     """As prepare, for gqa_decode_paged_fp8."""
     args, keep = _paged_args(q, k_pool, v_pool, block_table, seq_lens, scale, None, out_dtype, max_seq_len,
                              chunk_tokens, seq_len_hint, None, stream, tiles, merge, per_cu, (k_scale, v_scale))
-    pr = Prepared(lib().gqa_decode_paged_fp8, args, keep)
-    pr()
-    return pr
+    return Prepared(lib().gqa_decode_paged_fp8, args, keep)

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libgqa_decode.so")
-SOURCES = [os.path.join(CSRC, "gqa_decode.hip")]
+SOURCES = [os.path.join(CSRC, "gqa_decode.hip"), os.path.join(CSRC, "probe.hip")]
 ARCH = "gfx950"
 
 

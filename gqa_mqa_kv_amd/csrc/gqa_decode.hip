@@ -25,24 +25,43 @@ bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Compute units of the current device (queried once per device; 256, the
-// MI355X count, when no device answers, e.g. in a build environment).
+// Compute units of the current device (queried once per device, under
+// std::call_once, so any thread may ask; 256, the MI355X count, when no
+// device answers, e.g. in a build environment).
+constexpr int kMaxCuDevices = 64;
+struct CuCount {
+  std::once_flag once;
+  int n = 256;
+};
+CuCount g_cu[kMaxCuDevices];
+
 int cu_count() {
-  static int cached[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxCuDevices) {
+    (void)hipGetLastError();
+    return 256;
   }
-  return cached[dev];
+  CuCount& c = g_cu[dev];
+  std::call_once(c.once, [&] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      c.n = n;
+    else
+      (void)hipGetLastError();
+  });
+  return c.n;
 }
+
+// The kernel family a call launches: the cache's element type and layout,
+// and whether the append of the new token is fused in.
+struct KernelKind {
+  bool kv8 = false, paged = false, append = false;
+};
 
 int max_waves(int hb);
 int max_tiles(int hb, bool kv8);
 int default_tiles(int hb, bool kv8);
-int resident_groups_per_cu(const gqa_dims* d, int waves, int tiles);
+int resident_groups_per_cu(const gqa_dims* d, const KernelKind& kind, int waves, int tiles);
 
 bool use_mfma(const gqa_dims* d) {
   if (d->path == GQA_PATH_MFMA) return true;
@@ -93,8 +112,10 @@ struct Plan {
   size_t ws_bytes, cnt_bytes, desc_bytes, ml_bytes;
 };
 
-// kv8: the cache holds one-byte elements (the E4M3 entry point).
-Plan make_plan(const gqa_dims* d, int32_t L, bool kv8 = false) {
+// kind: the kernel the call launches (its tile default and, for more than
+// one workgroup per CU, its occupancy).
+Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind{}) {
+  const bool kv8 = kind.kv8;
   Plan p;
   p.mfma = use_mfma(d);
   p.units = (int64_t)L * d->batch * d->num_kv_heads;
@@ -126,7 +147,8 @@ Plan make_plan(const gqa_dims* d, int32_t L, bool kv8 = false) {
       // every workgroup must be resident at once (equal spans: a second
       // dispatch round would double the time)
       const int want = d->workgroups_per_cu ? d->workgroups_per_cu : 1;
-      const int64_t per_cu = std::max(1, std::min(want, resident_groups_per_cu(d, p.waves, p.tiles)));
+      const int64_t per_cu =
+          want == 1 ? 1 : std::max(1, std::min(want, resident_groups_per_cu(d, kind, p.waves, p.tiles)));
       p.groups = (int32_t)std::max<int64_t>(1, std::min<int64_t>(cu_count() * per_cu, ceil_div(upper, 16)));
     }
     slots = 2 * (int64_t)p.groups;
@@ -225,37 +247,41 @@ struct CacheArgs {
   double rope_base = 0.0;
 };
 
-kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan, const CacheArgs& ca) {
+KernelKind kind_of(const CacheArgs& ca) {
+  KernelKind k;
+  k.kv8 = ca.e4m3;
+  k.paged = ca.block_table != nullptr;
+  k.append = ca.k_new != nullptr;
+  return k;
+}
+
+// The matrix-core kernel of a kind (waves and tiles as planned).
+kernel_fn mfma_kernel_of(const gqa_dims* d, const KernelKind& kind, int waves, int tiles) {
   const int G = d->num_q_heads / d->num_kv_heads;
-  if (plan.mfma) {
-    const int hb = (G + 15) / 16;
-    if (ca.k_new && ca.block_table)
-      return d->head_dim == 128 ? mfma_append_kernel<128, true>(hb, plan.tiles)
-                                : mfma_append_kernel<64, true>(hb, plan.tiles);
-    if (ca.k_new)
-      return d->head_dim == 128 ? mfma_append_kernel<128>(hb, plan.tiles) : mfma_append_kernel<64>(hb, plan.tiles);
-    if (ca.e4m3 && ca.block_table)
-      return d->head_dim == 128 ? mfma_kernel<128, true, true>(hb, plan.waves, plan.tiles)
-                                : mfma_kernel<64, true, true>(hb, plan.waves, plan.tiles);
-    if (ca.e4m3)
-      return d->head_dim == 128 ? mfma_kernel<128, false, true>(hb, plan.waves, plan.tiles)
-                                : mfma_kernel<64, false, true>(hb, plan.waves, plan.tiles);
-    if (ca.block_table)
-      return d->head_dim == 128 ? mfma_kernel<128, true>(hb, plan.waves, plan.tiles)
-                                : mfma_kernel<64, true>(hb, plan.waves, plan.tiles);
-    return d->head_dim == 128 ? mfma_kernel<128>(hb, plan.waves, plan.tiles)
-                              : mfma_kernel<64>(hb, plan.waves, plan.tiles);
-  }
+  const int hb = (G + 15) / 16;
+  const bool d128 = d->head_dim == 128;
+  if (kind.append && kind.paged)
+    return d128 ? mfma_append_kernel<128, true>(hb, tiles) : mfma_append_kernel<64, true>(hb, tiles);
+  if (kind.append) return d128 ? mfma_append_kernel<128>(hb, tiles) : mfma_append_kernel<64>(hb, tiles);
+  if (kind.kv8 && kind.paged)
+    return d128 ? mfma_kernel<128, true, true>(hb, waves, tiles) : mfma_kernel<64, true, true>(hb, waves, tiles);
+  if (kind.kv8)
+    return d128 ? mfma_kernel<128, false, true>(hb, waves, tiles) : mfma_kernel<64, false, true>(hb, waves, tiles);
+  if (kind.paged) return d128 ? mfma_kernel<128, true>(hb, waves, tiles) : mfma_kernel<64, true>(hb, waves, tiles);
+  return d128 ? mfma_kernel<128>(hb, waves, tiles) : mfma_kernel<64>(hb, waves, tiles);
+}
+
+kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan, const CacheArgs& ca) {
+  if (plan.mfma) return mfma_kernel_of(d, kind_of(ca), plan.waves, plan.tiles);
   if (d->dtype == GQA_DTYPE_F32)
     return d->head_dim == 128 ? gqa::gqa_decode_valu<float, 128> : gqa::gqa_decode_valu<float, 64>;
   return d->head_dim == 128 ? gqa::gqa_decode_valu<uint16_t, 128> : gqa::gqa_decode_valu<uint16_t, 64>;
 }
 
-// Workgroups of the chosen matrix-core kernel that fit on one CU together
-// (HIP occupancy query; 1 when no device answers).
-int resident_groups_per_cu(const gqa_dims* d, int waves, int tiles) {
-  const int hb = (d->num_q_heads / d->num_kv_heads + 15) / 16;
-  const kernel_fn k = d->head_dim == 128 ? mfma_kernel<128>(hb, waves, tiles) : mfma_kernel<64>(hb, waves, tiles);
+// Workgroups of the matrix-core kernel a call of this kind launches that fit
+// on one CU together (HIP occupancy query; 1 when no device answers).
+int resident_groups_per_cu(const gqa_dims* d, const KernelKind& kind, int waves, int tiles) {
+  const kernel_fn k = mfma_kernel_of(d, kind, waves, tiles);
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k), 64 * waves, 0) !=
           hipSuccess ||
@@ -266,19 +292,35 @@ int resident_groups_per_cu(const gqa_dims* d, int waves, int tiles) {
   return n;
 }
 
-gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const CacheArgs& ca,
-                  const int32_t* seq_lens, float scale, void* out, const gqa_dims* d, void* ws, size_t ws_bytes,
-                  void* stream) {
+// Every argument check of a decode launch, on the host; fills the plan.
+// *nothing_to_do is set for an empty batch (valid, nothing is enqueued).
+gqa_status check_launch(int32_t L, const void* q, const void* k, const void* v, const CacheArgs& ca,
+                        const int32_t* seq_lens, float scale, const void* out, const gqa_dims* d, const void* ws,
+                        size_t ws_bytes, Plan* plan, bool* nothing_to_do) {
+  *nothing_to_do = false;
   gqa_status st = check_dims(d, L);
   if (st != GQA_OK) return st;
   if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
-  if (d->batch == 0) return GQA_OK;
+  if (d->batch == 0) {
+    *nothing_to_do = true;
+    return GQA_OK;
+  }
   if (!q || !k || !v || !seq_lens || !out) return GQA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
     return GQA_ERR_INVALID_ARG;
   if (ca.kv_offsets && !aligned(ca.kv_offsets, 8)) return GQA_ERR_INVALID_ARG;
-  const Plan plan = make_plan(d, L, ca.e4m3);
-  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned(ws, 256))) return GQA_ERR_WORKSPACE;
+  *plan = make_plan(d, L, kind_of(ca));
+  if (plan->ws_bytes > 0 && (!ws || ws_bytes < plan->ws_bytes || !aligned(ws, 256))) return GQA_ERR_WORKSPACE;
+  return GQA_OK;
+}
+
+gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const CacheArgs& ca,
+                  const int32_t* seq_lens, float scale, void* out, const gqa_dims* d, void* ws, size_t ws_bytes,
+                  void* stream) {
+  Plan plan;
+  bool nothing;
+  gqa_status st = check_launch(L, q, k, v, ca, seq_lens, scale, out, d, ws, ws_bytes, &plan, &nothing);
+  if (st != GQA_OK || nothing) return st;
 
   gqa::Problem p;
   p.q = q;
@@ -352,7 +394,18 @@ extern "C" {
 
 size_t gqa_decode_workspace_bytes(const gqa_dims* dims, int32_t num_layers) {
   if (check_dims(dims, num_layers) != GQA_OK) return 0;
-  return make_plan(dims, num_layers).ws_bytes;
+  // the most any entry point taking these dims can need: the kernels of the
+  // cache kinds differ in their tile default and occupancy
+  size_t most = 0;
+  for (int v = 0; v < 8; ++v) {
+    KernelKind k;
+    k.kv8 = v & 1;
+    k.paged = v & 2;
+    k.append = v & 4;
+    if (k.append && k.kv8) continue;   // no such kernel
+    most = std::max(most, make_plan(dims, num_layers, k).ws_bytes);
+  }
+  return most;
 }
 
 gqa_status gqa_decode_plan(const gqa_dims* dims, int32_t num_layers, int32_t* chunk_tokens, int32_t* num_chunks) {
@@ -538,7 +591,13 @@ gqa_status decode_append_launch(const void* q, const void* k_new, const void* v_
     // Two head blocks: there the fused kernel needs more registers than a
     // SIMD holds and spills at every piece end, and the append kernel followed
     // by the decode of the grown cache is faster, with the same results (both
-    // turn, round and substitute alike).
+    // turn, round and substitute alike).  Every argument of both launches is
+    // checked before the first is enqueued.
+    Plan plan;
+    bool nothing;
+    st = check_launch(1, q_out, k_cache, v_cache, cb, new_seq_lens, scale, out, dims, workspace, workspace_bytes,
+                      &plan, &nothing);
+    if (st != GQA_OK) return st;
     st = append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, block_table, max_pages, page, seq_lens,
                        new_seq_lens, rope_base, q_out, dims, stream);
     if (st != GQA_OK) return st;

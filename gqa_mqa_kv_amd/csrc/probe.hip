@@ -1,0 +1,81 @@
+// HBM read probe (include/gqa_probe.h): a plain streaming read of two
+// buffers in one launch, the ceiling for a decode step that reads the same
+// bytes.
+#include "gqa_probe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;   // 16-byte loads in flight per thread
+
+// Reads vectors [lo, hi) of src: rounds of kUnroll loads per thread, kThreads
+// vectors apart, then one vector per thread for a ragged end.
+__device__ __forceinline__ void read_range(const u32x4* __restrict__ src, int64_t lo, int64_t hi, u32x4& acc) {
+  int64_t i = lo + threadIdx.x;
+  for (; i + (int64_t)(kUnroll - 1) * kThreads < hi; i += (int64_t)kUnroll * kThreads) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + (int64_t)u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  for (; i < hi; i += kThreads) acc ^= __builtin_nontemporal_load(src + i);
+}
+
+// The stream is a's na vectors, then b's nb; workgroup w reads stream
+// vectors [w * per_wg, min((w + 1) * per_wg, na + nb)).
+__global__ __launch_bounds__(kThreads) void hbm_read_probe(const u32x4* __restrict__ a, int64_t na,
+                                                           const u32x4* __restrict__ b, int64_t nb,
+                                                           int64_t per_wg, uint32_t* sink) {
+  const int64_t s0 = (int64_t)blockIdx.x * per_wg;
+  const int64_t s1 = s0 + per_wg < na + nb ? s0 + per_wg : na + nb;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  if (s0 < na) read_range(a, s0, s1 < na ? s1 : na, acc);
+  if (s1 > na) read_range(b, (s0 > na ? s0 : na) - na, s1 - na, acc);
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, x);
+}
+
+int cu_count_now() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" gqa_status gqa_hbm_read_probe(const void* a, size_t a_bytes, const void* b, size_t b_bytes,
+                                         int32_t workgroups_per_cu, uint32_t* sink, void* stream) {
+  if (workgroups_per_cu < 1 || workgroups_per_cu > 8 || a_bytes % 16 != 0 || b_bytes % 16 != 0)
+    return GQA_ERR_INVALID_ARG;
+  if (a_bytes + b_bytes == 0) return GQA_OK;
+  if ((a_bytes && (!a || !aligned16(a))) || (b_bytes && (!b || !aligned16(b))) || !sink ||
+      (reinterpret_cast<uintptr_t>(sink) & 3))
+    return GQA_ERR_INVALID_ARG;
+  const int64_t na = (int64_t)(a_bytes / 16), nb = (int64_t)(b_bytes / 16), n = na + nb;
+  const int64_t groups = (int64_t)cu_count_now() * workgroups_per_cu;
+  // spans of whole rounds (kUnroll * kThreads vectors), at least one round
+  const int64_t round = (int64_t)kUnroll * kThreads;
+  const int64_t per_wg = ((n + groups - 1) / groups + round - 1) / round * round;
+  const int64_t grid = (n + per_wg - 1) / per_wg;
+  const u32x4* pa = static_cast<const u32x4*>(a);
+  const u32x4* pb = static_cast<const u32x4*>(b);
+  int64_t na_ = na, nb_ = nb, per_ = per_wg;
+  void* args[] = {&pa, &na_, &pb, &nb_, &per_, &sink};
+  if (hipLaunchKernel(reinterpret_cast<const void*>(hbm_read_probe), dim3((unsigned)grid), dim3(kThreads), args, 0,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GQA_ERR_LAUNCH;
+  return GQA_OK;
+}

@@ -14,15 +14,20 @@ from gqa_mqa_kv_amd import _binding, build, workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 FAKE = 0x100000          # 16-byte aligned stand-in address; never dereferenced on these error paths
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gqa_\w+)\s*\(", src)))
+    """Every function include/*.h declares."""
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gqa_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -443,3 +448,44 @@ def test_noalloc_validates_and_refuses_plans_beyond_its_buffer():
     src = open(HEADER).read()
     assert "#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in src
     assert _binding.NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_read_probe_validates_its_arguments():
+    """gqa_hbm_read_probe refuses bad sizes, pointers and launch shapes on the
+    host, and treats an empty read as a no-op."""
+    lib = gqa.lib()
+    assert lib.gqa_hbm_read_probe(None, 0, None, 0, 1, None, None) == OK
+    assert lib.gqa_hbm_read_probe(FAKE, 1000, None, 0, 1, FAKE, None) == INVALID      # not a multiple of 16
+    assert lib.gqa_hbm_read_probe(FAKE, 1024, FAKE, 8, 1, FAKE, None) == INVALID      # b not a multiple of 16
+    assert lib.gqa_hbm_read_probe(FAKE + 8, 1024, None, 0, 1, FAKE, None) == INVALID  # misaligned
+    assert lib.gqa_hbm_read_probe(None, 1024, None, 0, 1, FAKE, None) == INVALID
+    assert lib.gqa_hbm_read_probe(FAKE, 1024, None, 16, 1, FAKE, None) == INVALID     # b missing
+    assert lib.gqa_hbm_read_probe(FAKE, 1024, None, 0, 1, None, None) == INVALID      # no sink
+    assert lib.gqa_hbm_read_probe(FAKE, 1024, None, 0, 1, FAKE + 2, None) == INVALID  # sink misaligned
+    for wpc in (0, 9, -1):
+        assert lib.gqa_hbm_read_probe(FAKE, 1024, None, 0, wpc, FAKE, None) == INVALID
+
+
+def test_two_kernel_append_path_checks_everything_before_enqueueing():
+    """With G > 16 and new lengths written, gqa_decode_append_rope (and its
+    paged form) runs as the append kernel followed by the decode: every
+    argument of the decode is checked before the append is enqueued, so a
+    missing workspace, or a missing or misaligned output, is reported as
+    such (no kernel launch is attempted on this GPU-less host, which would
+    report GQA_ERR_LAUNCH)."""
+    lib = gqa.lib()
+    Q, KN, VN, KC, VC, SL, NL, QO, OUT = (FAKE + 0x1000 * i for i in range(9))
+    for H_q in (32, 64):                          # two head blocks; two head groups
+        d = dims(H_q=H_q, H_kv=1, T_max=4096, d=128)
+        assert gqa.workspace_bytes(d) > 0
+        call = lambda out=OUT, ws=None, nb=0: lib.gqa_decode_append_rope(Q, KN, VN, KC, VC, None, SL, NL, 10000.0,
+                                                                        0.125, QO, out, ctypes.byref(d), ws, nb, None)
+        assert call() == WORKSPACE
+        assert call(ws=FAKE, nb=gqa.workspace_bytes(d) - 256) == WORKSPACE
+        assert call(out=None) == INVALID
+        assert call(out=OUT + 8) == INVALID
+        paged = lambda ws=None, nb=0: lib.gqa_decode_append_rope_paged(Q, KN, VN, KC, VC, FAKE, 256, 16, SL, NL,
+                                                                       10000.0, 0.125, QO, OUT, ctypes.byref(d), ws,
+                                                                       nb, None)
+        assert paged() == WORKSPACE
+

@@ -43,3 +43,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_samples_layers_of_a_layer_batched_workload():
+    """A layer-batched workload's baseline times the oracle on whole layers
+    (0, 1, ...) until the budget is spent and scales the mean to all layers;
+    a tiny budget samples exactly one layer."""
+    w = workloads.Workload("stack-tiny", 3, 8, 2, 64, 20, 60, torch.bfloat16, 5, layers=4, packed=True)
+    x = workloads.generate(w, "cpu")
+    r = bench.cpu_baseline(w, budget_s=0.0, x=x)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0 and r["cores"] >= 1
+    assert r["sample"].startswith("1 of 4 layers of stack-tiny")
+    nbytes = bench.algorithmic_bytes(w, x["seq_lens"], 2)
+    assert abs(nbytes / (r["us_per_step"] * 1e-6) / 1e9 - r["value"]) <= 1e-3 * r["value"] + 1e-3
+    r = bench.cpu_baseline(w, budget_s=60.0, x=x)
+    assert r["sample"].startswith("4 of 4 layers")
