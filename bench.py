@@ -55,7 +55,7 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "GQA decode effective HBM GB/s (% of MI355X peak) + µs/step"
 DEFAULT_WORKLOAD = "llama3-8b-32-layer-stack"
 KERNEL_SOURCES = ["common.h", "kernel_mfma.h", "kernel_valu.h", "gqa_decode.hip"]
-LONG_STEP_MS = 0.5   # steps at least this long carry events of their own inside the timed region
+LONG_STEP_BYTES = 8e9   # steps that move this many bytes (>1 ms) carry events of their own inside the timed region
 
 
 def traffic_profile(key: str) -> str:
@@ -224,7 +224,7 @@ def read_probe(torch, gqa, pairs, stream, launches: int = 0, sustained_s: float 
     res = {"GB/s": rates[best][0], "us_per_pass": rates[best][1], "bytes_per_pass": nbytes,
            "launches_per_pass": len(pairs), "workgroups_per_cu": best,
            "GB/s_by_workgroups_per_cu": {str(k): v[0] for k, v in rates.items()},
-           "kernel": "gqa_hbm_read_probe: 16-byte non-temporal loads, 8 in flight per thread, one span per workgroup"}
+           "kernel": "gqa_hbm_read_probe: 16-byte non-temporal loads in double-buffered rounds of 8 per thread, one span per workgroup"}
     if sustained_s > 0:
         res["sustained"] = sustained_rates(torch, lambda i: one_pass(best), stream, nbytes,
                                            max(20, int(sustained_s * 1e6 / rates[best][1])))
@@ -454,18 +454,16 @@ def main():
     def step(i):
         return launchers[i % reps]()
 
-    we0, we1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    we0.record(stream)
     for i in range(args.warmup):
         step(i)
-    we1.record(stream)
     torch.cuda.synchronize()
-    warm_ms = we0.elapsed_time(we1) / max(args.warmup, 1)
+    nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4, args.paged, 1 if fp8 else 0)
     # Long steps carry an event of their own at every step boundary inside the
     # timed region (a marker between launches that are milliseconds long);
-    # short steps are timed as one block, and their percentiles come from a
-    # pass after it.
-    long_steps = args.warmup > 0 and warm_ms >= LONG_STEP_MS
+    # short steps are timed as one block (a marker between launches tens of
+    # microseconds long would cost a few microseconds each), and their
+    # percentiles come from a pass after it.
+    long_steps = nbytes >= LONG_STEP_BYTES
     # timed region: exactly K steps, synchronised on both sides
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1 if long_steps else 2)]
     torch.cuda.synchronize()
@@ -482,7 +480,6 @@ def main():
     total_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = total_ms / args.steps
     step_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)] if long_steps else None
-    nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4, args.paged, 1 if fp8 else 0)
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
 
     # The decode kernel's average launch duration: HIP events bracket the

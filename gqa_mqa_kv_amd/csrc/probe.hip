@@ -12,24 +12,51 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;   // 16-byte loads in flight per thread
+constexpr int kUnroll = 8;   // 16-byte loads per thread and buffer; two buffers alternate
 
-// Reads vectors [lo, hi) of src: rounds of kUnroll loads per thread, kThreads
-// vectors apart, then one vector per thread for a ragged end.
+__device__ __forceinline__ void load_round(const u32x4* __restrict__ src, int64_t i, u32x4 (&v)[kUnroll]) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + (int64_t)u * kThreads);
+}
+__device__ __forceinline__ void fold(const u32x4 (&v)[kUnroll], u32x4& acc) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+}
+
+// Reads vectors [lo, hi) of src.  Full rounds (kUnroll vectors per thread,
+// kThreads vectors apart) go through two register buffers: the next round
+// is issued before the current one is folded, so a thread always has a
+// round in flight.  The rounds are counted for the whole workgroup, so every
+// load of a round is unconditional and in bounds; what is left is read one
+// vector per thread.
 __device__ __forceinline__ void read_range(const u32x4* __restrict__ src, int64_t lo, int64_t hi, u32x4& acc) {
-  int64_t i = lo + threadIdx.x;
-  for (; i + (int64_t)(kUnroll - 1) * kThreads < hi; i += (int64_t)kUnroll * kThreads) {
-    u32x4 v[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + (int64_t)u * kThreads);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  constexpr int64_t R1 = (int64_t)kUnroll * kThreads;   // vectors per round
+  const int64_t rounds = (hi - lo) / R1;
+  const int64_t base = lo + threadIdx.x;
+  u32x4 a[kUnroll], b[kUnroll];
+  if (rounds > 0) load_round(src, base, a);
+  int64_t r = 1;
+  for (; r + 1 < rounds; r += 2) {
+    load_round(src, base + r * R1, b);
+    fold(a, acc);
+    load_round(src, base + (r + 1) * R1, a);
+    fold(b, acc);
   }
-  for (; i < hi; i += kThreads) acc ^= __builtin_nontemporal_load(src + i);
+  if (r < rounds) {
+    load_round(src, base + r * R1, b);
+    fold(a, acc);
+    fold(b, acc);
+  } else if (rounds > 0) {
+    fold(a, acc);
+  }
+  for (int64_t i = lo + rounds * R1 + threadIdx.x; i < hi; i += kThreads) acc ^= __builtin_nontemporal_load(src + i);
 }
 
 // The stream is a's na vectors, then b's nb; workgroup w reads stream
-// vectors [w * per_wg, min((w + 1) * per_wg, na + nb)).
+// vectors [w * per_wg, min((w + 1) * per_wg, na + nb)).  What a wavefront
+// read is stored to *sink only in the (one in 2^32) case that its fold
+// equals a fixed word: the loads cannot be dropped, and no two workgroups
+// contend for the sink.
 __global__ __launch_bounds__(kThreads) void hbm_read_probe(const u32x4* __restrict__ a, int64_t na,
                                                            const u32x4* __restrict__ b, int64_t nb,
                                                            int64_t per_wg, uint32_t* sink) {
@@ -41,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void hbm_read_probe(const u32x4* __restri
   uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off);
-  if ((threadIdx.x & 63) == 0) atomicXor(sink, x);
+  if ((threadIdx.x & 63) == 0 && x == 0x9e3779b9u) *sink = x;
 }
 
 int cu_count_now() {

@@ -27,9 +27,12 @@ extern "C" {
  * launch, with 16-byte non-temporal vector loads (the loads of the decode
  * kernels), and nothing else.  The two buffers form one stream (a, then b)
  * cut into equal contiguous spans, one per workgroup, as the decode kernel's
- * token split cuts the K and V it reads; each thread keeps eight loads in
- * flight.  What is read is folded into *sink by XOR, so that no load can be
- * dropped (the value left in *sink means nothing).
+ * token split cuts the K and V it reads; each thread issues its loads in
+ * rounds of eight and issues the next round before folding the current
+ * one, so eight to sixteen loads are in flight.  What a wavefront reads is
+ * folded by XOR and stored to *sink only when the fold equals one fixed
+ * word, so that no load can be dropped and no workgroups contend for the
+ * sink (the value left in *sink means nothing; it may stay untouched).
  *   a, b              : device memory, 16-byte aligned; caller-owned, only
  *                       read.  b may be NULL when b_bytes is 0.
  *   a_bytes, b_bytes  : multiples of 16 (both 0: a no-op)

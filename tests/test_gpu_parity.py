@@ -333,6 +333,35 @@ def test_graph_replays_match_eager(merge):
         gpu_decode(small(2, 8, 2, 64, 100, seed=43))   # eager work on the device between replays
 
 
+def test_two_streams_use_their_own_default_workspaces():
+    """Calls of different shapes issued on two streams that may overlap in
+    time, each on the binding's default workspace and each using the fused
+    merge's arrival counters: every stream gets a buffer of its own, and
+    every result matches the oracle."""
+    x = small(3, 32, 8, 128, 3000, seed=81, lo=1000)
+    y = small(2, 64, 8, 128, 2500, seed=82, lo=500)
+    rx = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
+    ry = oracle.decode(y["q"], y["k"], y["v"], y["seq_lens"], y["scale"])
+    xd, yd = to_dev(x), to_dev(y)
+    s1, s2 = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(8):
+        with torch.cuda.stream(s1):
+            a = gqa.decode(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], chunk_tokens=64, merge="fused",
+                           out_dtype=torch.float32)
+        with torch.cuda.stream(s2):
+            b = gqa.decode(yd["q"], yd["k"], yd["v"], yd["seq_lens"], y["scale"], chunk_tokens=128, merge="fused",
+                           out_dtype=torch.float32)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    w1 = gqa.default_workspace(1, DEV, s1.cuda_stream)
+    w2 = gqa.default_workspace(1, DEV, s2.cuda_stream)
+    assert w1.data_ptr() != w2.data_ptr()
+    for a, b in outs:
+        assert err(a, rx) <= 2e-3 and err(b, ry) <= 2e-3
+
+
 def test_paths_and_chunkings_agree():
     x = small(2, 32, 8, 128, 1500, seed=41, lo=1000)
     ref = oracle.decode(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"])
