@@ -69,3 +69,39 @@ def test_noalloc_vector_path_and_bf16_out():
     b = gqa.decode(yd["q"], yd["k"], yd["v"], yd["seq_lens"], y["scale"])
     torch.cuda.synchronize()
     assert a.dtype == torch.bfloat16 and torch.equal(a, b)
+
+
+def test_noalloc_under_graph_capture():
+    """The entry point is for callers that cannot allocate, such as code under
+    HIP graph capture: calls captured in a graph (two shapes, the fused
+    merge's counters in use) replay bitwise like the eager calls, with eager
+    work between the replays."""
+    x, xd = case(3, 32, 8, 128, 2000, 500, seed=41)
+    y, yd = case(2, 32, 1, 128, 1500, 1000, seed=42)
+    s = torch.cuda.Stream(DEV)
+    outs = [torch.empty(3, 32, 128, dtype=torch.float32, device=DEV),
+            torch.empty(2, 32, 128, dtype=torch.float32, device=DEV)]
+    f32 = torch.float32
+    calls = [lambda: gqa.decode_noalloc(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], out=outs[0],
+                                        out_dtype=f32, chunk_tokens=128, merge="fused", stream=s.cuda_stream),
+             lambda: gqa.decode_noalloc(yd["q"], yd["k"], yd["v"], yd["seq_lens"], y["scale"], out=outs[1],
+                                        out_dtype=f32, chunk_tokens=64, merge="kernel", stream=s.cuda_stream)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for c in calls:
+            c()
+    s.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in calls:
+            c()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), "replay %d differs" % rep
+        run_pair(x, xd, chunk_tokens=256)   # eager work between the replays
