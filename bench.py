@@ -312,9 +312,10 @@ def time_append(torch, gqa, w, x, stream, steps: int, warmup: int):
 def time_fused_append(torch, gqa, w, batches, stream, steps: int, warmup: int):
     """One decode step including its append: gqa_append_rope then gqa_decode
     (two launches) against gqa_decode_append_rope (one), over the rotated
-    input batches.  Every sequence holds one token fewer than in the plain
-    step and appends one, so the attention covers the same tokens.  Both
-    sides rewrite the same cache rows with the same values at every step."""
+    input batches (their paged and E4M3 forms for --paged and --kv fp8).
+    Every sequence holds one token fewer than in the plain step and appends
+    one, so the attention covers the same tokens.  Both sides rewrite the
+    same cache rows with the same values at every step."""
     two, one = [], []
     for x in batches:
         g = torch.Generator(device=x["q"].device).manual_seed(w.seed + 19)
@@ -323,6 +324,23 @@ def time_fused_append(torch, gqa, w, batches, stream, steps: int, warmup: int):
         lens = (x["seq_lens"] - 1).clamp(min=0).to(torch.int32)
         new_lens = torch.empty_like(lens)
         q_out = torch.empty_like(x["q"])
+        if "k_scale" in x:   # E4M3 cache: the quantising append and the E4M3 decode
+            sc = (x["k_scale"], x["v_scale"])
+            if "pool" in x:
+                kp, vp, table = x["pool"]
+                app = gqa.prepare_append_paged_fp8(x["q"], kn, vn, kp, vp, table, lens, 500000.0, *sc,
+                                                   max_seq_len=w.T_max, q_out=q_out, new_seq_lens=new_lens)
+                dec = gqa.prepare_paged_fp8(q_out, kp, vp, table, new_lens, x["scale"], *sc, max_seq_len=w.T_max)
+                one.append(gqa.prepare_decode_append_paged_fp8(x["q"], kn, vn, kp, vp, table, lens, 500000.0,
+                                                               x["scale"], *sc, max_seq_len=w.T_max))
+            else:
+                app = gqa.prepare_append_fp8(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, *sc, q_out=q_out,
+                                             new_seq_lens=new_lens)
+                dec = gqa.prepare_fp8(q_out, x["k"], x["v"], new_lens, x["scale"], *sc)
+                one.append(gqa.prepare_decode_append_fp8(x["q"], kn, vn, x["k"], x["v"], lens, 500000.0, x["scale"],
+                                                         *sc))
+            two.append((app, dec))
+            continue
         if "pool" in x:   # paged: the pool and table of the plain step (every appended row has its page)
             kp, vp, table = x["pool"]
             app = gqa.prepare_append_paged(x["q"], kn, vn, kp, vp, table, lens, 500000.0, max_seq_len=w.T_max,
@@ -560,8 +578,8 @@ def main():
     if w.layers > 1 and not args.no_extras:
         result["sequential_single_layer_launches"] = time_layers_one_by_one(torch, gqa, workloads, w, batches[0],
                                                                             stream, out_dtype, fp8=fp8)
-    if w.layers == 1 and w.dtype == torch.bfloat16 and not fp8 and not args.no_extras:
-        if not args.paged:
+    if w.layers == 1 and w.dtype == torch.bfloat16 and not args.no_extras:
+        if not args.paged and not fp8:
             result["append_rope"] = time_append(torch, gqa, w, batches[0], stream, args.steps, args.warmup)
         result["step_with_append"] = time_fused_append(torch, gqa, w, batches, stream, min(args.steps, 100),
                                                        args.warmup)

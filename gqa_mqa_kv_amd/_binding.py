@@ -22,7 +22,8 @@ STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED", 3: "G
           4: "GQA_ERR_LAUNCH", 5: "GQA_ERR_SCRATCH"}
 NOALLOC_SCRATCH_BYTES = 32 << 20   # GQA_NOALLOC_SCRATCH_BYTES
 SYMBOLS = ("gqa_append_rope", "gqa_append_rope_fp8", "gqa_append_rope_paged", "gqa_append_rope_paged_fp8",
-           "gqa_decode", "gqa_decode_append_rope", "gqa_decode_append_rope_paged", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8",
+           "gqa_decode", "gqa_decode_append_rope", "gqa_decode_append_rope_fp8", "gqa_decode_append_rope_paged",
+           "gqa_decode_append_rope_paged_fp8", "gqa_decode_fp8", "gqa_decode_layers", "gqa_decode_layers_fp8",
            "gqa_decode_paged",
            "gqa_decode_paged_fp8", "gqa_decode_noalloc",
            "gqa_decode_workspace_bytes", "gqa_decode_plan", "gqa_status_string",
@@ -70,6 +71,13 @@ def lib() -> ctypes.CDLL:
         L.gqa_decode_append_rope_paged.restype = ctypes.c_int
         L.gqa_decode_append_rope_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, ctypes.c_float,
                                                    ctypes.c_float, vp, vp, dims_p, vp, sz, vp]
+        f = ctypes.c_float
+        L.gqa_decode_append_rope_fp8.restype = ctypes.c_int
+        L.gqa_decode_append_rope_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f, f, f, f, vp, vp, dims_p, vp, sz,
+                                                 vp]
+        L.gqa_decode_append_rope_paged_fp8.restype = ctypes.c_int
+        L.gqa_decode_append_rope_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, f, f, f, f, vp, vp,
+                                                       dims_p, vp, sz, vp]
         L.gqa_decode_layers_fp8.restype = ctypes.c_int
         L.gqa_decode_layers_fp8.argtypes = [i32, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                             vp, dims_p, vp, sz, vp]
@@ -522,7 +530,10 @@ def append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k
 
 
 def _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets, max_seq_len, q_out,
-                        new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream, tiles, merge, per_cu):
+                        new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream, tiles, merge, per_cu,
+                        scales=None):
+    """Validated arguments of gqa_decode_append_rope, or of
+    gqa_decode_append_rope_fp8 when ``scales`` = (k_scale, v_scale)."""
     dev = q.device
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (seq_lens, "seq_lens")):
@@ -545,9 +556,11 @@ def _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, 
         if v_cache.numel() != k_cache.numel() or k_cache.numel() % (H_kv * d):
             raise ValueError("packed cache size mismatch")
         T_max = max_seq_len
-    for t in (k_new, v_new, k_cache, v_cache):
+    for t in (k_new, v_new) + (() if scales else (k_cache, v_cache)):
         if t.dtype != q.dtype:
             raise TypeError("q, k_new, v_new and the caches must share one dtype")
+    if scales and (k_cache.dtype not in E4M3_DTYPES or v_cache.dtype not in E4M3_DTYPES):
+        raise TypeError("E4M3 caches are uint8 or float8_e4m3fn")
     dims = make_dims(B, H_q, H_kv, d, T_max, q.dtype, out_dtype, 0, chunk_tokens, "mfma", 0, tiles, merge, per_cu)
     if q_out is None:
         q_out = torch.empty_like(q)
@@ -566,9 +579,10 @@ def _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, 
         raise ValueError("out must be [B,H_q,d] of the output dtype")
     s = _stream_handle(dev, stream)
     ws = default_workspace(workspace_bytes(dims), dev, s) if workspace is None else workspace
+    sc = (float(scale),) if scales is None else (float(scale), float(scales[0]), float(scales[1]))
     args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(kv_offsets), _ptr(seq_lens),
-            _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out), ctypes.byref(dims), _ptr(ws),
-            0 if ws is None else ws.numel() * ws.element_size(), s)
+            _ptr(new_seq_lens), float(rope_base)) + sc + (_ptr(q_out), _ptr(out), ctypes.byref(dims), _ptr(ws),
+                                                          0 if ws is None else ws.numel() * ws.element_size(), s)
     return args, (out, q_out, new_seq_lens, q, k_new, v_new, k_cache, v_cache, kv_offsets, seq_lens, ws, dims)
 
 
@@ -592,7 +606,9 @@ def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: f
 
 def _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, scale, max_seq_len,
                               q_out, new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream, tiles, merge,
-                              per_cu):
+                              per_cu, scales=None):
+    """Validated arguments of gqa_decode_append_rope_paged, or of
+    gqa_decode_append_rope_paged_fp8 when ``scales`` = (k_scale, v_scale)."""
     dev = q.device
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool"),
                  (block_table, "block_table"), (seq_lens, "seq_lens")):
@@ -607,9 +623,11 @@ def _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_
     if k_new.shape != (B, H_kv, d) or k_pool.shape[3] != d or block_table.shape[0] != B or \
             block_table.dtype != torch.int32 or seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
         raise ValueError("shape mismatch between q, k_new/v_new, pools, block_table and seq_lens")
-    for t in (k_new, v_new, k_pool, v_pool):
+    for t in (k_new, v_new) + (() if scales else (k_pool, v_pool)):
         if t.dtype != q.dtype:
             raise TypeError("q, k_new, v_new and the pools must share one dtype")
+    if scales and (k_pool.dtype not in E4M3_DTYPES or v_pool.dtype not in E4M3_DTYPES):
+        raise TypeError("E4M3 pools are uint8 or float8_e4m3fn")
     T = max_pages * page if max_seq_len is None else int(max_seq_len)
     dims = make_dims(B, H_q, H_kv, d, T, q.dtype, out_dtype, 0, chunk_tokens, "mfma", 0, tiles, merge, per_cu)
     if q_out is None:
@@ -629,9 +647,10 @@ def _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_
         raise ValueError("out must be [B,H_q,d] of the output dtype")
     s = _stream_handle(dev, stream)
     ws = default_workspace(workspace_bytes(dims), dev, s) if workspace is None else workspace
+    sc = (float(scale),) if scales is None else (float(scale), float(scales[0]), float(scales[1]))
     args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), int(max_pages),
-            int(page), _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base), float(scale), _ptr(q_out), _ptr(out),
-            ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
+            int(page), _ptr(seq_lens), _ptr(new_seq_lens), float(rope_base)) + sc + (
+        _ptr(q_out), _ptr(out), ctypes.byref(dims), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), s)
     return args, (out, q_out, new_seq_lens, q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, ws, dims)
 
 
@@ -649,6 +668,56 @@ def decode_append_rope_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_l
                                            stream, tiles, merge, per_cu)
     _check(lib().gqa_decode_append_rope_paged(*args))
     return keep[0], keep[1], keep[2]
+
+
+def decode_append_rope_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, scale: float,
+                           k_scale: float, v_scale: float, kv_offsets=None, max_seq_len: Optional[int] = None,
+                           q_out=None, new_seq_lens=None, out=None, out_dtype=None, chunk_tokens: int = 0,
+                           workspace=None, stream=None, tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """decode_append_rope on caches of one-byte E4M3 codes (uint8 or
+    float8_e4m3fn, plain or packed): append_rope_fp8 followed by decode_fp8
+    (gqa_decode_append_rope_fp8).  Returns (out, q_out, new_seq_lens)."""
+    args, keep = _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets,
+                                     max_seq_len, q_out, new_seq_lens, out, out_dtype, chunk_tokens, workspace, stream,
+                                     tiles, merge, per_cu, (k_scale, v_scale))
+    _check(lib().gqa_decode_append_rope_fp8(*args))
+    return keep[0], keep[1], keep[2]
+
+
+def decode_append_rope_paged_fp8(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
+                                 scale: float, k_scale: float, v_scale: float, max_seq_len: Optional[int] = None,
+                                 q_out=None, new_seq_lens=None, out=None, out_dtype=None, chunk_tokens: int = 0,
+                                 workspace=None, stream=None, tiles: int = 0, merge: str = "auto", per_cu: int = 0):
+    """decode_append_rope_paged on pools of one-byte E4M3 codes:
+    append_rope_paged_fp8 followed by decode_paged_fp8
+    (gqa_decode_append_rope_paged_fp8).  Returns (out, q_out, new_seq_lens)."""
+    args, keep = _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, scale,
+                                           max_seq_len, q_out, new_seq_lens, out, out_dtype, chunk_tokens, workspace,
+                                           stream, tiles, merge, per_cu, (k_scale, v_scale))
+    _check(lib().gqa_decode_append_rope_paged_fp8(*args))
+    return keep[0], keep[1], keep[2]
+
+
+def prepare_decode_append_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, scale: float,
+                              k_scale: float, v_scale: float, kv_offsets=None, max_seq_len=None, out_dtype=None,
+                              chunk_tokens: int = 0, stream=None, tiles: int = 0, merge: str = "auto",
+                              per_cu: int = 0):
+    """As prepare_decode_append, for gqa_decode_append_rope_fp8."""
+    args, keep = _decode_append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, scale, kv_offsets,
+                                     max_seq_len, None, None, None, out_dtype, chunk_tokens, None, stream, tiles, merge,
+                                     per_cu, (k_scale, v_scale))
+    return Prepared(lib().gqa_decode_append_rope_fp8, args, keep)
+
+
+def prepare_decode_append_paged_fp8(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
+                                    scale: float, k_scale: float, v_scale: float, max_seq_len=None, out_dtype=None,
+                                    chunk_tokens: int = 0, stream=None, tiles: int = 0, merge: str = "auto",
+                                    per_cu: int = 0):
+    """As prepare_decode_append_paged, for gqa_decode_append_rope_paged_fp8."""
+    args, keep = _decode_append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base, scale,
+                                           max_seq_len, None, None, None, out_dtype, chunk_tokens, None, stream, tiles,
+                                           merge, per_cu, (k_scale, v_scale))
+    return Prepared(lib().gqa_decode_append_rope_paged_fp8, args, keep)
 
 
 def prepare_decode_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
@@ -772,6 +841,24 @@ def prepare_append(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float
     same rows."""
     fn, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets, max_seq_len,
                                   q_out, new_seq_lens, stream, None)
+    return Prepared(fn, args, keep)
+
+
+def prepare_append_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base: float, k_scale: float,
+                       v_scale: float, kv_offsets=None, max_seq_len: Optional[int] = None, stream=None, q_out=None,
+                       new_seq_lens=None):
+    """As prepare_append, for append_rope_fp8."""
+    fn, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, seq_lens, rope_base, kv_offsets, max_seq_len,
+                                  q_out, new_seq_lens, stream, (k_scale, v_scale))
+    return Prepared(fn, args, keep)
+
+
+def prepare_append_paged_fp8(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base: float,
+                             k_scale: float, v_scale: float, max_seq_len: Optional[int] = None, stream=None,
+                             q_out=None, new_seq_lens=None):
+    """As prepare_append, for append_rope_paged_fp8."""
+    fn, args, keep = _append_paged_args(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, rope_base,
+                                        max_seq_len, q_out, new_seq_lens, stream, (k_scale, v_scale))
     return Prepared(fn, args, keep)
 
 

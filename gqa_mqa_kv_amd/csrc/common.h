@@ -65,6 +65,9 @@ struct Problem {
   void* q_out;                // [B][H_q][D] turned queries
   int32_t* new_seq_lens;      // [B] or nullptr
   double rope_base;
+  // The fused append into an E4M3 cache: the new key (value) is stored as the
+  // code of key / k_scale (value / v_scale).
+  float k_scale, v_scale;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -75,6 +78,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// The OCP E4M3 byte of y, from the format's definition: |y| >= 448
+// saturates; below 2^-6 the grid is m * 2^-9 (m = 0 .. 8, m = 8 being the
+// smallest normal); above, three mantissa bits rounded to nearest even, a
+// carry moving into the exponent; NaN is 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7Fu;                 // NaN
+  if (a >= 0x43e00000u) return sign | 0x7Eu;         // |y| >= 448 (and infinities)
+  if (a < 0x3c800000u) return sign | (uint32_t)rintf(__uint_as_float(a) * 512.f);   // |y| < 2^-6
+  const uint32_t e = (a >> 23) - 127u + 7u;          // biased E4M3 exponent, 1 .. 15
+  const uint32_t m = a & 0x7fffffu;
+  const uint32_t rem = m & 0xfffffu;
+  const uint32_t q = (m >> 20) + ((rem > 0x80000u || (rem == 0x80000u && ((m >> 20) & 1u))) ? 1u : 0u);
+  return sign | ((e << 3) + q);
 }
 
 // Rotary embedding ("Grouped-Query Attention (GQA) and Multi-Query

@@ -219,16 +219,17 @@ kernel_fn mfma_kernel(int hb, int, int tiles) {
   }
 }
 
-// The decode fused with the append (bf16 cache: plain, packed or paged): two
-// tiles per batch for one head block, one otherwise.
-template <int D, bool PAGED = false>
+// The decode fused with the append (cache of bf16 or E4M3 elements: plain,
+// packed or paged): up to two tiles per batch for one head block (a request
+// of four runs as two), one otherwise.
+template <int D, bool PAGED = false, bool KV8 = false>
 kernel_fn mfma_append_kernel(int hb, int tiles) {
   switch (hb) {
     case 1:
-      return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, PAGED, false, true>
-                        : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, PAGED, false, true>;
-    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1, PAGED, false, true>;
-    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, PAGED, false, true>;
+      return tiles >= 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, PAGED, KV8, true>
+                        : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, PAGED, KV8, true>;
+    case 2: return gqa::gqa_decode_mfma<D, 2, 1, 4, 1, PAGED, KV8, true>;
+    default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, PAGED, KV8, true>;
   }
 }
 
@@ -260,6 +261,10 @@ kernel_fn mfma_kernel_of(const gqa_dims* d, const KernelKind& kind, int waves, i
   const int G = d->num_q_heads / d->num_kv_heads;
   const int hb = (G + 15) / 16;
   const bool d128 = d->head_dim == 128;
+  if (kind.append && kind.paged && kind.kv8)
+    return d128 ? mfma_append_kernel<128, true, true>(hb, tiles) : mfma_append_kernel<64, true, true>(hb, tiles);
+  if (kind.append && kind.kv8)
+    return d128 ? mfma_append_kernel<128, false, true>(hb, tiles) : mfma_append_kernel<64, false, true>(hb, tiles);
   if (kind.append && kind.paged)
     return d128 ? mfma_append_kernel<128, true>(hb, tiles) : mfma_append_kernel<64, true>(hb, tiles);
   if (kind.append) return d128 ? mfma_append_kernel<128>(hb, tiles) : mfma_append_kernel<64>(hb, tiles);
@@ -364,6 +369,8 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   p.q_out = ca.q_out;
   p.new_seq_lens = ca.new_seq_lens;
   p.rope_base = ca.rope_base;
+  p.k_scale = ca.k_scale;
+  p.v_scale = ca.v_scale;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* args[] = {&p};
@@ -402,7 +409,6 @@ size_t gqa_decode_workspace_bytes(const gqa_dims* dims, int32_t num_layers) {
     k.kv8 = v & 1;
     k.paged = v & 2;
     k.append = v & 4;
-    if (k.append && k.kv8) continue;   // no such kernel
     most = std::max(most, make_plan(dims, num_layers, k).ws_bytes);
   }
   return most;
@@ -564,16 +570,21 @@ gqa_status append_launch(const void* q, const void* k_new, const void* v_new, vo
 namespace {
 // The fused append and decode on a plain or packed cache (block_table null)
 // or on a paged pool.
+// e4m3: the cache holds one-byte E4M3 codes of key / k_scale and
+// value / v_scale, and the new row is quantised so.
 gqa_status decode_append_launch(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                 const int64_t* kv_offsets, const int32_t* block_table, int32_t max_pages,
                                 int32_t page, const int32_t* seq_lens, int32_t* new_seq_lens, float rope_base,
                                 float scale, void* q_out, void* out, const gqa_dims* dims, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                size_t workspace_bytes, void* stream, bool e4m3 = false, float k_scale = 1.f,
+                                float v_scale = 1.f) {
   gqa_status st = check_dims(dims, 1);
   if (st != GQA_OK) return st;
   if (dims->dtype != GQA_DTYPE_BF16 || !use_mfma(dims)) return GQA_ERR_UNSUPPORTED;   // matrix-core kernel only
   if (dims->seq_len_hint != 0) return GQA_ERR_INVALID_ARG;   // the lengths grow inside the call
   if (!std::isfinite(rope_base) || !(rope_base > 0.f)) return GQA_ERR_INVALID_ARG;
+  if (e4m3 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) || !(v_scale > 0.f)))
+    return GQA_ERR_INVALID_ARG;
   if (dims->batch == 0) return GQA_OK;
   if (!k_new || !v_new || !q_out) return GQA_ERR_INVALID_ARG;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q_out, 16)) return GQA_ERR_INVALID_ARG;
@@ -586,6 +597,9 @@ gqa_status decode_append_launch(const void* q, const void* k_new, const void* v_
   cb.block_table = block_table;
   cb.max_pages = max_pages;
   cb.page = page;
+  cb.e4m3 = e4m3;
+  cb.k_scale = k_scale;
+  cb.v_scale = v_scale;
   const int64_t G = dims->num_q_heads / dims->num_kv_heads;
   if (G > 16 && new_seq_lens) {
     // Two head blocks: there the fused kernel needs more registers than a
@@ -599,7 +613,7 @@ gqa_status decode_append_launch(const void* q, const void* k_new, const void* v_
                       &plan, &nothing);
     if (st != GQA_OK) return st;
     st = append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, block_table, max_pages, page, seq_lens,
-                       new_seq_lens, rope_base, q_out, dims, stream);
+                       new_seq_lens, rope_base, q_out, dims, stream, e4m3, k_scale, v_scale);
     if (st != GQA_OK) return st;
     return launch(1, q_out, k_cache, v_cache, cb, new_seq_lens, scale, out, dims, workspace, workspace_bytes, stream);
   }
@@ -631,6 +645,30 @@ gqa_status gqa_decode_append_rope_paged(const void* q, const void* k_new, const 
   if (!block_table || !aligned(block_table, 4)) return GQA_ERR_INVALID_ARG;
   return decode_append_launch(q, k_new, v_new, k_pool, v_pool, nullptr, block_table, max_pages, page_size, seq_lens,
                               new_seq_lens, rope_base, scale, q_out, out, dims, workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_append_rope_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int64_t* kv_offsets, const int32_t* seq_lens,
+                                      int32_t* new_seq_lens, float rope_base, float scale, float k_scale,
+                                      float v_scale, void* q_out, void* out, const gqa_dims* dims, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return decode_append_launch(q, k_new, v_new, k_cache, v_cache, kv_offsets, nullptr, 0, 0, seq_lens, new_seq_lens,
+                              rope_base, scale, q_out, out, dims, workspace, workspace_bytes, stream, true, k_scale,
+                              v_scale);
+}
+
+gqa_status gqa_decode_append_rope_paged_fp8(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                            void* v_pool, const int32_t* block_table, int32_t max_pages,
+                                            int32_t page_size, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                            float rope_base, float scale, float k_scale, float v_scale, void* q_out,
+                                            void* out, const gqa_dims* dims, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (page_size <= 0 || page_size % 16 != 0 || max_pages <= 0) return GQA_ERR_INVALID_ARG;
+  if (dims && (int64_t)max_pages * page_size < dims->max_seq_len) return GQA_ERR_INVALID_ARG;
+  if (!block_table || !aligned(block_table, 4)) return GQA_ERR_INVALID_ARG;
+  return decode_append_launch(q, k_new, v_new, k_pool, v_pool, nullptr, block_table, max_pages, page_size, seq_lens,
+                              new_seq_lens, rope_base, scale, q_out, out, dims, workspace, workspace_bytes, stream,
+                              true, k_scale, v_scale);
 }
 
 gqa_status gqa_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -204,17 +204,19 @@ __device__ __forceinline__ u32x2 v_operand(const Tile16K8<D>& T, int r) {
 // KV8: cache elements are one-byte E4M3 values (bf16 queries).  Tiles move
 // as bytes and are widened to bf16, exactly, just before the products; the
 // key scale is folded into p.scale_log2 and the value scale into p.out_mul.
-// APPEND (bf16 cache: plain, packed or paged): the decode step fused with
-// the append of each sequence's new token.  The token's position m comes
-// from seq_lens[b]; the queries are turned by the rotary embedding in
-// registers when a piece becomes current (and written to q_out by the
-// unit's first piece), and the attention covers the new token: the piece
-// that ends a grown unit turns the new key, its tile holding row m takes
-// the turned key and the value instead of the cache's row, and wavefront 0
-// writes them to cache row m.
+// APPEND (cache of bf16 or E4M3 elements: plain, packed or paged): the
+// decode step fused with the append of each sequence's new token.  The
+// token's position m comes from seq_lens[b]; the queries are turned by the
+// rotary embedding in registers when a piece becomes current (and written
+// to q_out by the unit's first piece), and the attention covers the new
+// token: the piece that ends a grown unit turns the new key, its tile
+// holding row m takes the turned key and the value instead of the cache's
+// row, and wavefront 0 writes them to cache row m.  With KV8 the new row is
+// what the quantising append stores: the key turned in fp32 and divided by
+// k_scale, the value divided by v_scale, each encoded to E4M3 bytes; the
+// tile takes those bytes before it is widened.
 template <int D, int HB, int HG, int NW, int TPW, bool PAGED, bool KV8, bool APPEND = false>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
-  static_assert(!APPEND || !KV8, "the fused append takes a bf16 cache");
   static_assert(NW % HG == 0, "head groups must divide the wavefronts");
   constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
   constexpr int NL = NW / HG;             // tile lanes
@@ -232,7 +234,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   __shared__ int sm_flag;
   __shared__ int32_t sm_M[APPEND ? kMaxBatch : 1];        // APPEND: new token positions
   __shared__ float sm_cs[APPEND ? NW : 1][2][2][D / 2];  // APPEND: each wavefront's cosines and sines, two tables
-  // APPEND: each wavefront's turned new key and new value, one row each per table
+  // APPEND: each wavefront's turned new key and new value, one row each per
+  // table (bf16 elements, or E4M3 bytes in the first half of each row)
   __shared__ __align__(16) uint16_t sm_kvn[APPEND ? NW : 1][2][2][D];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -491,24 +494,43 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   };
   // APPEND: the tile that holds the new token (row m of the unit, in
   // registers from the cache's stale row) takes the turned key and the value
-  // from LDS in the lanes holding that row (the tail's clamped rows too).
-  auto compute_tile = [&](const auto& T, const Ctx& c, int t0, auto may_hold_new) __attribute__((always_inline)) {
+  // from LDS in the lanes holding that row (the tail's clamped rows too); an
+  // E4M3 tile takes the new row's bytes before it is widened.
+  auto compute_tile = [&](const tile_t& T, const Ctx& c, int t0, auto may_hold_new) __attribute__((always_inline)) {
     if constexpr (APPEND && decltype(may_hold_new)::value) {
       // one product either way: only the substitution is conditional
-      Tile16<D> U = T;
+      tile_t U = T;
       if (c.mnew >= t0 && c.mnew < t0 + TILE) {   // wave-uniform
         const int mn = c.mnew, last = c.c1 - 1;
-        const uint16_t* kn = &sm_kvn[wave][c.tab][0][0];
-        const uint16_t* vn = &sm_kvn[wave][c.tab][1][0];
-        if (min(t0 + m16, last) == mn) {
+        if constexpr (KV8) {
+          typedef typename std::remove_reference<decltype(U.v[0])>::type vraw_t;
+          const uint8_t* kn = reinterpret_cast<const uint8_t*>(&sm_kvn[wave][c.tab][0][0]);
+          const uint8_t* vn = reinterpret_cast<const uint8_t*>(&sm_kvn[wave][c.tab][1][0]);
+          if (min(t0 + m16, last) == mn) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) U.k[s] = *reinterpret_cast<const u32x4*>(kn + 32 * s + 8 * q4);
+            for (int h = 0; h < D / 64; ++h) U.k[h] = *reinterpret_cast<const u32x4*>(kn + 64 * h + 16 * q4);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (min(t0 + 4 * q4 + i, last) == mn) U.v[i] = *reinterpret_cast<const vraw_t*>(vn + VW * m16);
+        } else {
+          const uint16_t* kn = &sm_kvn[wave][c.tab][0][0];
+          const uint16_t* vn = &sm_kvn[wave][c.tab][1][0];
+          if (min(t0 + m16, last) == mn) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) U.k[s] = *reinterpret_cast<const u32x4*>(kn + 32 * s + 8 * q4);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (min(t0 + 4 * q4 + i, last) == mn) U.v[i] = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (min(t0 + 4 * q4 + i, last) == mn) U.v[i] = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
       }
-      compute_core(U, t0, c.c1);
+      if constexpr (KV8)
+        compute_core(widen(U), t0, c.c1);
+      else
+        compute_core(U, t0, c.c1);
+    } else if constexpr (KV8) {
+      compute_core(widen(T), t0, c.c1);
     } else {
       compute_core(T, t0, c.c1);
     }
@@ -516,9 +538,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   // APPEND: the queries (and the new key) of a piece are turned when the
   // piece becomes current: after the prologue's loads, or after the previous
   // piece's end (its tiles and accumulators are then free, only the next
-  // batch is in flight), with the angle table the piece's opening filled; a
-  // lane's columns 32s + 8q4 .. +7 are pairs 16s + 4q4 .. +3.  The unit's
-  // first piece writes the turned queries of its heads to q_out.
+  // batch is in flight), with the angle table the piece's opening filled.
+  // Score step s of a lane covers the 8 columns qcol(s) .. +7 (see load_q),
+  // that is the 4 pairs qcol(s)/2 .. +3.  The unit's first piece writes the
+  // turned queries of its heads to q_out.
+  auto qcol = [&](int s) __attribute__((always_inline)) {
+    return KV8 ? 64 * (s >> 1) + 16 * q4 + 8 * (s & 1) : 32 * s + 8 * q4;
+  };
   auto turn_words = [&](const u32x4& w, const float (&cc)[4], const float (&ss)[4]) __attribute__((always_inline)) {
     u32x4 r;
 #pragma unroll
@@ -529,15 +555,30 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     }
     return r;
   };
+  // KV8: the E4M3 bytes of the key pairs in w turned in fp32 and divided by
+  // k_scale (the quantising append's arithmetic), 8 bytes as two words.
+  auto turn_encode_words = [&](const u32x4& w, const float (&cc)[4], const float (&ss)[4])
+                               __attribute__((always_inline)) {
+    uint32_t b[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float y0, y1;
+      rope_turn(bf16_to_f32(w[k] & 0xffffu), bf16_to_f32(w[k] >> 16), cc[k], ss[k], y0, y1);
+      b[2 * k] = e4m3_encode(y0 / p.k_scale);
+      b[2 * k + 1] = e4m3_encode(y1 / p.k_scale);
+    }
+    return u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+  };
   auto turn_piece = [&](Ctx& c) __attribute__((always_inline)) {
     if constexpr (APPEND) {
       const float* tab = &sm_cs[wave][c.tab][0][0];
-      // the cosines and sines of the lane's pairs 16s + 4q4 .. +3
+      // the cosines and sines of the lane's pairs of score step s
       auto angles = [&](int s, float (&cc)[4], float (&ss)[4]) __attribute__((always_inline)) {
+        const int j0 = qcol(s) / 2;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          cc[k] = tab[16 * s + 4 * q4 + k];
-          ss[k] = tab[D / 2 + 16 * s + 4 * q4 + k];
+          cc[k] = tab[j0 + k];
+          ss[k] = tab[D / 2 + j0 + k];
         }
       };
 #pragma unroll
@@ -560,33 +601,73 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + nrow;
         u32x4 knew[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) knew[s] = *reinterpret_cast<const u32x4*>(kn + 32 * s + 8 * q4);
+        for (int s = 0; s < KS; ++s) knew[s] = *reinterpret_cast<const u32x4*>(kn + qcol(s));
         const vrow_t vnew = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
+        // cache row m: the unit's row m, or row m % page of the page the
+        // sequence's table names for it (within the pool shifted to head g)
+        int64_t crow = c.mnew;
+        if constexpr (PAGED) crow = (int64_t)c.pages[c.mnew / p.page] * p.H_kv * p.page + c.mnew % p.page;
+        if constexpr (KV8) {
+          u32x2 kcode[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          float cc[4], ss[4];
-          angles(s, cc, ss);
-          knew[s] = turn_words(knew[s], cc, ss);
-        }
-        uint16_t* ks = &sm_kvn[wave][c.tab][0][0];
-        uint16_t* vs = &sm_kvn[wave][c.tab][1][0];
-        if (m16 == 0) {
+          for (int s = 0; s < KS; ++s) {
+            float cc[4], ss[4];
+            angles(s, cc, ss);
+            kcode[s] = turn_encode_words(knew[s], cc, ss);
+          }
+          // the value's bytes at columns VW*m16 .. +VW-1
+          uint32_t vb[VW];
 #pragma unroll
-          for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(ks + 32 * s + 8 * q4) = knew[s];
-        }
-        if (q4 == 0) *reinterpret_cast<vrow_t*>(vs + VW * m16) = vnew;
-        if (wave == 0) {
-          // cache row m: the unit's row m, or row m % page of the page the
-          // sequence's table names for it (within the pool shifted to head g)
-          int64_t crow = c.mnew;
-          if constexpr (PAGED) crow = (int64_t)c.pages[c.mnew / p.page] * p.H_kv * p.page + c.mnew % p.page;
-          uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + crow * D;
-          uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + crow * D;
+          for (int e = 0; e < VW; ++e) {
+            const uint32_t wd = vnew[e >> 1];
+            vb[e] = e4m3_encode(bf16_to_f32((e & 1) ? (wd >> 16) : (wd & 0xffffu)) / p.v_scale);
+          }
+          typedef typename std::conditional<D == 128, u32x2, uint32_t>::type vcode_t;
+          vcode_t vcode;
+          if constexpr (D == 128)
+            vcode = u32x2{vb[0] | (vb[1] << 8) | (vb[2] << 16) | (vb[3] << 24),
+                          vb[4] | (vb[5] << 8) | (vb[6] << 16) | (vb[7] << 24)};
+          else
+            vcode = vb[0] | (vb[1] << 8) | (vb[2] << 16) | (vb[3] << 24);
+          uint8_t* ks = reinterpret_cast<uint8_t*>(&sm_kvn[wave][c.tab][0][0]);
+          uint8_t* vs = reinterpret_cast<uint8_t*>(&sm_kvn[wave][c.tab][1][0]);
           if (m16 == 0) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(kc + 32 * s + 8 * q4) = knew[s];
+            for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x2*>(ks + qcol(s)) = kcode[s];
           }
-          if (q4 == 0) *reinterpret_cast<vrow_t*>(vc + VW * m16) = vnew;
+          if (q4 == 0) *reinterpret_cast<vcode_t*>(vs + VW * m16) = vcode;
+          if (wave == 0) {
+            uint8_t* kc = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(c.kg)) + crow * D;
+            uint8_t* vc = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(c.vg)) + crow * D;
+            if (m16 == 0) {
+#pragma unroll
+              for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x2*>(kc + qcol(s)) = kcode[s];
+            }
+            if (q4 == 0) *reinterpret_cast<vcode_t*>(vc + VW * m16) = vcode;
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            float cc[4], ss[4];
+            angles(s, cc, ss);
+            knew[s] = turn_words(knew[s], cc, ss);
+          }
+          uint16_t* ks = &sm_kvn[wave][c.tab][0][0];
+          uint16_t* vs = &sm_kvn[wave][c.tab][1][0];
+          if (m16 == 0) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(ks + qcol(s)) = knew[s];
+          }
+          if (q4 == 0) *reinterpret_cast<vrow_t*>(vs + VW * m16) = vnew;
+          if (wave == 0) {
+            uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + crow * D;
+            uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + crow * D;
+            if (m16 == 0) {
+#pragma unroll
+              for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(kc + qcol(s)) = knew[s];
+            }
+            if (q4 == 0) *reinterpret_cast<vrow_t*>(vc + VW * m16) = vnew;
+          }
         }
       }
       if (c.c0 == 0 && tl == 0) {
@@ -596,7 +677,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
           if (h >= G) continue;
           uint16_t* qo = reinterpret_cast<uint16_t*>(p.q_out) + (c.orow + h) * D;
 #pragma unroll
-          for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(qo + 32 * s + 8 * q4) = qf[hb][s];
+          for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(qo + qcol(s)) = qf[hb][s];
         }
       }
     }
@@ -617,12 +698,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
                            auto may_hold_new) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      if (j + NL * u < c.ntiles) {
-        if constexpr (KV8)
-          compute_tile(widen(T[u]), c, c.c0 + (j + NL * u) * TILE, may_hold_new);
-        else
-          compute_tile(T[u], c, c.c0 + (j + NL * u) * TILE, may_hold_new);
-      }
+      if (j + NL * u < c.ntiles) compute_tile(T[u], c, c.c0 + (j + NL * u) * TILE, may_hold_new);
     }
   };
 

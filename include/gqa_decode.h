@@ -350,6 +350,40 @@ gqa_status gqa_decode_append_rope_paged(const void* q, const void* k_new, const 
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_append_rope_fp8 followed by gqa_decode_fp8, and gqa_append_rope_paged_fp8
+ * followed by gqa_decode_paged_fp8: the fused step of gqa_decode_append_rope
+ * and gqa_decode_append_rope_paged on caches of one-byte OCP E4M3 elements
+ * ("Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): ...",
+ * section 4, "Rotary Position Embeddings (RoPE) Interaction", with the
+ * bytes-per-element factor of section 1 halved).  The new key is turned in
+ * fp32 and stored as the code of key / k_scale, the value as the code of
+ * value / v_scale (nearest E4M3 value, ties to even, saturating at +-448),
+ * exactly as the quantising append stores them; the attention reads every
+ * element, the new ones included, as k_scale (v_scale) times its E4M3 value,
+ * as gqa_decode_fp8 does.  Results (out, q_out, the cache bytes, the lengths)
+ * equal the two calls in sequence, bit for bit.
+ *   q, k_new, v_new, q_out : bf16 (dims->dtype), 16-byte aligned
+ *   k_cache, v_cache / k_pool, v_pool : E4M3 bytes in the layouts of
+ *                  gqa_decode_fp8 / gqa_decode_paged_fp8, 16-byte aligned
+ *   k_scale, v_scale : finite and > 0 (GQA_ERR_INVALID_ARG otherwise)
+ * One launch up to G = 16 query heads per KV head, or with new_seq_lens
+ * NULL; else the append kernel and the decode.  Every other argument rule
+ * and error as for gqa_decode_append_rope (dense or packed caches) and
+ * gqa_decode_append_rope_paged (paged pools).
+ */
+gqa_status gqa_decode_append_rope_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int64_t* kv_offsets, const int32_t* seq_lens,
+                                      int32_t* new_seq_lens, float rope_base, float scale, float k_scale,
+                                      float v_scale, void* q_out, void* out, const gqa_dims* dims, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+gqa_status gqa_decode_append_rope_paged_fp8(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                            void* v_pool, const int32_t* block_table, int32_t max_pages,
+                                            int32_t page_size, const int32_t* seq_lens, int32_t* new_seq_lens,
+                                            float rope_base, float scale, float k_scale, float v_scale, void* q_out,
+                                            void* out, const gqa_dims* dims, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
  * The same step for a cache held in pages of a pool (the layout of
  * gqa_decode_paged): the rotated key and the value of sequence b's new token
  * go to row m % page_size of page block_table[b][m / page_size] of each KV

@@ -489,3 +489,29 @@ def test_two_kernel_append_path_checks_everything_before_enqueueing():
                                                                        nb, None)
         assert paged() == WORKSPACE
 
+
+
+def test_decode_append_rope_fp8_validation():
+    """The fused append into E4M3 caches checks what the bf16 fused call
+    checks, plus positive finite scales; its paged form the page rules."""
+    lib = gqa.lib()
+    d = dims(T_max=1024)
+    Q, KN, VN, KC, VC, SL, NL, QO, OUT = (FAKE + 0x1000 * i for i in range(9))
+    call = lambda dd=d, ks=0.5, vs=0.25, qo=QO, base=10000.0: lib.gqa_decode_append_rope_fp8(
+        Q, KN, VN, KC, VC, None, SL, NL, base, 0.125, ks, vs, qo, OUT, ctypes.byref(dd), None, 0, None)
+    assert call() == WORKSPACE                                          # valid: only the workspace is missing
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(ks=bad) == INVALID and call(vs=bad) == INVALID
+    assert call(base=0.0) == INVALID
+    assert call(qo=Q) == INVALID
+    assert call(dims(T_max=1024, dtype=torch.float32)) == UNSUPPORTED
+    assert call(dims(T_max=1024, seq_len_hint=10)) == INVALID
+    paged = lambda pg=16, mp=64, bt=FAKE, ks=0.5: lib.gqa_decode_append_rope_paged_fp8(
+        Q, KN, VN, KC, VC, bt, mp, pg, SL, NL, 10000.0, 0.125, ks, 0.25, QO, OUT, ctypes.byref(d), None, 0, None)
+    assert paged() == WORKSPACE
+    assert paged(pg=24) == INVALID and paged(mp=63) == INVALID and paged(bt=None) == INVALID
+    assert paged(ks=-1.0) == INVALID
+    # G > 16 with lengths: the append kernel and the decode, every argument checked first
+    d32 = dims(H_q=32, H_kv=1, T_max=4096)
+    assert lib.gqa_decode_append_rope_fp8(Q, KN, VN, KC, VC, None, SL, NL, 10000.0, 0.125, 0.5, 0.25, QO, OUT,
+                                          ctypes.byref(d32), None, 0, None) == WORKSPACE

@@ -593,3 +593,148 @@ def test_prepared_paged_calls_repeat_the_direct_ones():
     assert torch.equal(q2, qo)
     assert torch.equal(kc.view(torch.int16), ka.view(torch.int16))
     assert torch.equal(vc.view(torch.int16), va.view(torch.int16))
+
+
+
+# ------------------------------------------------ fused append into E4M3 caches --
+def e4m3_case(B, H_q, H_kv, d, T, lens, seed, packed_caps=None):
+    """bf16 queries and new rows, and an E4M3 cache (codes drawn from N(0, 1)
+    keys and values with per-array scales) of T rows per (sequence, KV head),
+    or packed with the capacities ``packed_caps``."""
+    x = make(B, H_q, H_kv, d, T, torch.bfloat16, seed, lens)
+    if packed_caps is not None:
+        offs = torch.tensor([0] + list(np.cumsum(packed_caps)), dtype=torch.int64)
+        g = torch.Generator().manual_seed(seed + 1)
+        rows = int(offs[-1]) * H_kv
+        x["k"] = torch.randn(rows, d, generator=g).to(torch.bfloat16)
+        x["v"] = torch.randn(rows, d, generator=g).to(torch.bfloat16)
+        x["kv_offsets"] = offs
+    k8, ks = workloads.quantize_e4m3(x["k"])
+    v8, vs = workloads.quantize_e4m3(x["v"])
+    x.update(k=k8, v=v8, k_scale=ks, v_scale=vs)
+    return x
+
+
+def fused_vs_pipeline_fp8(x, base, scale, lens_out=True, paged=None, **kw):
+    """gqa_decode_append_rope_fp8 (or its paged form) against
+    gqa_append_rope_fp8 + gqa_decode_fp8 (or the paged pair) on copies of the
+    same cache: outputs, turned queries, cache bytes and lengths bitwise.
+    Returns the pipeline's (out, k cache, v cache, lengths)."""
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    ks, vs = x["k_scale"], x["v_scale"]
+    if paged:
+        page, table = paged
+        kpool, vpool = xd["k"], xd["v"]
+        td = table.to(DEV)
+        T = kw.pop("max_seq_len")
+        ka, va, kb, vb = kpool.clone(), vpool.clone(), kpool.clone(), vpool.clone()
+        qo, nl = gqa.append_rope_paged_fp8(xd["q"], xd["k_new"], xd["v_new"], ka, va, td, xd["seq_lens"], base, ks, vs,
+                                           max_seq_len=T)
+        ref = gqa.decode_paged_fp8(qo, ka, va, td, nl, scale, ks, vs, out_dtype=torch.float32, max_seq_len=T, **kw)
+        out, qf, nlf = gqa.decode_append_rope_paged_fp8(xd["q"], xd["k_new"], xd["v_new"], kb, vb, td,
+                                                        xd["seq_lens"], base, scale, ks, vs, max_seq_len=T,
+                                                        out_dtype=torch.float32,
+                                                        new_seq_lens=None if lens_out else False, **kw)
+    else:
+        ext = dict(kv_offsets=xd["kv_offsets"], max_seq_len=kw.pop("max_seq_len")) if "kv_offsets" in x else {}
+        ka, va, kb, vb = xd["k"].clone(), xd["v"].clone(), xd["k"].clone(), xd["v"].clone()
+        qo, nl = gqa.append_rope_fp8(xd["q"], xd["k_new"], xd["v_new"], ka, va, xd["seq_lens"], base, ks, vs, **ext)
+        if ext:
+            H_kv = x["k_new"].shape[1]
+            ref = gqa.decode_layers_fp8(qo[None], ka, va, nl, scale, ks, vs, kv_offsets=ext["kv_offsets"],
+                                        max_seq_len=ext["max_seq_len"], num_kv_heads=H_kv, out_dtype=torch.float32,
+                                        **kw)[0]
+        else:
+            ref = gqa.decode_fp8(qo, ka, va, nl, scale, ks, vs, out_dtype=torch.float32, **kw)
+        out, qf, nlf = gqa.decode_append_rope_fp8(xd["q"], xd["k_new"], xd["v_new"], kb, vb, xd["seq_lens"], base,
+                                                  scale, ks, vs, out_dtype=torch.float32,
+                                                  new_seq_lens=None if lens_out else False, **ext, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(qf, qo), "turned queries differ"
+    assert (nlf is None) if not lens_out else torch.equal(nlf, nl), "new lengths differ"
+    assert torch.equal(kb, ka) and torch.equal(vb, va), "cache bytes differ"
+    assert torch.equal(out, ref), "outputs differ: max %.3e" % float((out - ref).abs().max())
+    return ref, ka, va, nl, qo
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d_T%d" % c[:5])
+@pytest.mark.parametrize("span,merge,tiles,lens_out", [(0, "auto", 0, True), (0, "auto", 0, False),
+                                                       (64, "fused", 1, False), (64, "kernel", 2, True),
+                                                       (128, "auto", 4, False)])
+def test_decode_append_rope_fp8_equals_the_two_calls(case, span, merge, tiles, lens_out):
+    """gqa_decode_append_rope_fp8 against gqa_append_rope_fp8 followed by
+    gqa_decode_fp8 (plain E4M3 cache): every output bitwise, with the
+    planner's split and forced spans that cut units into pieces, both merges
+    and one, two or four tiles per batch, with and without lengths written;
+    and the attention against the oracle on the updated cache."""
+    B, H_q, H_kv, d, T, lens = case
+    x = e4m3_case(B, H_q, H_kv, d, T, lens, 151 + B + d)
+    note("fused append e4m3", case, span, merge, tiles, lens_out)
+    scale = d ** -0.5
+    ref, ka, va, nl, qo = fused_vs_pipeline_fp8(x, 10000.0, scale, lens_out=lens_out, chunk_tokens=span, merge=merge,
+                                                tiles=tiles)
+    want = oracle.default().decode_fp8(qo.cpu(), ka.cpu(), va.cpu(), nl.cpu(), scale, x["k_scale"], x["v_scale"])
+    assert float(np.abs(ref.double().cpu().numpy() - want).max()) <= 2e-3
+
+
+def test_decode_append_rope_fp8_packed_cache():
+    """The fused E4M3 step on the packed layout (capacities of their own, one
+    full, one empty), against the two calls."""
+    caps, lens = [40, 0, 17, 300], [12, 0, 17, 299]
+    x = e4m3_case(4, 32, 8, 128, 1, lens, 161, packed_caps=caps)
+    for span in (0, 64):
+        fused_vs_pipeline_fp8(x, 500000.0, 128 ** -0.5, chunk_tokens=span, max_seq_len=max(caps))
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d_T%d" % c[:5])
+@pytest.mark.parametrize("page", [16, 48])
+@pytest.mark.parametrize("span,merge,lens_out", [(0, "auto", True), (64, "fused", False), (64, "kernel", True)])
+def test_decode_append_rope_paged_fp8_equals_the_two_calls(case, page, span, merge, lens_out):
+    """gqa_decode_append_rope_paged_fp8 against gqa_append_rope_paged_fp8
+    followed by gqa_decode_paged_fp8 on copies of one shuffled E4M3 pool:
+    outputs, turned queries, pool bytes (NaN codes in unused rows included)
+    and lengths bitwise."""
+    B, H_q, H_kv, d, T, lens = case
+    x = e4m3_case(B, H_q, H_kv, d, T, lens, 171 + B + d + page)
+    alloc = dict(x, seq_lens=(x["seq_lens"].clamp(min=0) + 1).clamp(max=T))
+    kp, vp, table = workloads.to_pages(alloc, page, seed=13 + page)
+    xp = dict(x, k=kp, v=vp)
+    note("fused paged append e4m3", case, page, span, merge, lens_out)
+    fused_vs_pipeline_fp8(xp, 10000.0, d ** -0.5, lens_out=lens_out, paged=(page, table), chunk_tokens=span,
+                          merge=merge, max_seq_len=T)
+
+
+def test_decode_append_rope_fp8_matches_oracle():
+    """The fused E4M3 step against the oracle directly: its rotation of q and
+    of the new key, its E4M3 encoder for the new row (the key turned in fp32
+    on the GPU, so a code may sit one step off where the fp64 value lies
+    within fp32 rounding of a code boundary: the new row is compared code by
+    code within that slack), and its attention over the updated cache."""
+    B, H_q, H_kv, d, T = 3, 32, 8, 128, 500
+    lens = [0, 250, 499]
+    x = e4m3_case(B, H_q, H_kv, d, T, lens, 181)
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    kc, vc = xd["k"].clone(), xd["v"].clone()
+    out, q_rot, nl = gqa.decode_append_rope_fp8(xd["q"], xd["k_new"], xd["v_new"], kc, vc, xd["seq_lens"], 10000.0,
+                                                d ** -0.5, x["k_scale"], x["v_scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    orc = oracle.default()
+    m = torch.tensor(lens)
+    ref_q = orc.rope(x["q"].double(), m.view(B, 1), 10000.0)
+    assert rot_err_ok(q_rot, ref_q, torch.bfloat16)
+    k_rot = orc.rope(x["k_new"].double(), m.view(B, 1), 10000.0)
+    ks, vs = float(np.float32(x["k_scale"])), float(np.float32(x["v_scale"]))
+    kn, vn = kc.cpu(), vc.cpu()
+    for b in range(B):
+        xk = x["k_new"][b].double().numpy()
+        pair_mag = np.abs(xk.reshape(H_kv, d // 2, 2)).sum(-1).repeat(2, -1)   # |x0| + |x1| of each element's pair
+        yk = k_rot[b] / ks
+        assert codes_within(kn[b, :, lens[b]], yk, 4 * 2.0 ** -23 * pair_mag / ks + 2.0 ** -22 * np.abs(yk))
+        yv = x["v_new"][b].double().numpy() / vs
+        assert codes_within(vn[b, :, lens[b]], yv, 2.0 ** -22 * np.abs(yv))
+    keep = torch.ones(kn.shape[:3], dtype=torch.bool)
+    for b in range(B):
+        keep[b, :, lens[b]] = False
+    assert torch.equal(kn[keep], x["k"][keep]) and torch.equal(vn[keep], x["v"][keep])
+    ref = orc.decode_fp8(q_rot.cpu(), kn, vn, nl.cpu(), d ** -0.5, x["k_scale"], x["v_scale"])
+    assert float(np.abs(out.double().cpu().numpy() - ref).max()) <= 2e-3
