@@ -56,8 +56,9 @@ struct Problem {
   const int32_t* block_table; // paged cache: [B][max_pages] page ids, or nullptr
   int32_t max_pages, page;    // paged cache: table entries per sequence, tokens per page (a multiple of 16)
   float out_mul;              // factor of every normalised output (the value scale of an E4M3 cache, else 1)
-  // Decode with the append of the new token (one layer, plain or packed bf16
-  // cache): sequence b's token at position m = max(seq_lens[b], 0) is turned
+  // Decode with the append of the new token (one layer; plain, packed or
+  // paged cache of bf16 or E4M3 elements): sequence b's token at position
+  // m = max(seq_lens[b], 0) is turned
   // by the rotary embedding and written to cache row m (when m < capacity),
   // and the attention covers it.
   const void* k_new;          // [B][H_kv][D] keys before the rotation
