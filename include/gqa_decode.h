@@ -149,15 +149,20 @@ typedef struct gqa_dims {
 
 /*
  * Bytes of workspace a call with these dims and `num_layers` layers needs
- * (0 when no partial state can arise).  Depends on its arguments and on the
- * CU count of the current device (taken as 256 when no device answers);
+ * (0 when no partial state can arise): the most that any entry point taking
+ * these dims (plain, packed, paged, E4M3, fused append) can need, since their
+ * kernels differ in tile default and occupancy.  Depends on its arguments,
+ * on the CU count of the current device (taken as 256 when no device
+ * answers) and, with workgroups_per_cu > 1, on the kernels' occupancy;
  * touches no device memory.  Returns 0 for invalid dims as well; the decode
  * call then reports the error.
  */
 size_t gqa_decode_workspace_bytes(const gqa_dims* dims, int32_t num_layers);
 
 /*
- * The work split planned for these dims.  Matrix-core path: *chunk_tokens is
+ * The work split planned for these dims (as gqa_decode and gqa_decode_layers
+ * plan it; with workgroups_per_cu > 1 the other entry points may plan fewer
+ * workgroups, by their kernels' occupancy).  Matrix-core path: *chunk_tokens is
  * the forced tokens per workgroup (0 when the valid tokens are shared evenly
  * at run time) and *num_chunks the number of workgroups.  Vector path: tokens
  * per chunk and the chunk count of the longest possible sequence.  Returns
