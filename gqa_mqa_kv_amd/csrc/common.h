@@ -199,10 +199,15 @@ __global__ __launch_bounds__(256) void gqa_merge_chunks(Problem p) {
 // units per layer; with P the exclusive prefix sums of n_b, the stream
 // position of token t of unit (l, b, g) is
 //     l * H_kv * P[B]  +  H_kv * P[b]  +  g * n_b  +  t.
-// Workgroup w owns positions [w * span, (w + 1) * span); every unit that lies
-// inside one span is finished by that workgroup, and only the first and the
-// last unit piece of a span can be partial (state slots 2w and 2w + 1; a
-// piece covering a whole span uses slot 2w).
+// Each layer's positions are cut into spans of `span` positions, numbered
+// v = l * groups + w ("virtual spans"): span v covers
+//     [l * per_layer + w * span, min(l * per_layer + (w + 1) * span, (l + 1) * per_layer)),
+// and workgroup w takes spans w, groups + w, 2 groups + w, ... in turn, one
+// layer after the other, so that at any time the workgroups stream the same
+// layer.  Every unit that lies inside one span is finished there; only the
+// first and the last unit piece of a span can be partial (state slots 2v and
+// 2v + 1; a piece covering a whole span uses slot 2v).  A unit never crosses
+// a layer, so the spans holding its pieces are consecutive.
 
 // Exclusive prefix sums of the units' stream lengths into sm_P[0..B] (all
 // threads of the workgroup take part; B <= kMaxBatch).  A unit's stream
@@ -268,17 +273,34 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 struct TokenSpace {
   int64_t per_layer;   // H_kv * P[B]
   int64_t total;       // L * per_layer
-  int64_t span;        // positions per workgroup, a multiple of 16
+  int64_t span;        // positions per span of a layer, a multiple of 16
+  int64_t groups;      // spans per layer (the workgroups launched)
+
+  // first position of span v, one past its last, and the span holding
+  // position x
+  __device__ __forceinline__ int64_t start(int64_t v) const {
+    const int64_t l = v / groups;
+    return l * per_layer + (v - l * groups) * span;
+  }
+  __device__ __forceinline__ int64_t end(int64_t v) const {
+    const int64_t l = v / groups;
+    return min(start(v) + span, (l + 1) * per_layer);
+  }
+  __device__ __forceinline__ int64_t span_of(int64_t x) const {
+    const int64_t l = x / per_layer;
+    return l * groups + (x - l * per_layer) / span;
+  }
 };
 
 __device__ __forceinline__ TokenSpace token_space(const Problem& p, const int32_t* sm_P) {
   TokenSpace ts;
   ts.per_layer = (int64_t)p.H_kv * uniform(sm_P[p.B]);
   ts.total = ts.per_layer * p.L;
+  ts.groups = p.groups;
   if (p.span > 0) {
     ts.span = p.span;
   } else {
-    const int64_t s = (ts.total + p.groups - 1) / p.groups;
+    const int64_t s = (ts.per_layer + p.groups - 1) / p.groups;
     ts.span = (s + 15) / 16 * 16;
     if (ts.span == 0) ts.span = 16;
   }
@@ -544,35 +566,23 @@ __device__ __forceinline__ void fused_merge(const Problem& p, int64_t w0, int64_
   if (threadIdx.x == 0) __hip_atomic_store(p.ws_cnt + w0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge descriptor written by decode workgroup m for the merge kernel:
+// Merge descriptor of span m for the merge kernel, written by the decode
+// workgroup that streams span m (threads 0..3):
 //   {w0, w_last, output row of the unit's first head, first piece slot}
-// when m's span starts inside a unit that began in an earlier span (w0 < m is
-// the workgroup holding the unit's first token, w_last the one holding its
-// last), else w0 = -1.  The workgroups w0+1 .. w_last of such a unit share
-// its merge.
-template <bool PAGED>
-__device__ __forceinline__ void write_merge_desc(const Problem& p, const int32_t* sm_P, const int32_t* sm_N,
-                                                 const TokenSpace& ts, int m) {
-  int64_t d[4] = {-1, -1, 0, 0};
-  const int64_t s0 = (int64_t)m * ts.span;
-  if (s0 < ts.total) {
-    const Piece pc = locate<PAGED>(p, sm_P, sm_N, ts, s0);
-    if (pc.t > 0) {
-      d[0] = pc.start / ts.span;
-      d[1] = (pc.start + pc.ui.n - 1) / ts.span;
-      d[2] = out_row0(p, pc.ui);
-      d[3] = 2 * d[0] + (pc.start != d[0] * ts.span ? 1 : 0);   // the first piece is w0's last one unless
-                                                                 // the unit starts w0's span
-    }
-  }
+// when span m starts inside a unit that began in an earlier span (w0 < m is
+// the span holding the unit's first token, w_last the one holding its last),
+// else w0 = -1.  The spans w0+1 .. w_last of such a unit share its merge.
+__device__ __forceinline__ void write_merge_desc(const Problem& p, int64_t m, int64_t w0, int64_t w_last,
+                                                 int64_t orow, int64_t first_slot) {
   const int i = threadIdx.x;
-  if (i < 4) p.ws_desc[4 * (int64_t)m + i] = i == 0 ? d[0] : (i == 1 ? d[1] : (i == 2 ? d[2] : d[3]));
+  if (i < 4) p.ws_desc[4 * m + i] = i == 0 ? w0 : (i == 1 ? w_last : (i == 2 ? orow : first_slot));
 }
 
-// Merge of the token-split path: one workgroup of 256 threads per decode
-// workgroup m.  The H = w_last - w0 workgroups w0+1 .. w_last of a split unit
-// share its merge: helper h = m - w0 - 1 combines a contiguous block of the
-// unit's output quads (four columns of one head), one quad per thread.
+// Merge of the token-split path: one workgroup of 256 threads per span m
+// (every span of every layer).  The H = w_last - w0 spans w0+1 .. w_last of
+// a split unit share its merge: helper h = m - w0 - 1 combines a contiguous
+// block of the unit's output quads (four columns of one head), one quad per
+// thread.
 template <int D>
 __global__ __launch_bounds__(256) void gqa_merge_spans(Problem p) {
   constexpr int NT = 256;

@@ -131,18 +131,19 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
     if (p.waves > max_waves(hb)) p.waves = max_waves(hb);
     p.tiles = d->tiles_in_flight ? d->tiles_in_flight : default_tiles(hb, kv8);
     if (p.tiles > max_tiles(hb, kv8)) p.tiles = max_tiles(hb, kv8);
-    // Token split: the valid tokens (at most units * T) are shared evenly by
-    // the workgroups, by default one per CU: co-resident workgroups (and
-    // wavefronts beyond four per CU) are served unevenly by the memory
-    // system, and with equal static shares the slowest one sets the time.
-    // A forced chunk_tokens sets the span instead.
-    // stream positions, at most: a paged cache counts each unit's length
-    // rounded up to 16 (plain caches use the same bound, so one workspace size
-    // serves both)
-    const int64_t upper = p.units * ((T + 15) / 16 * 16);
+    // Token split: each layer's valid tokens (at most B * H_kv * T) are
+    // shared evenly by the workgroups, by default one per CU, and every
+    // workgroup takes its share of one layer after the other: co-resident
+    // workgroups (and wavefronts beyond four per CU) are served unevenly by
+    // the memory system, and with equal static shares the slowest one sets
+    // the time.  A forced chunk_tokens sets the span instead.
+    // stream positions of a layer, at most: a paged cache counts each unit's
+    // length rounded up to 16 (plain caches use the same bound, so one
+    // workspace size serves both)
+    const int64_t upper = (int64_t)d->batch * d->num_kv_heads * ((T + 15) / 16 * 16);
     if (d->chunk_tokens > 0) {
       p.span = d->chunk_tokens;
-      p.groups = (int32_t)std::min<int64_t>(std::max<int64_t>(ceil_div(upper, p.span), 1), INT32_MAX);
+      p.groups = (int32_t)std::min<int64_t>(std::max<int64_t>(ceil_div(upper, p.span), 1), INT32_MAX / 2 / L);
     } else {
       // every workgroup must be resident at once (equal spans: a second
       // dispatch round would double the time)
@@ -151,7 +152,7 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
           want == 1 ? 1 : std::max(1, std::min(want, resident_groups_per_cu(d, kind, p.waves, p.tiles)));
       p.groups = (int32_t)std::max<int64_t>(1, std::min<int64_t>(cu_count() * per_cu, ceil_div(upper, 16)));
     }
-    slots = 2 * (int64_t)p.groups;
+    slots = 2 * (int64_t)p.groups * L;   // two per span, one span per workgroup and layer
   } else {
     int64_t c;
     if (d->chunk_tokens > 0) {
@@ -174,8 +175,9 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
   // all of its pieces at the end); with many pieces per unit the separate
   // merge kernel spreads the merge over every workgroup the unit touches.
   p.fused = false;
-  if (p.mfma && p.groups <= kCounterSlots) {
-    const int64_t span_est = p.span > 0 ? p.span : std::max<int64_t>(16, ceil_div(p.units * T, p.groups));
+  if (p.mfma && (int64_t)p.groups * L <= kCounterSlots) {
+    const int64_t span_est =
+        p.span > 0 ? p.span : std::max<int64_t>(16, ceil_div((int64_t)d->batch * d->num_kv_heads * T, p.groups));
     const int64_t pieces = ceil_div(T, span_est) + 1;
     p.fused = d->merge == GQA_MERGE_FUSED || (d->merge == GQA_MERGE_AUTO && pieces <= kFusedMaxPieces);
   }
@@ -183,7 +185,7 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
     p.ws_bytes = p.cnt_bytes = p.ml_bytes = p.desc_bytes = 0;
   } else {
     p.cnt_bytes = kCounterBytes;   // reserved on every path: nothing but counters is ever stored there
-    p.desc_bytes = p.mfma ? (size_t)ceil_div(4 * 8 * (int64_t)p.groups, 256) * 256 : 0;
+    p.desc_bytes = p.mfma ? (size_t)ceil_div(4 * 8 * (int64_t)p.groups * L, 256) * 256 : 0;
     p.ml_bytes = (size_t)ceil_div(slots * G * 2 * 4, 256) * 256;
     p.ws_bytes = p.cnt_bytes + p.desc_bytes + p.ml_bytes + (size_t)(slots * G * d->head_dim * 4);
   }
@@ -383,7 +385,7 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   if (plan.mfma && !plan.fused) {
     const void* mk = d->head_dim == 128 ? reinterpret_cast<const void*>(gqa::gqa_merge_spans<128>)
                                         : reinterpret_cast<const void*>(gqa::gqa_merge_spans<64>);
-    e = hipLaunchKernel(mk, dim3((unsigned)plan.groups), dim3(256), args, 0, s);
+    e = hipLaunchKernel(mk, dim3((unsigned)(plan.groups * L)), dim3(256), args, 0, s);   // one per span
   } else if (plan.n_chunks > 1) {
     const int hpb = 256 / d->head_dim;
     const int64_t mgrid = plan.units * ((p.G + hpb - 1) / hpb);

@@ -250,11 +250,16 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   const TokenSpace ts = token_space(p, sm_P);
   zero_empty_sequences<D, NT>(p, sm_P, blockIdx.x, gridDim.x);
   if constexpr (APPEND) append_side_outputs<D, NT>(p, sm_P, sm_M, blockIdx.x, gridDim.x);
-  if (!p.fused) write_merge_desc<PAGED>(p, sm_P, sm_N, ts, blockIdx.x);
-  const int64_t s0 = (int64_t)blockIdx.x * ts.span;
-  const int64_t s1 = min(s0 + ts.span, ts.total);
-
-  if (s0 >= s1) return;   // no tokens for this workgroup (uniform)
+  // This workgroup streams spans v = blockIdx.x, + groups, + 2 groups, ...
+  // (its span of each layer in turn); [s0, s1) is the current one.
+  const int64_t nspans = (int64_t)p.L * ts.groups;
+  int64_t v = blockIdx.x;
+  int64_t s0 = ts.start(v), s1 = ts.end(v);
+  if (s0 >= s1) {   // w * span >= per_layer: this workgroup's span of every layer is empty (uniform)
+    if (!p.fused)
+      for (int64_t m = v; m < nspans; m += ts.groups) write_merge_desc(p, m, -1, -1, 0, 0);
+    return;
+  }
 
   // Per-lane element offsets inside a tile (relative to the tile's first row).
   // E4M3 keys: the lane holds columns 64h + 16q4 .. +15 (step s of the score
@@ -272,10 +277,11 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     int64_t next;     // stream position after the piece (past the unit's padding when it ends the unit)
     int64_t start;    // stream position of the unit's token 0
     int64_t orow;     // output row of the unit's first head
-    int64_t w0, w_last;
+    int64_t w0, w_last;      // a split unit: the spans holding its first and its last token
+    int64_t slot;            // state slot of a split piece: 2v for the span's first piece, else 2v + 1
+    int64_t first_slot;      // a split unit: the slot of its piece in span w0
     int c0, c1, ntiles;
     bool whole;
-    int slot_id;      // only the first and the last piece of a span can be partial
     Piece at;         // the unit and the piece's first token
     // APPEND: the new token's position and its index in the unit when this
     // piece holds it (else -1)
@@ -295,11 +301,15 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     if constexpr (PAGED) c.pages = p.block_table + (int64_t)pc.ui.b * p.max_pages;
     c.ntiles = (c.c1 - c.c0 + TILE - 1) / TILE;
     c.whole = c.c0 == 0 && c.c1 == pc.ui.n;
-    c.slot_id = x == s0 ? 0 : 1;
-    // the workgroups holding the unit's first and last token (a split unit's
-    // merge only)
-    c.w0 = c.whole ? 0 : pc.start / ts.span;
-    c.w_last = c.whole ? 0 : (pc.start + pc.ui.n - 1) / ts.span;
+    c.slot = 2 * v + (x == s0 ? 0 : 1);
+    // a split unit's merge only: the spans holding its first and last token,
+    // and its first piece, w0's last one unless the unit starts w0's span
+    c.w0 = c.w_last = c.first_slot = 0;
+    if (!c.whole) {
+      c.w0 = ts.span_of(pc.start);
+      c.w_last = ts.span_of(pc.start + pc.ui.n - 1);
+      c.first_slot = 2 * c.w0 + (pc.start != ts.start(c.w0) ? 1 : 0);
+    }
     c.kg = reinterpret_cast<const kv_t*>(p.k) + pc.ui.row0 * D;
     c.vg = reinterpret_cast<const kv_t*>(p.v) + pc.ui.row0 * D;
     c.orow = out_row0(p, pc.ui);
@@ -315,6 +325,15 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   };
   auto open_piece = [&](int64_t x) __attribute__((always_inline)) {
     return open_at(locate<PAGED>(p, sm_P, sm_N, ts, x), x);
+  };
+  // The first piece of span v (s0 and s1 set to its bounds); its merge
+  // descriptor goes out with it.
+  auto open_span = [&]() __attribute__((always_inline)) {
+    s0 = ts.start(v);
+    s1 = ts.end(v);
+    const Ctx c = open_piece(s0);
+    if (!p.fused) write_merge_desc(p, v, c.c0 > 0 ? c.w0 : -1, c.w_last, c.orow, c.first_slot);
+    return c;
   };
   // B operands of the score product: query head head0 + 16 hb, columns 32s + 8q4 .. +7.
   auto load_q = [&](u32x4 (&qf)[HB][KS], const Ctx& c) __attribute__((always_inline)) {
@@ -766,7 +785,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 
     // Lane (q4, m16) holds head head0 + 16 hb of each block, columns D/16*(4*q4+i) + r.
     if (tl == 0) {
-      const int64_t slot = 2 * (int64_t)blockIdx.x + c.slot_id;
+      const int64_t slot = c.slot;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         const int h = head0 + 16 * hb;
@@ -834,18 +853,17 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
         }
         __syncthreads();
       }
-      // the piece of w0 is its last piece (slot 2*w0 + 1) unless the unit starts w0's span
-      const int64_t first_slot = 2 * c.w0 + (c.start != c.w0 * ts.span ? 1 : 0);
-      fused_merge<D, NT>(p, c.w0, c.w_last, first_slot, c.orow, &sm_flag);
+      fused_merge<D, NT>(p, c.w0, c.w_last, c.first_slot, c.orow, &sm_flag);
     }
   };
 
   // ---- main loop ------------------------------------------------------------
   // Two tile buffers in turn: while one batch is computed the next one (of the
-  // same piece, or the first batch of the next piece of the span) is already
-  // loading, so the end of a piece (the combine across wavefronts and the
-  // stores) overlaps the next piece's first loads.
-  Ctx pc = open_piece(s0);
+  // same piece, or the first batch of the next piece: of the span, or of the
+  // workgroup's span of the next layer) is already loading, so the end of a
+  // piece (the combine across wavefronts and the stores) overlaps the next
+  // piece's first loads.
+  Ctx pc = open_span();
   int j = tl;
   int32_t pid[TPW];   // paged: page ids of the next batch to load
   fetch_pages(pid, pc, j);
@@ -856,17 +874,25 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   fetch_pages(pid, pc, j + NL * TPW);
   fill_angles(pc);
   turn_piece(pc);
-  // One step with `cur` loaded: false if it is the span's last batch (left
-  // for the caller), else load the next batch into `nxt` and compute `cur`.
+  // One step with `cur` loaded: false if it is the workgroup's last batch
+  // (left for the caller), else load the next batch into `nxt` and compute
+  // `cur`.
+  auto next_span = [&]() __attribute__((always_inline)) {
+    v += ts.groups;
+    return open_span();
+  };
   auto step = [&](const tile_t (&cur)[TPW], tile_t (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
     const bool piece_done = j + NL * TPW >= pc.ntiles;
     const int64_t xn = PAGED ? pc.next : pc.x + (pc.c1 - pc.c0);
-    if (piece_done && xn >= s1) {
+    const bool span_done = xn >= s1;
+    if (piece_done && span_done && v + ts.groups >= nspans) {
       return false;
     }
     if (piece_done) {
-      // the piece ran to its unit's end: the next one starts the next unit
-      const Ctx pn = open_at(next_unit<PAGED>(p, sm_P, sm_N, pc.at), xn);
+      // the piece ran to its unit's end (the next one starts the next unit)
+      // or to its span's (the next one starts this workgroup's span of the
+      // next layer)
+      const Ctx pn = span_done ? next_span() : open_at(next_unit<PAGED>(p, sm_P, sm_N, pc.at), xn);
       fetch_pages(pid, pn, tl);
       load_batch(nxt, pn, tl, pid);
       fetch_pages(pid, pn, tl + NL * TPW);

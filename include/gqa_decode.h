@@ -39,9 +39,10 @@
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls
  *   only enqueue work and return; inputs must stay unchanged, and out is
  *   valid, once the stream reaches the call.  No host synchronisation.
- * Work split.  The matrix-core path divides all valid tokens of the call,
- *   in (layer, sequence, KV head, token) order, evenly among its workgroups
- *   (one per CU by default), whatever the sequence lengths; the vector path cuts
+ * Work split.  The matrix-core path divides each layer's valid tokens, in
+ *   (sequence, KV head, token) order, evenly among its workgroups (one per
+ *   CU by default), whatever the sequence lengths; each workgroup takes its
+ *   share of layer 0, then of layer 1, and so on.  The vector path cuts
  *   each sequence into chunks of a planned size.  Pieces of a (layer,
  *   sequence, KV head) computed by different workgroups leave partial
  *   softmax states in the workspace that are combined in a fixed order
@@ -122,8 +123,9 @@ typedef struct gqa_dims {
                             seq_lens[b]; the split is planned over it and
                             larger values are clamped to it on the device */
   int32_t chunk_tokens;  /* 0: the planner splits the work; otherwise a positive
-                            multiple of 64: tokens per workgroup (matrix-core
-                            path) or per chunk of a sequence (vector path) */
+                            multiple of 64: tokens per workgroup and layer
+                            (matrix-core path) or per chunk of a sequence
+                            (vector path) */
   int32_t path;          /* gqa_path */
   int32_t workgroup_waves; /* 0, 4, 8 or 16 (others are invalid): wavefronts
                               per workgroup of the matrix-core kernel.  Every
@@ -163,8 +165,9 @@ size_t gqa_decode_workspace_bytes(const gqa_dims* dims, int32_t num_layers);
  * The work split planned for these dims (as gqa_decode and gqa_decode_layers
  * plan it; with workgroups_per_cu > 1 the other entry points may plan fewer
  * workgroups, by their kernels' occupancy).  Matrix-core path: *chunk_tokens is
- * the forced tokens per workgroup (0 when the valid tokens are shared evenly
- * at run time) and *num_chunks the number of workgroups.  Vector path: tokens
+ * the forced tokens per workgroup and layer (0 when each layer's valid
+ * tokens are shared evenly at run time) and *num_chunks the number of
+ * workgroups (each takes its share of every layer in turn).  Vector path: tokens
  * per chunk and the chunk count of the longest possible sequence.  Returns
  * GQA_OK or GQA_ERR_INVALID_ARG / GQA_ERR_UNSUPPORTED (outputs untouched
  * then).  Host only (it may ask the HIP runtime for the CU count).
