@@ -554,13 +554,13 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       compute_core(T, t0, c.c1);
     }
   };
-  // APPEND: the queries (and the new key) of a piece are turned when the
-  // piece becomes current: after the prologue's loads, or after the previous
-  // piece's end (its tiles and accumulators are then free, only the next
-  // batch is in flight), with the angle table the piece's opening filled.
-  // Score step s of a lane covers the 8 columns qcol(s) .. +7 (see load_q),
-  // that is the 4 pairs qcol(s)/2 .. +3.  The unit's first piece writes the
-  // turned queries of its heads to q_out.
+  // APPEND: the queries (and the new key) of a piece are turned once its
+  // first batch and the batch after it have been issued (the first compute
+  // of the piece; see ensure_turned), so that loads stay in flight meanwhile,
+  // with the angle table the piece's opening filled.  Score step s of a lane
+  // covers the 8 columns qcol(s) .. +7 (see load_q), that is the 4 pairs
+  // qcol(s)/2 .. +3.  The unit's first piece writes the turned queries of
+  // its heads to q_out.
   auto qcol = [&](int s) __attribute__((always_inline)) {
     return KV8 ? 64 * (s >> 1) + 16 * q4 + 8 * (s & 1) : 32 * s + 8 * q4;
   };
@@ -574,19 +574,20 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     }
     return r;
   };
-  // KV8: the E4M3 bytes of the key pairs in w turned in fp32 and divided by
-  // k_scale (the quantising append's arithmetic), 8 bytes as two words.
-  auto turn_encode_words = [&](const u32x4& w, const float (&cc)[4], const float (&ss)[4])
-                               __attribute__((always_inline)) {
-    uint32_t b[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float y0, y1;
-      rope_turn(bf16_to_f32(w[k] & 0xffffu), bf16_to_f32(w[k] >> 16), cc[k], ss[k], y0, y1);
-      b[2 * k] = e4m3_encode(y0 / p.k_scale);
-      b[2 * k + 1] = e4m3_encode(y1 / p.k_scale);
+  // APPEND: the new row of the piece that ends a grown unit, one element
+  // pair per lane: lane jp < D/2 holds key and value elements 2jp, 2jp+1 (two
+  // bf16 each).  Loaded when the piece is opened, with its queries, and used
+  // by turn_piece.
+  const int jp = lane & (D / 2 - 1);
+  uint32_t kn_pair = 0, vn_pair = 0;
+  auto load_new_row = [&](const Ctx& c) __attribute__((always_inline)) {
+    if constexpr (APPEND) {
+      if (c.mnew >= 0) {   // wave-uniform
+        const int64_t nrow = ((int64_t)c.at.ui.b * p.H_kv + c.at.ui.g) * (D / 2);   // in pairs
+        kn_pair = reinterpret_cast<const uint32_t*>(p.k_new)[nrow + jp];
+        vn_pair = reinterpret_cast<const uint32_t*>(p.v_new)[nrow + jp];
+      }
     }
-    return u32x2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24), b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
   };
   auto turn_piece = [&](Ctx& c) __attribute__((always_inline)) {
     if constexpr (APPEND) {
@@ -607,85 +608,41 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) qf[hb][s] = turn_words(qf[hb][s], cc, ss);
       }
-      // Only the piece that ends a grown unit needs the new row: its key and
-      // value are loaded here (a wait of one load latency, once per unit), the
-      // key turned, both kept in the wavefront's slot for the tile that holds
-      // the row (lanes of one m16 hold the whole key, lanes of one q4 the
-      // whole value), and wavefront 0 writes them to cache row m (no other
-      // workgroup reads that row, and this piece's tile holding it takes the
-      // slot's copy whatever it loaded).
+      // Only the piece that ends a grown unit needs the new row (loaded with
+      // the piece's queries): lane jp turns key pair jp, and the row goes to
+      // the wavefront's slot for the tile that holds it (the substitution in
+      // compute_tile reads it back in its own lane layout) and, from
+      // wavefront 0, to cache row m (no other workgroup reads that row, and
+      // this piece's tile holding it takes the slot's copy whatever it
+      // loaded).
       if (c.mnew >= 0) {   // wave-uniform
-        const int64_t nrow = ((int64_t)c.at.ui.b * p.H_kv + c.at.ui.g) * D;
-        const uint16_t* kn = reinterpret_cast<const uint16_t*>(p.k_new) + nrow;
-        const uint16_t* vn = reinterpret_cast<const uint16_t*>(p.v_new) + nrow;
-        u32x4 knew[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) knew[s] = *reinterpret_cast<const u32x4*>(kn + qcol(s));
-        const vrow_t vnew = *reinterpret_cast<const vrow_t*>(vn + VW * m16);
         // cache row m: the unit's row m, or row m % page of the page the
         // sequence's table names for it (within the pool shifted to head g)
         int64_t crow = c.mnew;
         if constexpr (PAGED) crow = (int64_t)c.pages[c.mnew / p.page] * p.H_kv * p.page + c.mnew % p.page;
-        if constexpr (KV8) {
-          u32x2 kcode[KS];
-#pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            float cc[4], ss[4];
-            angles(s, cc, ss);
-            kcode[s] = turn_encode_words(knew[s], cc, ss);
-          }
-          // the value's bytes at columns VW*m16 .. +VW-1
-          uint32_t vb[VW];
-#pragma unroll
-          for (int e = 0; e < VW; ++e) {
-            const uint32_t wd = vnew[e >> 1];
-            vb[e] = e4m3_encode(bf16_to_f32((e & 1) ? (wd >> 16) : (wd & 0xffffu)) / p.v_scale);
-          }
-          typedef typename std::conditional<D == 128, u32x2, uint32_t>::type vcode_t;
-          vcode_t vcode;
-          if constexpr (D == 128)
-            vcode = u32x2{vb[0] | (vb[1] << 8) | (vb[2] << 16) | (vb[3] << 24),
-                          vb[4] | (vb[5] << 8) | (vb[6] << 16) | (vb[7] << 24)};
-          else
-            vcode = vb[0] | (vb[1] << 8) | (vb[2] << 16) | (vb[3] << 24);
-          uint8_t* ks = reinterpret_cast<uint8_t*>(&sm_kvn[wave][c.tab][0][0]);
-          uint8_t* vs = reinterpret_cast<uint8_t*>(&sm_kvn[wave][c.tab][1][0]);
-          if (m16 == 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x2*>(ks + qcol(s)) = kcode[s];
-          }
-          if (q4 == 0) *reinterpret_cast<vcode_t*>(vs + VW * m16) = vcode;
-          if (wave == 0) {
-            uint8_t* kc = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(c.kg)) + crow * D;
-            uint8_t* vc = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(c.vg)) + crow * D;
-            if (m16 == 0) {
-#pragma unroll
-              for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x2*>(kc + qcol(s)) = kcode[s];
+        float k0, k1;
+        rope_turn(bf16_to_f32(kn_pair & 0xffffu), bf16_to_f32(kn_pair >> 16), tab[jp], tab[D / 2 + jp], k0, k1);
+        if (lane < D / 2) {
+          if constexpr (KV8) {
+            // the quantising append's arithmetic: the turned fp32 key and the
+            // value divided by their scales, each to its E4M3 code
+            const uint32_t kc = e4m3_encode(k0 / p.k_scale) | (e4m3_encode(k1 / p.k_scale) << 8);
+            const uint32_t vc = e4m3_encode(bf16_to_f32(vn_pair & 0xffffu) / p.v_scale) |
+                                (e4m3_encode(bf16_to_f32(vn_pair >> 16) / p.v_scale) << 8);
+            reinterpret_cast<uint16_t*>(&sm_kvn[wave][c.tab][0][0])[jp] = (uint16_t)kc;
+            reinterpret_cast<uint16_t*>(&sm_kvn[wave][c.tab][1][0])[jp] = (uint16_t)vc;
+            if (wave == 0) {
+              reinterpret_cast<uint16_t*>(const_cast<kv_t*>(c.kg) + crow * D)[jp] = (uint16_t)kc;
+              reinterpret_cast<uint16_t*>(const_cast<kv_t*>(c.vg) + crow * D)[jp] = (uint16_t)vc;
             }
-            if (q4 == 0) *reinterpret_cast<vcode_t*>(vc + VW * m16) = vcode;
-          }
-        } else {
-#pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            float cc[4], ss[4];
-            angles(s, cc, ss);
-            knew[s] = turn_words(knew[s], cc, ss);
-          }
-          uint16_t* ks = &sm_kvn[wave][c.tab][0][0];
-          uint16_t* vs = &sm_kvn[wave][c.tab][1][0];
-          if (m16 == 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(ks + qcol(s)) = knew[s];
-          }
-          if (q4 == 0) *reinterpret_cast<vrow_t*>(vs + VW * m16) = vnew;
-          if (wave == 0) {
-            uint16_t* kc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.kg)) + crow * D;
-            uint16_t* vc = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(c.vg)) + crow * D;
-            if (m16 == 0) {
-#pragma unroll
-              for (int s = 0; s < KS; ++s) *reinterpret_cast<u32x4*>(kc + qcol(s)) = knew[s];
+          } else {
+            const uint32_t kt = f32_to_bf16_rne(k0) | (f32_to_bf16_rne(k1) << 16);
+            reinterpret_cast<uint32_t*>(&sm_kvn[wave][c.tab][0][0])[jp] = kt;
+            reinterpret_cast<uint32_t*>(&sm_kvn[wave][c.tab][1][0])[jp] = vn_pair;   // the value row as it is
+            if (wave == 0) {
+              reinterpret_cast<uint32_t*>(const_cast<kv_t*>(c.kg) + crow * D)[jp] = kt;
+              reinterpret_cast<uint32_t*>(const_cast<kv_t*>(c.vg) + crow * D)[jp] = vn_pair;
             }
-            if (q4 == 0) *reinterpret_cast<vrow_t*>(vc + VW * m16) = vnew;
           }
         }
       }
@@ -868,12 +825,28 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   int32_t pid[TPW];   // paged: page ids of the next batch to load
   fetch_pages(pid, pc, j);
   load_q(qf, pc);
+  load_new_row(pc);
   reset_state();
   tile_t TA[TPW], TB[TPW];
   load_batch(TA, pc, j, pid);
   fetch_pages(pid, pc, j + NL * TPW);
   fill_angles(pc);
-  turn_piece(pc);
+  // APPEND: whether the current piece's queries and new row are still to
+  // be turned.  A piece of several batches (for this wavefront) is turned
+  // right before its first compute, which a step (not the steady-state loop)
+  // makes after issuing the next batch, so that a batch stays in flight
+  // while the turn waits for the queries; the first piece, and a piece of
+  // one batch, are turned when opened.
+  bool turn_pending = APPEND;
+  auto ensure_turned = [&]() __attribute__((always_inline)) {
+    if constexpr (APPEND) {
+      if (turn_pending) {   // wave-uniform
+        turn_piece(pc);
+        turn_pending = false;
+      }
+    }
+  };
+  ensure_turned();   // the first piece's queries and new row were issued before its first batch
   // One step with `cur` loaded: false if it is the workgroup's last batch
   // (left for the caller), else load the next batch into `nxt` and compute
   // `cur`.
@@ -897,16 +870,21 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
       load_batch(nxt, pn, tl, pid);
       fetch_pages(pid, pn, tl + NL * TPW);
       compute_batch(cur, pc, j, std::true_type{});
-      load_q(qf, pn);   // the next piece's queries: their latency overlaps end_piece
+      load_q(qf, pn);   // the next piece's queries (and new row): their latency overlaps end_piece
+      load_new_row(pn);
       end_piece(pc);
       reset_state();
       pc = pn;
       fill_angles(pc);
-      turn_piece(pc);
+      turn_pending = APPEND;
+      // a piece of one batch for this wavefront (or none): its only compute is
+      // its last, made by the step that ends it, so it is turned now
+      if (tl + NL * TPW >= pc.ntiles) ensure_turned();
       j = tl;
     } else {
       load_batch(nxt, pc, j + NL * TPW, pid);
       fetch_pages(pid, pc, j + 2 * NL * TPW);
+      ensure_turned();
       compute_batch(cur, pc, j, std::true_type{});
       j += NL * TPW;
     }
@@ -916,7 +894,8 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
     // Steady state: while the piece has two more batches, neither step ends
     // it, and this loop carries only the running softmax state.  Its tiles
     // all lie below j + 2 NL TPW <= ntiles - 1, so none is the piece's last.
-    while (j + 2 * NL * TPW < pc.ntiles) {
+    // A piece whose queries are not turned yet first goes through a step.
+    while (!turn_pending && j + 2 * NL * TPW < pc.ntiles) {
       load_batch(TB, pc, j + NL * TPW, pid);
       fetch_pages(pid, pc, j + 2 * NL * TPW);
       compute_batch(TA, pc, j, std::false_type{});

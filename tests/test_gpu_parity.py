@@ -404,6 +404,61 @@ def test_layers(packed, path):
         assert err(out[l], ref) <= 2e-3, l
 
 
+LAYER_SPLIT_CASES = [
+    # (H_q, H_kv, d), cached tokens per sequence, layers, packed layouts too
+    ((16, 2, 128), [0, 1, 15, 16, 17, 0, 333, 1000, 64, 0, 129, 2], 5, True),   # G = 8, every kind of edge
+    ((32, 1, 128), [700, 0, 1, 450], 3, True),    # MQA, G = 32: units split into many pieces per layer
+    ((32, 8, 128), [3, 0, 5], 4, True),           # 64 positions per layer: most workgroups hold no span
+    ((64, 8, 128), [17, 250], 2, True),           # G = 8, the whole layer inside few spans
+    ((8, 2, 64), [0, 0, 0], 3, False),            # no tokens in any layer
+]
+
+
+@pytest.mark.parametrize("case", [(i, p) for i, c in enumerate(LAYER_SPLIT_CASES) for p in (False, True)
+                                  if c[3] or not p], ids=lambda c: "case%d_%s" % (c[0], "packed" if c[1] else "dense"))
+def test_layer_interleaved_split(case):
+    """Layer batches: every workgroup streams its span of layer 0, then of
+    layer 1, and so on.  Each layer meets the bar against the oracle under
+    the planner's split and under forced spans (spans ending on a layer's
+    last position, workgroups without a span in any layer, units split over
+    many spans of one layer), with both merges; and since the spans of a
+    layer are those a one-layer call plans, each layer's output is bitwise
+    that of the one-layer call."""
+    i, packed = case
+    (H_q, H_kv, d), lens, L, _ = LAYER_SPLIT_CASES[i]
+    sl = torch.tensor(lens, dtype=torch.int32)
+    T = max(max(lens), 1)
+    w = workloads.Workload("layer-split", len(lens), H_q, H_kv, d, 1, T, torch.bfloat16, 80 + i, layers=L,
+                           packed=packed)
+    x = workloads.generate(w, "cpu", poison_padding=True, seq_lens=sl)
+    xd = to_dev(x)
+    kw = dict(kv_offsets=xd["kv_offsets"], max_seq_len=T, num_kv_heads=H_kv) if packed else {}
+    refs = []
+    for l in range(L):
+        xl = workloads.layer_view(x, l)
+        refs.append(oracle.decode(xl["q"], xl["k"], xl["v"], x["seq_lens"], x["scale"],
+                                  kv_offsets=x["kv_offsets"].numpy() if packed else None, num_kv_heads=H_kv))
+    for span in (0, 64, 192):
+        for merge in ("fused", "kernel"):
+            note("layer split", i, packed, span, merge)
+            run = lambda dt: gqa.decode_layers(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"],
+                                               out_dtype=dt, path="mfma", chunk_tokens=span, merge=merge, **kw)
+            out32, out16 = run(torch.float32), run(torch.bfloat16)
+            torch.cuda.synchronize()
+            assert torch.equal(out16, out32.to(torch.bfloat16))
+            for l in range(L):
+                assert err(out32[l], refs[l]) <= 2e-3, (span, merge, l)
+                xl = workloads.layer_view(xd, l)
+                if packed:
+                    one = gqa.decode_layers(xl["q"][None], xl["k"], xl["v"], xd["seq_lens"], x["scale"],
+                                            out_dtype=torch.float32, path="mfma", chunk_tokens=span, merge=merge,
+                                            **kw)[0]
+                else:
+                    one = gqa.decode(xl["q"], xl["k"], xl["v"], xd["seq_lens"], x["scale"], out_dtype=torch.float32,
+                                     path="mfma", chunk_tokens=span, merge=merge)
+                assert torch.equal(one, out32[l]), (span, merge, l)
+
+
 # -------------------------------------------------------- full-size loads --
 def sample_heads(B, H_q, n, seed):
     g = torch.Generator().manual_seed(seed)
