@@ -197,7 +197,11 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
  *                own capacity (the logical cache size of "Grouped-Query
  *                Attention Shares Keys Without Sharing Every Query", without
  *                padding to T_max).  The dense layout is kv_offsets[b] = b*T_max.
- * The result equals num_layers separate gqa_decode calls.
+ * The result equals num_layers separate gqa_decode calls, bit for bit: each
+ * layer is split among the workgroups as a one-layer call with these dims
+ * splits it, and every workgroup takes its share of each layer in turn.
+ * The workspace grows with num_layers (two partial-state slots per
+ * workgroup and layer).
  */
 gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
                              const int64_t* kv_offsets, const int32_t* seq_lens, float scale, void* out,
