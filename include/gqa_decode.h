@@ -197,9 +197,12 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
  *                own capacity (the logical cache size of "Grouped-Query
  *                Attention Shares Keys Without Sharing Every Query", without
  *                padding to T_max).  The dense layout is kv_offsets[b] = b*T_max.
- * The result equals num_layers separate gqa_decode calls, bit for bit: each
- * layer is split among the workgroups as a one-layer call with these dims
- * splits it, and every workgroup takes its share of each layer in turn.
+ * The result equals num_layers separate gqa_decode calls: each layer is
+ * split among the workgroups as a one-layer call with these dims splits it,
+ * and every workgroup takes its share of each layer in turn, so with the
+ * same merge (dims->merge FUSED or KERNEL; AUTO picks KERNEL for a batch
+ * whose num_layers x workgroups exceed the fused merge's counters) the
+ * results are bitwise those of the one-layer calls.
  * The workspace grows with num_layers (two partial-state slots per
  * workgroup and layer).
  */
