@@ -41,16 +41,16 @@ struct Problem {
   const int64_t* kv_offsets;  // [B+1] or nullptr (dense)
   const int32_t* seq_lens;    // [B]
   float* ws_ml;               // partial states (m, l): chunk path [units][n_chunks][G][2],
-                              //   token-split path [groups][2][G][2]
-  float* ws_o;                // partial O: [units][n_chunks][G][D] or [groups][2][G][D]
-  int64_t* ws_desc;           // token-split path: [groups][4] merge descriptors
-  int32_t* ws_cnt;            // token-split path, fused merge: [groups] arrival counters (zero between calls)
+                              //   token-split path [L * groups spans][2][G][2]
+  float* ws_o;                // partial O: [units][n_chunks][G][D] or [L * groups][2][G][D]
+  int64_t* ws_desc;           // token-split path: [L * groups][4] merge descriptors
+  int32_t* ws_cnt;            // token-split path, fused merge: [L * groups] arrival counters (zero between calls)
   int32_t fused;              // token-split path: 1 = the last piece of a split unit to finish merges it
   int32_t B, H_q, H_kv, G, T_max, L;
   int32_t T_cap;              // planned bound on valid tokens (seq_len_hint, else T_max)
   int32_t chunk, n_chunks;    // chunk path: tokens per chunk, chunks of the longest sequence
   int32_t groups;             // token-split path: decode workgroups launched
-  int32_t span;               // token-split path: tokens per workgroup (0: balanced split)
+  int32_t span;               // token-split path: positions per span (one per workgroup and layer; 0: balanced)
   int32_t out_bf16;
   float scale_log2;           // scale * log2(e): scores are kept in base 2
   const int32_t* block_table; // paged cache: [B][max_pages] page ids, or nullptr
@@ -478,9 +478,9 @@ __device__ __forceinline__ f32x4 merge_finish(const Problem& p, const MergeAcc& 
 }
 
 // Merge state of output columns c .. c+3 (c a multiple of 4) of head hd of a
-// split unit over the pieces of workgroups w_first, w_first + stride, ...
-// up to w_last (workgroup w0's piece is in slot first_slot, workgroup w's in
-// slot 2w), in that order:
+// split unit over the pieces of spans w_first, w_first + stride, ... up to
+// w_last (span w0's piece is in slot first_slot, span w's in slot 2w), in
+// that order:
 //   M = max_k m_k,  out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k,
 // with a running maximum.  The loads of kMergeBatch pieces are issued
 // together (indices past the last piece are clamped to an in-bounds piece and
@@ -537,12 +537,12 @@ __device__ __forceinline__ void store_out4(const Problem& p, int64_t row, int c,
 // Fused merge of a split unit, run by every thread of the workgroup that just
 // published one piece of it with the sc1 stores (from wavefront 0).  Thread 0
 // waits until those stores have completed, then counts the piece in the
-// unit's arrival counter (indexed by w0, the workgroup holding the unit's
-// first token; agent-scope atomic).  The workgroup that brings the count to
+// unit's arrival counter (indexed by w0, the span holding the unit's first
+// token; agent-scope atomic).  The workgroup that brings the count to
 // the number of pieces reads every piece back with sc1 loads, in piece
 // order (deterministic), writes the output and resets the counter to zero
 // for the next call.  Pieces: w0's slot first_slot, then slot 2w of every
-// later workgroup w <= w_last.
+// later span w <= w_last.
 template <int D, int NT>
 __device__ __forceinline__ void fused_merge(const Problem& p, int64_t w0, int64_t w_last, int64_t first_slot, int64_t orow,
                             int* sm_flag) {
