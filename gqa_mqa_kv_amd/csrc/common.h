@@ -41,16 +41,18 @@ struct Problem {
   const int64_t* kv_offsets;  // [B+1] or nullptr (dense)
   const int32_t* seq_lens;    // [B]
   float* ws_ml;               // partial states (m, l): chunk path [units][n_chunks][G][2],
-                              //   token-split path [L * groups spans][2][G][2]
-  float* ws_o;                // partial O: [units][n_chunks][G][D] or [L * groups][2][G][D]
-  int64_t* ws_desc;           // token-split path: [L * groups][4] merge descriptors
-  int32_t* ws_cnt;            // token-split path, fused merge: [L * groups] arrival counters (zero between calls)
+                              //   token-split path [spans][2][G][2]
+  float* ws_o;                // partial O: [units][n_chunks][G][D] or [spans][2][G][D]
+  int64_t* ws_desc;           // token-split path: [spans][4] merge descriptors
+  int32_t* ws_cnt;            // token-split path, fused merge: [spans] arrival counters (zero between calls)
   int32_t fused;              // token-split path: 1 = the last piece of a split unit to finish merges it
   int32_t B, H_q, H_kv, G, T_max, L;
   int32_t T_cap;              // planned bound on valid tokens (seq_len_hint, else T_max)
   int32_t chunk, n_chunks;    // chunk path: tokens per chunk, chunks of the longest sequence
   int32_t groups;             // token-split path: decode workgroups launched
   int32_t span;               // token-split path: positions per span (one per workgroup and layer; 0: balanced)
+  int32_t dyn_chunks;         // token-split path, layer batches: chunks of the last layer claimed at run time (0: none)
+  int32_t* ws_ticket;         // their arrival ticket (a counter of the workspace, zero between calls)
   int32_t out_bf16;
   float scale_log2;           // scale * log2(e): scores are kept in base 2
   const int32_t* block_table; // paged cache: [B][max_pages] page ids, or nullptr
@@ -204,10 +206,16 @@ __global__ __launch_bounds__(256) void gqa_merge_chunks(Problem p) {
 //     [l * per_layer + w * span, min(l * per_layer + (w + 1) * span, (l + 1) * per_layer)),
 // and workgroup w takes spans w, groups + w, 2 groups + w, ... in turn, one
 // layer after the other, so that at any time the workgroups stream the same
-// layer.  Every unit that lies inside one span is finished there; only the
-// first and the last unit piece of a span can be partial (state slots 2v and
-// 2v + 1; a piece covering a whole span uses slot 2v).  A unit never crosses
-// a layer, so the spans holding its pieces are consecutive.
+// layer.  A layer batch (L >= 2) under the balanced split instead cuts its
+// last layer into `dyn` chunks of `dspan` positions (spans
+// v = (L - 1) * groups + c), which the workgroups claim one at a time from an
+// arrival ticket once their static spans are done: workgroups that streamed
+// faster take more of the last layer, and all end close together.  Every
+// unit that lies inside one span is finished there; only the first and the
+// last unit piece of a span can be partial (state slots 2v and 2v + 1; a
+// piece covering a whole span uses slot 2v).  A unit never crosses a layer,
+// so the spans holding its pieces are consecutive.  A span's pieces depend
+// only on its bounds, whichever workgroup streams it.
 
 // Exclusive prefix sums of the units' stream lengths into sm_P[0..B] (all
 // threads of the workgroup take part; B <= kMaxBatch).  A unit's stream
@@ -270,30 +278,46 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-struct TokenSpace {
+// CLAIMS: the kernel instance of layer batches whose last layer is claimed
+// in chunks (the other instances compile none of that).
+template <bool CLAIMS>
+struct TokenSpaceT {
   int64_t per_layer;   // H_kv * P[B]
   int64_t total;       // L * per_layer
-  int64_t span;        // positions per span of a layer, a multiple of 16
-  int64_t groups;      // spans per layer (the workgroups launched)
+  int64_t span;        // positions per static span of a layer, a multiple of 16
+  int64_t groups;      // static spans per layer (the workgroups launched)
+  int64_t sl;          // layers cut into static spans: L, or L - 1 with a claimed last layer
+  int64_t dyn;         // CLAIMS: chunks of the claimed last layer (0: none)
+  int64_t dspan;       // CLAIMS: positions per chunk of the claimed last layer, a multiple of 16
 
-  // first position of span v, one past its last, and the span holding
-  // position x
+  // first position of span v, one past its last (a chunk past the layer's
+  // last position is empty), and the span holding position x
   __device__ __forceinline__ int64_t start(int64_t v) const {
+    if constexpr (CLAIMS) {
+      if (v >= sl * groups) return sl * per_layer + (v - sl * groups) * dspan;
+    }
     const int64_t l = v / groups;
     return l * per_layer + (v - l * groups) * span;
   }
   __device__ __forceinline__ int64_t end(int64_t v) const {
+    if constexpr (CLAIMS) {
+      if (v >= sl * groups) return min(start(v) + dspan, (sl + 1) * per_layer);
+    }
     const int64_t l = v / groups;
     return min(start(v) + span, (l + 1) * per_layer);
   }
   __device__ __forceinline__ int64_t span_of(int64_t x) const {
     const int64_t l = x / per_layer;
+    if constexpr (CLAIMS) {
+      if (l >= sl) return sl * groups + (x - sl * per_layer) / dspan;
+    }
     return l * groups + (x - l * per_layer) / span;
   }
 };
 
-__device__ __forceinline__ TokenSpace token_space(const Problem& p, const int32_t* sm_P) {
-  TokenSpace ts;
+template <bool CLAIMS>
+__device__ __forceinline__ TokenSpaceT<CLAIMS> token_space(const Problem& p, const int32_t* sm_P) {
+  TokenSpaceT<CLAIMS> ts;
   ts.per_layer = (int64_t)p.H_kv * uniform(sm_P[p.B]);
   ts.total = ts.per_layer * p.L;
   ts.groups = p.groups;
@@ -303,6 +327,13 @@ __device__ __forceinline__ TokenSpace token_space(const Problem& p, const int32_
     const int64_t s = (ts.per_layer + p.groups - 1) / p.groups;
     ts.span = (s + 15) / 16 * 16;
     if (ts.span == 0) ts.span = 16;
+  }
+  ts.dyn = CLAIMS ? p.dyn_chunks : 0;
+  ts.sl = ts.dyn > 0 ? p.L - 1 : p.L;
+  ts.dspan = 16;
+  if (ts.dyn > 0) {
+    const int64_t s = (ts.per_layer + ts.dyn - 1) / ts.dyn;
+    ts.dspan = s > 16 ? (s + 15) / 16 * 16 : 16;
   }
   return ts;
 }
@@ -344,9 +375,9 @@ __device__ __forceinline__ Piece fill_piece(const Problem& p, const int32_t* sm_
 
 // The unit holding stream position x (0 <= x < total): a binary search over
 // the prefix sums.
-template <bool PAGED>
-__device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, const int32_t* sm_N,
-                                        const TokenSpace& ts, int64_t x) {
+template <bool PAGED, typename TS>
+__device__ __forceinline__ Piece locate(const Problem& p, const int32_t* sm_P, const int32_t* sm_N, const TS& ts,
+                                        int64_t x) {
   const int l = (int)(x / ts.per_layer);
   const int64_t r = x - (int64_t)l * ts.per_layer;
   int lo = 0, hi = p.B - 1;   // largest b with H_kv * P[b] <= r (such b holds tokens)

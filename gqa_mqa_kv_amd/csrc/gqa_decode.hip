@@ -56,6 +56,7 @@ int cu_count() {
 // and whether the append of the new token is fused in.
 struct KernelKind {
   bool kv8 = false, paged = false, append = false;
+  bool claims = false;   // a layer batch whose last layer is claimed in chunks
 };
 
 int max_waves(int hb);
@@ -102,12 +103,22 @@ gqa_status check_dims(const gqa_dims* d, int32_t L) {
 constexpr int64_t kCounterSlots = 1 << 18;
 constexpr size_t kCounterBytes = (size_t)kCounterSlots * 4;
 constexpr int64_t kFusedMaxPieces = 8;
+// A layer batch under the balanced split hands out its last layer in this
+// many chunks per workgroup, claimed at run time (the ticket is the last
+// counter of the region).
+constexpr int64_t kDynChunksPerGroup = 8;
+constexpr int64_t kTicketSlot = kCounterSlots - 1;
+// The matrix-core instances that can claim chunks (the kernel's CLAIMS): one
+// head block, neither paged nor fused with the append.
+bool claims_last_layer(int hb, const KernelKind& kind) { return hb == 1 && !kind.paged && !kind.append; }
 
 struct Plan {
   bool mfma, fused;
   int32_t waves, tiles;
   int32_t chunk, n_chunks;   // vector path
   int32_t groups, span;      // matrix-core path (span 0: balanced over the groups)
+  int64_t dyn;               // matrix-core layer batch: chunks of the last layer claimed at run time
+  int64_t nspans;            // matrix-core path: spans of the call (static ones and chunks)
   int64_t units;
   size_t ws_bytes, cnt_bytes, desc_bytes, ml_bytes;
 };
@@ -125,6 +136,7 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
   p.waves = 4;
   p.tiles = 1;
   p.chunk = p.n_chunks = p.groups = p.span = 0;
+  p.dyn = p.nspans = 0;
   int64_t slots;
   if (p.mfma) {
     p.waves = d->workgroup_waves ? d->workgroup_waves : 4;
@@ -152,7 +164,12 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
           want == 1 ? 1 : std::max(1, std::min(want, resident_groups_per_cu(d, kind, p.waves, p.tiles)));
       p.groups = (int32_t)std::max<int64_t>(1, std::min<int64_t>(cu_count() * per_cu, ceil_div(upper, 16)));
     }
-    slots = 2 * (int64_t)p.groups * L;   // two per span, one span per workgroup and layer
+    // a layer batch under the balanced split: the last layer in chunks that
+    // the workgroups claim once their static spans are done, so that the
+    // ones that streamed faster take more of it
+    if (L >= 2 && d->chunk_tokens <= 0 && claims_last_layer(hb, kind)) p.dyn = kDynChunksPerGroup * p.groups;
+    p.nspans = (int64_t)(p.dyn > 0 ? L - 1 : L) * p.groups + p.dyn;
+    slots = 2 * p.nspans;   // two per span
   } else {
     int64_t c;
     if (d->chunk_tokens > 0) {
@@ -175,9 +192,11 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
   // all of its pieces at the end); with many pieces per unit the separate
   // merge kernel spreads the merge over every workgroup the unit touches.
   p.fused = false;
-  if (p.mfma && (int64_t)p.groups * L <= kCounterSlots) {
+  if (p.mfma && p.nspans <= kTicketSlot) {
     const int64_t span_est =
-        p.span > 0 ? p.span : std::max<int64_t>(16, ceil_div((int64_t)d->batch * d->num_kv_heads * T, p.groups));
+        p.span > 0 ? p.span
+                   : std::max<int64_t>(16, ceil_div((int64_t)d->batch * d->num_kv_heads * T,
+                                                    p.dyn > 0 ? p.dyn : (int64_t)p.groups));
     const int64_t pieces = ceil_div(T, span_est) + 1;
     p.fused = d->merge == GQA_MERGE_FUSED || (d->merge == GQA_MERGE_AUTO && pieces <= kFusedMaxPieces);
   }
@@ -185,7 +204,7 @@ Plan make_plan(const gqa_dims* d, int32_t L, const KernelKind& kind = KernelKind
     p.ws_bytes = p.cnt_bytes = p.ml_bytes = p.desc_bytes = 0;
   } else {
     p.cnt_bytes = kCounterBytes;   // reserved on every path: nothing but counters is ever stored there
-    p.desc_bytes = p.mfma ? (size_t)ceil_div(4 * 8 * (int64_t)p.groups * L, 256) * 256 : 0;
+    p.desc_bytes = p.mfma ? (size_t)ceil_div(4 * 8 * p.nspans, 256) * 256 : 0;
     p.ml_bytes = (size_t)ceil_div(slots * G * 2 * 4, 256) * 256;
     p.ws_bytes = p.cnt_bytes + p.desc_bytes + p.ml_bytes + (size_t)(slots * G * d->head_dim * 4);
   }
@@ -219,6 +238,15 @@ kernel_fn mfma_kernel(int hb, int, int tiles) {
       return tiles == 2 ? gqa::gqa_decode_mfma<D, 2, 1, 4, 2, PAGED, KV8> : gqa::gqa_decode_mfma<D, 2, 1, 4, 1, PAGED, KV8>;
     default: return gqa::gqa_decode_mfma<D, 2, 2, 4, 1, PAGED, KV8>;
   }
+}
+
+// A layer batch whose last layer the workgroups claim in chunks (one head
+// block, plain or packed layout).
+template <int D, bool KV8 = false>
+kernel_fn mfma_claims_kernel(int tiles) {
+  if (KV8 && tiles == 4) return gqa::gqa_decode_mfma<D, 1, 1, 4, KV8 ? 4 : 2, false, KV8, false, true>;
+  return tiles == 2 ? gqa::gqa_decode_mfma<D, 1, 1, 4, 2, false, KV8, false, true>
+                    : gqa::gqa_decode_mfma<D, 1, 1, 4, 1, false, KV8, false, true>;
 }
 
 // The decode fused with the append (cache of bf16 or E4M3 elements: plain,
@@ -263,6 +291,9 @@ kernel_fn mfma_kernel_of(const gqa_dims* d, const KernelKind& kind, int waves, i
   const int G = d->num_q_heads / d->num_kv_heads;
   const int hb = (G + 15) / 16;
   const bool d128 = d->head_dim == 128;
+  if (kind.claims)
+    return kind.kv8 ? (d128 ? mfma_claims_kernel<128, true>(tiles) : mfma_claims_kernel<64, true>(tiles))
+                    : (d128 ? mfma_claims_kernel<128>(tiles) : mfma_claims_kernel<64>(tiles));
   if (kind.append && kind.paged && kind.kv8)
     return d128 ? mfma_append_kernel<128, true, true>(hb, tiles) : mfma_append_kernel<64, true, true>(hb, tiles);
   if (kind.append && kind.kv8)
@@ -279,7 +310,11 @@ kernel_fn mfma_kernel_of(const gqa_dims* d, const KernelKind& kind, int waves, i
 }
 
 kernel_fn pick_kernel(const gqa_dims* d, const Plan& plan, const CacheArgs& ca) {
-  if (plan.mfma) return mfma_kernel_of(d, kind_of(ca), plan.waves, plan.tiles);
+  if (plan.mfma) {
+    KernelKind k = kind_of(ca);
+    k.claims = plan.dyn > 0;
+    return mfma_kernel_of(d, k, plan.waves, plan.tiles);
+  }
   if (d->dtype == GQA_DTYPE_F32)
     return d->head_dim == 128 ? gqa::gqa_decode_valu<float, 128> : gqa::gqa_decode_valu<float, 64>;
   return d->head_dim == 128 ? gqa::gqa_decode_valu<uint16_t, 128> : gqa::gqa_decode_valu<uint16_t, 64>;
@@ -359,6 +394,8 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   p.n_chunks = plan.n_chunks;
   p.groups = plan.groups;
   p.span = plan.span;
+  p.dyn_chunks = (int32_t)plan.dyn;
+  p.ws_ticket = plan.dyn > 0 ? p.ws_cnt + kTicketSlot : nullptr;
   p.out_bf16 = d->out_dtype == GQA_DTYPE_BF16;
   // Scores are kept in base 2.  An E4M3 cache folds its key scale into the
   // score factor (one rounding of the exact product) and its value scale
@@ -385,7 +422,7 @@ gqa_status launch(int32_t L, const void* q, const void* k, const void* v, const 
   if (plan.mfma && !plan.fused) {
     const void* mk = d->head_dim == 128 ? reinterpret_cast<const void*>(gqa::gqa_merge_spans<128>)
                                         : reinterpret_cast<const void*>(gqa::gqa_merge_spans<64>);
-    e = hipLaunchKernel(mk, dim3((unsigned)(plan.groups * L)), dim3(256), args, 0, s);   // one per span
+    e = hipLaunchKernel(mk, dim3((unsigned)plan.nspans), dim3(256), args, 0, s);   // one per span
   } else if (plan.n_chunks > 1) {
     const int hpb = 256 / d->head_dim;
     const int64_t mgrid = plan.units * ((p.G + hpb - 1) / hpb);

@@ -215,9 +215,13 @@ __device__ __forceinline__ u32x2 v_operand(const Tile16K8<D>& T, int r) {
 // what the quantising append stores: the key turned in fp32 and divided by
 // k_scale, the value divided by v_scale, each encoded to E4M3 bytes; the
 // tile takes those bytes before it is widened.
-template <int D, int HB, int HG, int NW, int TPW, bool PAGED, bool KV8, bool APPEND = false>
+template <int D, int HB, int HG, int NW, int TPW, bool PAGED, bool KV8, bool APPEND = false, bool CLAIMS = false>
 __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   static_assert(NW % HG == 0, "head groups must divide the wavefronts");
+  // CLAIMS: the instance for layer batches whose last layer is claimed in
+  // chunks (layer batches are neither paged nor fused with the append; two
+  // head blocks would spill with the claim's code)
+  static_assert(!CLAIMS || (!PAGED && !APPEND && HB == 1), "claimed chunks: one head block, plain layout");
   constexpr int NT = NW * 64, TILE = 16, KS = D / 32, VW = D / 16;
   constexpr int NL = NW / HG;             // tile lanes
   constexpr int HP = HB * 16;             // heads per wavefront
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   __shared__ int32_t sm_N[PAGED ? kMaxBatch : 1];
   __shared__ int32_t sm_wave[NW];
   __shared__ int sm_flag;
+  __shared__ int32_t sm_claim;
   __shared__ int32_t sm_M[APPEND ? kMaxBatch : 1];        // APPEND: new token positions
   __shared__ float sm_cs[APPEND ? NW : 1][2][2][D / 2];  // APPEND: each wavefront's cosines and sines, two tables
   // APPEND: each wavefront's turned new key and new value, one row each per
@@ -247,18 +252,60 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   const float sl2 = p.scale_log2;
 
   build_prefix<NT, PAGED, APPEND>(p, sm_P, sm_N, sm_wave, sm_M);
-  const TokenSpace ts = token_space(p, sm_P);
+  const TokenSpaceT<CLAIMS> ts = token_space<CLAIMS>(p, sm_P);
   zero_empty_sequences<D, NT>(p, sm_P, blockIdx.x, gridDim.x);
   if constexpr (APPEND) append_side_outputs<D, NT>(p, sm_P, sm_M, blockIdx.x, gridDim.x);
   // This workgroup streams spans v = blockIdx.x, + groups, + 2 groups, ...
-  // (its span of each layer in turn); [s0, s1) is the current one.
-  const int64_t nspans = (int64_t)p.L * ts.groups;
+  // (its span of each static layer in turn), then chunks of a claimed last
+  // layer until none is left; [s0, s1) is the current span.
+  //
+  // The next chunk of the claimed layer, or -1: thread 0 takes a ticket and
+  // LDS hands it to the workgroup (every wavefront claims at the same point
+  // of the workgroup's span sequence, so the barriers match).  Each
+  // workgroup's last claim is the one that finds the chunks gone, so the
+  // call makes dyn + groups claims; the last of them sets the ticket back to
+  // zero for the next call.  A chunk past the layer's last position gets its
+  // empty merge descriptor here.
+  auto claim = [&]() __attribute__((always_inline)) -> int64_t {
+    if constexpr (!CLAIMS) return -1;
+    for (;;) {
+      if (tid == 0) {
+        const int32_t c = __hip_atomic_fetch_add(p.ws_ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int64_t)c == ts.dyn + ts.groups - 1)
+          __hip_atomic_store(p.ws_ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_claim = c;
+      }
+      __syncthreads();
+      const int64_t c = uniform(sm_claim);
+      __syncthreads();   // sm_claim is rewritten by the next claim
+      if (c >= ts.dyn) return -1;
+      const int64_t vc = ts.sl * ts.groups + c;
+      if (ts.start(vc) < ts.end(vc)) return vc;
+      if (!p.fused) write_merge_desc(p, vc, -1, -1, 0, 0);
+    }
+  };
+  // The span after v in this workgroup's sequence, or -1.
+  auto following_span = [&](int64_t vv) __attribute__((always_inline)) -> int64_t {
+    if (vv + ts.groups < ts.sl * ts.groups) return vv + ts.groups;   // its span of the next static layer
+    return CLAIMS && ts.dyn > 0 ? claim() : -1;
+  };
   int64_t v = blockIdx.x;
+  if constexpr (CLAIMS) {
+    if (v * ts.span >= ts.per_layer) {
+      // this workgroup's static span of every layer is empty (uniform)
+      if (!p.fused)
+        for (int64_t m = v; m < ts.sl * ts.groups; m += ts.groups) write_merge_desc(p, m, -1, -1, 0, 0);
+      v = ts.dyn > 0 ? claim() : -1;
+      if (v < 0) return;
+    }
+  }
   int64_t s0 = ts.start(v), s1 = ts.end(v);
-  if (s0 >= s1) {   // w * span >= per_layer: this workgroup's span of every layer is empty (uniform)
-    if (!p.fused)
-      for (int64_t m = v; m < nspans; m += ts.groups) write_merge_desc(p, m, -1, -1, 0, 0);
-    return;
+  if constexpr (!CLAIMS) {
+    if (s0 >= s1) {   // w * span >= per_layer: this workgroup's span of every layer is empty (uniform)
+      if (!p.fused)
+        for (int64_t m = v; m < (int64_t)p.L * ts.groups; m += ts.groups) write_merge_desc(p, m, -1, -1, 0, 0);
+      return;
+    }
   }
 
   // Per-lane element offsets inside a tile (relative to the tile's first row).
@@ -850,22 +897,27 @@ __global__ __launch_bounds__(NW * 64) void gqa_decode_mfma(Problem p) {
   // One step with `cur` loaded: false if it is the workgroup's last batch
   // (left for the caller), else load the next batch into `nxt` and compute
   // `cur`.
-  auto next_span = [&]() __attribute__((always_inline)) {
-    v += ts.groups;
-    return open_span();
-  };
   auto step = [&](const tile_t (&cur)[TPW], tile_t (&nxt)[TPW]) __attribute__((always_inline)) -> bool {
     const bool piece_done = j + NL * TPW >= pc.ntiles;
     const int64_t xn = PAGED ? pc.next : pc.x + (pc.c1 - pc.c0);
     const bool span_done = xn >= s1;
-    if (piece_done && span_done && v + ts.groups >= nspans) {
-      return false;
+    int64_t vn = v + ts.groups;   // without claims: the workgroup's span of the next layer
+    if constexpr (CLAIMS) {
+      if (piece_done && span_done) {
+        vn = following_span(v);
+        if (vn < 0) return false;
+      }
+    } else {
+      if (piece_done && span_done && vn >= (int64_t)p.L * ts.groups) return false;
     }
     if (piece_done) {
       // the piece ran to its unit's end (the next one starts the next unit)
-      // or to its span's (the next one starts this workgroup's span of the
-      // next layer)
-      const Ctx pn = span_done ? next_span() : open_at(next_unit<PAGED>(p, sm_P, sm_N, pc.at), xn);
+      // or to its span's (the next one starts the workgroup's next span)
+      auto to_span = [&]() __attribute__((always_inline)) {
+        v = vn;
+        return open_span();
+      };
+      const Ctx pn = span_done ? to_span() : open_at(next_unit<PAGED>(p, sm_P, sm_N, pc.at), xn);
       fetch_pages(pid, pn, tl);
       load_batch(nxt, pn, tl, pid);
       fetch_pages(pid, pn, tl + NL * TPW);

@@ -199,12 +199,16 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
  *                padding to T_max).  The dense layout is kv_offsets[b] = b*T_max.
  * The result equals num_layers separate gqa_decode calls: each layer is
  * split among the workgroups as a one-layer call with these dims splits it,
- * and every workgroup takes its share of each layer in turn, so with the
- * same merge (dims->merge FUSED or KERNEL; AUTO picks KERNEL for a batch
- * whose num_layers x workgroups exceed the fused merge's counters) the
- * results are bitwise those of the one-layer calls.
- * The workspace grows with num_layers (two partial-state slots per
- * workgroup and layer).
+ * and every workgroup takes its share of each layer in turn.  Under the
+ * balanced split (chunk_tokens 0) with G <= 16, the last layer is instead
+ * cut into eight chunks per workgroup that the workgroups claim at run time
+ * once their shares of the other layers are done, so that the workgroups
+ * that streamed faster take more of it.  Results are deterministic (a
+ * chunk's result does not depend on which workgroup computes it, and
+ * partial results are merged in a fixed order); with the same merge
+ * (dims->merge FUSED or KERNEL) every layer but such a claimed last one is
+ * bitwise the one-layer call's.  The workspace grows with num_layers (two
+ * partial-state slots per workgroup and layer, and per claimed chunk).
  */
 gqa_status gqa_decode_layers(int32_t num_layers, const void* q, const void* k_cache, const void* v_cache,
                              const int64_t* kv_offsets, const int32_t* seq_lens, float scale, void* out,
