@@ -9,9 +9,10 @@ batch of synthetic inputs that are already resident in HBM.  The default
 workload is the 32-layer stack (B 64, H_q 32, H_kv 8, d 128, lengths
 U[4096, 32768] shared by the layers, about 160 GB of packed bf16 cache): the
 largest configuration, one launch of gqa_decode_layers per step.  Steps
-rotate over enough independent input batches (``--replicas``) that the
-working set exceeds the 256 MB last-level (Infinity) cache, so every step
-streams its K/V from HBM.  ``--paged PAGE`` lays each batch's cache out in
+rotate over enough independent input batches (``--replicas``) that one
+round of the rotation reads at least 2 GiB of K/V, far beyond the 256 MB
+last-level (Infinity) cache, so every step streams its K/V from HBM (with
+one batch reused every step, a 1.1 GB step ran 0.7 % faster).  ``--paged PAGE`` lays each batch's cache out in
 pages of PAGE tokens (shuffled in a pool, read through a block table) and
 times gqa_decode_paged instead.  ``--kv fp8`` stores each batch's cache as
 one-byte E4M3 codes with one scale per array and times gqa_decode_fp8 (the
@@ -429,7 +430,10 @@ def main():
         2 if w.dtype == torch.bfloat16 else 4)
     if fp8:
         resident //= 2
-    reps = args.replicas or max(1, min(16, -(-(2 << 30) // resident)))
+    # rotate over enough batches that one round reads at least 2 GiB of K/V
+    # (counted as read: the valid tokens' bytes, not the allocation)
+    step_bytes = kv_bytes // 2 if fp8 else kv_bytes
+    reps = args.replicas or max(1, min(16, -(-(2 << 30) // max(step_bytes, 1))))
     free, _ = torch.cuda.mem_get_info(dev)
     reps = max(1, min(reps, int((free * 0.85) // max(resident, 1))))
     print("[bench] workload %s, %d input batch(es) of %.3f GB resident" % (w.name, reps, resident / 1e9),
