@@ -312,11 +312,18 @@ def test_graph_replays_match_eager(merge):
     and synchronisations between the replays."""
     shapes = [(3, 32, 8, 128, 4000, 1), (2, 32, 1, 128, 600, 100)]
     xs = [to_dev(small(*sh[:5], seed=seed_of(sh, 41), lo=sh[5])) for sh in shapes]
+    # and a layer batch under the planner's split, whose last layer is
+    # claimed in chunks: its arrival ticket must be back at zero for the
+    # next call in the graph and for every replay
+    wl = workloads.Workload("graph-layers", 4, 32, 8, 128, 1, 1500, torch.bfloat16, 44, layers=3, packed=True)
+    xl = to_dev(workloads.generate(wl, "cpu"))
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
         ls = [gqa.prepare(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], merge=merge, stream=s.cuda_stream,
                           chunk_tokens=256) for x in xs]
+        ls.append(gqa.prepare(xl["q"], xl["k"], xl["v"], xl["seq_lens"], xl["scale"], kv_offsets=xl["kv_offsets"],
+                              max_seq_len=1500, num_kv_heads=8, merge=merge, stream=s.cuda_stream))
         eager = [l().clone() for l in ls]
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
