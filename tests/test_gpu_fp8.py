@@ -261,18 +261,19 @@ def test_full_llama3_8b_layer_paged_fp8():
 
 # ------------------------------------------------------------ layer batches --
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("H_kv", [8, 1])
+@pytest.mark.parametrize("H_kv,d", [(8, 128), (1, 128), (8, 64)])
 @pytest.mark.parametrize("span,merge", [(0, "auto"), (192, "fused"), (192, "kernel")])
-def test_layers_fp8(packed, H_kv, span, merge):
+def test_layers_fp8(packed, H_kv, d, span, merge):
     """gqa_decode_layers_fp8: four layers of E4M3 caches (one scale pair for
-    all of them), dense and packed, G = 4 and G = 32, the planner's split
-    and forced spans with both merges; each layer against the oracle on the
-    same bytes."""
-    w = workloads.Workload("layers-fp8", 3, 32, H_kv, 128, 100, 900, torch.bfloat16, 61 + H_kv, layers=4,
+    all of them), dense and packed, G = 4 and G = 32, d = 128 and 64, the
+    planner's split (its last layer claimed in chunks at G = 4) and forced
+    spans with both merges; each layer against the oracle on the same
+    bytes."""
+    w = workloads.Workload("layers-fp8", 3, 32, H_kv, d, 100, 900, torch.bfloat16, 61 + H_kv + d, layers=4,
                            packed=packed)
     x8 = workloads.to_e4m3(workloads.generate(w, "cpu", poison_padding=True))
     xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x8.items()}
-    note("layers fp8", packed, H_kv, span, merge)
+    note("layers fp8", packed, H_kv, d, span, merge)
     kw = dict(kv_offsets=xd["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if packed else {}
     run = lambda dt: gqa.decode_layers_fp8(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x8["scale"], x8["k_scale"],
                                            x8["v_scale"], out_dtype=dt, chunk_tokens=span, merge=merge, **kw)

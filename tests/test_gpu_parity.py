@@ -418,6 +418,7 @@ LAYER_SPLIT_CASES = [
     ((32, 8, 128), [3, 0, 5], 4, True),           # 64 positions per layer: most workgroups hold no span
     ((64, 8, 128), [17, 250], 2, True),           # G = 8, the whole layer inside few spans
     ((8, 2, 64), [0, 0, 0], 3, False),            # no tokens in any layer
+    ((16, 4, 64), [5, 700, 0, 129, 2048], 3, True),   # d = 64, G = 4
 ]
 
 
