@@ -101,3 +101,70 @@ def test_random_config(i):
     for b, n in enumerate(c["lens"]):
         if n == 0:
             assert not o[b].any(), "empty sequence %d not zero" % b
+
+
+N_LAYER_CASES = 32
+
+
+def draw_layers(i):
+    r = random.Random(5000 + i)
+    H_kv = r.choice([1, 2, 4, 8])
+    G = r.choice([g for g in (1, 2, 4, 4, 8, 16, 24, 32, 48) if g * H_kv <= 128])
+    T = r.randint(1, 900)
+    B = r.randint(1, 8)
+    cache = r.choice(["bf16", "bf16", "fp8"])
+    lens = [r.choice([0, r.randint(0, T), T]) for _ in range(B)]
+    packed = r.random() < 0.5
+    if packed and not any(lens):
+        lens[-1] = T   # a packed cache of no rows has no storage (a null pointer, which the call rejects)
+    return dict(i=i, B=B, H_q=G * H_kv, H_kv=H_kv, d=r.choice([64, 128]), T=T, L=r.randint(2, 6),
+                lens=lens, cache=cache, packed=packed,
+                chunk=r.choice([0, 0, 0, 64, 256]), merge=r.choice(["auto", "fused", "kernel"]),
+                tiles=r.choice([0, 1, 2, 4]) if cache == "fp8" else r.choice([0, 1, 2]),
+                per_cu=r.choice([0, 0, 1, 2]), out=r.choice([torch.float32, torch.bfloat16]))
+
+
+@pytest.mark.parametrize("i", range(N_LAYER_CASES))
+def test_random_layer_batch(i):
+    """Seeded random layer batches (2 to 6 layers, dense or packed, bf16 or
+    E4M3 caches, ragged lengths with zeros, the planner's split with its
+    claimed last layer or forced spans, either merge, tiles and workgroups
+    per CU): every output of every layer against the oracle, at the bars of
+    the one-layer cases above."""
+    c = draw_layers(i)
+    note = {k: v for k, v in c.items() if k != "lens"}
+    print("[gpu-case] random layers", note, "lens", c["lens"], flush=True)
+    sl = torch.tensor(c["lens"], dtype=torch.int32)
+    w = workloads.Workload("rand-layers", c["B"], c["H_q"], c["H_kv"], c["d"], 1, c["T"], torch.bfloat16,
+                           9000 + i, layers=c["L"], packed=c["packed"])
+    x = workloads.generate(w, "cpu", poison_padding=True, seq_lens=sl)
+    if c["cache"] == "fp8":
+        x = workloads.to_e4m3(x)
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    kw = dict(out_dtype=c["out"], chunk_tokens=c["chunk"], merge=c["merge"], tiles=c["tiles"], per_cu=c["per_cu"])
+    if c["packed"]:
+        kw.update(kv_offsets=xd["kv_offsets"], max_seq_len=c["T"], num_kv_heads=c["H_kv"])
+    if c["cache"] == "fp8":
+        out = gqa.decode_layers_fp8(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], x["k_scale"],
+                                    x["v_scale"], **kw)
+    else:
+        out = gqa.decode_layers(xd["q"], xd["k"], xd["v"], xd["seq_lens"], x["scale"], **kw)
+    torch.cuda.synchronize()
+    o = out.double().cpu().numpy()
+    assert np.isfinite(o).all(), "non-finite output"
+    orc = oracle.default()
+    offs = x["kv_offsets"].numpy() if c["packed"] else None
+    for l in range(c["L"]):
+        xl = workloads.layer_view(x, l)
+        if c["cache"] == "fp8":
+            ref = orc.decode_fp8(xl["q"], xl["k"], xl["v"], x["seq_lens"], x["scale"], x["k_scale"], x["v_scale"],
+                                 kv_offsets=offs, num_kv_heads=c["H_kv"])
+        else:
+            ref = orc.decode(xl["q"], xl["k"], xl["v"], x["seq_lens"], x["scale"], kv_offsets=offs,
+                             num_kv_heads=c["H_kv"])
+        bar = 2e-3 + (2.0 ** -8 * (np.abs(ref) + 2e-3) if c["out"] == torch.bfloat16 else 0.0)
+        e = np.abs(o[l] - ref)
+        assert (e <= bar).all(), "layer %d: max err %.3e" % (l, float(e.max()))
+        for b, n in enumerate(c["lens"]):
+            if n == 0:
+                assert not o[l, b].any(), "layer %d: empty sequence %d not zero" % (l, b)
