@@ -439,6 +439,7 @@ def main():
     print("[bench] workload %s, %d input batch(es) of %.3f GB resident" % (w.name, reps, resident / 1e9),
           file=sys.stderr, flush=True)
     batches = [workloads.generate(w, dev, replica=r) for r in range(reps)]
+    print("[bench] inputs generated", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
     kw = dict(out_dtype=out_dtype, chunk_tokens=args.chunk_tokens, path=args.path)
     launchers = []
@@ -473,12 +474,15 @@ def main():
         extra = dict(kv_offsets=x["kv_offsets"], max_seq_len=w.T_max, num_kv_heads=w.H_kv) if w.packed else {}
         launchers.append(gqa.prepare(x["q"], x["k"], x["v"], x["seq_lens"], x["scale"], **extra, **kw))
 
+    print("[bench] calls prepared%s" % (" (E4M3 caches)" if fp8 else ""), file=sys.stderr, flush=True)
+
     def step(i):
         return launchers[i % reps]()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    print("[bench] warm-up done", file=sys.stderr, flush=True)
     nbytes = algorithmic_bytes(w, seq_lens, 2 if out_dtype == torch.bfloat16 else 4, args.paged, 1 if fp8 else 0)
     # Long steps carry an event of their own at every step boundary inside the
     # timed region (a marker between launches that are milliseconds long);
