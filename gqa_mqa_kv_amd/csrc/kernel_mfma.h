@@ -3,10 +3,13 @@
 // one-byte E4M3 elements (dense or paged), which are widened to bf16 exactly
 // before the products.
 //
-// Work split ("token split", see common.h): the valid tokens of all units
-// form one stream cut into equal spans, one per workgroup (one per CU),
+// Work split ("token split", see common.h): the valid tokens of each layer's
+// units form one stream cut into equal spans, one per workgroup (one per CU),
 // so every workgroup streams the same number of bytes whatever the sequence
-// lengths.  A workgroup walks its span unit piece by unit piece.  Its
+// lengths; in a layer batch a workgroup takes its span of each layer in turn
+// (and, when the batch's last layer is claimed, chunks of that layer from a
+// ticket once its spans are done).  A workgroup walks a span unit piece by
+// unit piece.  Its
 // wavefronts each serve HB blocks of 16 heads (one block for up to 16 heads,
 // two beyond) and are laid out as (head group, tile lane): up to 32 heads all
 // four wavefronts are tile lanes of one group, 33..64 heads use two groups
