@@ -515,3 +515,17 @@ def test_decode_append_rope_fp8_validation():
     d32 = dims(H_q=32, H_kv=1, T_max=4096)
     assert lib.gqa_decode_append_rope_fp8(Q, KN, VN, KC, VC, None, SL, NL, 10000.0, 0.125, 0.5, 0.25, QO, OUT,
                                           ctypes.byref(d32), None, 0, None) == WORKSPACE
+
+
+def test_c_boundary_check_compiles_against_the_header(tmp_path):
+    """The header is valid C (gcc -std=c11 -Wall -Wextra -Werror) and the C
+    check program links against the library, the HIP runtime and the oracle
+    (it runs on a GPU, in tests/test_gpu_c_abi.py)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "c_abi_build", os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    out = str(tmp_path / "c_abi_check")
+    mod.build(out)
+    assert os.path.getsize(out) > 0
