@@ -21,10 +21,10 @@ def command(out: str = OUT) -> list:
     rpath = ":".join(["$ORIGIN/" + rel(lib_dir), "$ORIGIN/" + rel(oracle_dir), os.path.join(ROCM, "lib")])
     # __HIP_PLATFORM_AMD__ selects the AMD runtime API in the HIP headers
     # when they are read by a compiler other than hipcc
-    return ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+    return ["gcc", "-std=c11", "-pthread", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"), SOURCE, "-o", out,
             "-L", lib_dir, "-lgqa_decode", "-L", oracle_dir, "-loracle", "-L", os.path.join(ROCM, "lib"),
-            "-lamdhip64", "-lm", "-Wl,-rpath," + rpath]
+            "-lamdhip64", "-lm", "-pthread", "-Wl,-rpath," + rpath]
 
 
 def build(out: str = OUT) -> str:

@@ -6,8 +6,12 @@
  * test only).  Bar: max |gpu - oracle| <= 2e-3 for bf16 inputs with fp32
  * accumulation and fp32 output.
  *
- * Calls: gqa_decode_workspace_bytes, gqa_decode_plan, gqa_decode (a ragged
- * batch whose units split over several workgroups), gqa_decode_layers (the
+ * Calls: first, four host threads at once, each with a stream, a workspace
+ * and a shape of its own, make the process's first calls of the library
+ * (gqa_decode_workspace_bytes and gqa_decode, three times each: the library
+ * promises calls from any thread); then gqa_decode_workspace_bytes,
+ * gqa_decode_plan, gqa_decode (a ragged batch whose units split over
+ * several workgroups), gqa_decode_layers (the
  * packed layout, three layers in one launch), gqa_decode_noalloc (twice, the
  * second call smaller), and argument errors reported before anything is
  * enqueued (a short workspace, a null pointer, an unsupported head size).
@@ -19,6 +23,7 @@
  * (query head i reads KV head i / G, G = H_q / H_kv).
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -254,6 +259,91 @@ static void error_cases(hipStream_t s) {
   free(out);
 }
 
+/* One host thread's calls: its own inputs, stream and workspace. */
+typedef struct {
+  int B, H_q, H_kv, d, T_max;
+  int32_t lens[4];
+  uint64_t seed;
+  uint16_t *q, *k, *v;
+  float* out;
+  gqa_status st[3];
+} thread_case;
+
+static void* thread_calls(void* arg) {
+  thread_case* c = (thread_case*)arg;
+  const size_t nq = (size_t)c->B * c->H_q * c->d, nkv = (size_t)c->B * c->H_kv * c->T_max * c->d;
+  gqa_dims dm = make_dims(c->B, c->H_q, c->H_kv, c->d, c->T_max);
+  hipStream_t s;
+  HIP_OK(hipStreamCreate(&s));
+  const size_t ws_bytes = gqa_decode_workspace_bytes(&dm, 1);
+  void *dq = to_device(c->q, nq * 2), *dk = to_device(c->k, nkv * 2), *dv = to_device(c->v, nkv * 2);
+  void *dl = to_device(c->lens, (size_t)c->B * 4), *dout = to_device(NULL, nq * 4), *ws = to_device(NULL, ws_bytes);
+  for (int r = 0; r < 3; ++r)
+    c->st[r] = gqa_decode(dq, dk, dv, (const int32_t*)dl, 1.0f / sqrtf((float)c->d), dout, &dm, ws, ws_bytes, s);
+  HIP_OK(hipStreamSynchronize(s));
+  HIP_OK(hipMemcpy(c->out, dout, nq * 4, hipMemcpyDeviceToHost));
+  HIP_OK(hipFree(dq));
+  HIP_OK(hipFree(dk));
+  HIP_OK(hipFree(dv));
+  HIP_OK(hipFree(dl));
+  HIP_OK(hipFree(dout));
+  HIP_OK(hipFree(ws));
+  HIP_OK(hipStreamDestroy(s));
+  return NULL;
+}
+
+static void threads_case(void) {
+  thread_case cs[4] = {
+      {2, 32, 8, 128, 3000, {3000, 2500, 0, 0}, 41, NULL, NULL, NULL, NULL, {0}},
+      {3, 32, 1, 128, 1500, {1500, 700, 1, 0}, 42, NULL, NULL, NULL, NULL, {0}},
+      {4, 16, 2, 64, 900, {900, 1, 450, 899}, 43, NULL, NULL, NULL, NULL, {0}},
+      {1, 64, 8, 128, 5000, {4999, 0, 0, 0}, 44, NULL, NULL, NULL, NULL, {0}},
+  };
+  pthread_t th[4];
+  for (int i = 0; i < 4; ++i) {
+    thread_case* c = &cs[i];
+    const size_t nq = (size_t)c->B * c->H_q * c->d, nkv = (size_t)c->B * c->H_kv * c->T_max * c->d;
+    c->q = (uint16_t*)malloc(nq * 2);
+    c->k = (uint16_t*)malloc(nkv * 2);
+    c->v = (uint16_t*)malloc(nkv * 2);
+    c->out = (float*)malloc(nq * 4);
+    fill(c->q, nq, c->seed);
+    fill(c->k, nkv, c->seed + 1);
+    fill(c->v, nkv, c->seed + 2);
+  }
+  for (int i = 0; i < 4; ++i)
+    if (pthread_create(&th[i], NULL, thread_calls, &cs[i]) != 0) {
+      fprintf(stderr, "pthread_create failed\n");
+      exit(2);
+    }
+  for (int i = 0; i < 4; ++i) pthread_join(th[i], NULL);
+  double e = 0.0;
+  int ok = 1;
+  for (int i = 0; i < 4; ++i) {
+    thread_case* c = &cs[i];
+    const size_t nq = (size_t)c->B * c->H_q * c->d;
+    int64_t offs[5];
+    for (int b = 0; b <= c->B; ++b) offs[b] = (int64_t)b * c->T_max;
+    double* ref = (double*)malloc(nq * sizeof(double));
+    const float scale = 1.0f / sqrtf((float)c->d);
+    const int rc = oracle_gqa_decode(c->B, c->H_q, c->H_kv, c->d, 1, c->q, c->k, c->v, offs, c->lens, (double)scale,
+                                     0, NULL, ref);
+    const double ei = rc == 0 ? max_err(c->out, ref, nq) : INFINITY;
+    if (ei > e) e = ei;
+    for (int r = 0; r < 3; ++r) ok &= c->st[r] == GQA_OK;
+    ok &= rc == 0;
+    free(ref);
+    free(c->q);
+    free(c->k);
+    free(c->v);
+    free(c->out);
+  }
+  char msg[256];
+  snprintf(msg, sizeof msg, "four host threads, first calls of the process at once (own streams and workspaces): "
+           "statuses %s, max |gpu - oracle| = %.3e (bar 2e-3)", ok ? "GQA_OK" : "not all GQA_OK", e);
+  check(ok && e <= 2e-3, msg);
+}
+
 int main(void) {
   int n = 0;
   HIP_OK(hipGetDeviceCount(&n));
@@ -262,6 +352,7 @@ int main(void) {
     return 2;
   }
   HIP_OK(hipSetDevice(0));
+  threads_case();
   hipStream_t s;
   HIP_OK(hipStreamCreate(&s));
   {
