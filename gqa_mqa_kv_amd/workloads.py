@@ -19,7 +19,14 @@ grouping-sweep-mha          8   32   32    128  32768                   1      b
 grouping-sweep-gqa          8   32   8     128  32768                   1      bf16
 grouping-sweep-mqa          8   32   1     128  32768                   1      bf16
 llama3-8b-32-layer-stack    64  32   8     128  U[4096, 32768]          32     bf16
+llama-70b-tp8-shard         32  8    1     128  U[1024, 16384]          1      bf16
 ==========================  ==  ===  ====  ===  ======================  =====  ======
+
+llama-70b-tp8-shard is one GPU's share of llama-70b-ragged-layer under
+tensor parallelism over 8 GPUs by heads (section 4 of the first page,
+"Tensor Parallelism (TP) Head Partitioning"): one KV head and its 8 query
+heads, with the same sequence lengths (same seed for the lengths; its own
+values).  tp_shard cuts such a share out of a whole layer's inputs.
 
 Values are N(0, 1) drawn in float32 and rounded to nearest-even into the
 storage dtype.  Draw order: sequence lengths, then q, then K, then V.  Ragged
@@ -80,8 +87,27 @@ WORKLOADS = {
         Workload("grouping-sweep-mqa", 8, 32, 1, 128, 32768, 32768, torch.bfloat16, 1004 + 1, q_seed=1004),
         Workload("llama3-8b-32-layer-stack", 64, 32, 8, 128, 4096, 32768, torch.bfloat16, 1005, layers=32,
                  packed=True),
+        Workload("llama-70b-tp8-shard", 32, 8, 1, 128, 1024, 16384, torch.bfloat16, 1003),
     ]
 }
+
+
+def tp_shard(inputs: dict, tp: int, rank: int) -> dict:
+    """GPU ``rank``'s share of a one-layer dense input under tensor
+    parallelism over ``tp`` GPUs by heads: KV heads [rank*H_kv/tp,
+    (rank+1)*H_kv/tp) and the query heads [rank*H_q/tp, (rank+1)*H_q/tp)
+    that read them under the contiguous grouping (contiguous copies; the
+    lengths and scale are shared).  H_kv must be a multiple of tp."""
+    B, H_q, d = inputs["q"].shape
+    H_kv = inputs["k"].shape[1]
+    if inputs["k"].dim() != 4 or H_kv % tp or H_q % tp or not 0 <= rank < tp:
+        raise ValueError("tp_shard takes a dense one-layer input with H_kv divisible by tp")
+    qs, ks = H_q // tp, H_kv // tp
+    out = dict(inputs)
+    out["q"] = inputs["q"][:, rank * qs:(rank + 1) * qs].contiguous()
+    out["k"] = inputs["k"][:, rank * ks:(rank + 1) * ks].contiguous()
+    out["v"] = inputs["v"][:, rank * ks:(rank + 1) * ks].contiguous()
+    return out
 
 
 def _gen(seed: int, device) -> torch.Generator:

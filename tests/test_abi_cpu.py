@@ -529,3 +529,22 @@ def test_c_boundary_check_compiles_against_the_header(tmp_path):
     out = str(tmp_path / "c_abi_check")
     mod.build(out)
     assert os.path.getsize(out) > 0
+
+
+def test_tp_shard_follows_the_partition_figure():
+    """workloads.tp_shard cuts GPU r's share as the page's figure "TENSOR
+    PARALLEL PARTITIONING (Llama 3 70B on TP=8)" lists it (tests/golden):
+    query heads first..last and the one KV head they read."""
+    import oracle_pins
+    w = workloads.Workload("tp", 2, 64, 8, 16, 5, 9, torch.bfloat16, 7)
+    x = workloads.generate(w, "cpu")
+    rows = oracle_pins.golden_rows("tp8_head_partition_llama3_70b.txt")
+    assert len(rows) == 8
+    for gpu, lo, hi, kv in rows:
+        s = workloads.tp_shard(x, 8, int(gpu))
+        assert torch.equal(s["q"], x["q"][:, int(lo):int(hi) + 1])
+        assert torch.equal(s["k"], x["k"][:, int(kv):int(kv) + 1])
+        assert torch.equal(s["v"], x["v"][:, int(kv):int(kv) + 1])
+        assert s["seq_lens"] is x["seq_lens"]
+    with pytest.raises(ValueError):
+        workloads.tp_shard(x, 3, 0)

@@ -627,6 +627,36 @@ def test_full_size_fp32_inputs(name):
     full_check(name, dtype=torch.float32, path="valu")
 
 
+@pytest.mark.timeout(600)
+def test_tp8_shards_of_the_70b_layer():
+    """The ragged 70B layer split over eight GPUs by heads ([GQA-math]
+    section 4, "Tensor Parallelism (TP) Head Partitioning"): GPU r holds KV
+    head r and query heads 8r .. 8r+7, and runs this library's call on that
+    share alone (one KV head, the per-GPU shape).  Every output of every
+    share against the oracle of the whole layer's heads 8r .. 8r+7, and the
+    bf16 output the rounding of the fp32 one."""
+    w = workloads.WORKLOADS["llama-70b-ragged-layer"]
+    note("tp8", "generate")
+    x = workloads.generate(w, DEV, poison_padding=True)
+    xc = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    note("tp8", "oracle on the whole layer")
+    ref = oracle.decode(xc["q"], xc["k"], xc["v"], xc["seq_lens"], w.scale)
+    e = 0.0
+    for r in range(8):
+        s = workloads.tp_shard(x, 8, r)
+        note("tp8", "rank %d" % r)
+        out32 = gqa.decode(s["q"], s["k"], s["v"], s["seq_lens"], s["scale"], out_dtype=torch.float32)
+        out16 = gqa.decode(s["q"], s["k"], s["v"], s["seq_lens"], s["scale"], out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(out16, out32.to(torch.bfloat16))
+        e = max(e, err(out32, ref[:, 8 * r:8 * r + 8]))
+        del s
+    note("tp8", "max err %.3e" % e)
+    assert e <= 2e-3
+    del x
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.timeout(900)
 def test_full_32_layer_stack():
     """The 32-layer packed stack at full size (about 160 GB of cache), one
