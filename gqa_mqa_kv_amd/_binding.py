@@ -159,7 +159,10 @@ def default_workspace(nbytes: int, device: torch.device, stream=None) -> Optiona
     buffer replaced by a larger one is never freed: a kernel still running on
     that stream, or a captured graph, may hold its address.  Sizes are
     rounded up to a power of two, so a stream replaces its buffer a few
-    times at most."""
+    times at most.  Every stream used keeps its buffer for the life of the
+    process (the handle says nothing of when the stream is destroyed): a
+    caller that creates streams per call should pass ``workspace=`` (a
+    zero-filled buffer of ``workspace_bytes(dims)`` bytes it owns) instead."""
     if nbytes == 0:
         return None
     s = _stream_handle(device, stream)
